@@ -1,0 +1,193 @@
+"""fp64 CPU oracle for unified paged attention.
+
+TEST INFRASTRUCTURE ONLY.  The only code allowed to import, call or run this
+module is ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg
+of ``bench.py``.  The GPU library never links or calls it, and it shares no
+code with the GPU library.
+
+What it computes is the plain definition of the operation:
+
+* A varlen batch, as in the ``flash_attn_varlen_func`` statement of the problem
+  (page "[Kernel] Unified Triton kernel that doesn't distinguish between
+  prefill + decode", PR description): the queries of all sequences are
+  concatenated and ``cu_seqlens_q`` holds the offsets; each sequence may be a
+  decode step (one query), a chunk of a chunked prefill or a whole prefill, all
+  in one call (page "[Kernel] [V1] Improved performance for V1 Triton (ROCm)
+  backend", section "How is this performance improvement achieved?").
+* GQA: q-head ``h`` reads kv-head ``h // G`` with ``G = Hq // Hkv`` (the
+  flash-attn convention that the unified kernel mimics, same PR description).
+* The KV cache is ``[num_blocks, block_size, num_kv_heads, head_dim]`` (the
+  FlashAttention key-cache layout, same PR description; the value cache is taken
+  to have the same layout) and is reached through a per-sequence block table:
+  context token ``j`` of sequence ``s`` is slot ``j % block_size`` of physical
+  block ``block_table[s, j // block_size]``.
+* Masking is causal or off (the non-causal mode is the one requested in the
+  review of the unified-kernel page for cascade attention and MLA).  The causal
+  mask is aligned to the end of each sequence's context: query ``i`` of a
+  sequence with ``q_s`` queries and ``L_s`` context tokens sits at position
+  ``L_s - q_s + i`` and sees keys ``0 .. L_s - q_s + i``.  This is the only
+  reading under which a decode token sees its whole context and a prefill chunk
+  sees its cached prefix, which is what serving chunked prefill and decode in
+  one causal kernel requires.
+* Per row: ``softmax(scale * q . k_j)`` over the admissible keys, then the
+  weighted sum of the ``v_j``.  A row with no admissible key returns 0 and
+  ``lse = -inf`` (the pages are silent; this is the defined reading).
+
+All arithmetic is float64.  ``softmax_scale`` is first rounded to float32 so
+the oracle uses exactly the value a float32 kernel argument carries.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+__all__ = ["paged_attention", "paged_attention_rows", "gather_context",
+           "attend_rows", "merge_lse"]
+
+
+def gather_context(cache, block_table_row, context_len):
+    """Logical ``[L, Hkv, d]`` float64 view of one sequence's cache contents.
+
+    Only the first ``ceil(L / block_size)`` entries of the block-table row and
+    only slots below ``L`` are touched.
+    """
+    L = int(context_len)
+    B = cache.shape[1]
+    j = np.arange(L)
+    phys = np.asarray(block_table_row)[j // B]
+    return np.asarray(cache[phys, j % B], dtype=np.float64)
+
+
+def attend_rows(Qrows, positions, K, V, q_len, context_len, scale, causal,
+                key_window=None):
+    """Attention of query rows of one (sequence, kv-head) against its context.
+
+    Qrows: ``[n, d]`` queries.  positions: ``[n]`` index ``i`` of each row's
+    token within its sequence (``0 <= i < q_len``).  K, V: ``[L, d]``.
+    key_window: optional ``(lo, hi)``; keys outside it are not admissible (used
+    to form the partial results that the log-sum-exp merge combines).
+    Returns ``(out [n, d], lse [n])`` in float64; lse in natural-log units of
+    the scaled scores.
+    """
+    Qrows = np.asarray(Qrows, dtype=np.float64)
+    n, d = Qrows.shape
+    L = int(context_len)
+    out = np.zeros((n, d), dtype=np.float64)
+    lse = np.full(n, -np.inf, dtype=np.float64)
+    if n == 0 or L == 0:
+        return out, lse
+    i = np.asarray(positions, dtype=np.int64)[:, None]
+    j = np.arange(L, dtype=np.int64)[None, :]
+    admissible = np.ones((n, L), dtype=bool)
+    if causal:
+        admissible &= j <= (L - int(q_len) + i)
+    if key_window is not None:
+        lo, hi = key_window
+        admissible &= (j >= lo) & (j < hi)
+    scores = scale * (Qrows @ np.asarray(K, dtype=np.float64).T)   # [n, L]
+    scores = np.where(admissible, scores, -np.inf)
+    has_key = admissible.any(axis=1)
+    m = np.where(has_key, scores.max(axis=1, initial=-np.inf), 0.0)
+    p = np.where(admissible, np.exp(scores - m[:, None]), 0.0)
+    denom = p.sum(axis=1)
+    safe = np.where(has_key, denom, 1.0)
+    out = (p @ np.asarray(V, dtype=np.float64)) / safe[:, None]
+    out[~has_key] = 0.0
+    lse = np.where(has_key, m + np.log(safe), -np.inf)
+    return out, lse
+
+
+def _checked_meta(q, k_cache, cu_seqlens_q, seqused_k, block_table):
+    T, Hq, d = q.shape
+    NB, B, Hkv, dk = k_cache.shape
+    if dk != d:
+        raise ValueError("head_dim of q and cache differ")
+    if Hq % Hkv:
+        raise ValueError("num_q_heads must be a multiple of num_kv_heads")
+    cu = np.asarray(cu_seqlens_q, dtype=np.int64)
+    L = np.asarray(seqused_k, dtype=np.int64)
+    table = np.asarray(block_table, dtype=np.int64)
+    S = L.shape[0]
+    if cu.shape[0] != S + 1 or cu[0] != 0 or cu[-1] != T or np.any(np.diff(cu) < 0):
+        raise ValueError("cu_seqlens_q must be non-decreasing prefix sums from 0 to total_q")
+    for s in range(S):
+        need = -(-int(L[s]) // B)
+        if need > table.shape[1]:
+            raise ValueError(f"sequence {s}: block table too short for its context")
+        if need and (table[s, :need].min() < 0 or table[s, :need].max() >= NB):
+            raise ValueError(f"sequence {s}: block id out of range")
+    return T, Hq, d, Hkv, Hq // Hkv, cu, L, table
+
+
+def paged_attention(q, k_cache, v_cache, cu_seqlens_q, seqused_k, block_table,
+                    softmax_scale, causal, key_window=None):
+    """Whole-batch oracle.  Returns ``(out [T, Hq, d], lse [T, Hq])`` float64."""
+    T, Hq, d, Hkv, G, cu, L, table = _checked_meta(q, k_cache, cu_seqlens_q,
+                                                   seqused_k, block_table)
+    scale = float(np.float32(softmax_scale))
+    out = np.zeros((T, Hq, d), dtype=np.float64)
+    lse = np.full((T, Hq), -np.inf, dtype=np.float64)
+    for s in range(L.shape[0]):
+        t0, t1 = int(cu[s]), int(cu[s + 1])
+        q_len = t1 - t0
+        if q_len == 0:
+            continue
+        K = gather_context(k_cache, table[s], L[s])
+        V = gather_context(v_cache, table[s], L[s])
+        positions = np.repeat(np.arange(q_len), G)          # row = (token, head in group)
+        for g in range(Hkv):
+            heads = slice(g * G, (g + 1) * G)
+            Qrows = np.asarray(q[t0:t1, heads, :], dtype=np.float64).reshape(q_len * G, d)
+            o, l = attend_rows(Qrows, positions, K[:, g, :], V[:, g, :], q_len, L[s],
+                               scale, causal, key_window)
+            out[t0:t1, heads, :] = o.reshape(q_len, G, d)
+            lse[t0:t1, heads] = l.reshape(q_len, G)
+    return out, lse
+
+
+def paged_attention_rows(q, k_cache, v_cache, cu_seqlens_q, seqused_k, block_table,
+                         softmax_scale, causal, tokens, heads):
+    """Oracle for selected (token, q-head) rows only; returns ``(out [n, d], lse [n])``."""
+    T, Hq, d, Hkv, G, cu, L, table = _checked_meta(q, k_cache, cu_seqlens_q,
+                                                   seqused_k, block_table)
+    scale = float(np.float32(softmax_scale))
+    tokens = np.asarray(tokens, dtype=np.int64)
+    heads = np.asarray(heads, dtype=np.int64)
+    seq_of = np.searchsorted(cu, tokens, side="right") - 1
+    out = np.zeros((tokens.shape[0], d), dtype=np.float64)
+    lse = np.full(tokens.shape[0], -np.inf, dtype=np.float64)
+    for s in np.unique(seq_of):
+        K = gather_context(k_cache, table[s], L[s])
+        V = gather_context(v_cache, table[s], L[s])
+        q_len = int(cu[s + 1] - cu[s])
+        for g in np.unique(heads[seq_of == s] // G):
+            sel = np.nonzero((seq_of == s) & (heads // G == g))[0]
+            Qrows = np.asarray(q[tokens[sel], heads[sel], :], dtype=np.float64)
+            o, l = attend_rows(Qrows, tokens[sel] - cu[s], K[:, g, :], V[:, g, :], q_len,
+                               L[s], scale, causal)
+            out[sel] = o
+            lse[sel] = l
+    return out, lse
+
+
+def merge_lse(outs, lses):
+    """Combine partial results over disjoint key sets.
+
+    outs: ``[P, ..., d]`` each normalised over its own keys; lses: ``[P, ...]``
+    natural-log sums of exponentiated scaled scores (``-inf`` for a part with no
+    key).  With ``L* = max_p lse_p`` and ``w_p = exp(lse_p - L*)`` the merged
+    row is ``sum_p w_p out_p / sum_p w_p`` and its lse ``L* + ln sum_p w_p``.
+    A row whose parts are all empty gives 0 and ``-inf``.
+    """
+    outs = np.asarray(outs, dtype=np.float64)
+    lses = np.asarray(lses, dtype=np.float64)
+    top = lses.max(axis=0)
+    any_key = np.isfinite(top)
+    top_safe = np.where(any_key, top, 0.0)
+    w = np.where(np.isfinite(lses), np.exp(lses - top_safe[None]), 0.0)
+    wsum = w.sum(axis=0)
+    wsum_safe = np.where(any_key, wsum, 1.0)
+    merged = (w[..., None] * outs).sum(axis=0) / wsum_safe[..., None]
+    merged = np.where(any_key[..., None], merged, 0.0)
+    lse = np.where(any_key, top_safe + np.log(wsum_safe), -np.inf)
+    return merged, lse
