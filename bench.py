@@ -1,0 +1,227 @@
+"""Benchmark of unified paged attention on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                    [--no-cpu-baseline] [--all]
+
+A step is one call of pa_unified_attention over one synthetic batch (inputs
+resident in HBM).  Prints one JSON line: whole-job throughput in the metric's
+unit, plus the roofline of the forward kernel (algorithmic bytes or flops per
+launch over its average launch duration, from HIP events on the launch stream)
+and the fp64 CPU oracle timed on a bounded sample of the same workload.
+
+Algorithmic bytes per launch: every valid context token's K and V read once
+(sum_s L_s * Hkv * d * 2 B * 2) plus q read and out written (2 * T * Hq * d *
+2 B).  Algorithmic flops: 4 * d * Hq * (admissible (query, key) pairs per head).
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "paged varlen attn µs/batch; decode KV-read TB/s & prefill TFLOP/s vs peak"
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+DEFAULT_WORKLOAD = "decode_256seq_ctx1k"
+
+
+def algorithmic_work(b):
+    d, hq, hkv = b.head_dim, b.num_q_heads, b.num_kv_heads
+    kv_bytes = int(b.k_lens.sum()) * hkv * d * 2 * 2
+    qo_bytes = 2 * b.total_q * hq * d * 2
+    pairs = 0
+    for ql, L in zip(b.q_lens.tolist(), b.k_lens.tolist()):
+        if b.causal:
+            # query i sees min(L, max(0, L - ql + i + 1)) keys
+            i = np.arange(ql)
+            pairs += int(np.clip(L - ql + i + 1, 0, L).sum())
+        else:
+            pairs += ql * L
+    flops = 4 * d * hq * pairs
+    return kv_bytes + qo_bytes, kv_bytes, flops
+
+
+def source_hash():
+    h = hashlib.sha256()
+    for f in ("pa_kernels.hip", "pa_api.cpp", "pa_internal.h"):
+        with open(os.path.join(ROOT, "paged_kv_cache_unified_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_record(workload):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they were
+    taken on the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("source_hash") != source_hash():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(b, budget_s=20.0):
+    """The oracle, as it stands, on a bounded sample of the batch's sequences."""
+    import threadpoolctl
+
+    import oracle
+    cores = len(os.sched_getaffinity(0))
+    threads = min(cores, 64)
+    order = np.argsort(b.k_lens)[::-1]
+    picked, total = [], 0.0
+    with threadpoolctl.threadpool_limits(limits=threads):
+        t_all = 0.0
+        for s in list(order[::max(1, len(order) // 64)]) + list(order):
+            if s in picked:
+                continue
+            sub, _ = b.host_subset([int(s)])
+            t0 = time.perf_counter()
+            oracle.paged_attention(sub["q"], sub["k_cache"], sub["v_cache"], sub["cu_seqlens_q"],
+                                   sub["seqused_k"], sub["block_table"], sub["softmax_scale"],
+                                   sub["causal"])
+            t_all += time.perf_counter() - t0
+            picked.append(int(s))
+            if t_all >= budget_s or len(picked) == len(order):
+                break
+        info = threadpoolctl.threadpool_info()
+    blas = ",".join(sorted({i.get("internal_api", "?") for i in info})) or "none"
+    sample_bytes = int(b.k_lens[picked].sum()) * b.num_kv_heads * b.head_dim * 4 + \
+        2 * int(b.q_lens[picked].sum()) * b.num_q_heads * b.head_dim * 2
+    return {"value": sample_bytes / t_all / 1e12, "unit": "TB/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"{len(picked)} of {b.num_seqs} sequences ({int(b.k_lens[picked].sum())} "
+                      f"context tokens), fp64 numpy oracle, {t_all:.1f} s, BLAS {blas}, "
+                      f"{cores} host cores visible"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cold", type=int, default=20, help="extra cold-cache timed calls")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the operation runs on a single MI355X)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import paged_kv_cache_unified_amd as pa
+    from workloads import WORKLOADS, make_workload
+
+    if args.workload not in WORKLOADS:
+        sys.exit(f"unknown workload {args.workload}; choose from {sorted(WORKLOADS)}")
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    print(f"bench: generating {args.workload}", file=sys.stderr, flush=True)
+    b = make_workload(args.workload, device=dev)
+    out = torch.empty_like(b.q)
+    call_args = b.args(out)
+    plan = pa.plan_describe(*call_args[:9])
+    total_bytes, kv_bytes, flops = algorithmic_work(b)
+
+    stream = torch.cuda.current_stream(dev)
+    for _ in range(args.warmup):
+        pa.unified_attention(*call_args)
+    torch.cuda.synchronize()
+
+    # timed region: exactly K steps, per-launch events on the launch stream
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        starts[i].record(stream)
+        pa.unified_attention(*call_args)
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per_launch_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    ms_per_step = wall * 1e3 / args.steps
+    launch_ms = float(np.mean(per_launch_ms))
+
+    # cold calls: a 1 GiB write between calls evicts the 256 MB Infinity Cache
+    cold = []
+    if args.cold:
+        flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+        for _ in range(args.cold):
+            flush.fill_(1.0)
+            s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            s.record(stream)
+            pa.unified_attention(*call_args)
+            e.record(stream)
+            torch.cuda.synchronize()
+            cold.append(s.elapsed_time(e))
+        del flush
+
+    bound = "mfma" if flops / (BF16_PEAK_TFLOPS * 1e12) > total_bytes / (HBM_PEAK_GBS * 1e9) else "hbm"
+    if bound == "hbm":
+        achieved = total_bytes / (launch_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": traffic_record(args.workload)}
+        value = kv_bytes / (ms_per_step * 1e-3) / 1e12
+        unit = "TB/s"
+    else:
+        achieved = flops / (launch_ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4),
+                "traffic": traffic_record(args.workload)}
+        value = flops / (ms_per_step * 1e-3) / 1e12
+        unit = "TFLOP/s"
+
+    res = {
+        "metric": METRIC,
+        "value": round(value, 4),
+        "unit": unit,
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": args.workload,
+            "num_seqs": b.num_seqs, "total_q": b.total_q,
+            "context_tokens": int(b.k_lens.sum()), "max_seqlen_q": b.max_seqlen_q,
+            "max_seqlen_k": b.max_seqlen_k, "num_q_heads": b.num_q_heads,
+            "num_kv_heads": b.num_kv_heads, "head_dim": b.head_dim,
+            "block_size": b.block_size, "causal": b.causal, "parallelism": "single GPU",
+        },
+        "us_per_batch": round(ms_per_step * 1e3, 2),
+        "us_per_launch_events": round(launch_ms * 1e3, 2),
+        "us_per_launch_cold_p10_p50_p90": [round(float(np.percentile(cold, p)) * 1e3, 2)
+                                           for p in (10, 50, 90)] if cold else None,
+        "algorithmic_bytes_per_launch": total_bytes,
+        "algorithmic_flops_per_launch": flops,
+        "plan": plan,
+        "roofline": roof,
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        print("bench: timing the CPU oracle on a sample", file=sys.stderr, flush=True)
+        res["cpu_baseline"] = cpu_baseline(b)
+        if unit != "TB/s":
+            res["cpu_baseline"]["note"] = "reported in TB/s of algorithmic bytes"
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

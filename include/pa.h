@@ -1,0 +1,202 @@
+/*
+ * pa.h — C ABI of libpa: unified paged attention for AMD Instinct MI355X (gfx950).
+ *
+ * One call computes attention for a whole varlen batch in which every sequence
+ * may have a different query length: decode steps (one query), chunks of a
+ * chunked prefill and whole prefills are served by the same launch.  The call
+ * follows the flash_attn_varlen_func statement of the problem that the unified
+ * kernel adopts (page "[Kernel] Unified Triton kernel that doesn't distinguish
+ * between prefill + decode", PR description), reads keys and values from a
+ * paged cache in the FlashAttention layout (same passage), and needs no
+ * metadata beyond what a serving engine already has for chunked prefill plus
+ * decode in one batch (page "[Kernel] [V1] Improved performance for V1 Triton
+ * (ROCm) backend", section "How is this performance improvement achieved?").
+ *
+ * For query i (0-based) of sequence s, with q_s = cu_seqlens_q[s+1] -
+ * cu_seqlens_q[s] queries and L_s = seqused_k[s] context tokens (the new tokens
+ * included, already written to the cache), and q-head h reading kv-head
+ * h / (Hq / Hkv):
+ *
+ *     out[cu_seqlens_q[s] + i, h, :] = sum_j softmax_j(scale * q . k_j) v_j
+ *
+ * over the admissible keys j: all j < L_s when causal == 0, and
+ * j <= L_s - q_s + i when causal != 0 (the causal mask is aligned to the end
+ * of each sequence's context, so a decode query sees its whole context and a
+ * prefill chunk sees its cached prefix).  Key j of sequence s is slot
+ * j % block_size of physical block block_table[s, j / block_size].  A row
+ * with no admissible key (L_s == 0, or causal with q_s > L_s for the first
+ * q_s - L_s queries) is written as exactly 0.
+ *
+ * No HIP header is needed to include this file.  Every data pointer in a
+ * pa_tensor is a DEVICE pointer on the current HIP device; all shapes, strides
+ * and scalars are passed by value on the host.
+ */
+#ifndef PA_H_
+#define PA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PA_VERSION 1
+
+/* Return codes.  Every failure is reported before anything is launched, with
+ * one exception: PA_ERR_HIP, which may also come from the launch itself. */
+typedef enum {
+  PA_OK = 0,
+  PA_ERR_NULL = -1,        /* a required pointer is NULL                       */
+  PA_ERR_DTYPE = -2,       /* wrong dtype code for an argument                 */
+  PA_ERR_SHAPE = -3,       /* ndim or extents inconsistent between arguments   */
+  PA_ERR_UNSUPPORTED = -4, /* valid but not built: head_dim, block_size, G ... */
+  PA_ERR_ALIGN = -5,       /* pointer or stride breaks the 16-byte rule        */
+  PA_ERR_ALIAS = -6,       /* out overlaps q, k_cache or v_cache               */
+  PA_ERR_WORKSPACE = -7,   /* caller workspace missing or too small            */
+  PA_ERR_CONTENT = -8,     /* metadata contents invalid (only when checked)    */
+  PA_ERR_HIP = -9          /* the HIP runtime reported an error                */
+} pa_status;
+
+typedef enum { PA_BF16 = 1, PA_INT32 = 2, PA_FP32 = 3 } pa_dtype;
+
+/* A strided view of device memory.  shape/stride entries beyond ndim are
+ * ignored; strides are in ELEMENTS. */
+typedef struct {
+  void* data;
+  int32_t dtype;     /* pa_dtype */
+  int32_t ndim;
+  int64_t shape[4];
+  int64_t stride[4];
+} pa_tensor;
+
+/* Test and tuning switches for pa_unified_attention_ex.  Zero-initialise
+ * for defaults. */
+typedef struct {
+  int32_t force_num_splits; /* >0: split every row's keys into this many
+                               key ranges merged by log-sum-exp (clamped so each
+                               range holds at least one 64-key stage)          */
+  int32_t force_tile;       /* 0: heuristic; 1: one query tile per sequence of
+                               at most 16/G tokens (requires max_seqlen_q*G <=
+                               16); 2: 64-row query tiles, and the per-wave-rows
+                               code path even for tiles of <= 16 rows          */
+  int32_t check_contents;   /* !=0: copy the metadata to the host (synchronous)
+                               and return PA_ERR_CONTENT if it breaks the
+                               preconditions listed below                      */
+  int32_t reserved;
+} pa_options;
+
+/* Launch shape chosen for a batch (pa_plan_describe). */
+typedef struct {
+  int32_t tile_tokens;   /* query tokens per work-group tile                  */
+  int32_t tile_rows;     /* packed (token, q-head) rows per tile              */
+  int32_t num_slots;     /* query-tile slots in the grid                      */
+  int32_t slots_direct;  /* 1: slot == sequence index (one tile per sequence) */
+  int32_t num_splits;    /* key ranges per row (1: no merge kernel)           */
+  int32_t split_keys;    /* keys per range (multiple of 64)                   */
+  int64_t num_workgroups;/* main-kernel grid size                             */
+  int64_t workspace_bytes;
+} pa_plan_info;
+
+/*
+ * pa_unified_attention — the whole varlen batch in one call.
+ *
+ *  q            bf16 [T, Hq, d]; stride[2] == 1; stride[0], stride[1] multiples
+ *               of 8; 16-byte aligned.  T = total query tokens.
+ *  k_cache      bf16 [NB, B, Hkv, d]; stride[1..3] contiguous (B*Hkv*d is not
+ *               required for stride[0], which must be a multiple of 8 and at
+ *               least B*Hkv*d); 16-byte aligned.
+ *  v_cache      same shape and strides as k_cache.
+ *  out          bf16 [T, Hq, d]; same rules as q; fully overwritten; must not
+ *               overlap q, k_cache or v_cache.
+ *  cu_seqlens_q int32 [S+1], contiguous: query offsets of the S sequences.
+ *  seqused_k    int32 [S], contiguous: context length L_s of each sequence.
+ *  block_table  int32 [S, MB]; stride[1] == 1; entries j < ceil(L_s / B) of
+ *               row s are physical block ids in [0, NB).  Ids may repeat within
+ *               and across rows (shared prefixes); entries past ceil(L_s/B)
+ *               are never read.
+ *  max_seqlen_q upper bound on q_s (used only for launch sizing).
+ *  max_seqlen_k upper bound on L_s; must not exceed MB * B.
+ *  softmax_scale multiplies q . k before the softmax.
+ *  causal       0: every key of the context is admissible; else end-aligned
+ *               causal mask (see above).
+ *  stream       hipStream_t to launch on (NULL = the null stream).
+ *
+ * Supported: d in {64, 128}; B == 16; Hq % Hkv == 0 with G = Hq/Hkv in
+ * {1, 2, 4, 8, 16}.  Unsupported values return PA_ERR_UNSUPPORTED.
+ *
+ * Preconditions on device contents (unchecked unless check_contents is set;
+ * breaking them is undefined behaviour): cu_seqlens_q[0] == 0, non-decreasing,
+ * cu_seqlens_q[S] == T; q_s <= max_seqlen_q; 0 <= L_s <= max_seqlen_k; block
+ * ids in range.
+ *
+ * Ownership: the caller owns every buffer; the library keeps no pointer after
+ * return.  This entry point uses a library-owned split workspace (device
+ * memory, one per device, grown on demand with hipMalloc after synchronising
+ * the device, kept until process exit); use pa_unified_attention_ex with a
+ * caller workspace under stream capture.
+ *
+ * Asynchronous: returns after enqueueing on `stream`.  Deterministic: the
+ * same inputs and launch plan give bit-identical output, and the output does
+ * not depend on the physical placement of blocks.  Thread-safe.
+ */
+int pa_unified_attention(const pa_tensor* q, const pa_tensor* k_cache,
+                         const pa_tensor* v_cache, pa_tensor* out,
+                         const pa_tensor* cu_seqlens_q, const pa_tensor* seqused_k,
+                         const pa_tensor* block_table, int32_t max_seqlen_q,
+                         int32_t max_seqlen_k, float softmax_scale, int32_t causal,
+                         void* stream);
+
+/*
+ * pa_unified_attention_ex — as above with options and a caller workspace.
+ * workspace may be NULL iff pa_workspace_size(...) returns 0 for the same
+ * arguments and options; it must be 256-byte aligned, device memory, at least
+ * that many bytes, and not used by anything else until the work enqueued here
+ * has finished.  opt may be NULL (defaults).
+ */
+int pa_unified_attention_ex(const pa_tensor* q, const pa_tensor* k_cache,
+                            const pa_tensor* v_cache, pa_tensor* out,
+                            const pa_tensor* cu_seqlens_q, const pa_tensor* seqused_k,
+                            const pa_tensor* block_table, int32_t max_seqlen_q,
+                            int32_t max_seqlen_k, float softmax_scale, int32_t causal,
+                            const pa_options* opt, void* workspace,
+                            size_t workspace_bytes, void* stream);
+
+/*
+ * pa_workspace_size — bytes of workspace pa_unified_attention_ex needs for
+ * these arguments and options (0 when the batch needs no key split).  Host
+ * only: reads descriptors, never device memory.  Returns (size_t)-1 and sets
+ * pa_last_error when the arguments are invalid.
+ */
+size_t pa_workspace_size(const pa_tensor* q, const pa_tensor* k_cache,
+                         const pa_tensor* v_cache, const pa_tensor* out,
+                         const pa_tensor* cu_seqlens_q, const pa_tensor* seqused_k,
+                         const pa_tensor* block_table, int32_t max_seqlen_q,
+                         int32_t max_seqlen_k, const pa_options* opt);
+
+/*
+ * pa_plan_describe — the launch plan the library would use, without
+ * launching (host only).  num_cus: compute units to plan for (0 = the
+ * current device's count, or 256 when no device is visible).
+ */
+int pa_plan_describe(const pa_tensor* q, const pa_tensor* k_cache,
+                     const pa_tensor* v_cache, const pa_tensor* out,
+                     const pa_tensor* cu_seqlens_q, const pa_tensor* seqused_k,
+                     const pa_tensor* block_table, int32_t max_seqlen_q,
+                     int32_t max_seqlen_k, const pa_options* opt, int32_t num_cus,
+                     pa_plan_info* info);
+
+/* Static text for a status code. */
+const char* pa_status_string(int status);
+
+/* Detail text of the last failure on the calling thread ("" if none). */
+const char* pa_last_error(void);
+
+/* PA_VERSION of the built library. */
+int pa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_H_ */

@@ -1,0 +1,177 @@
+"""Unified paged attention for AMD MI355X (gfx950): thin Python binding of libpa.
+
+Every step of the computation runs in the HIP kernels of ``libpa.so``; this
+module only turns torch tensors into the C ABI's descriptors (``include/pa.h``)
+and passes the current HIP stream.  There is no fallback: if the library is not
+built, importing this package raises.
+
+    unified_attention(q, k_cache, v_cache, out, cu_seqlens_q, seqused_k,
+                      block_table, max_seqlen_q, max_seqlen_k, softmax_scale,
+                      causal)
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libpa.so")
+
+PA_BF16, PA_INT32, PA_FP32 = 1, 2, 3
+_DTYPES = {torch.bfloat16: PA_BF16, torch.int32: PA_INT32, torch.float32: PA_FP32}
+
+
+class PaTensor(ctypes.Structure):
+    _fields_ = [("data", ctypes.c_void_p), ("dtype", ctypes.c_int32), ("ndim", ctypes.c_int32),
+                ("shape", ctypes.c_int64 * 4), ("stride", ctypes.c_int64 * 4)]
+
+
+class PaOptions(ctypes.Structure):
+    _fields_ = [("force_num_splits", ctypes.c_int32), ("force_tile", ctypes.c_int32),
+                ("check_contents", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+
+
+class PaPlanInfo(ctypes.Structure):
+    _fields_ = [("tile_tokens", ctypes.c_int32), ("tile_rows", ctypes.c_int32),
+                ("num_slots", ctypes.c_int32), ("slots_direct", ctypes.c_int32),
+                ("num_splits", ctypes.c_int32), ("split_keys", ctypes.c_int32),
+                ("num_workgroups", ctypes.c_int64), ("workspace_bytes", ctypes.c_int64)]
+
+    def as_dict(self):
+        return {name: getattr(self, name) for name, _ in self._fields_}
+
+
+STATUS = {0: "PA_OK", -1: "PA_ERR_NULL", -2: "PA_ERR_DTYPE", -3: "PA_ERR_SHAPE",
+          -4: "PA_ERR_UNSUPPORTED", -5: "PA_ERR_ALIGN", -6: "PA_ERR_ALIAS",
+          -7: "PA_ERR_WORKSPACE", -8: "PA_ERR_CONTENT", -9: "PA_ERR_HIP"}
+
+# C-ABI symbols and their prototypes, in the order of include/pa.h
+_T = ctypes.POINTER(PaTensor)
+_SIGNATURES = {
+    "pa_unified_attention": (ctypes.c_int, [_T, _T, _T, _T, _T, _T, _T, ctypes.c_int32,
+                                            ctypes.c_int32, ctypes.c_float, ctypes.c_int32,
+                                            ctypes.c_void_p]),
+    "pa_unified_attention_ex": (ctypes.c_int, [_T, _T, _T, _T, _T, _T, _T, ctypes.c_int32,
+                                               ctypes.c_int32, ctypes.c_float, ctypes.c_int32,
+                                               ctypes.POINTER(PaOptions), ctypes.c_void_p,
+                                               ctypes.c_size_t, ctypes.c_void_p]),
+    "pa_workspace_size": (ctypes.c_size_t, [_T, _T, _T, _T, _T, _T, _T, ctypes.c_int32,
+                                            ctypes.c_int32, ctypes.POINTER(PaOptions)]),
+    "pa_plan_describe": (ctypes.c_int, [_T, _T, _T, _T, _T, _T, _T, ctypes.c_int32,
+                                        ctypes.c_int32, ctypes.POINTER(PaOptions),
+                                        ctypes.c_int32, ctypes.POINTER(PaPlanInfo)]),
+    "pa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "pa_last_error": (ctypes.c_char_p, []),
+    "pa_version": (ctypes.c_int, []),
+}
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run `python -m paged_kv_cache_unified_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    for name, (res, args) in _SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib
+
+
+lib = _load()
+
+
+class PaError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        self.status = status
+        super().__init__(f"{STATUS.get(status, status)}: {detail}")
+
+
+def describe(t: Optional[torch.Tensor]) -> PaTensor:
+    """Descriptor of a tensor (data pointer, dtype code, shape, strides)."""
+    d = PaTensor()
+    if t is None:
+        return d
+    if t.dim() > 4:
+        raise ValueError("at most 4 dimensions")
+    d.data = t.data_ptr() if t.numel() else (t.data_ptr() or None)
+    d.dtype = _DTYPES.get(t.dtype, 0)
+    d.ndim = t.dim()
+    for i in range(t.dim()):
+        d.shape[i] = t.shape[i]
+        d.stride[i] = t.stride(i)
+    return d
+
+
+def _stream_handle(device) -> int:
+    if device.type != "cuda":
+        return 0
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _check(rc: int):
+    if rc != 0:
+        raise PaError(rc, lib.pa_last_error().decode())
+
+
+def _descs(q, k_cache, v_cache, out, cu_seqlens_q, seqused_k, block_table):
+    ds = [describe(t) for t in (q, k_cache, v_cache, out, cu_seqlens_q, seqused_k, block_table)]
+    return ds, [ctypes.byref(x) for x in ds]
+
+
+def options(force_num_splits: int = 0, force_tile: int = 0, check_contents: bool = False) -> PaOptions:
+    return PaOptions(int(force_num_splits), int(force_tile), int(bool(check_contents)), 0)
+
+
+def unified_attention(q, k_cache, v_cache, out, cu_seqlens_q, seqused_k, block_table,
+                      max_seqlen_q: int, max_seqlen_k: int, softmax_scale: float, causal: bool,
+                      *, opts: Optional[PaOptions] = None,
+                      workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Attention of the whole varlen batch into ``out`` (bf16 [T, Hq, d]).
+
+    With ``opts`` or ``workspace`` given, calls ``pa_unified_attention_ex``
+    (``workspace`` then must be a device tensor of at least ``workspace_size``
+    bytes); otherwise ``pa_unified_attention`` with the library workspace.
+    """
+    ds, refs = _descs(q, k_cache, v_cache, out, cu_seqlens_q, seqused_k, block_table)
+    stream = ctypes.c_void_p(_stream_handle(q.device))
+    if opts is None and workspace is None:
+        rc = lib.pa_unified_attention(*refs, int(max_seqlen_q), int(max_seqlen_k),
+                                      float(softmax_scale), int(bool(causal)), stream)
+    else:
+        ws_ptr = workspace.data_ptr() if workspace is not None else None
+        ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+        rc = lib.pa_unified_attention_ex(*refs, int(max_seqlen_q), int(max_seqlen_k),
+                                         float(softmax_scale), int(bool(causal)),
+                                         ctypes.byref(opts) if opts is not None else None,
+                                         ws_ptr, ws_bytes, stream)
+    _check(rc)
+    return out
+
+
+def workspace_size(q, k_cache, v_cache, out, cu_seqlens_q, seqused_k, block_table,
+                   max_seqlen_q: int, max_seqlen_k: int, opts: Optional[PaOptions] = None) -> int:
+    ds, refs = _descs(q, k_cache, v_cache, out, cu_seqlens_q, seqused_k, block_table)
+    n = lib.pa_workspace_size(*refs, int(max_seqlen_q), int(max_seqlen_k),
+                              ctypes.byref(opts) if opts is not None else None)
+    if n == ctypes.c_size_t(-1).value:
+        raise PaError(-3, lib.pa_last_error().decode())
+    return int(n)
+
+
+def plan_describe(q, k_cache, v_cache, out, cu_seqlens_q, seqused_k, block_table,
+                  max_seqlen_q: int, max_seqlen_k: int, opts: Optional[PaOptions] = None,
+                  num_cus: int = 0) -> dict:
+    ds, refs = _descs(q, k_cache, v_cache, out, cu_seqlens_q, seqused_k, block_table)
+    info = PaPlanInfo()
+    _check(lib.pa_plan_describe(*refs, int(max_seqlen_q), int(max_seqlen_k),
+                                ctypes.byref(opts) if opts is not None else None, int(num_cus),
+                                ctypes.byref(info)))
+    return info.as_dict()
+
+
+def version() -> int:
+    return int(lib.pa_version())

@@ -1,0 +1,497 @@
+// Host side of libpa: descriptor validation, the launch-shape heuristic,
+// workspace management and kernel launches.  The C ABI is declared in
+// include/pa.h.  Validation and planning read descriptors only (never device
+// memory) so they run, and are tested, on machines without a GPU.
+
+#include <algorithm>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "pa.h"
+#include "pa_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+struct Shapes {
+  int64_t T, Hq, D, NB, B, Hkv, S, MB, G;
+  int64_t q_st, q_sh, o_st, o_sh, kv_sb, bt_stride;
+};
+
+struct Plan {
+  int32_t tile_tokens, tile_rows, num_slots, slots_direct, n_split, split_keys;
+  int64_t nwg;
+  size_t ws_bytes;
+  size_t ws_lse_offset;
+};
+
+constexpr int64_t kMaxInt32 = 0x7fffffff;
+
+int64_t extent_elems(const pa_tensor* t) {
+  int64_t e = 1;
+  for (int i = 0; i < t->ndim; ++i) {
+    if (t->shape[i] == 0) return 0;
+    e += (t->shape[i] - 1) * t->stride[i];
+  }
+  return e;
+}
+
+bool overlaps(const pa_tensor* a, const pa_tensor* b, int64_t elem_bytes) {
+  const int64_t ea = extent_elems(a), eb = extent_elems(b);
+  if (ea == 0 || eb == 0) return false;
+  const uintptr_t a0 = reinterpret_cast<uintptr_t>(a->data);
+  const uintptr_t b0 = reinterpret_cast<uintptr_t>(b->data);
+  const uintptr_t a1 = a0 + static_cast<uintptr_t>(ea * elem_bytes);
+  const uintptr_t b1 = b0 + static_cast<uintptr_t>(eb * elem_bytes);
+  return a0 < b1 && b0 < a1;
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int validate(const pa_tensor* q, const pa_tensor* k, const pa_tensor* v, const pa_tensor* out,
+             const pa_tensor* cu, const pa_tensor* sk, const pa_tensor* bt, int32_t max_q,
+             int32_t max_k, Shapes* sh) {
+  if (!q || !k || !v || !out || !cu || !sk || !bt)
+    return fail(PA_ERR_NULL, "a tensor descriptor pointer is NULL");
+  struct {
+    const pa_tensor* t;
+    const char* name;
+    int dtype;
+    int ndim;
+  } spec[] = {{q, "q", PA_BF16, 3},          {k, "k_cache", PA_BF16, 4},
+              {v, "v_cache", PA_BF16, 4},    {out, "out", PA_BF16, 3},
+              {cu, "cu_seqlens_q", PA_INT32, 1}, {sk, "seqused_k", PA_INT32, 1},
+              {bt, "block_table", PA_INT32, 2}};
+  for (auto& e : spec) {
+    if (e.t->dtype != e.dtype)
+      return fail(PA_ERR_DTYPE, "%s: dtype code %d, expected %d", e.name, e.t->dtype, e.dtype);
+    if (e.t->ndim != e.ndim)
+      return fail(PA_ERR_SHAPE, "%s: ndim %d, expected %d", e.name, e.t->ndim, e.ndim);
+    for (int i = 0; i < e.ndim; ++i)
+      if (e.t->shape[i] < 0 || e.t->stride[i] < 0)
+        return fail(PA_ERR_SHAPE, "%s: negative extent or stride in dim %d", e.name, i);
+  }
+  Shapes s{};
+  s.T = q->shape[0];
+  s.Hq = q->shape[1];
+  s.D = q->shape[2];
+  s.NB = k->shape[0];
+  s.B = k->shape[1];
+  s.Hkv = k->shape[2];
+  s.S = sk->shape[0];
+  s.MB = bt->shape[1];
+  for (int i = 0; i < 3; ++i)
+    if (out->shape[i] != q->shape[i])
+      return fail(PA_ERR_SHAPE, "out shape differs from q in dim %d", i);
+  for (int i = 0; i < 4; ++i)
+    if (v->shape[i] != k->shape[i] || v->stride[i] != k->stride[i])
+      return fail(PA_ERR_SHAPE, "v_cache shape/strides differ from k_cache in dim %d", i);
+  if (k->shape[3] != s.D) return fail(PA_ERR_SHAPE, "cache head_dim %lld != q head_dim %lld",
+                                      (long long)k->shape[3], (long long)s.D);
+  if (cu->shape[0] != s.S + 1)
+    return fail(PA_ERR_SHAPE, "cu_seqlens_q has %lld entries, expected num_seqs+1 = %lld",
+                (long long)cu->shape[0], (long long)(s.S + 1));
+  if (bt->shape[0] != s.S)
+    return fail(PA_ERR_SHAPE, "block_table has %lld rows, expected %lld",
+                (long long)bt->shape[0], (long long)s.S);
+  if (s.Hq == 0 || s.Hkv == 0 || s.Hq % s.Hkv)
+    return fail(PA_ERR_SHAPE, "num_q_heads %lld must be a positive multiple of num_kv_heads %lld",
+                (long long)s.Hq, (long long)s.Hkv);
+  if (s.S == 0 && s.T != 0) return fail(PA_ERR_SHAPE, "total_q > 0 with no sequences");
+  if (max_q < 0 || max_k < 0) return fail(PA_ERR_SHAPE, "negative max_seqlen");
+  s.G = s.Hq / s.Hkv;
+  if (s.D != 64 && s.D != 128)
+    return fail(PA_ERR_UNSUPPORTED, "head_dim %lld (supported: 64, 128)", (long long)s.D);
+  if (s.B != pa::kBlockSize)
+    return fail(PA_ERR_UNSUPPORTED, "block_size %lld (supported: 16)", (long long)s.B);
+  if (!pa::fwd_supported((int)s.D, (int)s.G))
+    return fail(PA_ERR_UNSUPPORTED, "GQA group %lld (supported: 1, 2, 4, 8, 16)", (long long)s.G);
+  if (s.S > 0 && (int64_t)max_k > s.MB * s.B)
+    return fail(PA_ERR_SHAPE, "max_seqlen_k %d exceeds block_table capacity %lld", max_k,
+                (long long)(s.MB * s.B));
+  if (s.T > kMaxInt32 / 2 || s.S > kMaxInt32 / 2 || s.NB > kMaxInt32 || s.Hq > 4096)
+    return fail(PA_ERR_UNSUPPORTED, "sizes beyond the 32-bit index range");
+  // strides
+  if (q->stride[2] != 1 || out->stride[2] != 1)
+    return fail(PA_ERR_UNSUPPORTED, "q/out need a unit stride along head_dim");
+  if (k->stride[3] != 1 || k->stride[2] != s.D || k->stride[1] != s.Hkv * s.D)
+    return fail(PA_ERR_UNSUPPORTED, "caches need contiguous [block_size, num_kv_heads, head_dim]");
+  if (s.NB > 1 && k->stride[0] < s.B * s.Hkv * s.D)
+    return fail(PA_ERR_SHAPE, "cache block stride smaller than one block");
+  if ((q->stride[0] | q->stride[1] | out->stride[0] | out->stride[1] | k->stride[0]) % 8)
+    return fail(PA_ERR_ALIGN, "q/out/cache strides must be multiples of 8 elements");
+  if (cu->stride[0] != 1 && cu->shape[0] > 1) return fail(PA_ERR_UNSUPPORTED, "cu_seqlens_q not contiguous");
+  if (sk->stride[0] != 1 && s.S > 1) return fail(PA_ERR_UNSUPPORTED, "seqused_k not contiguous");
+  if (bt->stride[1] != 1 && s.MB > 1) return fail(PA_ERR_UNSUPPORTED, "block_table rows not contiguous");
+  if (s.S > 1 && bt->stride[0] < s.MB) return fail(PA_ERR_SHAPE, "block_table row stride < width");
+  if (bt->stride[0] > kMaxInt32) return fail(PA_ERR_UNSUPPORTED, "block_table row stride too large");
+  // pointers
+  if (s.T > 0 && (!q->data || !out->data)) return fail(PA_ERR_NULL, "q/out data is NULL");
+  if (!cu->data) return fail(PA_ERR_NULL, "cu_seqlens_q data is NULL");
+  if (s.S > 0 && (!sk->data || !bt->data)) return fail(PA_ERR_NULL, "seqused_k/block_table data is NULL");
+  if (s.S > 0 && s.NB > 0 && (!k->data || !v->data)) return fail(PA_ERR_NULL, "cache data is NULL");
+  if (!aligned(q->data, 16) || !aligned(out->data, 16) || !aligned(k->data, 16) ||
+      !aligned(v->data, 16))
+    return fail(PA_ERR_ALIGN, "q/out/cache data must be 16-byte aligned");
+  if (!aligned(cu->data, 4) || !aligned(sk->data, 4) || !aligned(bt->data, 4))
+    return fail(PA_ERR_ALIGN, "int32 metadata must be 4-byte aligned");
+  if (overlaps(out, q, 2) || overlaps(out, k, 2) || overlaps(out, v, 2))
+    return fail(PA_ERR_ALIAS, "out overlaps q, k_cache or v_cache");
+  s.q_st = q->stride[0];
+  s.q_sh = q->stride[1];
+  s.o_st = out->stride[0];
+  s.o_sh = out->stride[1];
+  s.kv_sb = k->stride[0];
+  s.bt_stride = s.MB > 0 ? bt->stride[0] : 0;
+  *sh = s;
+  return PA_OK;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+// Launch shape from shapes only (no device reads, no autotuning):
+//  * a batch whose every sequence fits one narrow tile (max_seqlen_q * G <= 16:
+//    pure decode, or short chunks) gets one tile per sequence;
+//  * otherwise query tiles of 64 packed rows (64/G tokens); sequences are
+//    mapped to tile slots by the bound floor(cu[s]/Tq) + s, so the grid is
+//    known without reading cu_seqlens_q; tiles of <= 16 rows inside such a
+//    batch (its decode sequences) still run the narrow code path;
+//  * keys are split only when the items cannot fill the GPU: enough splits to
+//    reach ~8 work-groups per CU, each split at least 512 keys.  Split sizes
+//    depend on max_seqlen_k and the grid only, so results are deterministic.
+int make_plan(const Shapes& s, int32_t max_q, int32_t max_k, const pa_options* opt, int num_cus,
+              Plan* out) {
+  Plan p{};
+  const int force_tile = opt ? opt->force_tile : 0;
+  const int force_split = opt ? opt->force_num_splits : 0;
+  const int64_t G = s.G;
+  const int64_t mq = std::max<int64_t>(max_q, 1);
+  const bool narrow_fits = mq * G <= pa::kNarrowRows;
+  if (force_tile == 1 && !narrow_fits)
+    return fail(PA_ERR_UNSUPPORTED, "force_tile=1 needs max_seqlen_q * G <= 16");
+  if (force_tile != 0 && force_tile != 1 && force_tile != 2)
+    return fail(PA_ERR_UNSUPPORTED, "force_tile must be 0, 1 or 2");
+  if (force_tile == 1 || (force_tile == 0 && narrow_fits)) {
+    p.tile_tokens = (int32_t)mq;
+    p.slots_direct = 1;
+    p.num_slots = (int32_t)s.S;
+  } else {
+    p.tile_tokens = (int32_t)(pa::kTileRows / G);
+    if (mq <= p.tile_tokens) {
+      p.slots_direct = 1;
+      p.num_slots = (int32_t)s.S;
+    } else {
+      p.slots_direct = 0;
+      p.num_slots = (int32_t)(s.T / p.tile_tokens + s.S);
+    }
+  }
+  p.tile_rows = (int32_t)(p.tile_tokens * G);
+  const int64_t items = (int64_t)p.num_slots * s.Hkv;
+  const int64_t mk = std::max<int64_t>(max_k, 1);
+  int64_t n_split = 1;
+  if (force_split > 0) {
+    n_split = force_split;
+  } else if (items > 0) {
+    const int64_t target = 8LL * std::max(num_cus, 1);
+    if (items < target) {
+      const int64_t by_len = (mk + 511) / 512;
+      n_split = std::min((target + items - 1) / items, by_len);
+    }
+  }
+  n_split = std::max<int64_t>(n_split, 1);
+  int64_t split_keys = (mk + n_split - 1) / n_split;
+  split_keys = (split_keys + pa::kStageKeys - 1) / pa::kStageKeys * pa::kStageKeys;
+  n_split = (mk + split_keys - 1) / split_keys;
+  p.n_split = (int32_t)n_split;
+  p.split_keys = (int32_t)split_keys;
+  p.nwg = items * n_split;
+  if (p.nwg > 0xffffffffLL) return fail(PA_ERR_UNSUPPORTED, "grid too large");
+  if (n_split > 1) {
+    const size_t rows = (size_t)s.T * (size_t)s.Hq * (size_t)n_split;
+    p.ws_lse_offset = align256(rows * (size_t)s.D * sizeof(float));
+    p.ws_bytes = p.ws_lse_offset + align256(rows * sizeof(float));
+  }
+  *out = p;
+  return PA_OK;
+}
+
+int device_cu_count(bool* ok) {
+  static std::mutex mu;
+  static std::vector<int> cache;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) {
+    (void)hipGetLastError();
+    *ok = false;
+    return 256;
+  }
+  std::lock_guard<std::mutex> lock(mu);
+  if ((int)cache.size() <= dev) cache.resize(dev + 1, 0);
+  if (cache[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        n <= 0) {
+      (void)hipGetLastError();
+      *ok = false;
+      return 256;
+    }
+    cache[dev] = n;
+  }
+  *ok = true;
+  return cache[dev];
+}
+
+int check_contents(const Shapes& s, const pa_tensor* cu, const pa_tensor* sk, const pa_tensor* bt,
+                   int32_t max_q, int32_t max_k, hipStream_t stream) {
+  std::vector<int32_t> hcu(s.S + 1), hsk(s.S), hbt((size_t)s.S * (size_t)s.bt_stride);
+  hipError_t e = hipMemcpyAsync(hcu.data(), cu->data, hcu.size() * 4, hipMemcpyDeviceToHost, stream);
+  if (e == hipSuccess && s.S > 0)
+    e = hipMemcpyAsync(hsk.data(), sk->data, hsk.size() * 4, hipMemcpyDeviceToHost, stream);
+  if (e == hipSuccess && s.S > 0 && s.MB > 0)
+    e = hipMemcpyAsync(hbt.data(), bt->data, ((size_t)(s.S - 1) * s.bt_stride + s.MB) * 4,
+                       hipMemcpyDeviceToHost, stream);
+  if (e == hipSuccess) e = hipStreamSynchronize(stream);
+  if (e != hipSuccess) return fail(PA_ERR_HIP, "metadata copy: %s", hipGetErrorString(e));
+  if (hcu[0] != 0) return fail(PA_ERR_CONTENT, "cu_seqlens_q[0] = %d", hcu[0]);
+  for (int64_t i = 0; i < s.S; ++i) {
+    const int32_t ql = hcu[i + 1] - hcu[i];
+    if (ql < 0) return fail(PA_ERR_CONTENT, "cu_seqlens_q decreases at %lld", (long long)i);
+    if (ql > max_q) return fail(PA_ERR_CONTENT, "sequence %lld: q_len %d > max_seqlen_q %d", (long long)i, ql, max_q);
+    if (hsk[i] < 0 || hsk[i] > max_k)
+      return fail(PA_ERR_CONTENT, "sequence %lld: seqused_k %d outside [0, %d]", (long long)i, hsk[i], max_k);
+    const int64_t nb = (hsk[i] + s.B - 1) / s.B;
+    for (int64_t j = 0; j < nb; ++j) {
+      const int32_t id = hbt[(size_t)i * s.bt_stride + j];
+      if (id < 0 || id >= s.NB)
+        return fail(PA_ERR_CONTENT, "block_table[%lld, %lld] = %d outside [0, %lld)", (long long)i,
+                    (long long)j, id, (long long)s.NB);
+    }
+  }
+  if (hcu[s.S] != s.T) return fail(PA_ERR_CONTENT, "cu_seqlens_q[S] = %d != total_q %lld", hcu[s.S], (long long)s.T);
+  return PA_OK;
+}
+
+struct DeviceWorkspace {
+  void* ptr = nullptr;
+  size_t bytes = 0;
+};
+
+int library_workspace(size_t need, hipStream_t stream, void** ptr) {
+  static std::mutex mu;
+  static std::vector<DeviceWorkspace> per_dev;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(PA_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  std::lock_guard<std::mutex> lock(mu);
+  if ((int)per_dev.size() <= dev) per_dev.resize(dev + 1);
+  DeviceWorkspace& w = per_dev[dev];
+  if (w.bytes < need) {
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(stream, &cs) == hipSuccess && cs != hipStreamCaptureStatusNone)
+      return fail(PA_ERR_WORKSPACE,
+                  "library workspace must grow to %zu bytes during stream capture; use "
+                  "pa_unified_attention_ex with a caller workspace", need);
+    if (w.ptr) {
+      e = hipDeviceSynchronize();
+      if (e == hipSuccess) e = hipFree(w.ptr);
+      if (e != hipSuccess) return fail(PA_ERR_HIP, "workspace release: %s", hipGetErrorString(e));
+      w.ptr = nullptr;
+      w.bytes = 0;
+    }
+    const size_t grow = std::max(need, w.bytes + w.bytes / 2);
+    e = hipMalloc(&w.ptr, grow);
+    if (e != hipSuccess) {
+      w.ptr = nullptr;
+      return fail(PA_ERR_HIP, "workspace hipMalloc(%zu): %s", grow, hipGetErrorString(e));
+    }
+    w.bytes = grow;
+  }
+  *ptr = w.ptr;
+  return PA_OK;
+}
+
+int run(const pa_tensor* q, const pa_tensor* k, const pa_tensor* v, pa_tensor* out,
+        const pa_tensor* cu, const pa_tensor* sk, const pa_tensor* bt, int32_t max_q,
+        int32_t max_k, float scale, int32_t causal, const pa_options* opt, bool library_ws,
+        void* ws, size_t ws_bytes, void* stream_v) {
+  g_last_error.clear();
+  Shapes s;
+  int rc = validate(q, k, v, out, cu, sk, bt, max_q, max_k, &s);
+  if (rc != PA_OK) return rc;
+  if (s.T == 0 || s.S == 0) return PA_OK;
+  bool have_dev = false;
+  const int ncu = device_cu_count(&have_dev);
+  Plan plan;
+  rc = make_plan(s, max_q, max_k, opt, ncu, &plan);
+  if (rc != PA_OK) return rc;
+  hipStream_t stream = reinterpret_cast<hipStream_t>(stream_v);
+  if (library_ws) {
+    if (plan.ws_bytes) {
+      rc = library_workspace(plan.ws_bytes, stream, &ws);
+      if (rc != PA_OK) return rc;
+    }
+  } else if (plan.ws_bytes) {
+    if (!ws) return fail(PA_ERR_WORKSPACE, "workspace of %zu bytes required", plan.ws_bytes);
+    if (ws_bytes < plan.ws_bytes)
+      return fail(PA_ERR_WORKSPACE, "workspace %zu bytes < required %zu", ws_bytes, plan.ws_bytes);
+    if (!aligned(ws, 256)) return fail(PA_ERR_ALIGN, "workspace must be 256-byte aligned");
+  }
+  if (opt && opt->check_contents) {
+    rc = check_contents(s, cu, sk, bt, max_q, max_k, stream);
+    if (rc != PA_OK) return rc;
+  }
+  pa::FwdParams p{};
+  p.q = static_cast<const uint16_t*>(q->data);
+  p.out = static_cast<uint16_t*>(out->data);
+  p.k = static_cast<const uint16_t*>(k->data);
+  p.v = static_cast<const uint16_t*>(v->data);
+  p.cu_q = static_cast<const int32_t*>(cu->data);
+  p.seq_k = static_cast<const int32_t*>(sk->data);
+  p.bt = static_cast<const int32_t*>(bt->data);
+  p.ws_o = plan.n_split > 1 ? static_cast<float*>(ws) : nullptr;
+  p.ws_lse = plan.n_split > 1
+                 ? reinterpret_cast<float*>(static_cast<char*>(ws) + plan.ws_lse_offset)
+                 : nullptr;
+  p.q_st = s.q_st;
+  p.q_sh = s.q_sh;
+  p.o_st = s.o_st;
+  p.o_sh = s.o_sh;
+  p.kv_sb = s.kv_sb;
+  p.bt_stride = (int32_t)s.bt_stride;
+  p.num_seqs = (int32_t)s.S;
+  p.total_q = (int32_t)s.T;
+  p.num_q_heads = (int32_t)s.Hq;
+  p.num_kv_heads = (int32_t)s.Hkv;
+  p.tile_tokens = plan.tile_tokens;
+  p.num_slots = plan.num_slots;
+  p.slots_direct = plan.slots_direct;
+  p.n_split = plan.n_split;
+  p.split_keys = plan.split_keys;
+  p.causal = causal ? 1 : 0;
+  p.narrow_rows = (opt && opt->force_tile == 2) ? 0 : pa::kNarrowRows;
+  p.scale_log2 = (float)((double)scale * 1.4426950408889634);
+  if (plan.nwg > 0) {
+    hipError_t e = pa::launch_fwd(p, (int)s.D, (int)s.G, plan.nwg, stream);
+    if (e != hipSuccess) return fail(PA_ERR_HIP, "forward launch: %s", hipGetErrorString(e));
+  }
+  if (plan.n_split > 1) {
+    pa::MergeParams mp{};
+    mp.ws_o = p.ws_o;
+    mp.ws_lse = p.ws_lse;
+    mp.out = p.out;
+    mp.o_st = s.o_st;
+    mp.o_sh = s.o_sh;
+    mp.total_q = (int32_t)s.T;
+    mp.num_q_heads = (int32_t)s.Hq;
+    mp.n_split = plan.n_split;
+    hipError_t e = pa::launch_merge(mp, (int)s.D, stream);
+    if (e != hipSuccess) return fail(PA_ERR_HIP, "merge launch: %s", hipGetErrorString(e));
+  }
+  return PA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int pa_unified_attention(const pa_tensor* q, const pa_tensor* k_cache, const pa_tensor* v_cache,
+                         pa_tensor* out, const pa_tensor* cu_seqlens_q, const pa_tensor* seqused_k,
+                         const pa_tensor* block_table, int32_t max_seqlen_q, int32_t max_seqlen_k,
+                         float softmax_scale, int32_t causal, void* stream) {
+  return run(q, k_cache, v_cache, out, cu_seqlens_q, seqused_k, block_table, max_seqlen_q,
+             max_seqlen_k, softmax_scale, causal, nullptr, true, nullptr, 0, stream);
+}
+
+int pa_unified_attention_ex(const pa_tensor* q, const pa_tensor* k_cache, const pa_tensor* v_cache,
+                            pa_tensor* out, const pa_tensor* cu_seqlens_q,
+                            const pa_tensor* seqused_k, const pa_tensor* block_table,
+                            int32_t max_seqlen_q, int32_t max_seqlen_k, float softmax_scale,
+                            int32_t causal, const pa_options* opt, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+  return run(q, k_cache, v_cache, out, cu_seqlens_q, seqused_k, block_table, max_seqlen_q,
+             max_seqlen_k, softmax_scale, causal, opt, false, workspace, workspace_bytes, stream);
+}
+
+size_t pa_workspace_size(const pa_tensor* q, const pa_tensor* k_cache, const pa_tensor* v_cache,
+                         const pa_tensor* out, const pa_tensor* cu_seqlens_q,
+                         const pa_tensor* seqused_k, const pa_tensor* block_table,
+                         int32_t max_seqlen_q, int32_t max_seqlen_k, const pa_options* opt) {
+  g_last_error.clear();
+  Shapes s;
+  if (validate(q, k_cache, v_cache, out, cu_seqlens_q, seqused_k, block_table, max_seqlen_q,
+               max_seqlen_k, &s) != PA_OK)
+    return (size_t)-1;
+  if (s.T == 0 || s.S == 0) return 0;
+  bool have_dev = false;
+  const int ncu = device_cu_count(&have_dev);
+  Plan plan;
+  if (make_plan(s, max_seqlen_q, max_seqlen_k, opt, ncu, &plan) != PA_OK) return (size_t)-1;
+  return plan.ws_bytes;
+}
+
+int pa_plan_describe(const pa_tensor* q, const pa_tensor* k_cache, const pa_tensor* v_cache,
+                     const pa_tensor* out, const pa_tensor* cu_seqlens_q,
+                     const pa_tensor* seqused_k, const pa_tensor* block_table,
+                     int32_t max_seqlen_q, int32_t max_seqlen_k, const pa_options* opt,
+                     int32_t num_cus, pa_plan_info* info) {
+  g_last_error.clear();
+  if (!info) return fail(PA_ERR_NULL, "info is NULL");
+  Shapes s;
+  int rc = validate(q, k_cache, v_cache, out, cu_seqlens_q, seqused_k, block_table, max_seqlen_q,
+                    max_seqlen_k, &s);
+  if (rc != PA_OK) return rc;
+  bool have_dev = false;
+  const int ncu = num_cus > 0 ? num_cus : device_cu_count(&have_dev);
+  Plan plan;
+  rc = make_plan(s, max_seqlen_q, max_seqlen_k, opt, ncu, &plan);
+  if (rc != PA_OK) return rc;
+  if (s.T == 0 || s.S == 0) {
+    plan.nwg = 0;
+    plan.ws_bytes = 0;
+  }
+  info->tile_tokens = plan.tile_tokens;
+  info->tile_rows = plan.tile_rows;
+  info->num_slots = plan.num_slots;
+  info->slots_direct = plan.slots_direct;
+  info->num_splits = plan.n_split;
+  info->split_keys = plan.split_keys;
+  info->num_workgroups = plan.nwg;
+  info->workspace_bytes = (int64_t)plan.ws_bytes;
+  return PA_OK;
+}
+
+const char* pa_status_string(int status) {
+  switch (status) {
+    case PA_OK: return "ok";
+    case PA_ERR_NULL: return "null pointer";
+    case PA_ERR_DTYPE: return "wrong dtype";
+    case PA_ERR_SHAPE: return "inconsistent shape";
+    case PA_ERR_UNSUPPORTED: return "unsupported configuration";
+    case PA_ERR_ALIGN: return "misaligned pointer or stride";
+    case PA_ERR_ALIAS: return "output aliases an input";
+    case PA_ERR_WORKSPACE: return "workspace missing or too small";
+    case PA_ERR_CONTENT: return "invalid metadata contents";
+    case PA_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+const char* pa_last_error(void) { return g_last_error.c_str(); }
+
+int pa_version(void) { return PA_VERSION; }
+
+}  // extern "C"

@@ -1,0 +1,61 @@
+// Internal interface between the host library (pa_api.cpp) and the gfx950
+// kernels (pa_kernels.hip).  Not installed; not part of the C ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pa {
+
+constexpr int kBlockSize = 16;    // cache block size (tokens) the kernels are built for
+constexpr int kStageKeys = 64;    // keys staged in LDS per pipeline step
+constexpr int kThreads = 256;     // 4 wave64s per work-group
+constexpr int kTileRows = 64;     // packed rows of a wide query tile (16 per wave)
+constexpr int kNarrowRows = 16;   // rows of a narrow (decode) tile
+
+// Everything the forward kernel needs, by value.  Strides in elements.
+struct FwdParams {
+  const uint16_t* q;       // bf16 [T, Hq, d]
+  uint16_t* out;           // bf16 [T, Hq, d]
+  const uint16_t* k;       // bf16 [NB, B, Hkv, d]
+  const uint16_t* v;
+  const int32_t* cu_q;     // [S+1]
+  const int32_t* seq_k;    // [S]
+  const int32_t* bt;       // [S, bt_stride]
+  float* ws_o;             // fp32 [n_split, T, Hq, d]   (n_split > 1 only)
+  float* ws_lse;           // fp32 [n_split, T, Hq]      log2-domain lse
+  int64_t q_st, q_sh;      // q strides (token, head)
+  int64_t o_st, o_sh;      // out strides
+  int64_t kv_sb;           // cache stride between physical blocks
+  int32_t bt_stride;
+  int32_t num_seqs;
+  int32_t total_q;
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t tile_tokens;     // tokens per query tile
+  int32_t num_slots;       // query-tile slots
+  int32_t slots_direct;    // 1: slot index is the sequence index
+  int32_t n_split;
+  int32_t split_keys;      // multiple of kStageKeys
+  int32_t causal;
+  int32_t narrow_rows;     // tiles with at most this many packed rows take the narrow path
+  float scale_log2;        // softmax_scale * log2(e)
+};
+
+struct MergeParams {
+  const float* ws_o;
+  const float* ws_lse;
+  uint16_t* out;
+  int64_t o_st, o_sh;
+  int32_t total_q;
+  int32_t num_q_heads;
+  int32_t n_split;
+};
+
+// Launchers (pa_kernels.hip).  Return the hipError_t of the launch.
+hipError_t launch_fwd(const FwdParams& p, int head_dim, int group, int64_t num_workgroups,
+                      hipStream_t stream);
+hipError_t launch_merge(const MergeParams& p, int head_dim, hipStream_t stream);
+bool fwd_supported(int head_dim, int group);
+
+}  // namespace pa

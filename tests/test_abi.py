@@ -1,0 +1,202 @@
+"""C-ABI tests that need no GPU: the library loads, exports every function
+include/pa.h declares, and rejects every invalid descriptor with the right
+status before touching the device.  Descriptors here point at host memory,
+which validation never dereferences."""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+import torch
+
+import paged_kv_cache_unified_amd as pa
+from workloads import build_batch, make_workload
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "pa.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(pa_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_functions_are_exported():
+    names = declared_functions()
+    assert "pa_unified_attention" in names and "pa_unified_attention_ex" in names
+    for n in names:
+        assert hasattr(pa.lib, n), f"libpa.so does not export {n}"
+    assert set(names) == set(pa._SIGNATURES), "binding and header disagree"
+
+
+def test_version_and_status_strings():
+    assert pa.version() == 1
+    for code in range(-9, 1):
+        assert pa.lib.pa_status_string(code).decode()
+    assert pa.lib.pa_status_string(-100).decode() == "unknown status"
+
+
+def cpu_args(**over):
+    b = build_batch("abi", [1, 3, 2], [5, 17, 40], 8, 2, 128, True, seed=1)
+    a = dict(q=b.q, k_cache=b.k_cache, v_cache=b.v_cache, out=torch.empty_like(b.q),
+             cu_seqlens_q=b.cu_seqlens_q, seqused_k=b.seqused_k, block_table=b.block_table,
+             max_seqlen_q=b.max_seqlen_q, max_seqlen_k=b.max_seqlen_k,
+             softmax_scale=b.softmax_scale, causal=True)
+    a.update(over)
+    return a
+
+
+def call(a, opts=None):
+    ds = [pa.describe(a[n]) for n in ("q", "k_cache", "v_cache", "out", "cu_seqlens_q",
+                                       "seqused_k", "block_table")]
+    refs = [ctypes.byref(d) for d in ds]
+    if opts is None:
+        return pa.lib.pa_unified_attention(*refs, a["max_seqlen_q"], a["max_seqlen_k"],
+                                           a["softmax_scale"], int(a["causal"]), None)
+    return pa.lib.pa_unified_attention_ex(*refs, a["max_seqlen_q"], a["max_seqlen_k"],
+                                          a["softmax_scale"], int(a["causal"]),
+                                          ctypes.byref(opts), None, 0, None)
+
+
+def status_of(**over):
+    rc = call(cpu_args(**over))
+    return pa.STATUS[rc], pa.lib.pa_last_error().decode()
+
+
+def test_null_descriptor():
+    a = cpu_args()
+    ds = [pa.describe(a[n]) for n in ("q", "k_cache", "v_cache", "out", "cu_seqlens_q",
+                                       "seqused_k", "block_table")]
+    refs = [ctypes.byref(d) for d in ds]
+    refs[2] = None
+    rc = pa.lib.pa_unified_attention(*refs, 3, 40, 0.1, 1, None)
+    assert pa.STATUS[rc] == "PA_ERR_NULL"
+
+
+@pytest.mark.parametrize("over,expect", [
+    (dict(q=torch.zeros(6, 8, 128, dtype=torch.float16)), "PA_ERR_DTYPE"),
+    (dict(cu_seqlens_q=torch.tensor([0, 1, 4, 6], dtype=torch.int64)), "PA_ERR_DTYPE"),
+    (dict(out=torch.zeros(6, 8, 128, dtype=torch.float32)), "PA_ERR_DTYPE"),
+    (dict(q=torch.zeros(6, 8, 128, 1, dtype=torch.bfloat16)), "PA_ERR_SHAPE"),
+    (dict(out=torch.zeros(7, 8, 128, dtype=torch.bfloat16)), "PA_ERR_SHAPE"),
+    (dict(cu_seqlens_q=torch.tensor([0, 1, 6], dtype=torch.int32)), "PA_ERR_SHAPE"),
+    (dict(block_table=torch.zeros(2, 3, dtype=torch.int32)), "PA_ERR_SHAPE"),
+    (dict(max_seqlen_k=10_000), "PA_ERR_SHAPE"),
+    (dict(max_seqlen_q=-1), "PA_ERR_SHAPE"),
+])
+def test_shape_and_dtype_errors(over, expect):
+    st, msg = status_of(**over)
+    assert st == expect, msg
+    assert msg
+
+
+def test_head_ratio_and_unsupported():
+    b = cpu_args()
+    # Hq not a multiple of Hkv (= 2)
+    q = torch.zeros(6, 5, 128, dtype=torch.bfloat16)
+    assert status_of(q=q, out=torch.zeros_like(q))[0] == "PA_ERR_SHAPE"
+    # G = 3 is a valid ratio but not built
+    k = torch.zeros(b["k_cache"].shape[0], 16, 2, 128, dtype=torch.bfloat16)
+    q = torch.zeros(6, 6, 128, dtype=torch.bfloat16)
+    assert status_of(q=q, out=torch.zeros_like(q), k_cache=k, v_cache=k.clone())[0] == "PA_ERR_UNSUPPORTED"
+    # head_dim 96
+    q = torch.zeros(6, 8, 96, dtype=torch.bfloat16)
+    k = torch.zeros(b["k_cache"].shape[0], 16, 2, 96, dtype=torch.bfloat16)
+    assert status_of(q=q, out=torch.zeros_like(q), k_cache=k, v_cache=k.clone())[0] == "PA_ERR_UNSUPPORTED"
+    # block size 32
+    k = torch.zeros(4, 32, 2, 128, dtype=torch.bfloat16)
+    assert status_of(k_cache=k, v_cache=k.clone())[0] == "PA_ERR_UNSUPPORTED"
+
+
+def test_strides_alignment_alias():
+    a = cpu_args()
+    # q with a non-unit innermost stride
+    big = torch.zeros(6, 8, 256, dtype=torch.bfloat16)
+    assert status_of(q=big[:, :, ::2])[0] == "PA_ERR_UNSUPPORTED"
+    # q token stride not a multiple of 8 elements
+    odd = torch.zeros(6 * 8 * 128 + 4, dtype=torch.bfloat16)[4:].view(6, 8, 128)
+    st, _ = status_of(q=odd)
+    assert st == "PA_ERR_ALIGN"
+    # out aliasing q
+    assert status_of(q=a["q"], out=a["q"])[0] == "PA_ERR_ALIAS"
+    kv = a["k_cache"].reshape(-1)[: 6 * 8 * 128].view(6, 8, 128)
+    assert status_of(k_cache=a["k_cache"], v_cache=a["v_cache"], out=kv)[0] == "PA_ERR_ALIAS"
+    # v with different strides than k
+    k = a["k_cache"]
+    vv = torch.zeros(k.shape[0] * 2, *k.shape[1:], dtype=torch.bfloat16)[::2]
+    assert status_of(v_cache=vv)[0] == "PA_ERR_SHAPE"
+    # non-contiguous cache interior
+    kk = torch.zeros(k.shape[0], 16, 4, 128, dtype=torch.bfloat16)[:, :, ::2]
+    assert status_of(k_cache=kk, v_cache=kk.clone())[0] in ("PA_ERR_UNSUPPORTED", "PA_ERR_SHAPE")
+
+
+def test_empty_batch_is_ok_without_device():
+    q = torch.zeros(0, 8, 128, dtype=torch.bfloat16)
+    a = cpu_args(q=q, out=torch.zeros_like(q), cu_seqlens_q=torch.zeros(1, dtype=torch.int32),
+                 seqused_k=torch.zeros(0, dtype=torch.int32),
+                 block_table=torch.zeros(0, 3, dtype=torch.int32), max_seqlen_q=0, max_seqlen_k=0)
+    assert call(a) == 0
+    # queries present but no sequences: inconsistent
+    a2 = cpu_args(cu_seqlens_q=torch.zeros(1, dtype=torch.int32),
+                  seqused_k=torch.zeros(0, dtype=torch.int32),
+                  block_table=torch.zeros(0, 3, dtype=torch.int32))
+    assert pa.STATUS[call(a2)] == "PA_ERR_SHAPE"
+
+
+def test_bad_options_and_workspace():
+    a = cpu_args()
+    assert pa.STATUS[call(a, pa.options(force_tile=7))] == "PA_ERR_UNSUPPORTED"
+    # a narrow tile holds at most 16 packed rows: 5 tokens * G 4 do not fit
+    assert pa.STATUS[call(dict(a, max_seqlen_q=5), pa.options(force_tile=1))] == "PA_ERR_UNSUPPORTED"
+    # a forced split needs a workspace; none given (contexts > 64 keys so 2 splits remain)
+    b = build_batch("ws", [1, 3, 2], [5, 170, 300], 8, 2, 128, True, seed=1)
+    a2 = dict(a, q=b.q, out=torch.empty_like(b.q), k_cache=b.k_cache, v_cache=b.v_cache,
+              cu_seqlens_q=b.cu_seqlens_q, seqused_k=b.seqused_k, block_table=b.block_table,
+              max_seqlen_k=300)
+    assert pa.STATUS[call(a2, pa.options(force_num_splits=2))] == "PA_ERR_WORKSPACE"
+
+
+def plan_of(b, **opt):
+    out = torch.empty_like(b.q)
+    return pa.plan_describe(b.q, b.k_cache, b.v_cache, out, b.cu_seqlens_q, b.seqused_k,
+                            b.block_table, b.max_seqlen_q, b.max_seqlen_k,
+                            opts=pa.options(**opt) if opt else None, num_cus=256)
+
+
+def test_plan_heuristic_on_workload_shapes():
+    # decode: one narrow tile per sequence, no split (2048 items fill the GPU)
+    b = build_batch("d", np.ones(256, int), np.full(256, 1050), 32, 8, 128, True, 2)
+    p = plan_of(b)
+    assert p["slots_direct"] == 1 and p["tile_tokens"] == 1 and p["num_splits"] == 1
+    assert p["num_workgroups"] == 256 * 8 and p["workspace_bytes"] == 0
+    # few long sequences: split keys
+    b = build_batch("l", np.ones(16, int), np.full(16, 2048), 32, 8, 128, True, 5)
+    p = plan_of(b)
+    assert p["num_splits"] > 1 and p["split_keys"] % 64 == 0
+    assert p["num_splits"] * p["split_keys"] >= 2048
+    assert p["workspace_bytes"] >= p["num_splits"] * 16 * 32 * 129 * 4
+    # prefill chunks: 64-row tiles (16 tokens at G = 4), slots bounded by T/Tq + S
+    b = build_batch("p", [512, 1, 300], [700, 90, 300], 32, 8, 128, True, 3)
+    p = plan_of(b)
+    assert p["tile_tokens"] == 16 and p["slots_direct"] == 0
+    assert p["num_slots"] == 813 // 16 + 3
+    # a forced split count is honoured up to one 64-key stage per split
+    p = plan_of(b, force_num_splits=3)
+    assert p["num_splits"] == 3 and p["split_keys"] == 256
+    p = plan_of(b, force_num_splits=1000)
+    assert p["split_keys"] == 64 and p["num_splits"] == 700 // 64 + 1
+
+
+def test_workspace_size_matches_plan():
+    b = build_batch("ws", [1, 5, 16], [70, 200, 400], 4, 2, 64, True, seed=1)
+    out = torch.empty_like(b.q)
+    o = pa.options(force_num_splits=2)
+    n = pa.workspace_size(b.q, b.k_cache, b.v_cache, out, b.cu_seqlens_q, b.seqused_k,
+                          b.block_table, b.max_seqlen_q, b.max_seqlen_k, o)
+    p = pa.plan_describe(b.q, b.k_cache, b.v_cache, out, b.cu_seqlens_q, b.seqused_k,
+                         b.block_table, b.max_seqlen_q, b.max_seqlen_k, o)
+    assert n == p["workspace_bytes"] > 0
+    assert pa.workspace_size(b.q, b.k_cache, b.v_cache, out, b.cu_seqlens_q, b.seqused_k,
+                             b.block_table, b.max_seqlen_q, b.max_seqlen_k) == 0

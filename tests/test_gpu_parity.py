@@ -1,0 +1,188 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
+
+Shapes sweep head counts, head_dim, causal mode, query lengths (0, 1, short,
+several tiles, ragged tails) and contexts in one process, so a kernel
+specialisation keyed on the wrong constants shows up.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import paged_kv_cache_unified_amd as pa
+from gpu_util import bits, check_close, full_parity, require_gpu, run_pa, say
+from workloads import build_batch, make_workload, repermute_pool
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+def test_tiny_workload():
+    require_gpu()
+    b = make_workload("tiny_mixed_3seq", device=DEV)
+    say("tiny_mixed_3seq")
+    out = run_pa(b)
+    torch.cuda.synchronize()
+    err, frob = full_parity(b, out, "tiny_mixed_3seq")
+    say(f"  max err {err:.2e} frob {frob:.2e}")
+
+
+SWEEP_HEADS = [(4, 2), (32, 8), (32, 4), (8, 8), (16, 1)]
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("heads", SWEEP_HEADS, ids=lambda h: f"hq{h[0]}_hkv{h[1]}")
+@pytest.mark.parametrize("causal", [True, False], ids=["causal", "noncausal"])
+def test_random_sweep(d, heads, causal):
+    require_gpu()
+    hq, hkv = heads
+    rng = np.random.default_rng(1000 + 7 * d + hq + 3 * hkv + int(causal))
+    q_lens = np.array([0, 1, 2, 5, 16, 17, 33, 1, 64, 65, 3, 1])
+    # contexts from q_len up to ~600, a few with q_len > ctx for the causal case
+    k_lens = np.array([max(int(x), int(ql)) for x, ql in
+                       zip(rng.integers(1, 600, size=len(q_lens)), q_lens)])
+    k_lens[1] = 1
+    if causal:
+        k_lens[3] = 3          # 5 queries over 3 keys: first two rows have no key
+    b = build_batch("sweep", q_lens, k_lens, hq, hkv, d, causal, seed=int(rng.integers(1 << 30)),
+                    device=DEV)
+    say(f"sweep d={d} hq={hq} hkv={hkv} causal={causal}")
+    out = run_pa(b)
+    torch.cuda.synchronize()
+    full_parity(b, out, f"sweep d{d} {heads} causal={causal}")
+
+
+@pytest.mark.parametrize("splits", [1, 2, 3, 7, 1000])
+def test_forced_splits(splits):
+    require_gpu()
+    b = build_batch("split", [1, 1, 4, 17, 1, 40], [700, 129, 300, 1000, 64, 40], 32, 8, 128,
+                    True, seed=77, device=DEV)
+    say(f"forced splits {splits}")
+    out = run_pa(b, opts=pa.options(force_num_splits=splits))
+    torch.cuda.synchronize()
+    full_parity(b, out, f"splits={splits}")
+
+
+@pytest.mark.parametrize("tile", [1, 2])
+def test_forced_tiles_on_decode(tile):
+    require_gpu()
+    b = build_batch("tiles", [1, 2, 1, 3], [300, 17, 1, 64], 16, 4, 128, True, seed=78,
+                    device=DEV)
+    say(f"forced tile {tile}")
+    out = run_pa(b, opts=pa.options(force_tile=tile))
+    torch.cuda.synchronize()
+    full_parity(b, out, f"tile={tile}")
+
+
+def test_block_permutation_bit_exact():
+    require_gpu()
+    b = build_batch("perm", [1, 5, 16, 3, 100], [7, 20, 40, 300, 250], 32, 8, 128, True,
+                    seed=79, device=DEV)
+    b2 = repermute_pool(b, seed=80)
+    say("block permutation")
+    o1 = run_pa(b)
+    o2 = run_pa(b2)
+    torch.cuda.synchronize()
+    assert torch.equal(bits(o1), bits(o2))
+    full_parity(b, o1, "perm")
+
+
+def test_nan_poison_bit_exact():
+    require_gpu()
+    b = build_batch("poison", [1, 5, 16, 3, 1], [7, 20, 40, 300, 33], 8, 2, 64, True,
+                    seed=81, device=DEV)
+    clean = build_batch("poison", [1, 5, 16, 3, 1], [7, 20, 40, 300, 33], 8, 2, 64, True,
+                        seed=81, device=DEV, poison=False)
+    # same values where owned; zero everywhere else
+    nan_mask = torch.isnan(b.k_cache)
+    clean.k_cache = torch.where(nan_mask, torch.zeros_like(b.k_cache), b.k_cache)
+    clean.v_cache = torch.where(torch.isnan(b.v_cache), torch.zeros_like(b.v_cache), b.v_cache)
+    say("nan poison")
+    o1 = run_pa(b)
+    o2 = run_pa(clean)
+    torch.cuda.synchronize()
+    assert torch.isfinite(o1.float()).all()
+    assert torch.equal(bits(o1), bits(o2))
+
+
+def test_single_key_is_exact():
+    require_gpu()
+    for causal in (True, False):
+        b = build_batch("one", [1, 1, 7], [1, 1, 7], 8, 2, 128, causal, seed=82, device=DEV)
+        say(f"single key causal={causal}")
+        out = run_pa(b)
+        torch.cuda.synchronize()
+        for s in range(2):
+            v0 = b.v_cache[b.block_table[s, 0], 0]                 # [Hkv, d]
+            assert torch.equal(bits(out[s]), bits(v0.repeat_interleave(4, dim=0)))
+        if causal:   # row 0 of a fresh causal prefill sees key 0 only
+            v0 = b.v_cache[b.block_table[2, 0], 0]
+            assert torch.equal(bits(out[2]), bits(v0.repeat_interleave(4, dim=0)))
+
+
+def test_deterministic_runs():
+    require_gpu()
+    b = build_batch("det", [1, 33, 1, 200], [2000, 500, 900, 1000], 32, 8, 128, True,
+                    seed=83, device=DEV)
+    say("determinism")
+    outs = [run_pa(b) for _ in range(3)]
+    outs.append(run_pa(b, opts=pa.options(force_num_splits=5)))
+    outs.append(run_pa(b, opts=pa.options(force_num_splits=5)))
+    torch.cuda.synchronize()
+    assert torch.equal(bits(outs[0]), bits(outs[1])) and torch.equal(bits(outs[0]), bits(outs[2]))
+    assert torch.equal(bits(outs[3]), bits(outs[4]))
+
+
+def test_empty_rows_are_zero():
+    require_gpu()
+    b = build_batch("empty", [2, 0, 3, 1, 4], [0, 5, 2, 4, 0], 8, 2, 64, True, seed=84,
+                    device=DEV)
+    say("empty rows")
+    out = run_pa(b)
+    torch.cuda.synchronize()
+    assert torch.all(out[0:2] == 0) and torch.all(out[2] == 0)
+    assert torch.all(out[6:10] == 0)
+    full_parity(b, out, "empty rows")
+
+
+def test_shared_prefix_blocks():
+    """Block ids repeated across sequences (a shared, cached prefix)."""
+    require_gpu()
+    b = build_batch("share", [1, 3, 1], [100, 120, 64], 32, 8, 128, True, seed=85, device=DEV)
+    t = b.block_table.clone()
+    t[1, :4] = t[0, :4]     # sequence 1 reuses sequence 0's first 64 keys
+    t[2, :4] = t[0, :4]
+    b.block_table = t
+    say("shared prefix")
+    out = run_pa(b)
+    torch.cuda.synchronize()
+    full_parity(b, out, "shared prefix")
+
+
+def test_strided_views_and_side_stream():
+    """q/out as head-slices of wider buffers; launch on a non-default stream."""
+    require_gpu()
+    b = build_batch("strided", [1, 17, 4], [50, 80, 300], 8, 2, 128, True, seed=86, device=DEV)
+    wide = torch.zeros(b.total_q, 12, 128, dtype=torch.bfloat16, device=DEV)
+    wide[:, 2:10] = b.q
+    b.q = wide[:, 2:10]
+    out_wide = torch.full((b.total_q, 10, 128), float("nan"), dtype=torch.bfloat16, device=DEV)
+    out = out_wide[:, 1:9]
+    s = torch.cuda.Stream()
+    say("strided + side stream")
+    run_pa(b, out=out, stream=s)
+    s.synchronize()
+    full_parity(b, out, "strided")
+    assert torch.isnan(out_wide[:, 0].float()).all() and torch.isnan(out_wide[:, 9].float()).all()
+
+
+def test_check_contents_rejects_bad_metadata():
+    require_gpu()
+    b = build_batch("bad", [1, 2], [20, 40], 8, 2, 64, True, seed=87, device=DEV)
+    t = b.block_table.clone()
+    t[1, 1] = b.num_blocks + 5
+    b.block_table = t
+    out = torch.zeros_like(b.q)
+    with pytest.raises(pa.PaError, match="PA_ERR_CONTENT"):
+        pa.unified_attention(*b.args(out), opts=pa.options(check_contents=True))
