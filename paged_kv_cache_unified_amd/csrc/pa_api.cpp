@@ -35,6 +35,8 @@ struct Shapes {
 
 struct Plan {
   int32_t tile_tokens, tile_rows, num_slots, slots_direct, n_split, split_keys;
+  bool wide;  // launch the specialization with the wide-tile path
+  int64_t num_items;
   int64_t nwg;
   size_t ws_bytes;
   size_t ws_lse_offset;
@@ -190,7 +192,9 @@ int make_plan(const Shapes& s, int32_t max_q, int32_t max_k, const pa_options* o
     p.tile_tokens = (int32_t)mq;
     p.slots_direct = 1;
     p.num_slots = (int32_t)s.S;
+    p.wide = false;
   } else {
+    p.wide = true;
     p.tile_tokens = (int32_t)(pa::kTileRows / G);
     if (mq <= p.tile_tokens) {
       p.slots_direct = 1;
@@ -216,11 +220,13 @@ int make_plan(const Shapes& s, int32_t max_q, int32_t max_k, const pa_options* o
   n_split = std::max<int64_t>(n_split, 1);
   int64_t split_keys = (mk + n_split - 1) / n_split;
   split_keys = (split_keys + pa::kStageKeys - 1) / pa::kStageKeys * pa::kStageKeys;
+  split_keys = std::min<int64_t>(split_keys, pa::kMaxSplitKeys);
   n_split = (mk + split_keys - 1) / split_keys;
   p.n_split = (int32_t)n_split;
   p.split_keys = (int32_t)split_keys;
-  p.nwg = items * n_split;
-  if (p.nwg > 0xffffffffLL) return fail(PA_ERR_UNSUPPORTED, "grid too large");
+  p.num_items = items * n_split;
+  p.nwg = (p.num_items + 7) / 8 * 8;
+  if (p.num_items > kMaxInt32) return fail(PA_ERR_UNSUPPORTED, "grid too large");
   if (n_split > 1) {
     const size_t rows = (size_t)s.T * (size_t)s.Hq * (size_t)n_split;
     p.ws_lse_offset = align256(rows * (size_t)s.D * sizeof(float));
@@ -381,11 +387,14 @@ int run(const pa_tensor* q, const pa_tensor* k, const pa_tensor* v, pa_tensor* o
   p.slots_direct = plan.slots_direct;
   p.n_split = plan.n_split;
   p.split_keys = plan.split_keys;
+  p.num_items = (int32_t)plan.num_items;
+  p.items_per_xcd = (int32_t)(plan.nwg / 8);
+  p.kv_major = plan.wide ? 1 : 0;
   p.causal = causal ? 1 : 0;
   p.narrow_rows = (opt && opt->force_tile == 2) ? 0 : pa::kNarrowRows;
   p.scale_log2 = (float)((double)scale * 1.4426950408889634);
   if (plan.nwg > 0) {
-    hipError_t e = pa::launch_fwd(p, (int)s.D, (int)s.G, plan.nwg, stream);
+    hipError_t e = pa::launch_fwd(p, (int)s.D, (int)s.G, plan.wide, plan.nwg, stream);
     if (e != hipSuccess) return fail(PA_ERR_HIP, "forward launch: %s", hipGetErrorString(e));
   }
   if (plan.n_split > 1) {

@@ -12,6 +12,7 @@ constexpr int kStageKeys = 64;    // keys staged in LDS per pipeline step
 constexpr int kThreads = 256;     // 4 wave64s per work-group
 constexpr int kTileRows = 64;     // packed rows of a wide query tile (16 per wave)
 constexpr int kNarrowRows = 16;   // rows of a narrow (decode) tile
+constexpr int kMaxSplitKeys = 4096;  // keys per split: at most 64 blocks per wave (narrow)
 
 // Everything the forward kernel needs, by value.  Strides in elements.
 struct FwdParams {
@@ -37,6 +38,9 @@ struct FwdParams {
   int32_t slots_direct;    // 1: slot index is the sequence index
   int32_t n_split;
   int32_t split_keys;      // multiple of kStageKeys
+  int32_t num_items;       // num_slots * num_kv_heads * n_split
+  int32_t items_per_xcd;   // ceil(num_items / 8): contiguous item range per XCD
+  int32_t kv_major;        // item order: 1 = (kv-head, slot, split), 0 = (slot, kv-head, split)
   int32_t causal;
   int32_t narrow_rows;     // tiles with at most this many packed rows take the narrow path
   float scale_log2;        // softmax_scale * log2(e)
@@ -53,8 +57,9 @@ struct MergeParams {
 };
 
 // Launchers (pa_kernels.hip).  Return the hipError_t of the launch.
-hipError_t launch_fwd(const FwdParams& p, int head_dim, int group, int64_t num_workgroups,
-                      hipStream_t stream);
+// wide = false launches the narrow-only specialization (every tile <= 16 rows).
+hipError_t launch_fwd(const FwdParams& p, int head_dim, int group, bool wide,
+                      int64_t num_workgroups, hipStream_t stream);
 hipError_t launch_merge(const MergeParams& p, int head_dim, hipStream_t stream);
 bool fwd_supported(int head_dim, int group);
 

@@ -98,37 +98,36 @@ struct Layout {
   static __device__ __forceinline__ int v_chunk(int key, int c) { return key * CPR + (c ^ v_swz(key)); }
 };
 
-template <int D, int G>
-__global__ __launch_bounds__(kThreads) void pa_fwd_kernel(FwdParams p) {
-  using Lay = Layout<D>;
-  constexpr int CPR = Lay::CPR;
-  constexpr int BLK_BYTES = Lay::BLK_BYTES;
-  constexpr int NBS = kStageKeys / kBlockSize;           // cache blocks per stage
-  constexpr int HALF_BYTES = NBS * BLK_BYTES;            // K (or V) part of a stage
-  constexpr int STAGE_BYTES = 2 * HALF_BYTES;
-  constexpr int CPT = NBS * kBlockSize * CPR / kThreads; // chunks per thread per tensor
-  constexpr int KS = D / 32;                             // QK^T contraction steps
-  constexpr int DT = D / 16;                             // 16-wide output d tiles
-  static_assert(CPT * kThreads == NBS * kBlockSize * CPR, "stage must split evenly");
-  static_assert(2 * STAGE_BYTES >= (2 * 64 + 4 * D * 16) * 4, "merge scratch must fit");
+// One work item: (query tile, kv-head, key split) and the key range it covers.
+struct Item {
+  int s, kvh, sigma;
+  int q0, q_len, tok0, n_tok, rows;
+  int L, diag;        // context length; causal: token t sees keys < diag + t + 1
+  int kbeg, kend;     // keys [kbeg, kend) of this split that some row may need
+  int kmin;           // smallest per-row key limit within the tile
+};
 
-  __shared__ __attribute__((aligned(16))) unsigned char smem[2 * STAGE_BYTES];
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int h4 = lane >> 4;     // lane group: k-chunk of MFMA operands
-  const int l16 = lane & 15;    // column (packed row) of MFMA outputs
-
-  // ---------------- work item -------------------------------------------
-  int bid = blockIdx.x;
-  const int sigma = bid % p.n_split;
-  bid /= p.n_split;
-  const int kvh = bid % p.num_kv_heads;
-  const int slot = bid / p.num_kv_heads;
-  int s, tile;
+template <int G>
+__device__ __forceinline__ bool decode_item(const FwdParams& p, Item& it) {
+  // Work-groups are dispatched round-robin over the 8 XCDs (XCD = id % 8);
+  // give each XCD a contiguous range of items so items that share data
+  // (the q-tiles of one kv-head's context, or the kv-heads of one sequence's
+  // blocks) run close in time on the same L2.
+  const int item = (blockIdx.x & 7) * p.items_per_xcd + (blockIdx.x >> 3);
+  if (item >= p.num_items) return false;
+  it.sigma = item % p.n_split;
+  const int rest = item / p.n_split;
+  int slot;
+  if (p.kv_major) {
+    slot = rest % p.num_slots;
+    it.kvh = rest / p.num_slots;
+  } else {
+    it.kvh = rest % p.num_kv_heads;
+    slot = rest / p.num_kv_heads;
+  }
+  int tile;
   if (p.slots_direct) {
-    s = slot;
+    it.s = slot;
     tile = 0;
   } else {
     // sequence s owns slots [cu[s]/Tq + s, cu[s+1]/Tq + s + 1)
@@ -137,49 +136,321 @@ __global__ __launch_bounds__(kThreads) void pa_fwd_kernel(FwdParams p) {
       const int mid = (lo + hi + 1) >> 1;
       if (p.cu_q[mid] / p.tile_tokens + mid <= slot) lo = mid; else hi = mid - 1;
     }
-    s = lo;
-    tile = slot - (p.cu_q[s] / p.tile_tokens + s);
+    it.s = lo;
+    tile = slot - (p.cu_q[lo] / p.tile_tokens + lo);
   }
-  const int q0 = p.cu_q[s];
-  const int q_len = p.cu_q[s + 1] - q0;
-  const int tok0 = tile * p.tile_tokens;
-  if (tok0 >= q_len) return;                       // empty slot (whole work-group)
-  const int n_tok = min(p.tile_tokens, q_len - tok0);
-  const int rows = n_tok * G;
-  const int L = p.seq_k[s];
-  const int diag = L - q_len;                      // causal: token t sees keys < diag + t + 1
-  const int k_need = p.causal ? min(L, diag + tok0 + n_tok) : L;
-  const int kbeg = sigma * p.split_keys;
-  const int kend = min(k_need, kbeg + p.split_keys);      // exclusive
-  const int kmin = p.causal ? min(kend, diag + tok0 + 1) : kend;  // smallest row limit
-  const bool narrow = rows <= p.narrow_rows;
+  it.q0 = p.cu_q[it.s];
+  it.q_len = p.cu_q[it.s + 1] - it.q0;
+  it.tok0 = tile * p.tile_tokens;
+  if (it.tok0 >= it.q_len) return false;            // empty slot (whole work-group)
+  it.n_tok = min(p.tile_tokens, it.q_len - it.tok0);
+  it.rows = it.n_tok * G;
+  it.L = p.seq_k[it.s];
+  it.diag = it.L - it.q_len;
+  const int k_need = p.causal ? min(it.L, it.diag + it.tok0 + it.n_tok) : it.L;
+  it.kbeg = it.sigma * p.split_keys;
+  it.kend = min(k_need, it.kbeg + p.split_keys);
+  it.kmin = p.causal ? min(it.kend, it.diag + it.tok0 + 1) : it.kend;
+  return true;
+}
 
-  // ---------------- Q^T operand of this lane's packed row -----------------
-  const int row = narrow ? l16 : wave * 16 + l16;
+// Q^T operand (B of S^T = K Q^T) for packed row `row` of the tile: lane group
+// h4 holds d = 32 ks + 8 h4 .. +7 for each contraction step ks.
+template <int D, int G>
+__device__ __forceinline__ void load_q(const FwdParams& p, const Item& it, int row, int h4,
+                                       bf16x8 (&qB)[D / 32]) {
+  const bool ok = row < it.rows;
   const int t_in = row / G;
-  const int head = kvh * G + row % G;
-  const bool row_ok = row < rows;
-  const int klim = p.causal ? min(kend, diag + tok0 + t_in + 1) : kend;
-  bf16x8 qB[KS];
-  {
-    const uint16_t* qp = p.q + (int64_t)(q0 + tok0 + (row_ok ? t_in : 0)) * p.q_st +
-                         (int64_t)head * p.q_sh + 8 * h4;
+  const int head = it.kvh * G + row % G;
+  const uint16_t* qp = p.q + (int64_t)(it.q0 + it.tok0 + (ok ? t_in : 0)) * p.q_st +
+                       (int64_t)head * p.q_sh + 8 * h4;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (row_ok) v = *reinterpret_cast<const u32x4*>(qp + 32 * ks);
-      qB[ks] = __builtin_bit_cast(bf16x8, v);
+  for (int ks = 0; ks < D / 32; ++ks) {
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (ok) v = *reinterpret_cast<const u32x4*>(qp + 32 * ks);
+    qB[ks] = __builtin_bit_cast(bf16x8, v);
+  }
+}
+
+// Shared-memory budgets.
+template <int D>
+struct NarrowCfg {
+  static constexpr int BLK_BYTES = kBlockSize * D * 2;
+  static constexpr int VBUF_BYTES = 4 * 2 * BLK_BYTES;            // 2 V buffers per wave
+  static constexpr int RED_STRIDE = D + 4;                        // floats per merged row
+  static constexpr int RED_BYTES = (2 * 64 + 4 * 16 * RED_STRIDE) * 4;
+  static constexpr int SMEM = VBUF_BYTES > RED_BYTES ? VBUF_BYTES : RED_BYTES;
+};
+template <int D>
+struct WideCfg {
+  static constexpr int BLK_BYTES = kBlockSize * D * 2;
+  static constexpr int NBS = kStageKeys / kBlockSize;
+  static constexpr int HALF_BYTES = NBS * BLK_BYTES;
+  static constexpr int STAGE_BYTES = 2 * HALF_BYTES;
+  static constexpr int IDS_OFFSET = 2 * STAGE_BYTES;
+  static constexpr int SMEM_RAW = IDS_OFFSET + (kMaxSplitKeys / kBlockSize) * 4;
+  static constexpr int SMEM = SMEM_RAW > NarrowCfg<D>::SMEM ? SMEM_RAW : NarrowCfg<D>::SMEM;
+};
+
+// ---------------------------------------------------------------------------
+// Narrow tiles (<= 16 packed rows: decode steps, short chunks).
+//
+// All 16 columns of one MFMA tile hold the tile's rows in every wave; wave w
+// owns the item's cache blocks w, w+4, w+8, ... and streams them on its own,
+// with no work-group barrier until the final merge.  Each wave keeps a ring of
+// P blocks in flight in registers: K lands directly in the A-operand layout of
+// S^T = K Q^T (lane: key l16, d-chunk h4 + 4 ks), V in natural row order and
+// goes through a wave-private LDS buffer for the transpose read.  The block
+// ids of the wave's (at most 64) blocks are fetched once into one VGPR and
+// read per block with readlane, so no KV load waits on a block-table load.
+// ---------------------------------------------------------------------------
+template <int D, int G, int P>
+__device__ __forceinline__ void attend_narrow(const FwdParams& p, const Item& it,
+                                              unsigned char* smem) {
+  using Lay = Layout<D>;
+  using Cfg = NarrowCfg<D>;
+  constexpr int CPR = Lay::CPR;
+  constexpr int BLK_BYTES = Lay::BLK_BYTES;
+  constexpr int KS = D / 32;
+  constexpr int DT = D / 16;
+  constexpr int VPL = kBlockSize * CPR / 64;      // V chunks per lane per block
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int h4 = lane >> 4;
+  const int l16 = lane & 15;
+
+  bf16x8 qB[KS];
+  load_q<D, G>(p, it, l16, h4, qB);
+  const int t_in = l16 / G;
+  const int klim = p.causal ? min(it.kend, it.diag + it.tok0 + t_in + 1) : it.kend;
+
+  const int blk0 = it.kbeg / kBlockSize;
+  const int nblk = it.kend > it.kbeg ? (it.kend + kBlockSize - 1) / kBlockSize - blk0 : 0;
+  const int nb = nblk > wave ? (nblk - wave + 3) / 4 : 0;     // <= 64: split_keys <= 4096
+  const int32_t* btrow = p.bt + (int64_t)it.s * p.bt_stride;
+  int ids = 0;
+  if (lane < nb) ids = btrow[blk0 + wave + 4 * lane];
+
+  const int slot_stride = p.num_kv_heads * D;
+  const uint16_t* kbase = p.k + it.kvh * D;
+  const uint16_t* vbase = p.v + it.kvh * D;
+  const int koff = l16 * slot_stride + 8 * h4;
+  int voff[VPL], vlds[VPL];
+#pragma unroll
+  for (int u = 0; u < VPL; ++u) {
+    const int c = lane + 64 * u;
+    const int key = c / CPR, dc = c % CPR;
+    voff[u] = key * slot_stride + dc * 8;
+    vlds[u] = Lay::v_chunk(key, dc) * 16;
+  }
+
+  u32x4 kst[P][KS];
+  u32x4 vst[P][VPL];
+#pragma unroll
+  for (int j = 0; j < P; ++j) {
+    if (j < nb) {
+      const int64_t boff = (int64_t)__builtin_amdgcn_readlane(ids, j) * p.kv_sb;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        kst[j][ks] = *reinterpret_cast<const u32x4*>(kbase + boff + koff + 32 * ks);
+#pragma unroll
+      for (int u = 0; u < VPL; ++u)
+        vst[j][u] = *reinterpret_cast<const u32x4*>(vbase + boff + voff[u]);
     }
   }
 
-  // ---------------- KV stream ------------------------------------------
-  const int nblk = (kend + kBlockSize - 1) / kBlockSize;   // blocks the item may read
+  f32x4 acc[DT];
+#pragma unroll
+  for (int i = 0; i < DT; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m = kNegInf, l = 0.f;
+  unsigned char* vbuf0 = smem + wave * 2 * BLK_BYTES;
+  const int tr_key = 4 * h4 + (l16 >> 2);
+  const int tr_c_lo = (l16 & 3) >> 1;
+  const int tr_half = (l16 & 1) * 8;
+
+  for (int i0 = 0; i0 < nb; i0 += P) {
+#pragma unroll
+    for (int j = 0; j < P; ++j) {
+      const int i = i0 + j;
+      if (i < nb) {
+        const int kb = (blk0 + wave + 4 * i) * kBlockSize;
+        unsigned char* vbuf = vbuf0 + (i & 1) * BLK_BYTES;
+#pragma unroll
+        for (int u = 0; u < VPL; ++u) *reinterpret_cast<u32x4*>(vbuf + vlds[u]) = vst[j][u];
+        f32x4 sc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+          sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kst[j][ks]),
+                                                       qB[ks], sc, 0, 0, 0);
+        // refill this ring slot with block i + P
+        if (i + P < nb) {
+          const int64_t boff = (int64_t)__builtin_amdgcn_readlane(ids, i + P) * p.kv_sb;
+#pragma unroll
+          for (int ks = 0; ks < KS; ++ks)
+            kst[j][ks] = *reinterpret_cast<const u32x4*>(kbase + boff + koff + 32 * ks);
+#pragma unroll
+          for (int u = 0; u < VPL; ++u)
+            vst[j][u] = *reinterpret_cast<const u32x4*>(vbase + boff + voff[u]);
+        }
+        const bool need_mask = kb + kBlockSize > it.kmin;
+        float x[4];
+        float mx = kNegInf;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          x[r] = sc[r] * p.scale_log2;
+          if (need_mask && kb + 4 * h4 + r >= klim) x[r] = kNegInf;
+          mx = fmaxf(mx, x[r]);
+        }
+        mx = max_across_groups(mx);
+        const float m_new = fmaxf(m, mx);
+        const float m_use = m_new == kNegInf ? 0.f : m_new;
+        const float alpha = exp2_fast(m - m_use);
+        float pr[4], rs = 0.f;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          pr[r] = exp2_fast(x[r] - m_use);
+          rs += pr[r];
+        }
+        l = l * alpha + rs;
+        m = m_new;
+        u32x2 pk = {pack_bf16x2(pr[0], pr[1]), pack_bf16x2(pr[2], pr[3])};
+        const i16x4 pB = __builtin_bit_cast(i16x4, pk);
+        const bool vmask = kb + kBlockSize > it.kend;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+          const unsigned char* a =
+              vbuf + Lay::v_chunk(tr_key, 2 * dt + tr_c_lo) * 16 + tr_half;
+          i16x4 va = __builtin_bit_cast(
+              i16x4, __builtin_amdgcn_ds_read_tr16_b64_v4bf16((PA_LDS bf16x4*)(a)));
+          if (vmask) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              if (kb + 4 * h4 + e >= it.kend) va[e] = 0;
+          }
+          acc[dt] *= alpha;
+          acc[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pB, acc[dt], 0, 0, 0);
+        }
+      }
+    }
+  }
+
+  // merge the four waves' states of the same 16 rows
+  l = sum_across_groups(l);
+  __syncthreads();                        // every wave is done with its V buffers
+  float* red_m = reinterpret_cast<float*>(smem);
+  float* red_l = red_m + 64;
+  float* red_o = red_m + 128;             // [wave][row][RED_STRIDE]
+  constexpr int RS = Cfg::RED_STRIDE;
+  if (h4 == 0) {
+    red_m[wave * 16 + l16] = m;
+    red_l[wave * 16 + l16] = l;
+  }
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+    *reinterpret_cast<f32x4*>(red_o + (wave * 16 + l16) * RS + 16 * dt + 4 * h4) = acc[dt];
+  __syncthreads();
+
+  constexpr int DPER = D / 16;            // d values per thread (16 threads per row)
+  const int n = tid >> 4;
+  const int d0 = (tid & 15) * DPER;
+  if (n >= it.rows) return;
+  float mw[4], M = kNegInf;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    mw[w] = red_m[w * 16 + n];
+    M = fmaxf(M, mw[w]);
+  }
+  const float M_use = M == kNegInf ? 0.f : M;
+  float wt[4], Ls = 0.f;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    wt[w] = exp2_fast(mw[w] - M_use);
+    Ls += wt[w] * red_l[w * 16 + n];
+  }
+  const float inv = Ls > 0.f ? 1.f / Ls : 0.f;
+  float o[DPER];
+#pragma unroll
+  for (int e = 0; e < DPER; e += 4) {
+    f32x4 a = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int w = 0; w < 4; ++w)
+      a += wt[w] * *reinterpret_cast<const f32x4*>(red_o + (w * 16 + n) * RS + d0 + e);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) o[e + k] = a[k] * inv;
+  }
+  const int64_t tok = it.q0 + it.tok0 + n / G;
+  const int hn = it.kvh * G + n % G;
+  if (p.n_split == 1) {
+    uint16_t* op = p.out + tok * p.o_st + (int64_t)hn * p.o_sh + d0;
+    if constexpr (DPER == 8) {
+      u32x4 w = {pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]), pack_bf16x2(o[4], o[5]),
+                 pack_bf16x2(o[6], o[7])};
+      *reinterpret_cast<u32x4*>(op) = w;
+    } else {
+      u32x2 w = {pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
+      *reinterpret_cast<u32x2*>(op) = w;
+    }
+  } else {
+    const int64_t r = ((int64_t)it.sigma * p.total_q + tok) * p.num_q_heads + hn;
+    float* wp = p.ws_o + r * D + d0;
+#pragma unroll
+    for (int e = 0; e < DPER; e += 4)
+      *reinterpret_cast<f32x4*>(wp + e) = f32x4{o[e], o[e + 1], o[e + 2], o[e + 3]};
+    if ((tid & 15) == 0) p.ws_lse[r] = Ls > 0.f ? M + __log2f(Ls) : kNegInf;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Wide tiles (17..64 packed rows: prefill and longer chunks).
+//
+// Each wave owns 16 rows; the four waves sweep the same 64-key stages.  A
+// stage's 4 cache blocks of K and V are loaded row-contiguously into
+// registers while the previous stage is computed, then written into the other
+// of two LDS buffers (one barrier per stage).
+// ---------------------------------------------------------------------------
+template <int D, int G>
+__device__ __forceinline__ void attend_wide(const FwdParams& p, const Item& it,
+                                            unsigned char* smem) {
+  using Lay = Layout<D>;
+  using Cfg = WideCfg<D>;
+  constexpr int CPR = Lay::CPR;
+  constexpr int BLK_BYTES = Lay::BLK_BYTES;
+  constexpr int NBS = Cfg::NBS;
+  constexpr int HALF_BYTES = Cfg::HALF_BYTES;
+  constexpr int STAGE_BYTES = Cfg::STAGE_BYTES;
+  constexpr int CPT = NBS * kBlockSize * CPR / kThreads; // chunks per thread per tensor
+  constexpr int KS = D / 32;
+  constexpr int DT = D / 16;
+  static_assert(CPT * kThreads == NBS * kBlockSize * CPR, "stage must split evenly");
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int h4 = lane >> 4;
+  const int l16 = lane & 15;
+
+  const int row = wave * 16 + l16;
+  bf16x8 qB[KS];
+  load_q<D, G>(p, it, row, h4, qB);
+  const int t_in = row / G;
+  const int head = it.kvh * G + row % G;
+  const bool row_ok = row < it.rows;
+  const int klim = p.causal ? min(it.kend, it.diag + it.tok0 + t_in + 1) : it.kend;
+  const int kbeg = it.kbeg, kend = it.kend, kmin = it.kmin;
+
+  const int nblk = (kend + kBlockSize - 1) / kBlockSize;
   const int blk0 = kbeg / kBlockSize;
   const int n_stage = kend > kbeg ? (kend - kbeg + kStageKeys - 1) / kStageKeys : 0;
-  const int32_t* btrow = p.bt + (int64_t)s * p.bt_stride;
+  const int32_t* btrow = p.bt + (int64_t)it.s * p.bt_stride;
   const int64_t slot_stride = (int64_t)p.num_kv_heads * D;
-  const uint16_t* kbase = p.k + (int64_t)kvh * D;
-  const uint16_t* vbase = p.v + (int64_t)kvh * D;
+  const uint16_t* kbase = p.k + (int64_t)it.kvh * D;
+  const uint16_t* vbase = p.v + (int64_t)it.kvh * D;
+
+  // the item's block ids (at most kMaxSplitKeys / 16) staged once in LDS
+  int32_t* ids = reinterpret_cast<int32_t*>(smem + Cfg::IDS_OFFSET);
+  if (tid < nblk - blk0) ids[tid] = btrow[blk0 + tid];
+  __syncthreads();
 
   u32x4 kreg[CPT], vreg[CPT];
   auto load_stage = [&](int st) {
@@ -191,7 +462,7 @@ __global__ __launch_bounds__(kThreads) void pa_fwd_kernel(FwdParams p) {
       const int key = r / CPR, dc = r % CPR;
       const int jb = blk0 + st * NBS + blk;
       if (jb < nblk) {
-        const int64_t off = (int64_t)btrow[jb] * p.kv_sb + key * slot_stride + dc * 8;
+        const int64_t off = (int64_t)ids[jb - blk0] * p.kv_sb + key * slot_stride + dc * 8;
         kreg[u] = *reinterpret_cast<const u32x4*>(kbase + off);
         vreg[u] = *reinterpret_cast<const u32x4*>(vbase + off);
       }
@@ -217,31 +488,21 @@ __global__ __launch_bounds__(kThreads) void pa_fwd_kernel(FwdParams p) {
   f32x4 acc[DT];
 #pragma unroll
   for (int i = 0; i < DT; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m = kNegInf;   // running max of this lane's row (log2 domain), same in all groups
-  float l = 0.f;       // this lane's partial row sum (its own keys only)
-
-  // V^T operand address pieces for the transpose read: a lane group reads 4
-  // key rows x 16 d; lane j of the group points at row j/4, d 4*(j%4).
+  float m = kNegInf;
+  float l = 0.f;
   const int tr_key = 4 * h4 + (l16 >> 2);
   const int tr_c_lo = (l16 & 3) >> 1;
   const int tr_half = (l16 & 1) * 8;
-
   auto vt_read = [&](const unsigned char* vblk, int dt) -> i16x4 {
-    const int c = 2 * dt + tr_c_lo;
-    const unsigned char* a = vblk + Lay::v_chunk(tr_key, c) * 16 + tr_half;
-    bf16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((PA_LDS bf16x4*)(a));
-    return __builtin_bit_cast(i16x4, v);
+    const unsigned char* a = vblk + Lay::v_chunk(tr_key, 2 * dt + tr_c_lo) * 16 + tr_half;
+    return __builtin_bit_cast(i16x4,
+                              __builtin_amdgcn_ds_read_tr16_b64_v4bf16((PA_LDS bf16x4*)(a)));
   };
-  // zero V rows past the item's last key (tail slots may hold anything)
   auto vt_mask = [&](i16x4 v, int key_first) -> i16x4 {
 #pragma unroll
     for (int e = 0; e < 4; ++e)
       if (key_first + e >= kend) v[e] = 0;
     return v;
-  };
-  auto k_operand = [&](const unsigned char* kblk, int ks) -> bf16x8 {
-    const int dc = 4 * ks + h4;
-    return *reinterpret_cast<const bf16x8*>(kblk + Lay::k_chunk(l16, dc) * 16);
   };
 
   if (n_stage > 0) {
@@ -256,58 +517,18 @@ __global__ __launch_bounds__(kThreads) void pa_fwd_kernel(FwdParams p) {
     const unsigned char* Kb = smem + buf * STAGE_BYTES;
     const unsigned char* Vb = Kb + HALF_BYTES;
     const int kst = kbeg + st * kStageKeys;
-
-    if (narrow) {
-      // this wave's 16-key block of the stage
-      const int kb = kst + 16 * wave;
-      if (kb < kend) {
-        const unsigned char* kblk = Kb + wave * BLK_BYTES;
-        f32x4 sc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-          sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k_operand(kblk, ks), qB[ks], sc, 0, 0, 0);
-        const bool need_mask = kb + 16 > kmin;
-        float x[4];
-        float mx = kNegInf;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          x[r] = sc[r] * p.scale_log2;
-          if (need_mask && kb + 4 * h4 + r >= klim) x[r] = kNegInf;
-          mx = fmaxf(mx, x[r]);
-        }
-        mx = max_across_groups(mx);
-        const float m_new = fmaxf(m, mx);
-        const float m_use = m_new == kNegInf ? 0.f : m_new;
-        const float alpha = exp2_fast(m - m_use);
-        float pr[4], rs = 0.f;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          pr[r] = exp2_fast(x[r] - m_use);
-          rs += pr[r];
-        }
-        l = l * alpha + rs;
-        m = m_new;
-        u32x2 pk = {pack_bf16x2(pr[0], pr[1]), pack_bf16x2(pr[2], pr[3])};
-        const i16x4 pB = __builtin_bit_cast(i16x4, pk);
-        const unsigned char* vblk = Vb + wave * BLK_BYTES;
-        const bool vmask = kb + 16 > kend;
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) {
-          i16x4 va = vt_read(vblk, dt);
-          if (vmask) va = vt_mask(va, kb + 4 * h4);
-          acc[dt] *= alpha;
-          acc[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pB, acc[dt], 0, 0, 0);
-        }
-      }
-    } else if (wave * 16 < rows) {
+    if (wave * 16 < it.rows) {
       f32x4 sc[NBS];
 #pragma unroll
       for (int b = 0; b < NBS; ++b) {
         sc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
         const unsigned char* kblk = Kb + b * BLK_BYTES;
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-          sc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k_operand(kblk, ks), qB[ks], sc[b], 0, 0, 0);
+        for (int ks = 0; ks < KS; ++ks) {
+          const bf16x8 a = *reinterpret_cast<const bf16x8*>(
+              kblk + Lay::k_chunk(l16, 4 * ks + h4) * 16);
+          sc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qB[ks], sc[b], 0, 0, 0);
+        }
       }
       const bool need_mask = kst + kStageKeys > kmin;
       float mx = kNegInf;
@@ -362,97 +583,44 @@ __global__ __launch_bounds__(kThreads) void pa_fwd_kernel(FwdParams p) {
         }
       }
     }
-
     if (st + 1 < n_stage) store_stage(st + 1, buf ^ 1);
     __syncthreads();
   }
 
-  // ---------------- epilogue ----------------------------------------------
-  const bool split = p.n_split > 1;
-  const int Hq = p.num_q_heads;
   l = sum_across_groups(l);
-
-  if (!narrow) {
-    if (!row_ok) return;
-    const float inv = l > 0.f ? 1.f / l : 0.f;
-    const int64_t tok = q0 + tok0 + t_in;
-    if (!split) {
-      uint16_t* op = p.out + tok * p.o_st + (int64_t)head * p.o_sh + 4 * h4;
+  if (!row_ok) return;
+  const float inv = l > 0.f ? 1.f / l : 0.f;
+  const int64_t tok = it.q0 + it.tok0 + t_in;
+  if (p.n_split == 1) {
+    uint16_t* op = p.out + tok * p.o_st + (int64_t)head * p.o_sh + 4 * h4;
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        u32x2 w = {pack_bf16x2(acc[dt][0] * inv, acc[dt][1] * inv),
-                   pack_bf16x2(acc[dt][2] * inv, acc[dt][3] * inv)};
-        *reinterpret_cast<u32x2*>(op + 16 * dt) = w;
-      }
-    } else {
-      const int64_t r = ((int64_t)sigma * p.total_q + tok) * Hq + head;
-      float* wp = p.ws_o + r * D + 4 * h4;
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) *reinterpret_cast<f32x4*>(wp + 16 * dt) = acc[dt] * inv;
-      if (h4 == 0) p.ws_lse[r] = l > 0.f ? m + __log2f(l) : kNegInf;
-    }
-    return;
-  }
-
-  // narrow: merge the four waves' states for the same 16 rows through LDS
-  float* red_m = reinterpret_cast<float*>(smem);
-  float* red_l = red_m + 64;
-  float* red_o = red_m + 128;   // [wave][d][row]
-  if (h4 == 0) {
-    red_m[wave * 16 + l16] = m;
-    red_l[wave * 16 + l16] = l;
-  }
-#pragma unroll
-  for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) red_o[(wave * D + 16 * dt + 4 * h4 + r) * 16 + l16] = acc[dt][r];
-  __syncthreads();
-
-  constexpr int DPER = D / 16;          // d values per thread (16 threads per row)
-  const int n = tid >> 4;
-  const int d0 = (tid & 15) * DPER;
-  if (n >= rows) return;
-  float mw[4], M = kNegInf;
-#pragma unroll
-  for (int w = 0; w < 4; ++w) {
-    mw[w] = red_m[w * 16 + n];
-    M = fmaxf(M, mw[w]);
-  }
-  const float M_use = M == kNegInf ? 0.f : M;
-  float wt[4], Ls = 0.f;
-#pragma unroll
-  for (int w = 0; w < 4; ++w) {
-    wt[w] = exp2_fast(mw[w] - M_use);
-    Ls += wt[w] * red_l[w * 16 + n];
-  }
-  const float inv = Ls > 0.f ? 1.f / Ls : 0.f;
-  float o[DPER];
-#pragma unroll
-  for (int e = 0; e < DPER; ++e) {
-    float a = 0.f;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) a += wt[w] * red_o[(w * D + d0 + e) * 16 + n];
-    o[e] = a * inv;
-  }
-  const int64_t tok = q0 + tok0 + n / G;
-  const int hn = kvh * G + n % G;
-  if (!split) {
-    uint16_t* op = p.out + tok * p.o_st + (int64_t)hn * p.o_sh + d0;
-    if constexpr (DPER == 8) {
-      u32x4 w = {pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]), pack_bf16x2(o[4], o[5]),
-                 pack_bf16x2(o[6], o[7])};
-      *reinterpret_cast<u32x4*>(op) = w;
-    } else {
-      u32x2 w = {pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
-      *reinterpret_cast<u32x2*>(op) = w;
+    for (int dt = 0; dt < DT; ++dt) {
+      u32x2 w = {pack_bf16x2(acc[dt][0] * inv, acc[dt][1] * inv),
+                 pack_bf16x2(acc[dt][2] * inv, acc[dt][3] * inv)};
+      *reinterpret_cast<u32x2*>(op + 16 * dt) = w;
     }
   } else {
-    const int64_t r = ((int64_t)sigma * p.total_q + tok) * Hq + hn;
-    float* wp = p.ws_o + r * D + d0;
+    const int64_t r = ((int64_t)it.sigma * p.total_q + tok) * p.num_q_heads + head;
+    float* wp = p.ws_o + r * D + 4 * h4;
 #pragma unroll
-    for (int e = 0; e < DPER; e += 4)
-      *reinterpret_cast<f32x4*>(wp + e) = f32x4{o[e], o[e + 1], o[e + 2], o[e + 3]};
-    if ((tid & 15) == 0) p.ws_lse[r] = Ls > 0.f ? M + __log2f(Ls) : kNegInf;
+    for (int dt = 0; dt < DT; ++dt) *reinterpret_cast<f32x4*>(wp + 16 * dt) = acc[dt] * inv;
+    if (h4 == 0) p.ws_lse[r] = l > 0.f ? m + __log2f(l) : kNegInf;
+  }
+}
+
+constexpr int kRing = 2;   // cache blocks in flight per wave on the narrow path
+
+// WIDE = false: every tile of the batch is narrow (the plan guarantees it).
+template <int D, int G, bool WIDE>
+__global__ __launch_bounds__(kThreads) void pa_fwd_kernel(FwdParams p) {
+  constexpr int SMEM = WIDE ? WideCfg<D>::SMEM : NarrowCfg<D>::SMEM;
+  __shared__ __attribute__((aligned(16))) unsigned char smem[SMEM];
+  Item it;
+  if (!decode_item<G>(p, it)) return;
+  if (it.rows <= p.narrow_rows) {
+    attend_narrow<D, G, kRing>(p, it, smem);
+  } else {
+    if constexpr (WIDE) attend_wide<D, G>(p, it, smem);
   }
 }
 
@@ -489,19 +657,22 @@ __global__ __launch_bounds__(256) void pa_merge_kernel(MergeParams p) {
 }
 
 template <int D, int G>
-hipError_t launch_fwd_t(const FwdParams& p, int64_t nwg, hipStream_t stream) {
-  hipLaunchKernelGGL((pa_fwd_kernel<D, G>), dim3((unsigned)nwg), dim3(kThreads), 0, stream, p);
+hipError_t launch_fwd_t(const FwdParams& p, bool wide, int64_t nwg, hipStream_t stream) {
+  if (wide)
+    hipLaunchKernelGGL((pa_fwd_kernel<D, G, true>), dim3((unsigned)nwg), dim3(kThreads), 0, stream, p);
+  else
+    hipLaunchKernelGGL((pa_fwd_kernel<D, G, false>), dim3((unsigned)nwg), dim3(kThreads), 0, stream, p);
   return hipGetLastError();
 }
 
 template <int D>
-hipError_t launch_fwd_d(const FwdParams& p, int group, int64_t nwg, hipStream_t stream) {
+hipError_t launch_fwd_d(const FwdParams& p, int group, bool wide, int64_t nwg, hipStream_t stream) {
   switch (group) {
-    case 1: return launch_fwd_t<D, 1>(p, nwg, stream);
-    case 2: return launch_fwd_t<D, 2>(p, nwg, stream);
-    case 4: return launch_fwd_t<D, 4>(p, nwg, stream);
-    case 8: return launch_fwd_t<D, 8>(p, nwg, stream);
-    case 16: return launch_fwd_t<D, 16>(p, nwg, stream);
+    case 1: return launch_fwd_t<D, 1>(p, wide, nwg, stream);
+    case 2: return launch_fwd_t<D, 2>(p, wide, nwg, stream);
+    case 4: return launch_fwd_t<D, 4>(p, wide, nwg, stream);
+    case 8: return launch_fwd_t<D, 8>(p, wide, nwg, stream);
+    case 16: return launch_fwd_t<D, 16>(p, wide, nwg, stream);
     default: return hipErrorInvalidValue;
   }
 }
@@ -513,10 +684,10 @@ bool fwd_supported(int head_dim, int group) {
          (group == 1 || group == 2 || group == 4 || group == 8 || group == 16);
 }
 
-hipError_t launch_fwd(const FwdParams& p, int head_dim, int group, int64_t nwg,
+hipError_t launch_fwd(const FwdParams& p, int head_dim, int group, bool wide, int64_t nwg,
                       hipStream_t stream) {
-  if (head_dim == 128) return launch_fwd_d<128>(p, group, nwg, stream);
-  if (head_dim == 64) return launch_fwd_d<64>(p, group, nwg, stream);
+  if (head_dim == 128) return launch_fwd_d<128>(p, group, wide, nwg, stream);
+  if (head_dim == 64) return launch_fwd_d<64>(p, group, wide, nwg, stream);
   return hipErrorInvalidValue;
 }
 
