@@ -58,17 +58,93 @@ def source_hash():
     return h.hexdigest()[:16]
 
 
+def profile_path(workload):
+    return os.path.join(ROOT, "profiles", f"pa_fwd_{workload}.md")
+
+
 def traffic_record(workload):
-    """HBM bytes per launch from committed rocprofv3 counter runs, if they were
-    taken on the current kernel sources; else None."""
-    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    """HBM bytes per launch of the forward kernel from the committed rocprofv3
+    summary, if its counters were taken on the current kernel sources; else None."""
+    path = profile_path(workload)
     if not os.path.exists(path):
         return None
-    with open(path) as f:
-        rec = json.load(f)
+    text = open(path).read()
+    marker = "<!-- traffic "
+    if marker not in text:
+        return None
+    rec = json.loads(text.split(marker, 1)[1].split(" -->", 1)[0])
     if rec.get("source_hash") != source_hash():
         return None
-    return rec.get("bytes_per_launch")
+    return rec.get("traffic_bytes_per_launch")
+
+
+PROF_COMMANDS = """cd /tmp && export TMPDIR=/tmp
+rocprofv3 --kernel-trace --stats -d $OUT/trace_{w} -o run -- python3 $REPO/bench.py --workload {w} --steps 20 --warmup 5 --no-cpu-baseline --cold 0
+rocprofv3 --pmc FETCH_SIZE -d $OUT/pmc_FETCH_SIZE_{w} -o run -- python3 $REPO/bench.py --workload {w} --steps 3 --warmup 1 --no-cpu-baseline --cold 0
+rocprofv3 --pmc WRITE_SIZE -d $OUT/pmc_WRITE_SIZE_{w} -o run -- python3 $REPO/bench.py --workload {w} --steps 3 --warmup 1 --no-cpu-baseline --cold 0
+rocprofv3 --pmc FETCH_SIZE -d $OUT/pmc_FETCH_SIZE_copy -o run -- python3 $REPO/bench.py --calibrate-copy
+rocprofv3 --pmc WRITE_SIZE -d $OUT/pmc_WRITE_SIZE_copy -o run -- python3 $REPO/bench.py --calibrate-copy
+python3 $REPO/bench.py --summarize $OUT --workload {w}"""
+
+
+def summarize_profiles(out_dir, workload):
+    """Write profiles/pa_fwd_<workload>.md from rocprofv3 output databases."""
+    import sqlite3
+    import glob
+
+    def db(sub):
+        hits = glob.glob(os.path.join(out_dir, sub, "**", "*.db"), recursive=True)
+        if not hits:
+            raise SystemExit(f"no rocprofv3 database under {os.path.join(out_dir, sub)}")
+        return sqlite3.connect(hits[0])
+
+    con = db(f"trace_{workload}")
+    stats = list(con.execute("select name, total_calls, total_duration, average, percentage "
+                             "from top_kernels limit 8"))
+
+    def counter(sub, name, like):
+        rows = list(db(sub).execute(
+            "select avg(value), count(*) from counters_collection where counter_name = ? "
+            "and kernel_name like ?", (name, like)))
+        return rows[0]
+
+    fetch_k, n_f = counter(f"pmc_FETCH_SIZE_{workload}", "FETCH_SIZE", "%pa_fwd_kernel%")
+    write_k, n_w = counter(f"pmc_WRITE_SIZE_{workload}", "WRITE_SIZE", "%pa_fwd_kernel%")
+    copy_bytes = 1 << 30
+    fetch_c, _ = counter("pmc_FETCH_SIZE_copy", "FETCH_SIZE", "%copyBuffer%")
+    write_c, _ = counter("pmc_WRITE_SIZE_copy", "WRITE_SIZE", "%copyBuffer%")
+    f_scale = copy_bytes / (fetch_c * 1024.0)
+    w_scale = copy_bytes / (write_c * 1024.0)
+    fetch_bytes = fetch_k * 1024.0 * f_scale
+    write_bytes = write_k * 1024.0 * w_scale
+
+    lines = [f"# pa_fwd_kernel on workload `{workload}` (MI355X, rocprofv3)", "",
+             "Commands (OUT = an output folder, REPO = the repository root):", "", "```",
+             PROF_COMMANDS.format(w=workload), "```", "",
+             "## Kernel trace (--kernel-trace --stats), top kernels", "",
+             "| kernel | calls | total us | average us | % |", "|---|---|---|---|---|"]
+    for name, calls, total, avg, pct in stats:
+        short = name.replace("(anonymous namespace)::", "").split("(")[0][-70:]
+        lines.append(f"| `{short}` | {calls} | {total:.1f} | {avg:.2f} | {pct:.1f} |")
+    lines += ["", "(The run includes input generation kernels; the forward kernel's average "
+              "is the figure compared with the in-benchmark HIP-event timing.)", "",
+              "## HBM traffic of the forward kernel (--pmc, one counter per run)", "",
+              f"- FETCH_SIZE: {fetch_k:.1f} KiB per dispatch (mean of {n_f} dispatches)",
+              f"- WRITE_SIZE: {write_k:.1f} KiB per dispatch (mean of {n_w} dispatches)",
+              f"- Calibration, 1 GiB device copy (`__amd_rocclr_copyBuffer`, {copy_bytes} B read "
+              f"and written): FETCH_SIZE {fetch_c:.1f} KiB, WRITE_SIZE {write_c:.1f} KiB -> scale "
+              f"factors {f_scale:.4f} (fetch) and {w_scale:.4f} (write)",
+              f"- Scaled: fetched {fetch_bytes / 1e9:.4f} GB, written {write_bytes / 1e9:.4f} GB, "
+              f"total {(fetch_bytes + write_bytes) / 1e9:.4f} GB per launch", ""]
+    rec = {"workload": workload, "source_hash": source_hash(),
+           "traffic_bytes_per_launch": int(fetch_bytes + write_bytes),
+           "fetch_kib": fetch_k, "write_kib": write_k,
+           "fetch_scale": f_scale, "write_scale": w_scale}
+    lines.append("<!-- traffic " + json.dumps(rec) + " -->")
+    os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
+    with open(profile_path(workload), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print(profile_path(workload))
 
 
 def cpu_baseline(b, budget_s=20.0):
@@ -113,13 +189,30 @@ def main():
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cold", type=int, default=20, help="extra cold-cache timed calls")
+    ap.add_argument("--summarize", metavar="DIR",
+                    help="write profiles/pa_fwd_<workload>.md from rocprofv3 output in DIR")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a 1 GiB device-to-device copy three times (the known-size "
+                         "kernel that scales rocprofv3 FETCH_SIZE / WRITE_SIZE into bytes)")
     args = ap.parse_args()
+    if args.summarize:
+        summarize_profiles(args.summarize, args.workload)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(the operation runs on a single MI355X)", file=sys.stderr)
         sys.exit(2)
 
     import torch
+    if args.calibrate_copy:
+        src = torch.ones(1 << 28, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibration_copy_bytes": src.numel() * 4}))
+        return
+
     import paged_kv_cache_unified_amd as pa
     from workloads import WORKLOADS, make_workload
 
