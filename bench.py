@@ -189,6 +189,12 @@ def main():
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cold", type=int, default=20, help="extra cold-cache timed calls")
+    ap.add_argument("--force-tile", type=int, default=0,
+                    help="pa_options.force_tile (0 = heuristic plan)")
+    ap.add_argument("--force-splits", type=int, default=0,
+                    help="pa_options.force_num_splits (0 = heuristic plan)")
+    ap.add_argument("--decode-grid", type=int, default=0,
+                    help="pa_options.decode_grid (0 = resident work-groups)")
     ap.add_argument("--summarize", metavar="DIR",
                     help="write profiles/pa_fwd_<workload>.md from rocprofv3 output in DIR")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -224,12 +230,24 @@ def main():
     b = make_workload(args.workload, device=dev)
     out = torch.empty_like(b.q)
     call_args = b.args(out)
-    plan = pa.plan_describe(*call_args[:9])
+    opts, ws = None, None
+    if args.force_tile or args.force_splits or args.decode_grid:
+        opts = pa.options(force_num_splits=args.force_splits, force_tile=args.force_tile,
+                          decode_grid=args.decode_grid)
+        ws = torch.empty(max(1, pa.workspace_size(*call_args[:9], opts)), dtype=torch.uint8,
+                         device=dev)
+    plan = pa.plan_describe(*call_args[:9], opts=opts)
     total_bytes, kv_bytes, flops = algorithmic_work(b)
+
+    def call():
+        if opts is None:
+            pa.unified_attention(*call_args)
+        else:
+            pa.unified_attention(*call_args, opts=opts, workspace=ws)
 
     stream = torch.cuda.current_stream(dev)
     for _ in range(args.warmup):
-        pa.unified_attention(*call_args)
+        call()
     torch.cuda.synchronize()
 
     # timed region: exactly K steps, per-launch events on the launch stream
@@ -239,7 +257,7 @@ def main():
     t0 = time.perf_counter()
     for i in range(args.steps):
         starts[i].record(stream)
-        pa.unified_attention(*call_args)
+        call()
         ends[i].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -256,7 +274,7 @@ def main():
             flush.sum()
             s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             s.record(stream)
-            pa.unified_attention(*call_args)
+            call()
             e.record(stream)
             torch.cuda.synchronize()
             cold.append(s.elapsed_time(e))

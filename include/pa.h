@@ -78,12 +78,16 @@ typedef struct {
                                range holds at least one 64-key stage)          */
   int32_t force_tile;       /* 0: heuristic; 1: one query tile per sequence of
                                at most 16/G tokens (requires max_seqlen_q*G <=
-                               16); 2: 64-row query tiles, and the per-wave-rows
-                               code path even for tiles of <= 16 rows          */
+                               16), persistent decode kernel; 2: 64-row query
+                               tiles, and the per-wave-rows code path even for
+                               tiles of <= 16 rows; 3: as 1 but one work-group
+                               per item on the unified kernel                 */
   int32_t check_contents;   /* !=0: copy the metadata to the host (synchronous)
                                and return PA_ERR_CONTENT if it breaks the
                                preconditions listed below                      */
-  int32_t reserved;
+  int32_t decode_grid;      /* >0: work-groups of the persistent decode kernel
+                               (rounded down to a multiple of 8; default: the
+                               resident work-groups of the device)             */
 } pa_options;
 
 /* Launch shape chosen for a batch (pa_plan_describe). */
@@ -96,6 +100,13 @@ typedef struct {
   int32_t split_keys;    /* keys per range (multiple of 64)                   */
   int64_t num_workgroups;/* main-kernel grid size                             */
   int64_t workspace_bytes;
+  int32_t persistent;    /* 1: persistent decode kernel; items (sequence, key
+                            split, kv-head) are enumerated on the device, and
+                            num_splits bounds a row's split count            */
+  int32_t balanced;      /* 1 (persistent only): split sizes are chosen on the
+                            device from the batch's total context so every
+                            work-group streams about the same bytes; at least
+                            split_keys keys per split                        */
 } pa_plan_info;
 
 /*
@@ -132,9 +143,9 @@ typedef struct {
  *
  * Ownership: the caller owns every buffer; the library keeps no pointer after
  * return.  This entry point uses a library-owned split workspace (device
- * memory, one per device, grown on demand with hipMalloc after synchronising
- * the device, kept until process exit); use pa_unified_attention_ex with a
- * caller workspace under stream capture.
+ * memory, one per (device, stream), grown on demand with hipMalloc after
+ * synchronising the device, kept until process exit); use
+ * pa_unified_attention_ex with a caller workspace under stream capture.
  *
  * Asynchronous: returns after enqueueing on `stream`.  Deterministic: the
  * same inputs and launch plan give bit-identical output, and the output does

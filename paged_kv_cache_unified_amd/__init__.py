@@ -32,14 +32,15 @@ class PaTensor(ctypes.Structure):
 
 class PaOptions(ctypes.Structure):
     _fields_ = [("force_num_splits", ctypes.c_int32), ("force_tile", ctypes.c_int32),
-                ("check_contents", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+                ("check_contents", ctypes.c_int32), ("decode_grid", ctypes.c_int32)]
 
 
 class PaPlanInfo(ctypes.Structure):
     _fields_ = [("tile_tokens", ctypes.c_int32), ("tile_rows", ctypes.c_int32),
                 ("num_slots", ctypes.c_int32), ("slots_direct", ctypes.c_int32),
                 ("num_splits", ctypes.c_int32), ("split_keys", ctypes.c_int32),
-                ("num_workgroups", ctypes.c_int64), ("workspace_bytes", ctypes.c_int64)]
+                ("num_workgroups", ctypes.c_int64), ("workspace_bytes", ctypes.c_int64),
+                ("persistent", ctypes.c_int32), ("balanced", ctypes.c_int32)]
 
     def as_dict(self):
         return {name: getattr(self, name) for name, _ in self._fields_}
@@ -122,8 +123,10 @@ def _descs(q, k_cache, v_cache, out, cu_seqlens_q, seqused_k, block_table):
     return ds, [ctypes.byref(x) for x in ds]
 
 
-def options(force_num_splits: int = 0, force_tile: int = 0, check_contents: bool = False) -> PaOptions:
-    return PaOptions(int(force_num_splits), int(force_tile), int(bool(check_contents)), 0)
+def options(force_num_splits: int = 0, force_tile: int = 0, check_contents: bool = False,
+            decode_grid: int = 0) -> PaOptions:
+    return PaOptions(int(force_num_splits), int(force_tile), int(bool(check_contents)),
+                     int(decode_grid))
 
 
 def unified_attention(q, k_cache, v_cache, out, cu_seqlens_q, seqused_k, block_table,

@@ -7,6 +7,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <map>
 #include <mutex>
 #include <string>
 #include <vector>
@@ -35,11 +36,14 @@ struct Shapes {
 
 struct Plan {
   int32_t tile_tokens, tile_rows, num_slots, slots_direct, n_split, split_keys;
-  bool wide;  // launch the specialization with the wide-tile path
+  bool wide;        // launch the specialization with the wide-tile path
+  bool persistent;  // persistent decode kernel with per-sequence split counts
+  bool balanced;    // persistent: part sizes chosen on the device from the total context
   int64_t num_items;
   int64_t nwg;
   size_t ws_bytes;
   size_t ws_lse_offset;
+  size_t ws_parts_offset;
 };
 
 constexpr int64_t kMaxInt32 = 0x7fffffff;
@@ -177,18 +181,62 @@ size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 //    reach ~8 work-groups per CU, each split at least 512 keys.  Split sizes
 //    depend on max_seqlen_k and the grid only, so results are deterministic.
 int make_plan(const Shapes& s, int32_t max_q, int32_t max_k, const pa_options* opt, int num_cus,
-              Plan* out) {
+              int decode_blocks_per_cu, Plan* out) {
   Plan p{};
   const int force_tile = opt ? opt->force_tile : 0;
   const int force_split = opt ? opt->force_num_splits : 0;
   const int64_t G = s.G;
   const int64_t mq = std::max<int64_t>(max_q, 1);
+  const int64_t mk = std::max<int64_t>(max_k, 1);
   const bool narrow_fits = mq * G <= pa::kNarrowRows;
-  if (force_tile == 1 && !narrow_fits)
-    return fail(PA_ERR_UNSUPPORTED, "force_tile=1 needs max_seqlen_q * G <= 16");
-  if (force_tile != 0 && force_tile != 1 && force_tile != 2)
-    return fail(PA_ERR_UNSUPPORTED, "force_tile must be 0, 1 or 2");
-  if (force_tile == 1 || (force_tile == 0 && narrow_fits)) {
+  if ((force_tile == 1 || force_tile == 3) && !narrow_fits)
+    return fail(PA_ERR_UNSUPPORTED, "force_tile=%d needs max_seqlen_q * G <= 16", force_tile);
+  if (force_tile < 0 || force_tile > 3)
+    return fail(PA_ERR_UNSUPPORTED, "force_tile must be 0, 1, 2 or 3");
+  const bool narrow = force_tile == 1 || force_tile == 3 || (force_tile == 0 && narrow_fits);
+  // (the decode kernel's idle ring slots re-read pool block 0, so the pool
+  // must hold at least one block)
+  if (narrow && force_tile != 3 && s.S <= pa::kMaxDecodeSeqs && s.NB > 0) {
+    // Persistent decode kernel: one narrow tile per sequence; items are the
+    // (sequence, key split, kv-head) triples enumerated on the device.
+    p.persistent = true;
+    p.wide = false;
+    p.tile_tokens = (int32_t)mq;
+    p.tile_rows = (int32_t)(mq * G);
+    p.slots_direct = 1;
+    p.num_slots = (int32_t)s.S;
+    // resident work-groups, a multiple of 8 (the kernel deals items per XCD)
+    int64_t resident = (int64_t)std::max(num_cus, 1) * std::max(decode_blocks_per_cu, 1);
+    if (opt && opt->decode_grid > 0) resident = opt->decode_grid;
+    const int64_t grid = std::max<int64_t>(8, resident / 8 * 8);
+    int64_t split_keys;
+    p.balanced = false;
+    if (force_split > 0) {
+      split_keys = (mk + force_split - 1) / force_split;        // fixed-size parts
+    } else if (mk <= pa::kMaxSplitKeys && s.S * s.Hkv >= 4 * grid) {
+      split_keys = mk;                       // a whole (sequence, kv-head) for every wave
+    } else {
+      // balanced parts: the device sizes them from the total context so each
+      // wave gets ~kDecodeItemsPerWave equal items; at least kMinSplitKeys
+      p.balanced = true;
+      split_keys = pa::kMinSplitKeys;
+    }
+    split_keys = (split_keys + pa::kStageKeys - 1) / pa::kStageKeys * pa::kStageKeys;
+    split_keys = std::min<int64_t>(split_keys, pa::kMaxSplitKeys);
+    p.split_keys = (int32_t)split_keys;
+    p.n_split = (int32_t)((mk + split_keys - 1) / split_keys);   // bound on parts per row
+    p.num_items = 0;                         // known on the device only
+    p.nwg = grid;
+    if (p.n_split > 1) {
+      const size_t rows = (size_t)s.T * (size_t)s.Hq * (size_t)p.n_split;
+      p.ws_lse_offset = align256(rows * (size_t)s.D * sizeof(float));
+      p.ws_parts_offset = p.ws_lse_offset + align256(rows * sizeof(float));
+      p.ws_bytes = p.ws_parts_offset + align256((size_t)s.S * sizeof(int32_t));
+    }
+    *out = p;
+    return PA_OK;
+  }
+  if (narrow) {
     p.tile_tokens = (int32_t)mq;
     p.slots_direct = 1;
     p.num_slots = (int32_t)s.S;
@@ -206,7 +254,6 @@ int make_plan(const Shapes& s, int32_t max_q, int32_t max_k, const pa_options* o
   }
   p.tile_rows = (int32_t)(p.tile_tokens * G);
   const int64_t items = (int64_t)p.num_slots * s.Hkv;
-  const int64_t mk = std::max<int64_t>(max_k, 1);
   int64_t n_split = 1;
   if (force_split > 0) {
     n_split = force_split;
@@ -261,6 +308,18 @@ int device_cu_count(bool* ok) {
   return cache[dev];
 }
 
+int decode_blocks_per_cu_cached(int head_dim, int group) {
+  static std::mutex mu;
+  static int cache[2][17] = {};
+  const int di = head_dim == 128 ? 1 : 0;
+  std::lock_guard<std::mutex> lock(mu);
+  if (cache[di][group] == 0) {
+    const int n = pa::decode_blocks_per_cu(head_dim, group);
+    cache[di][group] = n > 0 ? n : -1;
+  }
+  return cache[di][group] > 0 ? cache[di][group] : 2;
+}
+
 int check_contents(const Shapes& s, const pa_tensor* cu, const pa_tensor* sk, const pa_tensor* bt,
                    int32_t max_q, int32_t max_k, hipStream_t stream) {
   std::vector<int32_t> hcu(s.S + 1), hsk(s.S), hbt((size_t)s.S * (size_t)s.bt_stride);
@@ -296,15 +355,16 @@ struct DeviceWorkspace {
   size_t bytes = 0;
 };
 
+// One workspace per (device, stream): calls on different streams never share
+// split partials; calls on one stream are ordered by the stream.
 int library_workspace(size_t need, hipStream_t stream, void** ptr) {
   static std::mutex mu;
-  static std::vector<DeviceWorkspace> per_dev;
+  static std::map<std::pair<int, hipStream_t>, DeviceWorkspace> pool;
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return fail(PA_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
   std::lock_guard<std::mutex> lock(mu);
-  if ((int)per_dev.size() <= dev) per_dev.resize(dev + 1);
-  DeviceWorkspace& w = per_dev[dev];
+  DeviceWorkspace& w = pool[std::make_pair(dev, stream)];
   if (w.bytes < need) {
     hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
     if (hipStreamIsCapturing(stream, &cs) == hipSuccess && cs != hipStreamCaptureStatusNone)
@@ -341,8 +401,9 @@ int run(const pa_tensor* q, const pa_tensor* k, const pa_tensor* v, pa_tensor* o
   if (s.T == 0 || s.S == 0) return PA_OK;
   bool have_dev = false;
   const int ncu = device_cu_count(&have_dev);
+  const int dbpc = have_dev ? decode_blocks_per_cu_cached((int)s.D, (int)s.G) : 2;
   Plan plan;
-  rc = make_plan(s, max_q, max_k, opt, ncu, &plan);
+  rc = make_plan(s, max_q, max_k, opt, ncu, dbpc, &plan);
   if (rc != PA_OK) return rc;
   hipStream_t stream = reinterpret_cast<hipStream_t>(stream_v);
   if (library_ws) {
@@ -387,6 +448,11 @@ int run(const pa_tensor* q, const pa_tensor* k, const pa_tensor* v, pa_tensor* o
   p.slots_direct = plan.slots_direct;
   p.n_split = plan.n_split;
   p.split_keys = plan.split_keys;
+  p.balanced = plan.balanced ? 1 : 0;
+  p.items_per_wg = pa::kDecodeItemsPerWave;
+  p.ws_parts = plan.persistent && plan.n_split > 1
+                   ? reinterpret_cast<int32_t*>(static_cast<char*>(ws) + plan.ws_parts_offset)
+                   : nullptr;
   p.num_items = (int32_t)plan.num_items;
   p.items_per_xcd = (int32_t)(plan.nwg / 8);
   p.kv_major = plan.wide ? 1 : 0;
@@ -394,7 +460,9 @@ int run(const pa_tensor* q, const pa_tensor* k, const pa_tensor* v, pa_tensor* o
   p.narrow_rows = (opt && opt->force_tile == 2) ? 0 : pa::kNarrowRows;
   p.scale_log2 = (float)((double)scale * 1.4426950408889634);
   if (plan.nwg > 0) {
-    hipError_t e = pa::launch_fwd(p, (int)s.D, (int)s.G, plan.wide, plan.nwg, stream);
+    hipError_t e = plan.persistent
+                       ? pa::launch_decode(p, (int)s.D, (int)s.G, plan.nwg, stream)
+                       : pa::launch_fwd(p, (int)s.D, (int)s.G, plan.wide, plan.nwg, stream);
     if (e != hipSuccess) return fail(PA_ERR_HIP, "forward launch: %s", hipGetErrorString(e));
   }
   if (plan.n_split > 1) {
@@ -407,6 +475,12 @@ int run(const pa_tensor* q, const pa_tensor* k, const pa_tensor* v, pa_tensor* o
     mp.total_q = (int32_t)s.T;
     mp.num_q_heads = (int32_t)s.Hq;
     mp.n_split = plan.n_split;
+    mp.per_seq_splits = plan.persistent ? 1 : 0;
+    mp.parts = p.ws_parts;
+    mp.cu_q = p.cu_q;
+    mp.seq_k = p.seq_k;
+    mp.num_seqs = (int32_t)s.S;
+    mp.split_keys = plan.split_keys;
     hipError_t e = pa::launch_merge(mp, (int)s.D, stream);
     if (e != hipSuccess) return fail(PA_ERR_HIP, "merge launch: %s", hipGetErrorString(e));
   }
@@ -447,8 +521,9 @@ size_t pa_workspace_size(const pa_tensor* q, const pa_tensor* k_cache, const pa_
   if (s.T == 0 || s.S == 0) return 0;
   bool have_dev = false;
   const int ncu = device_cu_count(&have_dev);
+  const int dbpc = have_dev ? decode_blocks_per_cu_cached((int)s.D, (int)s.G) : 2;
   Plan plan;
-  if (make_plan(s, max_seqlen_q, max_seqlen_k, opt, ncu, &plan) != PA_OK) return (size_t)-1;
+  if (make_plan(s, max_seqlen_q, max_seqlen_k, opt, ncu, dbpc, &plan) != PA_OK) return (size_t)-1;
   return plan.ws_bytes;
 }
 
@@ -465,8 +540,10 @@ int pa_plan_describe(const pa_tensor* q, const pa_tensor* k_cache, const pa_tens
   if (rc != PA_OK) return rc;
   bool have_dev = false;
   const int ncu = num_cus > 0 ? num_cus : device_cu_count(&have_dev);
+  if (num_cus > 0) (void)device_cu_count(&have_dev);
+  const int dbpc = have_dev ? decode_blocks_per_cu_cached((int)s.D, (int)s.G) : 2;
   Plan plan;
-  rc = make_plan(s, max_seqlen_q, max_seqlen_k, opt, ncu, &plan);
+  rc = make_plan(s, max_seqlen_q, max_seqlen_k, opt, ncu, dbpc, &plan);
   if (rc != PA_OK) return rc;
   if (s.T == 0 || s.S == 0) {
     plan.nwg = 0;
@@ -480,6 +557,8 @@ int pa_plan_describe(const pa_tensor* q, const pa_tensor* k_cache, const pa_tens
   info->split_keys = plan.split_keys;
   info->num_workgroups = plan.nwg;
   info->workspace_bytes = (int64_t)plan.ws_bytes;
+  info->persistent = plan.persistent ? 1 : 0;
+  info->balanced = plan.balanced ? 1 : 0;
   return PA_OK;
 }
 

@@ -13,6 +13,9 @@ constexpr int kThreads = 256;     // 4 wave64s per work-group
 constexpr int kTileRows = 64;     // packed rows of a wide query tile (16 per wave)
 constexpr int kNarrowRows = 16;   // rows of a narrow (decode) tile
 constexpr int kMaxSplitKeys = 4096;  // keys per split: at most 64 blocks per wave (narrow)
+constexpr int kMaxDecodeSeqs = 2048; // sequences the persistent decode kernel can enumerate
+constexpr int kMinSplitKeys = 512;   // smallest balanced split of the persistent decode kernel
+constexpr int kDecodeItemsPerWave = 2; // balanced decode: items per resident wave
 
 // Everything the forward kernel needs, by value.  Strides in elements.
 struct FwdParams {
@@ -38,6 +41,9 @@ struct FwdParams {
   int32_t slots_direct;    // 1: slot index is the sequence index
   int32_t n_split;
   int32_t split_keys;      // multiple of kStageKeys
+  int32_t balanced;        // persistent decode: parts per sequence chosen on the device
+  int32_t items_per_wg;    // balanced decode: target items per wave
+  int32_t* ws_parts;       // persistent decode with n_split > 1: parts of each sequence [S]
   int32_t num_items;       // num_slots * num_kv_heads * n_split
   int32_t items_per_xcd;   // ceil(num_items / 8): contiguous item range per XCD
   int32_t kv_major;        // item order: 1 = (kv-head, slot, split), 0 = (slot, kv-head, split)
@@ -50,10 +56,16 @@ struct MergeParams {
   const float* ws_o;
   const float* ws_lse;
   uint16_t* out;
+  const int32_t* cu_q;     // per_seq_splits only
+  const int32_t* seq_k;
   int64_t o_st, o_sh;
   int32_t total_q;
   int32_t num_q_heads;
-  int32_t n_split;
+  int32_t n_split;         // parts per row (upper bound when per_seq_splits)
+  int32_t per_seq_splits;  // 1: row of sequence s has parts[s] parts
+  const int32_t* parts;    // per_seq_splits: parts of each sequence
+  int32_t num_seqs;
+  int32_t split_keys;
 };
 
 // Launchers (pa_kernels.hip).  Return the hipError_t of the launch.
@@ -61,6 +73,11 @@ struct MergeParams {
 hipError_t launch_fwd(const FwdParams& p, int head_dim, int group, bool wide,
                       int64_t num_workgroups, hipStream_t stream);
 hipError_t launch_merge(const MergeParams& p, int head_dim, hipStream_t stream);
+// Persistent decode kernel (every tile narrow, num_seqs <= kMaxDecodeSeqs).
+hipError_t launch_decode(const FwdParams& p, int head_dim, int group, int64_t num_workgroups,
+                         hipStream_t stream);
+// Resident work-groups per CU of the decode kernel (0 if unknown).
+int decode_blocks_per_cu(int head_dim, int group);
 bool fwd_supported(int head_dim, int group);
 
 }  // namespace pa

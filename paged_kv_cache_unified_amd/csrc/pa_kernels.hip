@@ -216,7 +216,7 @@ __device__ __forceinline__ void attend_narrow(const FwdParams& p, const Item& it
   constexpr int VPL = kBlockSize * CPR / 64;      // V chunks per lane per block
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (SGPR)
   const int h4 = lane >> 4;
   const int l16 = lane & 15;
 
@@ -426,7 +426,7 @@ __device__ __forceinline__ void attend_wide(const FwdParams& p, const Item& it,
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (SGPR)
   const int h4 = lane >> 4;
   const int l16 = lane & 15;
 
@@ -624,23 +624,437 @@ __global__ __launch_bounds__(kThreads) void pa_fwd_kernel(FwdParams p) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Persistent decode kernel (batches whose every sequence is one narrow tile).
+//
+// Work list: sequence s contributes n_s key parts (one if L_s = 0, none if it
+// has no query) and every (s, part, kv-head) is one item, streamed by ONE
+// wave from start to end: no cross-wave merge and no work-group barrier after
+// the set-up.  Each work-group builds the prefix sums of n_s in LDS once and
+// stages the per-sequence metadata there; items are dealt to XCDs in
+// contiguous ranges and the waves of one XCD stride through its range, so the
+// kv-heads of a sequence (which share its cache blocks) stream together.
+//
+// A wave's block stream continues across items: the last refills of an item
+// already fetch the next item's first blocks (its block ids and Q were loaded
+// one item ahead), so HBM keeps streaming while the wave writes its rows.  A
+// sequence with one part writes its rows directly; rows of sequences with
+// several parts go to the workspace for pa_merge.
+// ---------------------------------------------------------------------------
+constexpr int kMaxItemBlocks = kMaxSplitKeys / kBlockSize;   // 256 blocks per item
+
+template <int D>
+struct DecodeCfg {
+  static constexpr int BLK_BYTES = kBlockSize * D * 2;
+  static constexpr int VBUF_BYTES = 4 * 2 * BLK_BYTES;            // 2 V buffers per wave
+  static constexpr int IDS_OFFSET = VBUF_BYTES;                   // int [4 waves][2][256]
+  static constexpr int PREF_OFFSET = IDS_OFFSET + 4 * 2 * kMaxItemBlocks * 4;  // int [S + 1]
+  static constexpr int Q0_OFFSET = PREF_OFFSET + (kMaxDecodeSeqs + 1) * 4;   // int [S + 1]
+  static constexpr int LEN_OFFSET = Q0_OFFSET + (kMaxDecodeSeqs + 1) * 4;   // int [S]
+  static constexpr int SCAN_OFFSET = (LEN_OFFSET + kMaxDecodeSeqs * 4 + 7) / 8 * 8;  // 4 x i64
+  static constexpr int SMEM = SCAN_OFFSET + 32;
+};
+
+__device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
+// Key parts of a sequence with `ql` queries and context L.  Fixed mode: parts
+// of `target` keys.  Balanced mode: round(L / target) equal parts (at least
+// one, each at most kMaxSplitKeys keys), where target ~ total context * Hkv /
+// (waves * items per wave), so waves stream similar byte counts.
+__device__ __forceinline__ int seq_parts(const FwdParams& p, int ql, int L, int target) {
+  if (ql <= 0) return 0;
+  int n;
+  if (p.balanced) {
+    n = (L + target / 2) / target;
+    n = max(n, (L + kMaxSplitKeys - 1) / kMaxSplitKeys);
+  } else {
+    n = (L + target - 1) / target;
+  }
+  return min(max(n, 1), p.n_split);
+}
+// keys per part (a multiple of the block size)
+__device__ __forceinline__ int part_keys(const FwdParams& p, int L, int parts, int target) {
+  if (!p.balanced) return target;
+  const int k = (L + parts - 1) / parts;
+  return max(kBlockSize, (k + kBlockSize - 1) / kBlockSize * kBlockSize);
+}
+
+struct DItem {
+  int valid;
+  int s, kvh, sigma, units;
+  int q0, q_len, rows, L, diag;
+  int kbeg, kend, kmin;
+  int blk0, nb;          // first block and number of blocks of the item
+};
+
+// Item -> (sequence, part, kv-head) from the LDS tables only.
+template <int G>
+__device__ __forceinline__ DItem describe_item(const FwdParams& p, const int* pref,
+                                               const int* q0t, const int* lent, int n_items,
+                                               int item, int target) {
+  DItem d = {};            // an invalid item is all zeros: kv-head 0, no blocks
+  d.valid = item < n_items;
+  if (!d.valid) return d;
+  const int unit = item / p.num_kv_heads;
+  d.kvh = item - unit * p.num_kv_heads;
+  int lo = 0, hi = p.num_seqs - 1;     // largest s with pref[s] <= unit
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (uniform(pref[mid]) <= unit) lo = mid; else hi = mid - 1;
+  }
+  d.s = lo;
+  d.sigma = unit - uniform(pref[lo]);
+  d.units = uniform(pref[lo + 1]) - uniform(pref[lo]);
+  d.q0 = uniform(q0t[lo]);
+  d.q_len = uniform(q0t[lo + 1]) - d.q0;
+  d.rows = d.q_len * G;
+  d.L = uniform(lent[lo]);
+  d.diag = d.L - d.q_len;
+  const int pk = part_keys(p, d.L, d.units, target);
+  d.kbeg = d.sigma * pk;
+  d.kend = max(0, min(d.L, d.kbeg + pk));
+  d.kmin = p.causal ? min(d.kend, d.diag + 1) : d.kend;
+  d.blk0 = d.kbeg / kBlockSize;
+  d.nb = d.kend > d.kbeg ? (d.kend + kBlockSize - 1) / kBlockSize - d.blk0 : 0;
+  return d;
+}
+
+template <int D, int G>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
+void pa_decode_kernel(FwdParams p) {
+  using Lay = Layout<D>;
+  using Cfg = DecodeCfg<D>;
+  constexpr int CPR = Lay::CPR;
+  constexpr int BLK_BYTES = Lay::BLK_BYTES;
+  constexpr int KS = D / 32;
+  constexpr int DT = D / 16;
+  constexpr int VPL = kBlockSize * CPR / 64;
+  constexpr int IDL = kMaxItemBlocks / 64;          // block ids per lane per item
+  __shared__ __attribute__((aligned(16))) unsigned char smem[Cfg::SMEM];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (SGPR)
+  const int h4 = lane >> 4;
+  const int l16 = lane & 15;
+  int* pref = reinterpret_cast<int*>(smem + Cfg::PREF_OFFSET);
+  int* q0t = reinterpret_cast<int*>(smem + Cfg::Q0_OFFSET);
+  int* lent = reinterpret_cast<int*>(smem + Cfg::LEN_OFFSET);
+  int* wsum = reinterpret_cast<int*>(smem + Cfg::SCAN_OFFSET);
+  int* idsw = reinterpret_cast<int*>(smem + Cfg::IDS_OFFSET) + wave * 2 * kMaxItemBlocks;
+
+  // ---- stage per-sequence metadata; part size; prefix sums of part counts ----
+  const int S = p.num_seqs;
+  const int C = (S + kThreads - 1) / kThreads;
+  const int s0 = min(S, tid * C), s1 = min(S, s0 + C);
+  long long ctx = 0;
+  for (int s = s0; s < s1; ++s) {
+    const int a = p.cu_q[s], L = p.seq_k[s];
+    q0t[s] = a;
+    lent[s] = L;
+    if (p.cu_q[s + 1] > a) ctx += L;
+  }
+  if (tid == 0) q0t[S] = p.cu_q[S];
+  const int workers = (int)gridDim.x * 4;
+  int target = p.split_keys;
+  if (p.balanced) {
+    // total context of sequences with queries (64-bit: can exceed 2^31)
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) ctx += __shfl_xor(ctx, d);
+    long long* tot = reinterpret_cast<long long*>(wsum);
+    if (lane == 0) tot[wave] = ctx;
+    __syncthreads();
+    // items are (sequence, part, kv-head): aim for items_per_wg items per wave
+    const long long all = (tot[0] + tot[1] + tot[2] + tot[3]) * p.num_kv_heads;
+    const long long denom = (long long)workers * p.items_per_wg;
+    long long t = (all + denom - 1) / denom;
+    t = (t + kBlockSize - 1) / kBlockSize * kBlockSize;
+    target = (int)min((long long)kMaxSplitKeys, max((long long)p.split_keys, t));
+  }
+  __syncthreads();                                  // tables written, tot read
+  {
+    int local = 0;
+    for (int s = s0; s < s1; ++s) local += seq_parts(p, q0t[s + 1] - q0t[s], lent[s], target);
+    int incl = local;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int y = __shfl_up(incl, d);
+      if (lane >= d) incl += y;
+    }
+    if (lane == 63) wsum[wave] = incl;
+    __syncthreads();
+    int base = 0;
+    for (int w = 0; w < wave; ++w) base += wsum[w];
+    int run = base + incl - local;
+    for (int s = s0; s < s1; ++s) {
+      const int n = seq_parts(p, q0t[s + 1] - q0t[s], lent[s], target);
+      pref[s] = run;
+      run += n;
+      if (p.n_split > 1 && blockIdx.x == 0) p.ws_parts[s] = n;   // for pa_merge
+    }
+    if (tid == kThreads - 1) pref[S] = base + incl;
+    __syncthreads();
+  }
+  const int n_items = uniform(pref[S]) * p.num_kv_heads;
+
+  // Items are dealt to XCDs in contiguous ranges (work-group w runs on XCD
+  // w % 8); the waves of one XCD stride through its range.
+  const int xcd = blockIdx.x & 7;
+  const int wpx = (int)(gridDim.x >> 3) * 4;           // waves per XCD (grid % 8 == 0)
+  const int per_xcd = (n_items + 7) >> 3;
+  const int range_end = min(n_items, (xcd + 1) * per_xcd);
+  // consecutive items (the kv-heads of one sequence, which read the same cache
+  // blocks) go to the waves of one work-group, i.e. one CU
+  const int item0 = xcd * per_xcd + (int)(blockIdx.x >> 3) * 4 + wave;
+  auto item_at = [&](int m) -> int {                   // m-th item of this wave
+    const int it = item0 + m * wpx;
+    return it < range_end ? it : n_items;              // n_items marks "none"
+  };
+  int mi = 0;
+  if (item_at(0) >= n_items) return;                   // whole wave idle
+
+  const int slot_stride = p.num_kv_heads * D;
+  const int koff = l16 * slot_stride + 8 * h4;
+  int voff[VPL], vlds[VPL];
+#pragma unroll
+  for (int u = 0; u < VPL; ++u) {
+    const int c = lane + 64 * u;
+    const int key = c / CPR, dc = c % CPR;
+    voff[u] = key * slot_stride + dc * 8;
+    vlds[u] = Lay::v_chunk(key, dc) * 16;
+  }
+  const int tr_key = 4 * h4 + (l16 >> 2);
+  const int tr_c_lo = (l16 & 3) >> 1;
+  const int tr_half = (l16 & 1) * 8;
+  unsigned char* vbuf0 = smem + wave * 2 * BLK_BYTES;
+
+  auto load_ids = [&](const DItem& d, int (&v)[IDL]) {
+#pragma unroll
+    for (int k = 0; k < IDL; ++k) {
+      v[k] = 0;
+      if (d.valid && lane + 64 * k < d.nb)
+        v[k] = p.bt[(int64_t)d.s * p.bt_stride + d.blk0 + lane + 64 * k];
+    }
+  };
+  auto store_ids = [&](int buf, const int (&v)[IDL]) {
+#pragma unroll
+    for (int k = 0; k < IDL; ++k) idsw[buf * kMaxItemBlocks + lane + 64 * k] = v[k];
+  };
+  auto load_qb = [&](const DItem& d, bf16x8 (&qB)[KS]) {
+    const bool ok = d.valid && l16 < d.rows;
+    const uint16_t* qp = p.q + (int64_t)(d.q0 + (ok ? l16 / G : 0)) * p.q_st +
+                         (int64_t)(d.kvh * G + l16 % G) * p.q_sh + 8 * h4;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (ok) v = *reinterpret_cast<const u32x4*>(qp + 32 * ks);
+      qB[ks] = __builtin_bit_cast(bf16x8, v);
+    }
+  };
+
+  // Ring of two cache blocks per wave.  Every refill issues the same buffer
+  // loads through a per-block resource; a slot with nothing left to fetch
+  // gets a resource of zero records, so its loads return zeros without
+  // touching memory while the wait counts stay the same on every path.
+  u32x4 kst[2][KS];
+  u32x4 vst[2][VPL];
+  const int blk_extent = kBlockSize * slot_stride * 2;      // bytes of one block, all heads
+  auto issue = [&](int kvh, int phys, bool live, int j) {
+    const int64_t boff = (int64_t)phys * p.kv_sb + (int64_t)kvh * D;
+    const int nrec = live ? blk_extent : 0;
+    const __amdgpu_buffer_rsrc_t rk =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(p.k + boff), (short)0, nrec, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rv =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(p.v + boff), (short)0, nrec, 0x00020000);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      kst[j][ks] = __builtin_amdgcn_raw_buffer_load_b128(rk, (koff + 32 * ks) * 2, 0, 0);
+#pragma unroll
+    for (int u = 0; u < VPL; ++u) vst[j][u] = __builtin_amdgcn_raw_buffer_load_b128(rv, voff[u] * 2, 0, 0);
+  };
+
+  // items m (cur), m+1 (nxt), m+2 (nx2): ids of cur and nxt live in LDS, ids of
+  // nx2 in VGPRs until cur finishes; Q of nxt is prefetched.
+  DItem cur = describe_item<G>(p, pref, q0t, lent, n_items, item_at(0), target);
+  DItem nxt = describe_item<G>(p, pref, q0t, lent, n_items, item_at(1), target);
+  int cb = 0;
+  {
+    int v[IDL];
+    load_ids(cur, v);
+    store_ids(0, v);
+    load_ids(nxt, v);
+    store_ids(1, v);
+  }
+  DItem nx2 = describe_item<G>(p, pref, q0t, lent, n_items, item_at(2), target);
+  int ids_v2[IDL];
+  load_ids(nx2, ids_v2);
+  bf16x8 qB[KS], qB_n[KS];
+  load_qb(cur, qB);
+  load_qb(nxt, qB_n);
+  // the first two blocks of the first item (idle slots load nothing)
+  issue(cur.kvh, cur.nb > 0 ? uniform(idsw[0]) : 0, cur.nb > 0, 0);
+  issue(cur.kvh, cur.nb > 1 ? uniform(idsw[1]) : 0, cur.nb > 1, 1);
+
+  while (true) {
+    const int* ids_c = idsw + cb * kMaxItemBlocks;
+    const int* ids_n = idsw + (cb ^ 1) * kMaxItemBlocks;
+    const int klim = p.causal ? min(cur.kend, cur.diag + l16 / G + 1) : cur.kend;
+    f32x4 acc[DT];
+#pragma unroll
+    for (int i = 0; i < DT; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float m = kNegInf, l = 0.f;
+    const int nbp = max(2, (cur.nb + 1) & ~1);
+    for (int i = 0; i < nbp; i += 2) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int b = i + j;
+        // what refills slot j once it is consumed: stream position b + 2 of
+        // this item, else of the next item, else nothing (a zero-record load)
+        const int t = b + 2;
+        const bool in_cur = t < cur.nb;
+        const bool in_nxt = !in_cur && t >= nbp && t - nbp < nxt.nb;
+        const int r_phys = in_cur ? uniform(ids_c[t]) : (in_nxt ? uniform(ids_n[t - nbp]) : 0);
+        const int r_kvh = in_cur ? cur.kvh : (in_nxt ? nxt.kvh : 0);
+        const bool r_live = in_cur || in_nxt;
+        // (1) consume slot j: V rows to LDS, scores S^T = K Q^T
+        const bool live = b < cur.nb;
+        const int kb = (cur.blk0 + b) * kBlockSize;
+        unsigned char* vbuf = vbuf0 + j * BLK_BYTES;
+        f32x4 sc = {0.f, 0.f, 0.f, 0.f};
+        if (live) {
+#pragma unroll
+          for (int u = 0; u < VPL; ++u) *reinterpret_cast<u32x4*>(vbuf + vlds[u]) = vst[j][u];
+#pragma unroll
+          for (int ks = 0; ks < KS; ++ks)
+            sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kst[j][ks]),
+                                                         qB[ks], sc, 0, 0, 0);
+        }
+        // (2) refill slot j (one call site, so the ring registers never move)
+        issue(r_kvh, r_phys, r_live, j);
+        // (3) online softmax and O^T += V^T P^T
+        if (live) {
+          const bool need_mask = kb + kBlockSize > cur.kmin;
+          float x[4];
+          float mx = kNegInf;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            x[r] = sc[r] * p.scale_log2;
+            if (need_mask && kb + 4 * h4 + r >= klim) x[r] = kNegInf;
+            mx = fmaxf(mx, x[r]);
+          }
+          mx = max_across_groups(mx);
+          const float m_new = fmaxf(m, mx);
+          const float m_use = m_new == kNegInf ? 0.f : m_new;
+          const float alpha = exp2_fast(m - m_use);
+          float pr[4], rs = 0.f;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            pr[r] = exp2_fast(x[r] - m_use);
+            rs += pr[r];
+          }
+          l = l * alpha + rs;
+          m = m_new;
+          u32x2 pk = {pack_bf16x2(pr[0], pr[1]), pack_bf16x2(pr[2], pr[3])};
+          const i16x4 pB = __builtin_bit_cast(i16x4, pk);
+          const bool vmask = kb + kBlockSize > cur.kend;
+#pragma unroll
+          for (int dt = 0; dt < DT; ++dt) {
+            const unsigned char* a =
+                vbuf + Lay::v_chunk(tr_key, 2 * dt + tr_c_lo) * 16 + tr_half;
+            i16x4 va = __builtin_bit_cast(
+                i16x4, __builtin_amdgcn_ds_read_tr16_b64_v4bf16((PA_LDS bf16x4*)(a)));
+            if (vmask) {
+#pragma unroll
+              for (int e = 0; e < 4; ++e)
+                if (kb + 4 * h4 + e >= cur.kend) va[e] = 0;
+            }
+            acc[dt] *= alpha;
+            acc[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pB, acc[dt], 0, 0, 0);
+          }
+        }
+      }
+    }
+
+    // ---- this wave's rows of the item ----
+    l = sum_across_groups(l);
+    if (l16 < cur.rows) {
+      const float inv = l > 0.f ? 1.f / l : 0.f;
+      const int64_t tok = cur.q0 + l16 / G;
+      const int hn = cur.kvh * G + l16 % G;
+      if (cur.units == 1) {
+        uint16_t* op = p.out + tok * p.o_st + (int64_t)hn * p.o_sh + 4 * h4;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+          u32x2 w = {pack_bf16x2(acc[dt][0] * inv, acc[dt][1] * inv),
+                     pack_bf16x2(acc[dt][2] * inv, acc[dt][3] * inv)};
+          *reinterpret_cast<u32x2*>(op + 16 * dt) = w;
+        }
+      } else {
+        const int64_t r = ((int64_t)cur.sigma * p.total_q + tok) * p.num_q_heads + hn;
+        float* wp = p.ws_o + r * D + 4 * h4;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) *reinterpret_cast<f32x4*>(wp + 16 * dt) = acc[dt] * inv;
+        if (h4 == 0) p.ws_lse[r] = l > 0.f ? m + __log2f(l) : kNegInf;
+      }
+    }
+    if (!nxt.valid) break;
+    // advance: nxt becomes current; nx2's ids move to LDS; fetch the one after
+    ++mi;
+    cur = nxt;
+    nxt = nx2;
+    cb ^= 1;
+    store_ids(cb ^ 1, ids_v2);
+    nx2 = describe_item<G>(p, pref, q0t, lent, n_items, item_at(mi + 2), target);
+    load_ids(nx2, ids_v2);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) qB[ks] = qB_n[ks];
+    load_qb(nxt, qB_n);
+  }
+}
+
 // Log-sum-exp merge of key-split partials (all lse in the log2 domain):
 // w_sigma = 2^(lse_sigma - max lse), out = sum w O_sigma / sum w.  Parts with no
 // key carry lse = -inf and are skipped (their O is never read).
+__device__ __forceinline__ int merge_parts(const MergeParams& p, int64_t row) {
+  if (!p.per_seq_splits) return p.n_split;
+  // decode plans: sequence s has parts[s] parts; a single part was written
+  // straight to out by the forward kernel
+  const int tok = (int)(row / p.num_q_heads);
+  int lo = 0, hi = p.num_seqs - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (p.cu_q[mid] <= tok) lo = mid; else hi = mid - 1;
+  }
+  return p.parts[lo];
+}
+
+__device__ __forceinline__ void merge_store(const MergeParams& p, int64_t row, int d0, f32x4 o,
+                                            float wsum) {
+  const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+  const int64_t tok = row / p.num_q_heads;
+  const int hd = (int)(row % p.num_q_heads);
+  uint16_t* op = p.out + tok * p.o_st + (int64_t)hd * p.o_sh + d0;
+  u32x2 w = {pack_bf16x2(o[0] * inv, o[1] * inv), pack_bf16x2(o[2] * inv, o[3] * inv)};
+  *reinterpret_cast<u32x2*>(op) = w;
+}
+
+// Few parts per row: D/4 threads per row, each loops over the parts.
 template <int D>
-__global__ __launch_bounds__(256) void pa_merge_kernel(MergeParams p) {
-  constexpr int TPR = D / 4;                 // threads per (token, head) row
-  constexpr int RPB = 256 / TPR;             // rows per block
+__global__ __launch_bounds__(256) void pa_merge_rows_kernel(MergeParams p) {
+  constexpr int TPR = D / 4;
+  constexpr int RPB = 256 / TPR;
   const int64_t row = (int64_t)blockIdx.x * RPB + threadIdx.x / TPR;
   const int64_t nrows = (int64_t)p.total_q * p.num_q_heads;
   if (row >= nrows) return;
+  const int n_part = merge_parts(p, row);
+  if (p.per_seq_splits && n_part <= 1) return;
   const int d0 = (threadIdx.x % TPR) * 4;
   float M = kNegInf;
-  for (int sg = 0; sg < p.n_split; ++sg) M = fmaxf(M, p.ws_lse[sg * nrows + row]);
+  for (int sg = 0; sg < n_part; ++sg) M = fmaxf(M, p.ws_lse[sg * nrows + row]);
   f32x4 a = {0.f, 0.f, 0.f, 0.f};
   float ws = 0.f;
   if (M != kNegInf) {
-    for (int sg = 0; sg < p.n_split; ++sg) {
+    for (int sg = 0; sg < n_part; ++sg) {
       const float ls = p.ws_lse[sg * nrows + row];
       if (ls == kNegInf) continue;
       const float w = exp2_fast(ls - M);
@@ -648,12 +1062,56 @@ __global__ __launch_bounds__(256) void pa_merge_kernel(MergeParams p) {
       a += w * *reinterpret_cast<const f32x4*>(p.ws_o + (sg * nrows + row) * D + d0);
     }
   }
-  const float inv = ws > 0.f ? 1.f / ws : 0.f;
-  const int64_t tok = row / p.num_q_heads;
-  const int hd = (int)(row % p.num_q_heads);
-  uint16_t* op = p.out + tok * p.o_st + (int64_t)hd * p.o_sh + d0;
-  u32x2 w = {pack_bf16x2(a[0] * inv, a[1] * inv), pack_bf16x2(a[2] * inv, a[3] * inv)};
-  *reinterpret_cast<u32x2*>(op) = w;
+  merge_store(p, row, d0, a, ws);
+}
+
+// Many parts per row: one work-group per row; its threads form NG groups that
+// take every NG-th part (several loads in flight each), then reduce in LDS.
+template <int D>
+__global__ __launch_bounds__(256) void pa_merge_wide_kernel(MergeParams p) {
+  constexpr int TPG = D / 4;                 // threads per group (4 outputs each)
+  constexpr int NG = 256 / TPG;              // groups
+  __shared__ float red[NG][D + 4];
+  __shared__ float wred[NG];
+  __shared__ float mred[4];
+  const int64_t row = blockIdx.x;
+  const int64_t nrows = (int64_t)p.total_q * p.num_q_heads;
+  const int n_part = merge_parts(p, row);
+  if (p.per_seq_splits && n_part <= 1) return;   // uniform over the work-group
+  const int t = threadIdx.x;
+  const int g = t / TPG;
+  const int d0 = (t % TPG) * 4;
+  float M = kNegInf;
+  for (int sg = t; sg < n_part; sg += 256) M = fmaxf(M, p.ws_lse[sg * nrows + row]);
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) M = fmaxf(M, __shfl_xor(M, d));
+  if ((t & 63) == 0) mred[t >> 6] = M;
+  __syncthreads();
+  M = fmaxf(fmaxf(mred[0], mred[1]), fmaxf(mred[2], mred[3]));
+  f32x4 a = {0.f, 0.f, 0.f, 0.f};
+  float ws = 0.f;
+  if (M != kNegInf) {
+#pragma unroll 4
+    for (int sg = g; sg < n_part; sg += NG) {
+      const float ls = p.ws_lse[sg * nrows + row];
+      if (ls == kNegInf) continue;
+      const float w = exp2_fast(ls - M);
+      ws += w;
+      a += w * *reinterpret_cast<const f32x4*>(p.ws_o + (sg * nrows + row) * D + d0);
+    }
+  }
+  *reinterpret_cast<f32x4*>(&red[g][d0]) = a;
+  if (t % TPG == 0) wred[g] = ws;
+  __syncthreads();
+  if (g != 0) return;
+  float wt = 0.f;
+  f32x4 o = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int k = 0; k < NG; ++k) {
+    wt += wred[k];
+    o += *reinterpret_cast<const f32x4*>(&red[k][d0]);
+  }
+  merge_store(p, row, d0, o, wt);
 }
 
 template <int D, int G>
@@ -677,7 +1135,47 @@ hipError_t launch_fwd_d(const FwdParams& p, int group, bool wide, int64_t nwg, h
   }
 }
 
+template <int D, int G>
+hipError_t launch_decode_t(const FwdParams& p, int64_t nwg, hipStream_t stream) {
+  hipLaunchKernelGGL((pa_decode_kernel<D, G>), dim3((unsigned)nwg), dim3(kThreads), 0, stream, p);
+  return hipGetLastError();
+}
+
+template <int D, int G>
+int decode_blocks_per_cu_t() {
+  int n = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, pa_decode_kernel<D, G>, kThreads, 0) !=
+      hipSuccess) {
+    (void)hipGetLastError();
+    return 0;
+  }
+  return n;
+}
+
 }  // namespace
+
+#define PA_DISPATCH_DG(D_, G_, CALL)                                   \
+  switch (G_) {                                                        \
+    case 1: { constexpr int GG = 1; CALL; }                            \
+    case 2: { constexpr int GG = 2; CALL; }                            \
+    case 4: { constexpr int GG = 4; CALL; }                            \
+    case 8: { constexpr int GG = 8; CALL; }                            \
+    case 16: { constexpr int GG = 16; CALL; }                          \
+    default: break;                                                    \
+  }
+
+hipError_t launch_decode(const FwdParams& p, int head_dim, int group, int64_t nwg,
+                         hipStream_t stream) {
+  if (head_dim == 128) { PA_DISPATCH_DG(128, group, return (launch_decode_t<128, GG>(p, nwg, stream))); }
+  if (head_dim == 64) { PA_DISPATCH_DG(64, group, return (launch_decode_t<64, GG>(p, nwg, stream))); }
+  return hipErrorInvalidValue;
+}
+
+int decode_blocks_per_cu(int head_dim, int group) {
+  if (head_dim == 128) { PA_DISPATCH_DG(128, group, return (decode_blocks_per_cu_t<128, GG>())); }
+  if (head_dim == 64) { PA_DISPATCH_DG(64, group, return (decode_blocks_per_cu_t<64, GG>())); }
+  return 0;
+}
 
 bool fwd_supported(int head_dim, int group) {
   return (head_dim == 64 || head_dim == 128) &&
@@ -693,12 +1191,20 @@ hipError_t launch_fwd(const FwdParams& p, int head_dim, int group, bool wide, in
 
 hipError_t launch_merge(const MergeParams& p, int head_dim, hipStream_t stream) {
   const int64_t rows = (int64_t)p.total_q * p.num_q_heads;
+  if (rows <= 0) return hipSuccess;
+  const bool wide = p.n_split > 4;           // many parts: a work-group per row
   if (head_dim == 128) {
-    const int64_t nb = (rows + 7) / 8;
-    hipLaunchKernelGGL(pa_merge_kernel<128>, dim3((unsigned)nb), dim3(256), 0, stream, p);
+    if (wide)
+      hipLaunchKernelGGL(pa_merge_wide_kernel<128>, dim3((unsigned)rows), dim3(256), 0, stream, p);
+    else
+      hipLaunchKernelGGL(pa_merge_rows_kernel<128>, dim3((unsigned)((rows + 7) / 8)), dim3(256), 0,
+                         stream, p);
   } else if (head_dim == 64) {
-    const int64_t nb = (rows + 15) / 16;
-    hipLaunchKernelGGL(pa_merge_kernel<64>, dim3((unsigned)nb), dim3(256), 0, stream, p);
+    if (wide)
+      hipLaunchKernelGGL(pa_merge_wide_kernel<64>, dim3((unsigned)rows), dim3(256), 0, stream, p);
+    else
+      hipLaunchKernelGGL(pa_merge_rows_kernel<64>, dim3((unsigned)((rows + 15) / 16)), dim3(256), 0,
+                         stream, p);
   } else {
     return hipErrorInvalidValue;
   }

@@ -166,21 +166,26 @@ def plan_of(b, **opt):
 
 
 def test_plan_heuristic_on_workload_shapes():
-    # decode: one narrow tile per sequence, no split (2048 items fill the GPU)
+    # decode: persistent kernel, one narrow tile per sequence, no split (2048
+    # (sequence, kv-head) items are 4x the 512 resident work-groups)
     b = build_batch("d", np.ones(256, int), np.full(256, 1050), 32, 8, 128, True, 2)
     p = plan_of(b)
-    assert p["slots_direct"] == 1 and p["tile_tokens"] == 1 and p["num_splits"] == 1
-    assert p["num_workgroups"] == 256 * 8 and p["workspace_bytes"] == 0
-    # few long sequences: split keys
+    assert p["persistent"] == 1 and p["tile_tokens"] == 1 and p["num_splits"] == 1
+    assert p["num_workgroups"] == 256 * 2 and p["workspace_bytes"] == 0
+    # few long sequences: balanced splits sized on the device, >= 512 keys each;
+    # num_splits bounds the parts of any row
     b = build_batch("l", np.ones(16, int), np.full(16, 2048), 32, 8, 128, True, 5)
     p = plan_of(b)
-    assert p["num_splits"] > 1 and p["split_keys"] % 64 == 0
-    assert p["num_splits"] * p["split_keys"] >= 2048
-    assert p["workspace_bytes"] >= p["num_splits"] * 16 * 32 * 129 * 4
+    assert p["persistent"] == 1 and p["balanced"] == 1
+    assert p["split_keys"] == 512 and p["num_splits"] == 4
+    # a forced split count gives fixed-size parts
+    p = plan_of(b, force_num_splits=3)
+    assert p["balanced"] == 0 and p["num_splits"] == 3 and p["split_keys"] == 704
+    assert p["workspace_bytes"] >= p["num_splits"] * 16 * 32 * 129 * 4 + 16 * 4
     # prefill chunks: 64-row tiles (16 tokens at G = 4), slots bounded by T/Tq + S
     b = build_batch("p", [512, 1, 300], [700, 90, 300], 32, 8, 128, True, 3)
     p = plan_of(b)
-    assert p["tile_tokens"] == 16 and p["slots_direct"] == 0
+    assert p["tile_tokens"] == 16 and p["slots_direct"] == 0 and p["persistent"] == 0
     assert p["num_slots"] == 813 // 16 + 3
     # a forced split count is honoured up to one 64-key stage per split
     p = plan_of(b, force_num_splits=3)

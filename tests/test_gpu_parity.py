@@ -186,3 +186,54 @@ def test_check_contents_rejects_bad_metadata():
     out = torch.zeros_like(b.q)
     with pytest.raises(pa.PaError, match="PA_ERR_CONTENT"):
         pa.unified_attention(*b.args(out), opts=pa.options(check_contents=True))
+
+
+@pytest.mark.parametrize("splits", [0, 1, 2, 3, 7, 1000])
+@pytest.mark.parametrize("shape", [(32, 8, 128), (16, 2, 64)], ids=["g4d128", "g8d64"])
+def test_persistent_decode_ragged(splits, shape):
+    """Narrow batches on the persistent decode kernel: ragged contexts (0 to
+    5000 keys), several query tokens per sequence, per-sequence split counts."""
+    require_gpu()
+    hq, hkv, d = shape
+    G = hq // hkv
+    qmax = 16 // G
+    q_lens = [1, 1, 2, qmax, qmax - 1 if qmax > 1 else 1, 1, 1, qmax, 0, 1, 2 if qmax >= 2 else 1, 1]
+    k_lens = [1, 17, 300, 1000, 2500, 64, 65, 4, 10, 0, 5000, 129]
+    b = build_batch("pers", q_lens, k_lens, hq, hkv, d, True, seed=90 + splits, device=DEV)
+    opts = None if splits == 0 else pa.options(force_num_splits=splits)
+    plan = pa.plan_describe(*b.args(torch.empty_like(b.q))[:9], opts=opts)
+    assert plan["persistent"] == 1
+    say(f"persistent decode splits={splits} shape={shape} plan={plan['num_splits']}x{plan['split_keys']}")
+    out = run_pa(b, opts=opts)
+    torch.cuda.synchronize()
+    full_parity(b, out, f"persistent splits={splits}")
+
+
+def test_narrow_grid_path():
+    """The one-work-group-per-item narrow path (force_tile=3)."""
+    require_gpu()
+    b = build_batch("grid", [1, 2, 1, 4, 1], [700, 33, 1, 2000, 64], 32, 8, 128, True, seed=95,
+                    device=DEV)
+    for splits in (0, 3):
+        o = pa.options(force_tile=3, force_num_splits=splits)
+        plan = pa.plan_describe(*b.args(torch.empty_like(b.q))[:9], opts=o)
+        assert plan["persistent"] == 0
+        say(f"narrow grid splits={splits}")
+        out = run_pa(b, opts=o)
+        torch.cuda.synchronize()
+        full_parity(b, out, f"narrow grid splits={splits}")
+
+
+def test_many_sequences_fall_back_to_grid():
+    """More sequences than the persistent kernel enumerates (2048)."""
+    require_gpu()
+    rng = np.random.default_rng(96)
+    S = 2100
+    b = build_batch("many", np.ones(S, int), rng.integers(1, 40, size=S), 8, 2, 64, True,
+                    seed=96, device=DEV)
+    plan = pa.plan_describe(*b.args(torch.empty_like(b.q))[:9])
+    assert plan["persistent"] == 0
+    say("2100 sequences")
+    out = run_pa(b)
+    torch.cuda.synchronize()
+    full_parity(b, out, "many sequences")
