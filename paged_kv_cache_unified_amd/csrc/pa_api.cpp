@@ -173,13 +173,15 @@ size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 // Launch shape from shapes only (no device reads, no autotuning):
 //  * a batch whose every sequence fits one narrow tile (max_seqlen_q * G <= 16:
 //    pure decode, or short chunks) gets one tile per sequence;
-//  * otherwise query tiles of 64 packed rows (64/G tokens); sequences are
+//  * otherwise query tiles of 128 packed rows (128/G tokens); sequences are
 //    mapped to tile slots by the bound floor(cu[s]/Tq) + s, so the grid is
 //    known without reading cu_seqlens_q; tiles of <= 16 rows inside such a
 //    batch (its decode sequences) still run the narrow code path;
 //  * keys are split only when the items cannot fill the GPU: enough splits to
-//    reach ~8 work-groups per CU, each split at least 512 keys.  Split sizes
-//    depend on max_seqlen_k and the grid only, so results are deterministic.
+//    reach ~4 work-groups per CU, each split at least 512 keys and at most
+//    kMaxSplitKeys.  A sequence has ceil(L_s / split) parts, so rows of short
+//    sequences are never split.  Split sizes depend on max_seqlen_k and the
+//    grid only, so results are deterministic.
 int make_plan(const Shapes& s, int32_t max_q, int32_t max_k, const pa_options* opt, int num_cus,
               int decode_blocks_per_cu, Plan* out) {
   Plan p{};
@@ -258,7 +260,9 @@ int make_plan(const Shapes& s, int32_t max_q, int32_t max_k, const pa_options* o
   if (force_split > 0) {
     n_split = force_split;
   } else if (items > 0) {
-    const int64_t target = 8LL * std::max(num_cus, 1);
+    // about two rounds of the 2 resident work-groups per CU; a split costs a
+    // workspace round trip of every row it touches, so fuller grids do not split
+    const int64_t target = 4LL * std::max(num_cus, 1);
     if (items < target) {
       const int64_t by_len = (mk + 511) / 512;
       n_split = std::min((target + items - 1) / items, by_len);
@@ -475,8 +479,7 @@ int run(const pa_tensor* q, const pa_tensor* k, const pa_tensor* v, pa_tensor* o
     mp.total_q = (int32_t)s.T;
     mp.num_q_heads = (int32_t)s.Hq;
     mp.n_split = plan.n_split;
-    mp.per_seq_splits = plan.persistent ? 1 : 0;
-    mp.parts = p.ws_parts;
+    mp.parts = plan.persistent ? p.ws_parts : nullptr;
     mp.cu_q = p.cu_q;
     mp.seq_k = p.seq_k;
     mp.num_seqs = (int32_t)s.S;

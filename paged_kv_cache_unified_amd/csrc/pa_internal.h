@@ -10,7 +10,7 @@ namespace pa {
 constexpr int kBlockSize = 16;    // cache block size (tokens) the kernels are built for
 constexpr int kStageKeys = 64;    // keys staged in LDS per pipeline step
 constexpr int kThreads = 256;     // 4 wave64s per work-group
-constexpr int kTileRows = 64;     // packed rows of a wide query tile (16 per wave)
+constexpr int kTileRows = 128;    // packed rows of a wide query tile (32 per wave)
 constexpr int kNarrowRows = 16;   // rows of a narrow (decode) tile
 constexpr int kMaxSplitKeys = 4096;  // keys per split: at most 64 blocks per wave (narrow)
 constexpr int kMaxDecodeSeqs = 2048; // sequences the persistent decode kernel can enumerate
@@ -56,14 +56,16 @@ struct MergeParams {
   const float* ws_o;
   const float* ws_lse;
   uint16_t* out;
-  const int32_t* cu_q;     // per_seq_splits only
-  const int32_t* seq_k;
+  const int32_t* cu_q;     // [S+1]: row -> sequence
+  const int32_t* seq_k;    // [S]: parts of a grid plan, ceil(L_s / split_keys)
   int64_t o_st, o_sh;
   int32_t total_q;
   int32_t num_q_heads;
-  int32_t n_split;         // parts per row (upper bound when per_seq_splits)
-  int32_t per_seq_splits;  // 1: row of sequence s has parts[s] parts
-  const int32_t* parts;    // per_seq_splits: parts of each sequence
+  int32_t n_split;         // upper bound on parts per row
+  const int32_t* parts;    // persistent decode: parts of each sequence [S]; null:
+                           // ceil(seq_k / split_keys) clamped to [1, n_split].
+                           // Rows with one part were written by the forward
+                           // kernel and are skipped.
   int32_t num_seqs;
   int32_t split_keys;
 };

@@ -42,6 +42,8 @@
 // one cache tensor can exceed 2^31 elements (the int64 cast discussed in the
 // review of page "[ROCM][KERNEL] Paged attention for V1").
 
+#include <type_traits>
+
 #include "pa_internal.h"
 
 namespace pa {
@@ -60,6 +62,20 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 constexpr float kNegInf = -__builtin_huge_valf();
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// A wave-uniform value as a scalar (lets the compiler keep branches scalar).
+__device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+__device__ __forceinline__ void* uniform_ptr(const void* ptr) {
+  const uint64_t a = reinterpret_cast<uint64_t>(ptr);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+  return reinterpret_cast<void*>(((uint64_t)hi << 32) | lo);
+}
+// x *= s in place (tied operands keep a conditionally rescaled accumulator in
+// its own registers instead of a copy per branch)
+__device__ __forceinline__ void scale_inplace(float& x, float s) {
+  asm volatile("v_mul_f32 %0, %0, %1" : "+v"(x) : "v"(s));
+}
 
 // Round-to-nearest-even fp32 -> bf16 pair, packed low|high.
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
@@ -101,6 +117,7 @@ struct Layout {
 // One work item: (query tile, kv-head, key split) and the key range it covers.
 struct Item {
   int s, kvh, sigma;
+  int parts;          // key splits of this sequence (1: rows are written to out)
   int q0, q_len, tok0, n_tok, rows;
   int L, diag;        // context length; causal: token t sees keys < diag + t + 1
   int kbeg, kend;     // keys [kbeg, kend) of this split that some row may need
@@ -146,6 +163,9 @@ __device__ __forceinline__ bool decode_item(const FwdParams& p, Item& it) {
   it.n_tok = min(p.tile_tokens, it.q_len - it.tok0);
   it.rows = it.n_tok * G;
   it.L = p.seq_k[it.s];
+  // a sequence has ceil(L / split) parts (at least one): items past them idle
+  it.parts = min(max((it.L + p.split_keys - 1) / p.split_keys, 1), p.n_split);
+  if (it.sigma >= it.parts) return false;
   it.diag = it.L - it.q_len;
   const int k_need = p.causal ? min(it.L, it.diag + it.tok0 + it.n_tok) : it.L;
   it.kbeg = it.sigma * p.split_keys;
@@ -180,16 +200,6 @@ struct NarrowCfg {
   static constexpr int RED_STRIDE = D + 4;                        // floats per merged row
   static constexpr int RED_BYTES = (2 * 64 + 4 * 16 * RED_STRIDE) * 4;
   static constexpr int SMEM = VBUF_BYTES > RED_BYTES ? VBUF_BYTES : RED_BYTES;
-};
-template <int D>
-struct WideCfg {
-  static constexpr int BLK_BYTES = kBlockSize * D * 2;
-  static constexpr int NBS = kStageKeys / kBlockSize;
-  static constexpr int HALF_BYTES = NBS * BLK_BYTES;
-  static constexpr int STAGE_BYTES = 2 * HALF_BYTES;
-  static constexpr int IDS_OFFSET = 2 * STAGE_BYTES;
-  static constexpr int SMEM_RAW = IDS_OFFSET + (kMaxSplitKeys / kBlockSize) * 4;
-  static constexpr int SMEM = SMEM_RAW > NarrowCfg<D>::SMEM ? SMEM_RAW : NarrowCfg<D>::SMEM;
 };
 
 // ---------------------------------------------------------------------------
@@ -381,7 +391,7 @@ __device__ __forceinline__ void attend_narrow(const FwdParams& p, const Item& it
   }
   const int64_t tok = it.q0 + it.tok0 + n / G;
   const int hn = it.kvh * G + n % G;
-  if (p.n_split == 1) {
+  if (it.parts == 1) {
     uint16_t* op = p.out + tok * p.o_st + (int64_t)hn * p.o_sh + d0;
     if constexpr (DPER == 8) {
       u32x4 w = {pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]), pack_bf16x2(o[4], o[5]),
@@ -402,209 +412,303 @@ __device__ __forceinline__ void attend_narrow(const FwdParams& p, const Item& it
 }
 
 // ---------------------------------------------------------------------------
-// Wide tiles (17..64 packed rows: prefill and longer chunks).
+// Wide tiles (17..128 packed rows: prefill and longer chunks).
 //
-// Each wave owns 16 rows; the four waves sweep the same 64-key stages.  A
-// stage's 4 cache blocks of K and V are loaded row-contiguously into
-// registers while the previous stage is computed, then written into the other
-// of two LDS buffers (one barrier per stage).
+// Each wave owns 32 packed rows of the tile and all four waves sweep the same
+// 64-key stages, so both contractions run on v_mfma_f32_32x32x16_bf16 (a
+// 32-row B operand halves the LDS bytes read per flop compared with 16-row
+// tiles).  Lane l holds row l % 32; lanes l and l ^ 32 split that row's keys
+// (S^T = K Q^T puts key 8(r/4) + 4(l/32) + r%4 of a 32-key block in
+// accumulator r), so a row maximum is a lane-local reduction plus one
+// exchange between lanes l and l ^ 32.  P^T feeds O^T += V^T P^T straight from the score
+// registers: the contraction index of a 16-key slice is permuted to the
+// order the score accumulators hold, and the V^T operand is read in that
+// same order with two LDS transpose reads.
+//
+// Online softmax (fp32, log2 domain).  The running reference max m is kept in
+// raw score units and p = exp2(s c - m c) with c = |scale| log2(e) (Q is
+// negated on load for a negative scale), one FMA and one exp per score.  The
+// reference is moved, and O and l rescaled, only when some row's max exceeds
+// it by more than 2^8 (or a row sees its first key): exact in real
+// arithmetic, since O and l share the reference, and P <= 256 stays well
+// inside bf16 and fp32 range.  Masks (causal diagonal, context end) are applied
+// only in the stages that reach them.
+//
+// K and V of stage st+1 are loaded (16-byte buffer loads; a block past the
+// context end has zero records, so it reads as zeros without touching
+// memory) into registers while stage st is computed, then written to the
+// other of two LDS buffers: one barrier per stage.
 // ---------------------------------------------------------------------------
+template <int D>
+struct WideCfg {
+  static constexpr int CPR = D / 8;                        // 16-byte chunks per key row
+  static constexpr int TENSOR_BYTES = kStageKeys * D * 2;  // K (or V) of one stage
+  static constexpr int STAGE_BYTES = 2 * TENSOR_BYTES;
+  static constexpr int IDS_OFFSET = 2 * STAGE_BYTES;
+  static constexpr int SMEM_RAW = IDS_OFFSET + (kMaxSplitKeys / kBlockSize + 4) * 4;
+  static constexpr int SMEM = SMEM_RAW > NarrowCfg<D>::SMEM ? SMEM_RAW : NarrowCfg<D>::SMEM;
+  static constexpr int RPI = 64 / CPR;                     // key rows per wave-wide 1 KB load
+  static constexpr int CPT = kStageKeys / (4 * RPI);       // loads per thread per tensor
+  // LDS chunk of (key row r, chunk c): r * CPR + (c ^ f(r)).  fk spreads the
+  // 16 keys one K-operand read takes at a fixed chunk over 16 bank windows;
+  // fv does the same for the 4 rows x 4 chunks of each half-wave of a V
+  // transpose read.  Both depend on r % 16 only.
+  static __device__ __forceinline__ int fk(int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); }
+  static __device__ __forceinline__ int fv(int r) {
+    return D == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1);
+  }
+};
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+// Lanes l and l ^ 32 hold halves of one row.  (ds_bpermute through
+// __shfl_xor; the permlane32 swap builtin is not used because the compiler
+// folds its two results into one when both inputs are the same value.)
+__device__ __forceinline__ float swap_halves_max(float x) { return fmaxf(x, __shfl_xor(x, 32)); }
+__device__ __forceinline__ float swap_halves_sum(float x) { return x + __shfl_xor(x, 32); }
+
 template <int D, int G>
 __device__ __forceinline__ void attend_wide(const FwdParams& p, const Item& it,
                                             unsigned char* smem) {
-  using Lay = Layout<D>;
   using Cfg = WideCfg<D>;
-  constexpr int CPR = Lay::CPR;
-  constexpr int BLK_BYTES = Lay::BLK_BYTES;
-  constexpr int NBS = Cfg::NBS;
-  constexpr int HALF_BYTES = Cfg::HALF_BYTES;
-  constexpr int STAGE_BYTES = Cfg::STAGE_BYTES;
-  constexpr int CPT = NBS * kBlockSize * CPR / kThreads; // chunks per thread per tensor
-  constexpr int KS = D / 32;
-  constexpr int DT = D / 16;
-  static_assert(CPT * kThreads == NBS * kBlockSize * CPR, "stage must split evenly");
+  constexpr int CPR = Cfg::CPR;
+  constexpr int KS = D / 16;             // contraction steps of S^T = K Q^T
+  constexpr int DT = D / 32;             // 32-wide d tiles of O^T
+  constexpr int CPT = Cfg::CPT;
+  constexpr int RPI = Cfg::RPI;
+  constexpr int TB = Cfg::TENSOR_BYTES;
+  constexpr int SB = Cfg::STAGE_BYTES;
+  constexpr float kThr = 8.f;            // log2 headroom before the reference max moves
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (SGPR)
-  const int h4 = lane >> 4;
-  const int l16 = lane & 15;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31;
+  const int h = lane >> 5;
 
-  const int row = wave * 16 + l16;
-  bf16x8 qB[KS];
-  load_q<D, G>(p, it, row, h4, qB);
+  // ---- rows of this lane
+  const int row = wave * 32 + l32;
+  const bool row_ok = row < it.rows;
   const int t_in = row / G;
   const int head = it.kvh * G + row % G;
-  const bool row_ok = row < it.rows;
-  const int klim = p.causal ? min(it.kend, it.diag + it.tok0 + t_in + 1) : it.kend;
-  const int kbeg = it.kbeg, kend = it.kend, kmin = it.kmin;
+  const float c = fmaxf(fabsf(p.scale_log2), 1e-30f);
+  const uint32_t qflip = p.scale_log2 < 0.f ? 0x80008000u : 0u;
+  bf16x8 qB[KS];                          // B operand of S^T: d = 16 ks + 8 h + e
+  {
+    const uint16_t* qp = p.q + (int64_t)(it.q0 + it.tok0 + (row_ok ? t_in : 0)) * p.q_st +
+                         (int64_t)head * p.q_sh + 8 * h;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (row_ok) v = *reinterpret_cast<const u32x4*>(qp + 16 * ks);
+      v ^= qflip;
+      qB[ks] = __builtin_bit_cast(bf16x8, v);
+    }
+  }
+  const int kbeg = it.kbeg, kend = it.kend;
+  const int klim = p.causal ? min(kend, it.diag + it.tok0 + t_in + 1) : kend;
+  // keys below w_kmin are admissible for every row of this wave (no mask)
+  const int w_kmin = p.causal ? min(kend, it.diag + it.tok0 + (wave * 32) / G + 1) : kend;
 
-  const int nblk = (kend + kBlockSize - 1) / kBlockSize;
   const int blk0 = kbeg / kBlockSize;
+  const int nblk = kend > kbeg ? (kend + kBlockSize - 1) / kBlockSize - blk0 : 0;
   const int n_stage = kend > kbeg ? (kend - kbeg + kStageKeys - 1) / kStageKeys : 0;
-  const int32_t* btrow = p.bt + (int64_t)it.s * p.bt_stride;
-  const int64_t slot_stride = (int64_t)p.num_kv_heads * D;
-  const uint16_t* kbase = p.k + (int64_t)it.kvh * D;
-  const uint16_t* vbase = p.v + (int64_t)it.kvh * D;
-
-  // the item's block ids (at most kMaxSplitKeys / 16) staged once in LDS
+  const int32_t* btrow = p.bt + (int64_t)it.s * p.bt_stride + blk0;
   int32_t* ids = reinterpret_cast<int32_t*>(smem + Cfg::IDS_OFFSET);
-  if (tid < nblk - blk0) ids[tid] = btrow[blk0 + tid];
+  for (int i = tid; i < nblk; i += kThreads) ids[i] = btrow[i];
   __syncthreads();
 
+  // ---- global -> register -> LDS staging of one stage of K and V
+  const int slot_elems = p.num_kv_heads * D;
+  const int ld_r = wave * RPI + lane / CPR;          // key row of load u = 0
+  const int ld_c = lane % CPR;
+  const int ld_goff = ((ld_r % kBlockSize) * slot_elems + ld_c * 8) * 2;   // bytes
+  const int ld_koff = (ld_r * CPR + (ld_c ^ Cfg::fk(ld_r))) * 16;
+  const int ld_voff = (ld_r * CPR + (ld_c ^ Cfg::fv(ld_r))) * 16;
+  const int64_t head_off = (int64_t)it.kvh * D;
   u32x4 kreg[CPT], vreg[CPT];
   auto load_stage = [&](int st) {
+    // the stage's 4 block ids in one read (the table has 4 entries of padding,
+    // so the read one stage past the end stays inside it)
+    const int4 ids4 = *reinterpret_cast<const int4*>(ids + 4 * st);
 #pragma unroll
     for (int u = 0; u < CPT; ++u) {
-      const int c = tid + kThreads * u;
-      const int blk = c / (kBlockSize * CPR);
-      const int r = c % (kBlockSize * CPR);
-      const int key = r / CPR, dc = r % CPR;
-      const int jb = blk0 + st * NBS + blk;
-      if (jb < nblk) {
-        const int64_t off = (int64_t)ids[jb - blk0] * p.kv_sb + key * slot_stride + dc * 8;
-        kreg[u] = *reinterpret_cast<const u32x4*>(kbase + off);
-        vreg[u] = *reinterpret_cast<const u32x4*>(vbase + off);
-      }
+      // block within the stage: u (d = 128: 4 key rows per load) or 2u + wave/2
+      // (d = 64: 8 key rows per load)
+      const bool hi = D == 64 && (wave & 2);
+      const int bi = D == 128 ? u : 2 * u + (hi ? 1 : 0);
+      const int id = uniform(D == 128 ? ids4[u] : (hi ? ids4[(2 * u + 1) & 3] : ids4[(2 * u) & 3]));
+      const int jl = st * (kStageKeys / kBlockSize) + bi;
+      // keys of the block inside the item (0 past its end: no memory access)
+      const int valid = min(max(kend - (blk0 + jl) * kBlockSize, 0), kBlockSize);
+      const int nrec = uniform(valid * slot_elems * 2);
+      const int64_t boff = (int64_t)id * p.kv_sb + head_off;
+      const __amdgpu_buffer_rsrc_t rk =
+          __builtin_amdgcn_make_buffer_rsrc(uniform_ptr(p.k + boff), (short)0, nrec, 0x00020000);
+      const __amdgpu_buffer_rsrc_t rv =
+          __builtin_amdgcn_make_buffer_rsrc(uniform_ptr(p.v + boff), (short)0, nrec, 0x00020000);
+      kreg[u] = __builtin_amdgcn_raw_buffer_load_b128(rk, ld_goff, 0, 0);
+      vreg[u] = __builtin_amdgcn_raw_buffer_load_b128(rv, ld_goff, 0, 0);
     }
   };
-  auto store_stage = [&](int st, int buf) {
-    unsigned char* kb = smem + buf * STAGE_BYTES;
-    unsigned char* vb = kb + HALF_BYTES;
+  auto store_stage = [&](unsigned char* base) {
 #pragma unroll
     for (int u = 0; u < CPT; ++u) {
-      const int c = tid + kThreads * u;
-      const int blk = c / (kBlockSize * CPR);
-      const int r = c % (kBlockSize * CPR);
-      const int key = r / CPR, dc = r % CPR;
-      const int jb = blk0 + st * NBS + blk;
-      if (jb < nblk) {
-        *reinterpret_cast<u32x4*>(kb + blk * BLK_BYTES + Lay::k_chunk(key, dc) * 16) = kreg[u];
-        *reinterpret_cast<u32x4*>(vb + blk * BLK_BYTES + Lay::v_chunk(key, dc) * 16) = vreg[u];
+      *reinterpret_cast<u32x4*>(base + u * 4 * RPI * CPR * 16 + ld_koff) = kreg[u];
+      *reinterpret_cast<u32x4*>(base + TB + u * 4 * RPI * CPR * 16 + ld_voff) = vreg[u];
+    }
+  };
+
+  // ---- per-lane LDS read offsets
+  int koff[KS];                          // K operand: key row l32 (+32 kb), chunk 2 ks + h
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) koff[ks] = (l32 * CPR + ((2 * ks + h) ^ Cfg::fk(l32))) * 16;
+  const int j16 = lane & 15;
+  const int tr_row = 4 * h + (j16 >> 2);               // + 16 slice + 8 half
+  int voff[DT];                          // V^T operand: transpose read of 4 rows x 16 d
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) {
+    const int chunk = 4 * dt + 2 * ((lane >> 4) & 1) + ((j16 & 3) >> 1);
+    voff[dt] = (tr_row * CPR + (chunk ^ Cfg::fv(tr_row))) * 16 + 8 * (j16 & 1);
+  }
+
+  f32x16 acc[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[dt][r] = 0.f;
+  float m = kNegInf;                     // reference max (raw score units)
+  float l = 0.f;                         // this lane's half of the row sum
+  const float thr = kThr / c;
+
+  // One stage: S^T for 64 keys, mask (only where a row limit falls inside the
+  // stage), online softmax, O^T += V^T P^T.  Written without branches that
+  // touch the accumulators, so they stay in place across stages.
+  auto compute = [&](const unsigned char* Kb, int kst) {
+    const unsigned char* Vb = Kb + TB;
+    f32x16 s[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {     // two independent accumulation chains
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(Kb + kb * 32 * CPR * 16 + koff[ks]);
+        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qB[ks], s[kb], 0, 0, 0);
+      }
+    // operand reads run 4 ahead of the MFMAs: latency hidden, 16 registers
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+    for (int i = 0; i < 2 * KS - 4; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one LDS read
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+    if (kst + kStageKeys > w_kmin) {
+      const int rel = klim - kst - 4 * h;     // element (kb, r) is key 32kb + 8(r/4) + r%4 + 4h
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (32 * kb + 8 * (r >> 2) + (r & 3) >= rel) s[kb][r] = kNegInf;
+    }
+    float mx = s[0][0];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+    mx = swap_halves_max(mx);
+    const float mnew = fmaxf(m, mx);
+    if (__builtin_amdgcn_ballot_w64(mnew > m + thr)) {
+      const float alpha = m == kNegInf ? 0.f : exp2_fast((m - mnew) * c);
+      m = mnew;
+      l *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          float x = acc[dt][r];
+          scale_inplace(x, alpha);
+          acc[dt][r] = x;
+        }
+    }
+    const float mc = m == kNegInf ? 0.f : m * c;
+    bf16x8 pb[4];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float pr = exp2_fast(__builtin_fmaf(s[kb][r], c, -mc));
+        l += pr;
+        pb[2 * kb + (r >> 3)][r & 7] = (__bf16)pr;
+      }
+#pragma unroll
+    for (int sl = 0; sl < 4; ++sl) {
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        const unsigned char* a = Vb + sl * 16 * CPR * 16 + voff[dt];
+        const i16x4 a0 = __builtin_bit_cast(
+            i16x4, __builtin_amdgcn_ds_read_tr16_b64_v4bf16((PA_LDS bf16x4*)(a)));
+        const i16x4 a1 = __builtin_bit_cast(
+            i16x4, __builtin_amdgcn_ds_read_tr16_b64_v4bf16((PA_LDS bf16x4*)(a + 8 * CPR * 16)));
+        const u32x4 packed = {__builtin_bit_cast(u32x2, a0)[0], __builtin_bit_cast(u32x2, a0)[1],
+                              __builtin_bit_cast(u32x2, a1)[0], __builtin_bit_cast(u32x2, a1)[1]};
+        acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, packed),
+                                                          pb[sl], acc[dt], 0, 0, 0);
       }
     }
   };
 
-  f32x4 acc[DT];
-#pragma unroll
-  for (int i = 0; i < DT; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m = kNegInf;
-  float l = 0.f;
-  const int tr_key = 4 * h4 + (l16 >> 2);
-  const int tr_c_lo = (l16 & 3) >> 1;
-  const int tr_half = (l16 & 1) * 8;
-  auto vt_read = [&](const unsigned char* vblk, int dt) -> i16x4 {
-    const unsigned char* a = vblk + Lay::v_chunk(tr_key, 2 * dt + tr_c_lo) * 16 + tr_half;
-    return __builtin_bit_cast(i16x4,
-                              __builtin_amdgcn_ds_read_tr16_b64_v4bf16((PA_LDS bf16x4*)(a)));
-  };
-  auto vt_mask = [&](i16x4 v, int key_first) -> i16x4 {
-#pragma unroll
-    for (int e = 0; e < 4; ++e)
-      if (key_first + e >= kend) v[e] = 0;
-    return v;
+  // One pipeline step; `buf` is a constant so LDS offsets fold into the reads.
+  // The loads of the step after the last one have zero records (no memory
+  // access) and their LDS buffer is never read.
+  auto step = [&](int st, auto bufc) {
+    constexpr int buf = decltype(bufc)::value;
+    load_stage(st + 1);
+    compute(smem + buf * SB, kbeg + st * kStageKeys);
+    store_stage(smem + (buf ^ 1) * SB);
+    __syncthreads();
   };
 
   if (n_stage > 0) {
     load_stage(0);
-    store_stage(0, 0);
+    store_stage(smem);
   }
   __syncthreads();
-
-  for (int st = 0; st < n_stage; ++st) {
-    const int buf = st & 1;
-    if (st + 1 < n_stage) load_stage(st + 1);
-    const unsigned char* Kb = smem + buf * STAGE_BYTES;
-    const unsigned char* Vb = Kb + HALF_BYTES;
-    const int kst = kbeg + st * kStageKeys;
-    if (wave * 16 < it.rows) {
-      f32x4 sc[NBS];
-#pragma unroll
-      for (int b = 0; b < NBS; ++b) {
-        sc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
-        const unsigned char* kblk = Kb + b * BLK_BYTES;
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(
-              kblk + Lay::k_chunk(l16, 4 * ks + h4) * 16);
-          sc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qB[ks], sc[b], 0, 0, 0);
-        }
-      }
-      const bool need_mask = kst + kStageKeys > kmin;
-      float mx = kNegInf;
-#pragma unroll
-      for (int b = 0; b < NBS; ++b)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          float x = sc[b][r] * p.scale_log2;
-          if (need_mask && kst + 16 * b + 4 * h4 + r >= klim) x = kNegInf;
-          sc[b][r] = x;
-          mx = fmaxf(mx, x);
-        }
-      mx = max_across_groups(mx);
-      const float m_new = fmaxf(m, mx);
-      const float m_use = m_new == kNegInf ? 0.f : m_new;
-      const float alpha = exp2_fast(m - m_use);
-      float rs = 0.f;
-#pragma unroll
-      for (int b = 0; b < NBS; ++b)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float pr = exp2_fast(sc[b][r] - m_use);
-          sc[b][r] = pr;
-          rs += pr;
-        }
-      l = l * alpha + rs;
-      m = m_new;
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) acc[dt] *= alpha;
-      const bool vmask = kst + kStageKeys > kend;
-#pragma unroll
-      for (int half = 0; half < NBS / 2; ++half) {
-        const int b0 = 2 * half;
-        u32x4 pk = {pack_bf16x2(sc[b0][0], sc[b0][1]), pack_bf16x2(sc[b0][2], sc[b0][3]),
-                    pack_bf16x2(sc[b0 + 1][0], sc[b0 + 1][1]),
-                    pack_bf16x2(sc[b0 + 1][2], sc[b0 + 1][3])};
-        const bf16x8 pB = __builtin_bit_cast(bf16x8, pk);
-        const unsigned char* vlo = Vb + b0 * BLK_BYTES;
-        const unsigned char* vhi = vlo + BLK_BYTES;
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) {
-          i16x4 a0 = vt_read(vlo, dt);
-          i16x4 a1 = vt_read(vhi, dt);
-          if (vmask) {
-            a0 = vt_mask(a0, kst + 16 * b0 + 4 * h4);
-            a1 = vt_mask(a1, kst + 16 * (b0 + 1) + 4 * h4);
-          }
-          u32x4 packed = {__builtin_bit_cast(u32x2, a0)[0], __builtin_bit_cast(u32x2, a0)[1],
-                          __builtin_bit_cast(u32x2, a1)[0], __builtin_bit_cast(u32x2, a1)[1]};
-          acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, packed), pB,
-                                                           acc[dt], 0, 0, 0);
-        }
-      }
-    }
-    if (st + 1 < n_stage) store_stage(st + 1, buf ^ 1);
-    __syncthreads();
+  for (int st = 0; st < n_stage; st += 2) {
+    step(st, std::integral_constant<int, 0>());
+    if (st + 1 < n_stage) step(st + 1, std::integral_constant<int, 1>());
   }
 
-  l = sum_across_groups(l);
+  // ---- epilogue: lanes l and l ^ 32 together hold the row
+  const float lt = swap_halves_sum(l);
   if (!row_ok) return;
-  const float inv = l > 0.f ? 1.f / l : 0.f;
+  const float inv = lt > 0.f ? 1.f / lt : 0.f;
   const int64_t tok = it.q0 + it.tok0 + t_in;
-  if (p.n_split == 1) {
-    uint16_t* op = p.out + tok * p.o_st + (int64_t)head * p.o_sh + 4 * h4;
+  if (it.parts == 1) {
+    uint16_t* op = p.out + tok * p.o_st + (int64_t)head * p.o_sh + 4 * h;
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-      u32x2 w = {pack_bf16x2(acc[dt][0] * inv, acc[dt][1] * inv),
-                 pack_bf16x2(acc[dt][2] * inv, acc[dt][3] * inv)};
-      *reinterpret_cast<u32x2*>(op + 16 * dt) = w;
-    }
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const u32x2 w = {pack_bf16x2(acc[dt][4 * j] * inv, acc[dt][4 * j + 1] * inv),
+                         pack_bf16x2(acc[dt][4 * j + 2] * inv, acc[dt][4 * j + 3] * inv)};
+        *reinterpret_cast<u32x2*>(op + 32 * dt + 8 * j) = w;
+      }
   } else {
     const int64_t r = ((int64_t)it.sigma * p.total_q + tok) * p.num_q_heads + head;
-    float* wp = p.ws_o + r * D + 4 * h4;
+    float* wp = p.ws_o + r * D + 4 * h;
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) *reinterpret_cast<f32x4*>(wp + 16 * dt) = acc[dt] * inv;
-    if (h4 == 0) p.ws_lse[r] = l > 0.f ? m + __log2f(l) : kNegInf;
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const f32x4 v = {acc[dt][4 * j] * inv, acc[dt][4 * j + 1] * inv,
+                         acc[dt][4 * j + 2] * inv, acc[dt][4 * j + 3] * inv};
+        *reinterpret_cast<f32x4*>(wp + 32 * dt + 8 * j) = v;
+      }
+    if (h == 0) p.ws_lse[r] = lt > 0.f ? m * c + __log2f(lt) : kNegInf;
   }
 }
 
@@ -612,7 +716,8 @@ constexpr int kRing = 2;   // cache blocks in flight per wave on the narrow path
 
 // WIDE = false: every tile of the batch is narrow (the plan guarantees it).
 template <int D, int G, bool WIDE>
-__global__ __launch_bounds__(kThreads) void pa_fwd_kernel(FwdParams p) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
+void pa_fwd_kernel(FwdParams p) {
   constexpr int SMEM = WIDE ? WideCfg<D>::SMEM : NarrowCfg<D>::SMEM;
   __shared__ __attribute__((aligned(16))) unsigned char smem[SMEM];
   Item it;
@@ -655,7 +760,6 @@ struct DecodeCfg {
   static constexpr int SMEM = SCAN_OFFSET + 32;
 };
 
-__device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
 // Key parts of a sequence with `ql` queries and context L.  Fixed mode: parts
 // of `target` keys.  Balanced mode: round(L / target) equal parts (at least
@@ -1016,16 +1120,17 @@ void pa_decode_kernel(FwdParams p) {
 // w_sigma = 2^(lse_sigma - max lse), out = sum w O_sigma / sum w.  Parts with no
 // key carry lse = -inf and are skipped (their O is never read).
 __device__ __forceinline__ int merge_parts(const MergeParams& p, int64_t row) {
-  if (!p.per_seq_splits) return p.n_split;
-  // decode plans: sequence s has parts[s] parts; a single part was written
-  // straight to out by the forward kernel
+  // sequence s has parts[s] parts (persistent decode) or ceil(L_s / split)
+  // parts (grid plans); a single part was written straight to out by the
+  // forward kernel
   const int tok = (int)(row / p.num_q_heads);
   int lo = 0, hi = p.num_seqs - 1;
   while (lo < hi) {
     const int mid = (lo + hi + 1) >> 1;
     if (p.cu_q[mid] <= tok) lo = mid; else hi = mid - 1;
   }
-  return p.parts[lo];
+  if (p.parts) return p.parts[lo];
+  return min(max((p.seq_k[lo] + p.split_keys - 1) / p.split_keys, 1), p.n_split);
 }
 
 __device__ __forceinline__ void merge_store(const MergeParams& p, int64_t row, int d0, f32x4 o,
@@ -1047,7 +1152,7 @@ __global__ __launch_bounds__(256) void pa_merge_rows_kernel(MergeParams p) {
   const int64_t nrows = (int64_t)p.total_q * p.num_q_heads;
   if (row >= nrows) return;
   const int n_part = merge_parts(p, row);
-  if (p.per_seq_splits && n_part <= 1) return;
+  if (n_part <= 1) return;
   const int d0 = (threadIdx.x % TPR) * 4;
   float M = kNegInf;
   for (int sg = 0; sg < n_part; ++sg) M = fmaxf(M, p.ws_lse[sg * nrows + row]);
@@ -1077,7 +1182,7 @@ __global__ __launch_bounds__(256) void pa_merge_wide_kernel(MergeParams p) {
   const int64_t row = blockIdx.x;
   const int64_t nrows = (int64_t)p.total_q * p.num_q_heads;
   const int n_part = merge_parts(p, row);
-  if (p.per_seq_splits && n_part <= 1) return;   // uniform over the work-group
+  if (n_part <= 1) return;   // uniform over the work-group
   const int t = threadIdx.x;
   const int g = t / TPG;
   const int d0 = (t % TPG) * 4;

@@ -182,11 +182,19 @@ def test_plan_heuristic_on_workload_shapes():
     p = plan_of(b, force_num_splits=3)
     assert p["balanced"] == 0 and p["num_splits"] == 3 and p["split_keys"] == 704
     assert p["workspace_bytes"] >= p["num_splits"] * 16 * 32 * 129 * 4 + 16 * 4
-    # prefill chunks: 64-row tiles (16 tokens at G = 4), slots bounded by T/Tq + S
+    # prefill chunks: 128-row tiles (32 tokens at G = 4), slots bounded by T/Tq + S;
+    # 28 slots x 8 kv-heads fill less than 4 work-groups per CU, so keys split
+    # into >= 512-key ranges (700 keys: 2 of 384)
     b = build_batch("p", [512, 1, 300], [700, 90, 300], 32, 8, 128, True, 3)
     p = plan_of(b)
-    assert p["tile_tokens"] == 16 and p["slots_direct"] == 0 and p["persistent"] == 0
-    assert p["num_slots"] == 813 // 16 + 3
+    assert p["tile_tokens"] == 32 and p["slots_direct"] == 0 and p["persistent"] == 0
+    assert p["num_slots"] == 813 // 32 + 3
+    assert p["num_splits"] == 2 and p["split_keys"] == 384
+    # a full prefill batch does not split: 8 x 512 queries over 2048 keys
+    bf = build_batch("f", np.full(8, 512), np.full(8, 2048), 32, 8, 128, True, 4)
+    pf = plan_of(bf)
+    assert pf["num_splits"] == 1 and pf["workspace_bytes"] == 0
+    assert pf["num_slots"] * 8 >= 4 * 256
     # a forced split count is honoured up to one 64-key stage per split
     p = plan_of(b, force_num_splits=3)
     assert p["num_splits"] == 3 and p["split_keys"] == 256
