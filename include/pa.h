@@ -107,6 +107,10 @@ typedef struct {
                             device from the batch's total context so every
                             work-group streams about the same bytes; at least
                             split_keys keys per split                        */
+  int32_t longest_first; /* 1 (grid plans with wide tiles, at most 2048
+                            sequences): work-group b takes the (b / Hkv)-th
+                            (sequence, query tile, key split) in order of
+                            decreasing key count, kv-head b % Hkv            */
 } pa_plan_info;
 
 /*

@@ -40,7 +40,8 @@ class PaPlanInfo(ctypes.Structure):
                 ("num_slots", ctypes.c_int32), ("slots_direct", ctypes.c_int32),
                 ("num_splits", ctypes.c_int32), ("split_keys", ctypes.c_int32),
                 ("num_workgroups", ctypes.c_int64), ("workspace_bytes", ctypes.c_int64),
-                ("persistent", ctypes.c_int32), ("balanced", ctypes.c_int32)]
+                ("persistent", ctypes.c_int32), ("balanced", ctypes.c_int32),
+                ("longest_first", ctypes.c_int32)]
 
     def as_dict(self):
         return {name: getattr(self, name) for name, _ in self._fields_}
@@ -73,7 +74,7 @@ _SIGNATURES = {
 
 def _load():
     if not os.path.exists(LIB_PATH):
-        raise ImportError(f"{LIB_PATH} is not built; run `python -m paged_kv_cache_unified_amd.build`")
+        raise ImportError(f"{LIB_PATH} is not built; run `python paged_kv_cache_unified_amd/build.py`")
     lib = ctypes.CDLL(LIB_PATH)
     for name, (res, args) in _SIGNATURES.items():
         fn = getattr(lib, name)

@@ -1,6 +1,6 @@
 """Build libpa.so in-tree for gfx950 with hipcc.
 
-    python -m paged_kv_cache_unified_amd.build [--verbose]
+    python paged_kv_cache_unified_amd/build.py [--verbose]
 
 Every HIP source is compiled with ``-Xclang -target-feature -Xclang
 -packed-fp32-ops`` so the compiler never emits packed fp32 VALU instructions.

@@ -37,6 +37,7 @@ struct Shapes {
 struct Plan {
   int32_t tile_tokens, tile_rows, num_slots, slots_direct, n_split, split_keys;
   bool wide;        // launch the specialization with the wide-tile path
+  bool lpt;         // grid plan with longest-first unit order
   bool persistent;  // persistent decode kernel with per-sequence split counts
   bool balanced;    // persistent: part sizes chosen on the device from the total context
   int64_t num_items;
@@ -277,6 +278,9 @@ int make_plan(const Shapes& s, int32_t max_q, int32_t max_k, const pa_options* o
   p.split_keys = (int32_t)split_keys;
   p.num_items = items * n_split;
   p.nwg = (p.num_items + 7) / 8 * 8;
+  // wide plans rank their units longest-first on the device (LDS tables of
+  // the sequence lengths); larger batches keep the index order
+  p.lpt = p.wide && s.S <= pa::kLptMaxSeqs;
   if (p.num_items > kMaxInt32) return fail(PA_ERR_UNSUPPORTED, "grid too large");
   if (n_split > 1) {
     const size_t rows = (size_t)s.T * (size_t)s.Hq * (size_t)n_split;
@@ -460,6 +464,7 @@ int run(const pa_tensor* q, const pa_tensor* k, const pa_tensor* v, pa_tensor* o
   p.num_items = (int32_t)plan.num_items;
   p.items_per_xcd = (int32_t)(plan.nwg / 8);
   p.kv_major = plan.wide ? 1 : 0;
+  p.lpt = plan.lpt ? 1 : 0;
   p.causal = causal ? 1 : 0;
   p.narrow_rows = (opt && opt->force_tile == 2) ? 0 : pa::kNarrowRows;
   p.scale_log2 = (float)((double)scale * 1.4426950408889634);
@@ -553,6 +558,7 @@ int pa_plan_describe(const pa_tensor* q, const pa_tensor* k_cache, const pa_tens
     plan.ws_bytes = 0;
   }
   info->tile_tokens = plan.tile_tokens;
+  info->longest_first = plan.lpt ? 1 : 0;
   info->tile_rows = plan.tile_rows;
   info->num_slots = plan.num_slots;
   info->slots_direct = plan.slots_direct;

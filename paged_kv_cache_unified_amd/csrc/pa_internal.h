@@ -16,6 +16,7 @@ constexpr int kMaxSplitKeys = 4096;  // keys per split: at most 64 blocks per wa
 constexpr int kMaxDecodeSeqs = 2048; // sequences the persistent decode kernel can enumerate
 constexpr int kMinSplitKeys = 512;   // smallest balanced split of the persistent decode kernel
 constexpr int kDecodeItemsPerWave = 2; // balanced decode: items per resident wave
+constexpr int kLptMaxSeqs = 2048;   // longest-first order: LDS tables of 3 ints per sequence
 
 // Everything the forward kernel needs, by value.  Strides in elements.
 struct FwdParams {
@@ -49,6 +50,7 @@ struct FwdParams {
   int32_t kv_major;        // item order: 1 = (kv-head, slot, split), 0 = (slot, kv-head, split)
   int32_t causal;
   int32_t narrow_rows;     // tiles with at most this many packed rows take the narrow path
+  int32_t lpt;             // grid plans: units in longest-first order (block b -> rank b / Hkv)
   float scale_log2;        // softmax_scale * log2(e)
 };
 

@@ -124,45 +124,21 @@ struct Item {
   int kmin;           // smallest per-row key limit within the tile
 };
 
+// Fills the item for (sequence s, query tile, split sigma, kv-head); false if
+// the tile or split does not exist for this sequence.
 template <int G>
-__device__ __forceinline__ bool decode_item(const FwdParams& p, Item& it) {
-  // Work-groups are dispatched round-robin over the 8 XCDs (XCD = id % 8);
-  // give each XCD a contiguous range of items so items that share data
-  // (the q-tiles of one kv-head's context, or the kv-heads of one sequence's
-  // blocks) run close in time on the same L2.
-  const int item = (blockIdx.x & 7) * p.items_per_xcd + (blockIdx.x >> 3);
-  if (item >= p.num_items) return false;
-  it.sigma = item % p.n_split;
-  const int rest = item / p.n_split;
-  int slot;
-  if (p.kv_major) {
-    slot = rest % p.num_slots;
-    it.kvh = rest / p.num_slots;
-  } else {
-    it.kvh = rest % p.num_kv_heads;
-    slot = rest / p.num_kv_heads;
-  }
-  int tile;
-  if (p.slots_direct) {
-    it.s = slot;
-    tile = 0;
-  } else {
-    // sequence s owns slots [cu[s]/Tq + s, cu[s+1]/Tq + s + 1)
-    int lo = 0, hi = p.num_seqs - 1;
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (p.cu_q[mid] / p.tile_tokens + mid <= slot) lo = mid; else hi = mid - 1;
-    }
-    it.s = lo;
-    tile = slot - (p.cu_q[lo] / p.tile_tokens + lo);
-  }
-  it.q0 = p.cu_q[it.s];
-  it.q_len = p.cu_q[it.s + 1] - it.q0;
+__device__ __forceinline__ bool fill_item(const FwdParams& p, int s, int tile, int sigma, int kvh,
+                                          Item& it) {
+  it.s = s;
+  it.kvh = kvh;
+  it.sigma = sigma;
+  it.q0 = p.cu_q[s];
+  it.q_len = p.cu_q[s + 1] - it.q0;
   it.tok0 = tile * p.tile_tokens;
   if (it.tok0 >= it.q_len) return false;            // empty slot (whole work-group)
   it.n_tok = min(p.tile_tokens, it.q_len - it.tok0);
   it.rows = it.n_tok * G;
-  it.L = p.seq_k[it.s];
+  it.L = p.seq_k[s];
   // a sequence has ceil(L / split) parts (at least one): items past them idle
   it.parts = min(max((it.L + p.split_keys - 1) / p.split_keys, 1), p.n_split);
   if (it.sigma >= it.parts) return false;
@@ -172,6 +148,198 @@ __device__ __forceinline__ bool decode_item(const FwdParams& p, Item& it) {
   it.kend = min(k_need, it.kbeg + p.split_keys);
   it.kmin = p.causal ? min(it.kend, it.diag + it.tok0 + 1) : it.kend;
   return true;
+}
+
+// Exclusive prefix sum over the work-group (256 threads); *total receives the
+// sum.  scratch: 8 ints of LDS.  Contains barriers: call from every thread.
+__device__ __forceinline__ int block_exclusive_scan(int v, int* scratch, int* total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int x = v;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int y = __shfl_up(x, d);
+    if (lane >= d) x += y;
+  }
+  if (lane == 63) scratch[wave] = x;
+  __syncthreads();
+  int before = 0, all = 0;
+#pragma unroll
+  for (int w = 0; w < kThreads / 64; ++w) {
+    const int t = scratch[w];
+    before += w < wave ? t : 0;
+    all += t;
+  }
+  __syncthreads();                                   // scratch may be reused
+  *total = all;
+  return before + x - v;
+}
+
+// Stages (64 keys) of unit (s, tile, sigma), from the per-sequence lengths.
+__device__ __forceinline__ int unit_stages(const FwdParams& p, int q_len, int L, int tile,
+                                           int sigma) {
+  const int tok0 = tile * p.tile_tokens;
+  const int n_tok = min(p.tile_tokens, q_len - tok0);
+  const int k_need = p.causal ? min(L, L - q_len + tok0 + n_tok) : L;
+  const int kbeg = sigma * p.split_keys;
+  const int kend = min(k_need, kbeg + p.split_keys);
+  return kend > kbeg ? (kend - kbeg + kStageKeys - 1) / kStageKeys : 0;
+}
+
+// Longest-first order of the batch's units (sequence, query tile, key split),
+// so the work-group scheduler starts the most expensive tiles first and the
+// grid drains with short ones (list scheduling, longest processing time
+// first).  Unit rank r is decoded by every work-group from the lengths alone:
+// units are ranked by (stages descending, unit index ascending), where sequence
+// s owns unit indices [P[s], P[s] + tiles_s * parts_s) and index j within it is
+// (tile j % tiles_s, split j / tiles_s).  Uses LDS `tab` (3 S + 80 ints) and
+// barriers: call from every thread.  Returns false if there is no unit r.
+__device__ bool lpt_unit(const FwdParams& p, int r, int* tab, int* s_out, int* t_out,
+                         int* sg_out) {
+  const int S = p.num_seqs;
+  int* qlen = tab;                 // [S]
+  int* klen = tab + S;             // [S]
+  int* pre = tab + 2 * S;          // [S + 1] first unit index of each sequence
+  int* hist = tab + 3 * S + 1;     // [65] units per stage count (0..64)
+  int* scr = hist + 65;            // [8] scan scratch
+  int* res = scr + 8;              // [4] the chosen unit
+  const int tid = threadIdx.x;
+  const int Tq = p.tile_tokens;
+  // per-sequence tables; threads own contiguous runs of sequences
+  const int per = (S + kThreads - 1) / kThreads;
+  const int s0 = min(S, tid * per), s1 = min(S, s0 + per);
+  int mine = 0;
+  for (int s = s0; s < s1; ++s) {
+    const int q = p.cu_q[s + 1] - p.cu_q[s];
+    const int L = p.seq_k[s];
+    qlen[s] = q;
+    klen[s] = L;
+    const int parts = min(max((L + p.split_keys - 1) / p.split_keys, 1), p.n_split);
+    mine += ((q + Tq - 1) / Tq) * parts;
+  }
+  if (tid < 65) hist[tid] = 0;
+  int U;
+  int run = block_exclusive_scan(mine, scr, &U);
+  for (int s = s0; s < s1; ++s) {
+    pre[s] = run;
+    const int q = qlen[s], L = klen[s];
+    const int parts = min(max((L + p.split_keys - 1) / p.split_keys, 1), p.n_split);
+    run += ((q + Tq - 1) / Tq) * parts;
+  }
+  if (tid == 0) pre[S] = U;
+  __syncthreads();
+  if (r >= U) return false;                         // uniform: r is per work-group
+  // each thread walks a contiguous run of unit indices
+  const int cu = (U + kThreads - 1) / kThreads;
+  const int u0 = min(U, tid * cu), u1 = min(U, u0 + cu);
+  int s_first = 0;
+  if (u0 < u1) {
+    int lo = 0, hi = S - 1;                          // last s with pre[s] <= u0
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (pre[mid] <= u0) lo = mid; else hi = mid - 1;
+    }
+    s_first = lo;
+  }
+  auto walk = [&](auto&& visit) {
+    int s = s_first;
+    for (int u = u0; u < u1; ++u) {
+      while (u >= pre[s + 1]) ++s;                   // skips sequences without units
+      const int q = qlen[s];
+      const int nt = (q + Tq - 1) / Tq;
+      const int j = u - pre[s];
+      const int tile = j % nt, sg = j / nt;
+      if (!visit(s, tile, sg, unit_stages(p, q, klen[s], tile, sg))) return;
+    }
+  };
+  walk([&](int, int, int, int w) { atomicAdd(&hist[w], 1); return true; });
+  __syncthreads();
+  // stage count W of rank r: ranks run over W = 64, 63, ..., 0
+  int Wsel = 0, before = 0;
+  {
+    const int lane = tid & 63;
+    const int h = hist[64 - lane];                   // lane l <-> W = 64 - l (W = 1..64)
+    int x = h;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int y = __shfl_up(x, d);
+      if (lane >= d) x += y;
+    }
+    const unsigned long long hit = __builtin_amdgcn_ballot_w64(r < x);
+    if (hit) {
+      const int l = __builtin_ctzll(hit);
+      Wsel = 64 - l;
+      before = __shfl(x - h, l);
+    } else {
+      Wsel = 0;                                      // units without keys come last
+      before = __shfl(x, 63);
+    }
+  }
+  const int rr = r - before;                         // rank among units with Wsel stages
+  int cnt = 0;
+  walk([&](int, int, int, int w) { cnt += w == Wsel; return true; });
+  int dummy;
+  const int ex = block_exclusive_scan(cnt, scr, &dummy);
+  if (ex <= rr && rr < ex + cnt) {
+    int k = rr - ex;
+    walk([&](int s, int tile, int sg, int w) {
+      if (w != Wsel) return true;
+      if (k-- > 0) return true;
+      res[0] = s;
+      res[1] = tile;
+      res[2] = sg;
+      return false;
+    });
+  }
+  __syncthreads();
+  *s_out = res[0];
+  *t_out = res[1];
+  *sg_out = res[2];
+  __syncthreads();                                   // tables may be overwritten next
+  return true;
+}
+
+template <int G>
+__device__ __forceinline__ bool decode_item(const FwdParams& p, Item& it, unsigned char* smem) {
+  if (p.lpt) {
+    // block b -> unit rank b / Hkv, kv-head b % Hkv: with 8 kv-heads every
+    // XCD (b % 8) serves one kv-head, so K/V of its sequences stay in its L2
+    const int r = blockIdx.x / p.num_kv_heads;
+    const int kvh = blockIdx.x % p.num_kv_heads;
+    int s, tile, sg;
+    if (!lpt_unit(p, r, reinterpret_cast<int*>(smem), &s, &tile, &sg)) return false;
+    return fill_item<G>(p, s, tile, sg, kvh, it);
+  }
+  // Work-groups are dispatched round-robin over the 8 XCDs (XCD = id % 8);
+  // give each XCD a contiguous range of items so items that share data
+  // (the q-tiles of one kv-head's context, or the kv-heads of one sequence's
+  // blocks) run close in time on the same L2.
+  const int item = (blockIdx.x & 7) * p.items_per_xcd + (blockIdx.x >> 3);
+  if (item >= p.num_items) return false;
+  const int sigma = item % p.n_split;
+  const int rest = item / p.n_split;
+  int slot, kvh;
+  if (p.kv_major) {
+    slot = rest % p.num_slots;
+    kvh = rest / p.num_slots;
+  } else {
+    kvh = rest % p.num_kv_heads;
+    slot = rest / p.num_kv_heads;
+  }
+  int s, tile;
+  if (p.slots_direct) {
+    s = slot;
+    tile = 0;
+  } else {
+    // sequence s owns slots [cu[s]/Tq + s, cu[s+1]/Tq + s + 1)
+    int lo = 0, hi = p.num_seqs - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (p.cu_q[mid] / p.tile_tokens + mid <= slot) lo = mid; else hi = mid - 1;
+    }
+    s = lo;
+    tile = slot - (p.cu_q[lo] / p.tile_tokens + lo);
+  }
+  return fill_item<G>(p, s, tile, sigma, kvh, it);
 }
 
 // Q^T operand (B of S^T = K Q^T) for packed row `row` of the tile: lane group
@@ -714,6 +882,10 @@ __device__ __forceinline__ void attend_wide(const FwdParams& p, const Item& it,
 
 constexpr int kRing = 2;   // cache blocks in flight per wave on the narrow path
 
+// the longest-first tables (3 ints per sequence + 80) fit the wide kernel's LDS
+static_assert((3 * kLptMaxSeqs + 80) * 4 <= WideCfg<64>::SMEM, "LPT tables exceed LDS");
+static_assert((3 * kLptMaxSeqs + 80) * 4 <= WideCfg<128>::SMEM, "LPT tables exceed LDS");
+
 // WIDE = false: every tile of the batch is narrow (the plan guarantees it).
 template <int D, int G, bool WIDE>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
@@ -721,7 +893,7 @@ void pa_fwd_kernel(FwdParams p) {
   constexpr int SMEM = WIDE ? WideCfg<D>::SMEM : NarrowCfg<D>::SMEM;
   __shared__ __attribute__((aligned(16))) unsigned char smem[SMEM];
   Item it;
-  if (!decode_item<G>(p, it)) return;
+  if (!decode_item<G>(p, it, smem)) return;
   if (it.rows <= p.narrow_rows) {
     attend_narrow<D, G, kRing>(p, it, smem);
   } else {

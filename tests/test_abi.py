@@ -190,11 +190,18 @@ def test_plan_heuristic_on_workload_shapes():
     assert p["tile_tokens"] == 32 and p["slots_direct"] == 0 and p["persistent"] == 0
     assert p["num_slots"] == 813 // 32 + 3
     assert p["num_splits"] == 2 and p["split_keys"] == 384
+    assert p["longest_first"] == 1
     # a full prefill batch does not split: 8 x 512 queries over 2048 keys
     bf = build_batch("f", np.full(8, 512), np.full(8, 2048), 32, 8, 128, True, 4)
     pf = plan_of(bf)
     assert pf["num_splits"] == 1 and pf["workspace_bytes"] == 0
-    assert pf["num_slots"] * 8 >= 4 * 256
+    assert pf["num_slots"] * 8 >= 4 * 256 and pf["longest_first"] == 1
+    # decode plans and batches of more than 2048 sequences keep the index order
+    assert plan_of(build_batch("d", np.ones(8, int), np.full(8, 100), 32, 8, 128, True, 2))[
+        "longest_first"] == 0
+    qs = np.ones(2049, int)
+    qs[0] = 64
+    assert plan_of(build_batch("m", qs, np.full(2049, 64), 8, 2, 64, True, 6))["longest_first"] == 0
     # a forced split count is honoured up to one 64-key stage per split
     p = plan_of(b, force_num_splits=3)
     assert p["num_splits"] == 3 and p["split_keys"] == 256

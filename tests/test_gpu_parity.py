@@ -237,3 +237,41 @@ def test_many_sequences_fall_back_to_grid():
     out = run_pa(b)
     torch.cuda.synchronize()
     full_parity(b, out, "many sequences")
+
+
+@pytest.mark.parametrize("splits", [0, 3])
+def test_longest_first_ragged_units(splits):
+    """Wide plans rank (sequence, tile, split) units longest-first on the device:
+    ragged prefills, chunks, decode rows, empty sequences and key splits must
+    each be computed exactly once (out starts as NaN)."""
+    require_gpu()
+    rng = np.random.default_rng(97 + splits)
+    q_lens = [300, 1, 0, 77, 5, 512, 33, 1, 128, 2]
+    k_lens = [max(q, int(x)) for q, x in zip(q_lens, rng.integers(0, 2500, size=len(q_lens)))]
+    k_lens[2] = 0
+    b = build_batch("lpt", q_lens, k_lens, 32, 8, 128, True, seed=int(rng.integers(1 << 30)),
+                    device=DEV)
+    opts = None if splits == 0 else pa.options(force_num_splits=splits)
+    plan = pa.plan_describe(*b.args(torch.empty_like(b.q))[:9], opts=opts)
+    assert plan["longest_first"] == 1
+    say(f"longest-first splits={splits} plan={plan['num_splits']}x{plan['split_keys']}")
+    out = run_pa(b, opts=opts)
+    torch.cuda.synchronize()
+    full_parity(b, out, f"longest-first splits={splits}")
+
+
+def test_many_sequences_with_wide_tiles_keep_index_order():
+    """More than 2048 sequences with a wide tile: index-ordered grid."""
+    require_gpu()
+    rng = np.random.default_rng(98)
+    S = 2100
+    q_lens = np.ones(S, int)
+    q_lens[[0, 700, 2099]] = [40, 17, 64]
+    k_lens = np.maximum(q_lens, rng.integers(1, 60, size=S))
+    b = build_batch("many_wide", q_lens, k_lens, 8, 2, 64, True, seed=98, device=DEV)
+    plan = pa.plan_describe(*b.args(torch.empty_like(b.q))[:9])
+    assert plan["longest_first"] == 0 and plan["persistent"] == 0
+    say("2100 sequences with wide tiles")
+    out = run_pa(b)
+    torch.cuda.synchronize()
+    full_parity(b, out, "many sequences, wide")
