@@ -58,24 +58,23 @@ def source_hash():
     return h.hexdigest()[:16]
 
 
-def profile_path(workload):
-    return os.path.join(ROOT, "profiles", f"pa_fwd_{workload}.md")
+def profile_path(workload, kernel):
+    return os.path.join(ROOT, "profiles", f"{kernel}_{workload}.md")
 
 
 def traffic_record(workload):
-    """HBM bytes per launch of the forward kernel from the committed rocprofv3
+    """HBM bytes per launch of the dominant kernel from the committed rocprofv3
     summary, if its counters were taken on the current kernel sources; else None."""
-    path = profile_path(workload)
-    if not os.path.exists(path):
-        return None
-    text = open(path).read()
-    marker = "<!-- traffic "
-    if marker not in text:
-        return None
-    rec = json.loads(text.split(marker, 1)[1].split(" -->", 1)[0])
-    if rec.get("source_hash") != source_hash():
-        return None
-    return rec.get("traffic_bytes_per_launch")
+    import glob
+    for path in sorted(glob.glob(os.path.join(ROOT, "profiles", f"*_{workload}.md"))):
+        text = open(path).read()
+        marker = "<!-- traffic "
+        if marker not in text:
+            continue
+        rec = json.loads(text.split(marker, 1)[1].split(" -->", 1)[0])
+        if rec.get("workload") == workload and rec.get("source_hash") == source_hash():
+            return rec.get("traffic_bytes_per_launch")
+    return None
 
 
 PROF_COMMANDS = """cd /tmp && export TMPDIR=/tmp
@@ -88,7 +87,8 @@ python3 $REPO/bench.py --summarize $OUT --workload {w}"""
 
 
 def summarize_profiles(out_dir, workload):
-    """Write profiles/pa_fwd_<workload>.md from rocprofv3 output databases."""
+    """Write profiles/<kernel>_<workload>.md from rocprofv3 output databases,
+    for the library kernel with the largest total time in the trace."""
     import sqlite3
     import glob
 
@@ -101,15 +101,22 @@ def summarize_profiles(out_dir, workload):
     con = db(f"trace_{workload}")
     stats = list(con.execute("select name, total_calls, total_duration, average, percentage "
                              "from top_kernels limit 8"))
+    ours = [r for r in stats if "pa::" in r[0] and "_kernel" in r[0]]
+    if not ours:
+        raise SystemExit("no library kernel in the trace")
+    top = max(ours, key=lambda r: r[2])
+    kernel = top[0].replace("(anonymous namespace)::", "").split("<")[0].split("(")[0]
+    kernel = kernel.split("::")[-1]
+    like = f"%{kernel}%"
 
-    def counter(sub, name, like):
+    def counter(sub, name, pattern):
         rows = list(db(sub).execute(
             "select avg(value), count(*) from counters_collection where counter_name = ? "
-            "and kernel_name like ?", (name, like)))
+            "and kernel_name like ?", (name, pattern)))
         return rows[0]
 
-    fetch_k, n_f = counter(f"pmc_FETCH_SIZE_{workload}", "FETCH_SIZE", "%pa_fwd_kernel%")
-    write_k, n_w = counter(f"pmc_WRITE_SIZE_{workload}", "WRITE_SIZE", "%pa_fwd_kernel%")
+    fetch_k, n_f = counter(f"pmc_FETCH_SIZE_{workload}", "FETCH_SIZE", like)
+    write_k, n_w = counter(f"pmc_WRITE_SIZE_{workload}", "WRITE_SIZE", like)
     copy_bytes = 1 << 30
     fetch_c, _ = counter("pmc_FETCH_SIZE_copy", "FETCH_SIZE", "%copyBuffer%")
     write_c, _ = counter("pmc_WRITE_SIZE_copy", "WRITE_SIZE", "%copyBuffer%")
@@ -118,7 +125,7 @@ def summarize_profiles(out_dir, workload):
     fetch_bytes = fetch_k * 1024.0 * f_scale
     write_bytes = write_k * 1024.0 * w_scale
 
-    lines = [f"# pa_fwd_kernel on workload `{workload}` (MI355X, rocprofv3)", "",
+    lines = [f"# {kernel} on workload `{workload}` (MI355X, rocprofv3)", "",
              "Commands (OUT = an output folder, REPO = the repository root):", "", "```",
              PROF_COMMANDS.format(w=workload), "```", "",
              "## Kernel trace (--kernel-trace --stats), top kernels", "",
@@ -126,9 +133,10 @@ def summarize_profiles(out_dir, workload):
     for name, calls, total, avg, pct in stats:
         short = name.replace("(anonymous namespace)::", "").split("(")[0][-70:]
         lines.append(f"| `{short}` | {calls} | {total:.1f} | {avg:.2f} | {pct:.1f} |")
-    lines += ["", "(The run includes input generation kernels; the forward kernel's average "
-              "is the figure compared with the in-benchmark HIP-event timing.)", "",
-              "## HBM traffic of the forward kernel (--pmc, one counter per run)", "",
+    lines += ["", f"(The run includes "
+              f"input generation kernels; `{kernel}` is the kernel whose average is compared "
+              f"with the in-benchmark HIP-event timing.)", "",
+              f"## HBM traffic of `{kernel}` (--pmc, one counter per run)", "",
               f"- FETCH_SIZE: {fetch_k:.1f} KiB per dispatch (mean of {n_f} dispatches)",
               f"- WRITE_SIZE: {write_k:.1f} KiB per dispatch (mean of {n_w} dispatches)",
               f"- Calibration, 1 GiB device copy (`__amd_rocclr_copyBuffer`, {copy_bytes} B read "
@@ -136,49 +144,77 @@ def summarize_profiles(out_dir, workload):
               f"factors {f_scale:.4f} (fetch) and {w_scale:.4f} (write)",
               f"- Scaled: fetched {fetch_bytes / 1e9:.4f} GB, written {write_bytes / 1e9:.4f} GB, "
               f"total {(fetch_bytes + write_bytes) / 1e9:.4f} GB per launch", ""]
-    rec = {"workload": workload, "source_hash": source_hash(),
+    rec = {"workload": workload, "kernel": kernel, "source_hash": source_hash(),
+           "kernel_avg_us": top[3],
            "traffic_bytes_per_launch": int(fetch_bytes + write_bytes),
            "fetch_kib": fetch_k, "write_kib": write_k,
            "fetch_scale": f_scale, "write_scale": w_scale}
     lines.append("<!-- traffic " + json.dumps(rec) + " -->")
     os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
-    with open(profile_path(workload), "w") as f:
+    path = profile_path(workload, kernel)
+    with open(path, "w") as f:
         f.write("\n".join(lines) + "\n")
-    print(profile_path(workload))
+    print(path)
 
 
-def cpu_baseline(b, budget_s=20.0):
-    """The oracle, as it stands, on a bounded sample of the batch's sequences."""
+def cpu_baseline(b, unit, min_s=10.0, budget_s=20.0):
+    """The oracle, as it stands, on a bounded sample of the batch's sequences.
+
+    Sequences are taken longest context first (every 64th first, for a spread
+    of lengths) until the oracle has spent budget_s; if the whole batch takes
+    less than min_s, it is run again until min_s is reached.  The rate is in
+    the metric's unit: algorithmic bytes (TB/s) or flops (TFLOP/s) of the
+    sample over oracle time."""
     import threadpoolctl
 
     import oracle
     cores = len(os.sched_getaffinity(0))
-    threads = min(cores, 64)
+    # the host share may be smaller than the visible cores (OMP_NUM_THREADS)
+    threads = min(cores, int(os.environ.get("OMP_NUM_THREADS", cores) or cores), 64)
     order = np.argsort(b.k_lens)[::-1]
-    picked, total = [], 0.0
+    first = list(order[::max(1, len(order) // 64)])
+    sequence = first + [s for s in order if s not in set(first)]
+    subsets = {}
+    picked, t_all, passes = [], 0.0, 0
     with threadpoolctl.threadpool_limits(limits=threads):
-        t_all = 0.0
-        for s in list(order[::max(1, len(order) // 64)]) + list(order):
-            if s in picked:
-                continue
-            sub, _ = b.host_subset([int(s)])
-            t0 = time.perf_counter()
-            oracle.paged_attention(sub["q"], sub["k_cache"], sub["v_cache"], sub["cu_seqlens_q"],
-                                   sub["seqused_k"], sub["block_table"], sub["softmax_scale"],
-                                   sub["causal"])
-            t_all += time.perf_counter() - t0
-            picked.append(int(s))
-            if t_all >= budget_s or len(picked) == len(order):
+        while True:
+            for s in sequence:
+                s = int(s)
+                if s not in subsets:
+                    subsets[s] = b.host_subset([s])[0]
+                sub = subsets[s]
+                t0 = time.perf_counter()
+                oracle.paged_attention(sub["q"], sub["k_cache"], sub["v_cache"],
+                                       sub["cu_seqlens_q"], sub["seqused_k"], sub["block_table"],
+                                       sub["softmax_scale"], sub["causal"])
+                t_all += time.perf_counter() - t0
+                picked.append(s)
+                if t_all >= budget_s:
+                    break
+            passes += 1
+            if t_all >= min_s or t_all >= budget_s:
                 break
         info = threadpoolctl.threadpool_info()
     blas = ",".join(sorted({i.get("internal_api", "?") for i in info})) or "none"
-    sample_bytes = int(b.k_lens[picked].sum()) * b.num_kv_heads * b.head_dim * 4 + \
-        2 * int(b.q_lens[picked].sum()) * b.num_q_heads * b.head_dim * 2
-    return {"value": sample_bytes / t_all / 1e12, "unit": "TB/s", "cores": threads,
-            "kind": "oracle",
-            "sample": f"{len(picked)} of {b.num_seqs} sequences ({int(b.k_lens[picked].sum())} "
-                      f"context tokens), fp64 numpy oracle, {t_all:.1f} s, BLAS {blas}, "
-                      f"{cores} host cores visible"}
+    sel = np.array(picked)
+    kl, ql = b.k_lens[sel], b.q_lens[sel]
+    d, hq, hkv = b.head_dim, b.num_q_heads, b.num_kv_heads
+    if unit == "TFLOP/s":
+        pairs = 0
+        for q, L in zip(ql.tolist(), kl.tolist()):
+            if b.causal:
+                pairs += int(np.clip(L - q + np.arange(q) + 1, 0, L).sum())
+            else:
+                pairs += q * L
+        value = 4 * d * hq * pairs / t_all / 1e12
+    else:
+        sample_bytes = int(kl.sum()) * hkv * d * 4 + 2 * int(ql.sum()) * hq * d * 2
+        value = sample_bytes / t_all / 1e12
+    distinct = len(set(picked))
+    return {"value": value, "unit": unit, "cores": threads, "kind": "oracle",
+            "sample": f"{distinct} of {b.num_seqs} sequences ({int(b.k_lens[sorted(set(picked))].sum())} "
+                      f"context tokens), {passes} pass(es), {len(picked)} sequence calls, fp64 "
+                      f"numpy oracle, {t_all:.1f} s, BLAS {blas}, {cores} host cores visible"}
 
 
 def main():
@@ -329,9 +365,7 @@ def main():
     }
     if not args.no_cpu_baseline:
         print("bench: timing the CPU oracle on a sample", file=sys.stderr, flush=True)
-        res["cpu_baseline"] = cpu_baseline(b)
-        if unit != "TB/s":
-            res["cpu_baseline"]["note"] = "reported in TB/s of algorithmic bytes"
+        res["cpu_baseline"] = cpu_baseline(b, unit)
     print(json.dumps(res), flush=True)
 
 
