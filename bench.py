@@ -51,10 +51,15 @@ def algorithmic_work(b):
 
 
 def source_hash():
+    """Hash of the library's code (line comments and blank lines dropped, so a
+    comment edit does not mark the recorded counters stale)."""
     h = hashlib.sha256()
     for f in ("pa_kernels.hip", "pa_api.cpp", "pa_internal.h"):
-        with open(os.path.join(ROOT, "paged_kv_cache_unified_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "paged_kv_cache_unified_amd", "csrc", f)) as fh:
+            for line in fh:
+                code = line.split("//", 1)[0].strip()
+                if code:
+                    h.update(code.encode() + b"\n")
     return h.hexdigest()[:16]
 
 

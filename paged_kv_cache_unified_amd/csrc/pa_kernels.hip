@@ -10,33 +10,31 @@
 // Improved performance for V1 Triton (ROCm) backend", section "How is this
 // performance improvement achieved?").
 //
-// Work decomposition.  One work-group (4 wave64s) owns one item
-// (query tile, kv-head, key split).  The q-heads of one kv-head (the GQA group,
-// G of them) are packed with the tile's tokens into the rows of the MFMA tiles
-// (row r <-> token r / G, head r % G), so one K/V read serves G heads (the
-// "GQA packing along the query dimension" of the unified-kernel page).
+// Kernels.
+//  * pa_fwd_kernel: the unified grid kernel.  One work-group (4 wave64s) owns
+//    one unit (sequence, query tile, key split) for one kv-head; decode rows,
+//    chunks and prefills share the launch.  The q-heads of one kv-head (the
+//    GQA group, G of them) are packed with the tile's tokens into the rows of
+//    the MFMA tiles (row r <-> token r / G, head r % G), so one K/V read
+//    serves G heads (the packing of a kv-head's query heads into the query
+//    dimension that the unified-kernel page adopts).  Tiles of at most 16
+//    packed rows take the narrow path (four waves split the keys), larger ones
+//    the wide path (each wave owns 32 rows, 32x32x16 MFMA).  Wide plans run
+//    their units longest-first.
+//  * pa_decode_kernel: persistent decode for batches whose every sequence is
+//    one narrow tile; each wave streams (sequence, key part, kv-head) items.
+//  * pa_merge_*: log-sum-exp merge of key-split partial results.
 //
-//  * Narrow tiles (at most 16 packed rows: decode, short chunks) keep all rows
-//    in one 16-column MFMA tile in every wave; the four waves take different
-//    16-key blocks of each 64-key stage and merge their softmax states through
-//    LDS at the end.  This keeps four waves streaming one item's cache blocks.
-//  * Wide tiles (17..64 rows) give each wave its own 16 rows; all four waves
-//    sweep the same 64-key stages.
+// Scores are computed transposed, S^T = K Q^T, so each lane holds one packed
+// row's scores and softmax row reductions stay within a lane plus cross-lane
+// steps; P^T (bf16) feeds O^T += V^T P^T straight from the score accumulators,
+// with V^T operands from the gfx950 LDS transpose read (ds_read_b64_tr_b16) of
+// row-major V.  Softmax runs online in fp32 in the log2 domain.
 //
-// Per stage, the 16-byte chunks of 4 cache blocks of K and V are loaded
-// row-contiguously from HBM (a wave reads whole 256-byte key rows), held in
-// registers while the previous stage is computed, and written to the other of
-// two LDS buffers.  Scores are computed transposed, S^T = K Q^T, with
-// v_mfma_f32_16x16x32_bf16 so each lane holds one row's scores and the softmax
-// row reductions stay within a lane plus two cross-lane steps.  P^T (bf16)
-// feeds O^T += V^T P^T directly from the score accumulators; V^T operands come
-// from the gfx950 LDS transpose read (ds_read_b64_tr_b16) of row-major V.
-// Softmax runs online in fp32 in the log2 domain (scale folded into log2 e).
-//
-// Key splits: with n_split > 1 each item covers keys [sigma*split, (sigma+1)
-// *split) and writes its normalised fp32 output and log2-domain lse to the
-// workspace; pa_merge combines them.  Split boundaries depend on lengths only,
-// so results are deterministic.
+// Key splits: a sequence of L keys has ceil(L / split) parts (balanced on the
+// device in the persistent decode kernel); a part writes its normalised fp32
+// output and log2-domain lse to the workspace and pa_merge combines them.
+// Split boundaries depend on lengths only, so results are deterministic.
 //
 // Address math for the cache is 64-bit (physical block * block stride), since
 // one cache tensor can exceed 2^31 elements (the int64 cast discussed in the
