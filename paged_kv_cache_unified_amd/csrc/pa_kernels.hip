@@ -69,6 +69,13 @@ __device__ __forceinline__ void* uniform_ptr(const void* ptr) {
   const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
   return reinterpret_cast<void*>(((uint64_t)hi << 32) | lo);
 }
+// 16-byte global -> LDS DMA: lane i's 16 bytes (at voffset of the buffer
+// resource) land at LDS byte address lds + 16 i.  Callers wait with
+// wait_dma() before the barrier that publishes the data.
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rs, uint32_t voff, uint32_t lds) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (PA_LDS void*)(uintptr_t)lds, 16, voff, 0, 0, 0);
+}
+__device__ __forceinline__ void wait_dma() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 // x *= s in place (tied operands keep a conditionally rescaled accumulator in
 // its own registers instead of a copy per branch)
 __device__ __forceinline__ void scale_inplace(float& x, float s) {
@@ -600,10 +607,10 @@ __device__ __forceinline__ void attend_narrow(const FwdParams& p, const Item& it
 // inside bf16 and fp32 range.  Masks (causal diagonal, context end) are applied
 // only in the stages that reach them.
 //
-// K and V of stage st+1 are loaded (16-byte buffer loads; a block past the
-// context end has zero records, so it reads as zeros without touching
-// memory) into registers while stage st is computed, then written to the
-// other of two LDS buffers: one barrier per stage.
+// K and V of stage st+1 are copied by 16-byte DMA (buffer loads into LDS; a
+// block past the context end has zero records, so it reads as zeros without
+// touching memory) into the other of two LDS buffers while stage st is
+// computed: one barrier per stage, no staging registers.
 // ---------------------------------------------------------------------------
 template <int D>
 struct WideCfg {
@@ -684,16 +691,17 @@ __device__ __forceinline__ void attend_wide(const FwdParams& p, const Item& it,
   for (int i = tid; i < nblk; i += kThreads) ids[i] = btrow[i];
   __syncthreads();
 
-  // ---- global -> register -> LDS staging of one stage of K and V
+  // ---- one stage of K and V: global -> LDS by 16-byte DMA.  Lane i of a
+  // wave's load lands at LDS base + 16 i, so each lane fetches the chunk the
+  // swizzled layout keeps at its slot: key row r, slot p holds chunk p ^ f(r).
   const int slot_elems = p.num_kv_heads * D;
   const int ld_r = wave * RPI + lane / CPR;          // key row of load u = 0
-  const int ld_c = lane % CPR;
-  const int ld_goff = ((ld_r % kBlockSize) * slot_elems + ld_c * 8) * 2;   // bytes
-  const int ld_koff = (ld_r * CPR + (ld_c ^ Cfg::fk(ld_r))) * 16;
-  const int ld_voff = (ld_r * CPR + (ld_c ^ Cfg::fv(ld_r))) * 16;
+  const int ld_p = lane % CPR;                       // slot within the row
+  const int ld_gk = ((ld_r % kBlockSize) * slot_elems + (ld_p ^ Cfg::fk(ld_r)) * 8) * 2;
+  const int ld_gv = ((ld_r % kBlockSize) * slot_elems + (ld_p ^ Cfg::fv(ld_r)) * 8) * 2;
   const int64_t head_off = (int64_t)it.kvh * D;
-  u32x4 kreg[CPT], vreg[CPT];
-  auto load_stage = [&](int st) {
+  const uint32_t lds0 = uniform((int)(uint32_t)(uintptr_t)smem) + wave * RPI * CPR * 16;
+  auto load_stage = [&](int st, int buf) {
     // the stage's 4 block ids in one read (the table has 4 entries of padding,
     // so the read one stage past the end stays inside it)
     const int4 ids4 = *reinterpret_cast<const int4*>(ids + 4 * st);
@@ -705,7 +713,8 @@ __device__ __forceinline__ void attend_wide(const FwdParams& p, const Item& it,
       const int bi = D == 128 ? u : 2 * u + (hi ? 1 : 0);
       const int id = uniform(D == 128 ? ids4[u] : (hi ? ids4[(2 * u + 1) & 3] : ids4[(2 * u) & 3]));
       const int jl = st * (kStageKeys / kBlockSize) + bi;
-      // keys of the block inside the item (0 past its end: no memory access)
+      // keys of the block inside the item (0 past its end: no memory access,
+      // the DMA writes zeros)
       const int valid = min(max(kend - (blk0 + jl) * kBlockSize, 0), kBlockSize);
       const int nrec = uniform(valid * slot_elems * 2);
       const int64_t boff = (int64_t)id * p.kv_sb + head_off;
@@ -713,15 +722,9 @@ __device__ __forceinline__ void attend_wide(const FwdParams& p, const Item& it,
           __builtin_amdgcn_make_buffer_rsrc(uniform_ptr(p.k + boff), (short)0, nrec, 0x00020000);
       const __amdgpu_buffer_rsrc_t rv =
           __builtin_amdgcn_make_buffer_rsrc(uniform_ptr(p.v + boff), (short)0, nrec, 0x00020000);
-      kreg[u] = __builtin_amdgcn_raw_buffer_load_b128(rk, ld_goff, 0, 0);
-      vreg[u] = __builtin_amdgcn_raw_buffer_load_b128(rv, ld_goff, 0, 0);
-    }
-  };
-  auto store_stage = [&](unsigned char* base) {
-#pragma unroll
-    for (int u = 0; u < CPT; ++u) {
-      *reinterpret_cast<u32x4*>(base + u * 4 * RPI * CPR * 16 + ld_koff) = kreg[u];
-      *reinterpret_cast<u32x4*>(base + TB + u * 4 * RPI * CPR * 16 + ld_voff) = vreg[u];
+      const uint32_t dst = lds0 + buf * SB + u * 4 * RPI * CPR * 16;
+      dma16(rk, ld_gk, dst);
+      dma16(rv, ld_gv, dst + TB);
     }
   };
 
@@ -828,20 +831,19 @@ __device__ __forceinline__ void attend_wide(const FwdParams& p, const Item& it,
   };
 
   // One pipeline step; `buf` is a constant so LDS offsets fold into the reads.
-  // The loads of the step after the last one have zero records (no memory
-  // access) and their LDS buffer is never read.
+  // The other buffer was released by the previous step's barrier; its DMA
+  // completes (vmcnt) before this step's barrier.  The loads of the step after
+  // the last one have zero records (no memory access) and are never read.
   auto step = [&](int st, auto bufc) {
     constexpr int buf = decltype(bufc)::value;
-    load_stage(st + 1);
+    load_stage(st + 1, buf ^ 1);
     compute(smem + buf * SB, kbeg + st * kStageKeys);
-    store_stage(smem + (buf ^ 1) * SB);
+    wait_dma();
     __syncthreads();
   };
 
-  if (n_stage > 0) {
-    load_stage(0);
-    store_stage(smem);
-  }
+  if (n_stage > 0) load_stage(0, 0);
+  wait_dma();
   __syncthreads();
   for (int st = 0; st < n_stage; st += 2) {
     step(st, std::integral_constant<int, 0>());
