@@ -16,6 +16,7 @@ constexpr int kMaxSplitKeys = 4096;  // keys per split: at most 64 blocks per wa
 constexpr int kMaxDecodeSeqs = 2048; // sequences the persistent decode kernel can enumerate
 constexpr int kMinSplitKeys = 512;   // smallest balanced split of the persistent decode kernel
 constexpr int kDecodeItemsPerWave = 2; // balanced decode: items per resident wave
+constexpr int kDecodeRing = 2;        // cache blocks in flight per wave (persistent decode; 3 measured no faster)
 constexpr int kLptMaxSeqs = 2048;   // longest-first order: LDS tables of 3 ints per sequence
 
 // Everything the forward kernel needs, by value.  Strides in elements.

@@ -1128,12 +1128,13 @@ void pa_decode_kernel(FwdParams p) {
     }
   };
 
-  // Ring of two cache blocks per wave.  Every refill issues the same buffer
-  // loads through a per-block resource; a slot with nothing left to fetch
-  // gets a resource of zero records, so its loads return zeros without
+  // Ring of kDecodeRing cache blocks per wave.  Every refill issues the same
+  // buffer loads through a per-block resource; a slot with nothing left to
+  // fetch gets a resource of zero records, so its loads return zeros without
   // touching memory while the wait counts stay the same on every path.
-  u32x4 kst[2][KS];
-  u32x4 vst[2][VPL];
+  constexpr int RING = kDecodeRing;
+  u32x4 kst[RING][KS];
+  u32x4 vst[RING][VPL];
   const int blk_extent = kBlockSize * slot_stride * 2;      // bytes of one block, all heads
   auto issue = [&](int kvh, int phys, bool live, int j) {
     const int64_t boff = (int64_t)phys * p.kv_sb + (int64_t)kvh * D;
@@ -1167,9 +1168,9 @@ void pa_decode_kernel(FwdParams p) {
   bf16x8 qB[KS], qB_n[KS];
   load_qb(cur, qB);
   load_qb(nxt, qB_n);
-  // the first two blocks of the first item (idle slots load nothing)
-  issue(cur.kvh, cur.nb > 0 ? uniform(idsw[0]) : 0, cur.nb > 0, 0);
-  issue(cur.kvh, cur.nb > 1 ? uniform(idsw[1]) : 0, cur.nb > 1, 1);
+  // the first RING blocks of the first item (idle slots load nothing)
+#pragma unroll
+  for (int j = 0; j < RING; ++j) issue(cur.kvh, cur.nb > j ? uniform(idsw[j]) : 0, cur.nb > j, j);
 
   while (true) {
     const int* ids_c = idsw + cb * kMaxItemBlocks;
@@ -1179,14 +1180,16 @@ void pa_decode_kernel(FwdParams p) {
 #pragma unroll
     for (int i = 0; i < DT; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
     float m = kNegInf, l = 0.f;
-    const int nbp = max(2, (cur.nb + 1) & ~1);
-    for (int i = 0; i < nbp; i += 2) {
+    // stream positions of this item, padded to whole ring turns so the next
+    // item's block k sits in slot k
+    const int nbp = max(RING, (cur.nb + RING - 1) / RING * RING);
+    for (int i = 0; i < nbp; i += RING) {
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
+      for (int j = 0; j < RING; ++j) {
         const int b = i + j;
-        // what refills slot j once it is consumed: stream position b + 2 of
-        // this item, else of the next item, else nothing (a zero-record load)
-        const int t = b + 2;
+        // what refills slot j once it is consumed: stream position b + RING
+        // of this item, else of the next item, else nothing (a zero-record load)
+        const int t = b + RING;
         const bool in_cur = t < cur.nb;
         const bool in_nxt = !in_cur && t >= nbp && t - nbp < nxt.nb;
         const int r_phys = in_cur ? uniform(ids_c[t]) : (in_nxt ? uniform(ids_n[t - nbp]) : 0);
@@ -1195,7 +1198,7 @@ void pa_decode_kernel(FwdParams p) {
         // (1) consume slot j: V rows to LDS, scores S^T = K Q^T
         const bool live = b < cur.nb;
         const int kb = (cur.blk0 + b) * kBlockSize;
-        unsigned char* vbuf = vbuf0 + j * BLK_BYTES;
+        unsigned char* vbuf = vbuf0 + (j & 1) * BLK_BYTES;   // two V buffers per wave
         f32x4 sc = {0.f, 0.f, 0.f, 0.f};
         if (live) {
 #pragma unroll
