@@ -10,8 +10,8 @@ launch over its average launch duration, from HIP events on the launch stream)
 and the fp64 CPU oracle timed on a bounded sample of the same workload.
 
 Algorithmic bytes per launch: every valid context token's K and V read once
-(sum_s L_s * Hkv * d * 2 B * 2) plus q read and out written (2 * T * Hq * d *
-2 B).  Algorithmic flops: 4 * d * Hq * (admissible (query, key) pairs per head).
+(sum_s L_s * Hkv * d * e * 2, e = 2 B for bf16 caches and 1 B for fp8) plus q
+read and out written (2 * T * Hq * d * 2 B).  Algorithmic flops: 4 * d * Hq * (admissible (query, key) pairs per head).
 """
 
 from __future__ import annotations
@@ -34,9 +34,13 @@ BF16_PEAK_TFLOPS = 2500.0
 DEFAULT_WORKLOAD = "decode_256seq_ctx1k"
 
 
+def kv_elem_bytes(b):
+    return 1 if b.kv_format == "fp8_e4m3fn" else 2
+
+
 def algorithmic_work(b):
     d, hq, hkv = b.head_dim, b.num_q_heads, b.num_kv_heads
-    kv_bytes = int(b.k_lens.sum()) * hkv * d * 2 * 2
+    kv_bytes = int(b.k_lens.sum()) * hkv * d * 2 * kv_elem_bytes(b)
     qo_bytes = 2 * b.total_q * hq * d * 2
     pairs = 0
     for ql, L in zip(b.q_lens.tolist(), b.k_lens.tolist()):
@@ -191,7 +195,7 @@ def cpu_baseline(b, unit, min_s=10.0, budget_s=20.0):
                 t0 = time.perf_counter()
                 oracle.paged_attention(sub["q"], sub["k_cache"], sub["v_cache"],
                                        sub["cu_seqlens_q"], sub["seqused_k"], sub["block_table"],
-                                       sub["softmax_scale"], sub["causal"])
+                                       sub["softmax_scale"], sub["causal"], **b.kv_kwargs())
                 t_all += time.perf_counter() - t0
                 picked.append(s)
                 if t_all >= budget_s:
@@ -213,7 +217,7 @@ def cpu_baseline(b, unit, min_s=10.0, budget_s=20.0):
                 pairs += q * L
         value = 4 * d * hq * pairs / t_all / 1e12
     else:
-        sample_bytes = int(kl.sum()) * hkv * d * 4 + 2 * int(ql.sum()) * hq * d * 2
+        sample_bytes = int(kl.sum()) * hkv * d * 2 * kv_elem_bytes(b) + 2 * int(ql.sum()) * hq * d * 2
         value = sample_bytes / t_all / 1e12
     distinct = len(set(picked))
     return {"value": value, "unit": unit, "cores": threads, "kind": "oracle",
@@ -272,9 +276,9 @@ def main():
     out = torch.empty_like(b.q)
     call_args = b.args(out)
     opts, ws = None, None
-    if args.force_tile or args.force_splits or args.decode_grid:
+    if args.force_tile or args.force_splits or args.decode_grid or b.kv_format != "bf16":
         opts = pa.options(force_num_splits=args.force_splits, force_tile=args.force_tile,
-                          decode_grid=args.decode_grid)
+                          decode_grid=args.decode_grid, k_scale=b.k_scale, v_scale=b.v_scale)
         ws = torch.empty(max(1, pa.workspace_size(*call_args[:9], opts)), dtype=torch.uint8,
                          device=dev)
     plan = pa.plan_describe(*call_args[:9], opts=opts)
@@ -348,7 +352,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "bf16" if b.kv_format == "bf16" else "bf16 q/out, fp8 e4m3 KV",
         "data": "synthetic",
         "config": {
             "workload": args.workload,

@@ -41,7 +41,7 @@
 extern "C" {
 #endif
 
-#define PA_VERSION 1
+#define PA_VERSION 2
 
 /* Return codes.  Every failure is reported before anything is launched, with
  * one exception: PA_ERR_HIP, which may also come from the launch itself. */
@@ -58,7 +58,12 @@ typedef enum {
   PA_ERR_HIP = -9          /* the HIP runtime reported an error                */
 } pa_status;
 
-typedef enum { PA_BF16 = 1, PA_INT32 = 2, PA_FP32 = 3 } pa_dtype;
+/* PA_FP8_E4M3: OCP 8-bit float E4M3 ("fn": finite, S.1111.111 is NaN), one
+ * byte per element, for k_cache / v_cache only (page "[Kernel] [V1] Improved
+ * performance for V1 Triton (ROCm) backend", review discussion of the
+ * fp8_e4m3fn KV cache).  Element (b, t, h, i) of a cache then stands for
+ * decode(code) * k_scale (keys) or * v_scale (values); see pa_options. */
+typedef enum { PA_BF16 = 1, PA_INT32 = 2, PA_FP32 = 3, PA_FP8_E4M3 = 4 } pa_dtype;
 
 /* A strided view of device memory.  shape/stride entries beyond ndim are
  * ignored; strides are in ELEMENTS. */
@@ -88,6 +93,10 @@ typedef struct {
   int32_t decode_grid;      /* >0: work-groups of the persistent decode kernel
                                (rounded down to a multiple of 8; default: the
                                resident work-groups of the device)             */
+  float k_scale;            /* fp8 caches: dequantisation scale of k_cache
+                               (0 reads as 1; ignored for bf16 caches)        */
+  float v_scale;            /* fp8 caches: dequantisation scale of v_cache
+                               (0 reads as 1; ignored for bf16 caches)        */
 } pa_options;
 
 /* Launch shape chosen for a batch (pa_plan_describe). */
@@ -118,10 +127,13 @@ typedef struct {
  *
  *  q            bf16 [T, Hq, d]; stride[2] == 1; stride[0], stride[1] multiples
  *               of 8; 16-byte aligned.  T = total query tokens.
- *  k_cache      bf16 [NB, B, Hkv, d]; stride[1..3] contiguous (B*Hkv*d is not
- *               required for stride[0], which must be a multiple of 8 and at
- *               least B*Hkv*d); 16-byte aligned.
- *  v_cache      same shape and strides as k_cache.
+ *  k_cache      bf16 or fp8 E4M3 [NB, B, Hkv, d]; stride[1..3] contiguous
+ *               (B*Hkv*d is not required for stride[0], which must be a
+ *               multiple of 16 bytes and at least B*Hkv*d); 16-byte aligned.
+ *               With fp8 caches, scores use k_scale * decode(code) and outputs
+ *               v_scale * decode(code); this entry point uses scales of 1
+ *               (pa_unified_attention_ex takes them in pa_options).
+ *  v_cache      same dtype, shape and strides as k_cache.
  *  out          bf16 [T, Hq, d]; same rules as q; fully overwritten; must not
  *               overlap q, k_cache or v_cache.
  *  cu_seqlens_q int32 [S+1], contiguous: query offsets of the S sequences.

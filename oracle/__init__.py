@@ -7,6 +7,7 @@ code with the GPU library in ``paged_kv_cache_unified_amd``.
 
 from .attention import (  # noqa: F401
     attend_rows,
+    decode_e4m3fn,
     gather_context,
     merge_lse,
     paged_attention,

@@ -35,6 +35,14 @@ What it computes is the plain definition of the operation:
 
 All arithmetic is float64.  ``softmax_scale`` is first rounded to float32 so
 the oracle uses exactly the value a float32 kernel argument carries.
+
+fp8 caches (``kv_format="fp8_e4m3fn"``): the cache holds one-byte codes of the
+OCP 8-bit floating point format E4M3 in its "fn" variant (finite only; the
+KV-cache format discussed in the review of page "[Kernel] [V1] Improved
+performance for V1 Triton (ROCm) backend").  A code stands for
+``decode(code) * scale`` with one scale per cache tensor (``k_scale``,
+``v_scale``, rounded to float32 like ``softmax_scale``); ``decode_e4m3fn``
+writes the format's definition out.
 """
 
 from __future__ import annotations
@@ -42,7 +50,36 @@ from __future__ import annotations
 import numpy as np
 
 __all__ = ["paged_attention", "paged_attention_rows", "gather_context",
-           "attend_rows", "merge_lse"]
+           "attend_rows", "merge_lse", "decode_e4m3fn"]
+
+KV_FORMATS = ("bf16", "fp8_e4m3fn")
+
+
+def decode_e4m3fn(codes):
+    """float64 values of OCP 8-bit E4M3 ("fn") codes.
+
+    Bit 7 is the sign, bits 6..3 the exponent field e (bias 7), bits 2..0 the
+    mantissa field m.  e > 0: (1 + m/8) * 2^(e-7); e = 0: (m/8) * 2^-6
+    (subnormals and zero); e = 15 with m = 7 is NaN, and there is no infinity,
+    so the largest finite magnitude is (1 + 6/8) * 2^8 = 448.
+    """
+    c = np.asarray(codes).astype(np.int64) & 0xFF
+    sign = np.where(c >> 7, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = (c & 0x7).astype(np.float64)
+    mag = np.where(e == 0, np.ldexp(m / 8.0, -6), np.ldexp(1.0 + m / 8.0, e - 7))
+    mag = np.where((e == 15) & (c & 0x7 == 7), np.nan, mag)
+    return sign * mag
+
+
+def _context(cache, table_row, context_len, kv_format, scale):
+    """Gathered ``[L, Hkv, d]`` float64 values of one sequence's cache."""
+    if kv_format == "bf16":
+        return gather_context(cache, table_row, context_len)
+    if kv_format == "fp8_e4m3fn":
+        codes = gather_context(cache, table_row, context_len).astype(np.int64)
+        return decode_e4m3fn(codes) * float(np.float32(scale))
+    raise ValueError(f"kv_format must be one of {KV_FORMATS}")
 
 
 def gather_context(cache, block_table_row, context_len):
@@ -120,7 +157,8 @@ def _checked_meta(q, k_cache, cu_seqlens_q, seqused_k, block_table):
 
 
 def paged_attention(q, k_cache, v_cache, cu_seqlens_q, seqused_k, block_table,
-                    softmax_scale, causal, key_window=None):
+                    softmax_scale, causal, key_window=None, kv_format="bf16", k_scale=1.0,
+                    v_scale=1.0):
     """Whole-batch oracle.  Returns ``(out [T, Hq, d], lse [T, Hq])`` float64."""
     T, Hq, d, Hkv, G, cu, L, table = _checked_meta(q, k_cache, cu_seqlens_q,
                                                    seqused_k, block_table)
@@ -132,8 +170,8 @@ def paged_attention(q, k_cache, v_cache, cu_seqlens_q, seqused_k, block_table,
         q_len = t1 - t0
         if q_len == 0:
             continue
-        K = gather_context(k_cache, table[s], L[s])
-        V = gather_context(v_cache, table[s], L[s])
+        K = _context(k_cache, table[s], L[s], kv_format, k_scale)
+        V = _context(v_cache, table[s], L[s], kv_format, v_scale)
         positions = np.repeat(np.arange(q_len), G)          # row = (token, head in group)
         for g in range(Hkv):
             heads = slice(g * G, (g + 1) * G)
@@ -146,7 +184,8 @@ def paged_attention(q, k_cache, v_cache, cu_seqlens_q, seqused_k, block_table,
 
 
 def paged_attention_rows(q, k_cache, v_cache, cu_seqlens_q, seqused_k, block_table,
-                         softmax_scale, causal, tokens, heads):
+                         softmax_scale, causal, tokens, heads, kv_format="bf16", k_scale=1.0,
+                         v_scale=1.0):
     """Oracle for selected (token, q-head) rows only; returns ``(out [n, d], lse [n])``."""
     T, Hq, d, Hkv, G, cu, L, table = _checked_meta(q, k_cache, cu_seqlens_q,
                                                    seqused_k, block_table)
@@ -157,8 +196,8 @@ def paged_attention_rows(q, k_cache, v_cache, cu_seqlens_q, seqused_k, block_tab
     out = np.zeros((tokens.shape[0], d), dtype=np.float64)
     lse = np.full(tokens.shape[0], -np.inf, dtype=np.float64)
     for s in np.unique(seq_of):
-        K = gather_context(k_cache, table[s], L[s])
-        V = gather_context(v_cache, table[s], L[s])
+        K = _context(k_cache, table[s], L[s], kv_format, k_scale)
+        V = _context(v_cache, table[s], L[s], kv_format, v_scale)
         q_len = int(cu[s + 1] - cu[s])
         for g in np.unique(heads[seq_of == s] // G):
             sel = np.nonzero((seq_of == s) & (heads // G == g))[0]

@@ -21,8 +21,9 @@ import torch
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libpa.so")
 
-PA_BF16, PA_INT32, PA_FP32 = 1, 2, 3
-_DTYPES = {torch.bfloat16: PA_BF16, torch.int32: PA_INT32, torch.float32: PA_FP32}
+PA_BF16, PA_INT32, PA_FP32, PA_FP8_E4M3 = 1, 2, 3, 4
+_DTYPES = {torch.bfloat16: PA_BF16, torch.int32: PA_INT32, torch.float32: PA_FP32,
+           torch.float8_e4m3fn: PA_FP8_E4M3}
 
 
 class PaTensor(ctypes.Structure):
@@ -32,7 +33,8 @@ class PaTensor(ctypes.Structure):
 
 class PaOptions(ctypes.Structure):
     _fields_ = [("force_num_splits", ctypes.c_int32), ("force_tile", ctypes.c_int32),
-                ("check_contents", ctypes.c_int32), ("decode_grid", ctypes.c_int32)]
+                ("check_contents", ctypes.c_int32), ("decode_grid", ctypes.c_int32),
+                ("k_scale", ctypes.c_float), ("v_scale", ctypes.c_float)]
 
 
 class PaPlanInfo(ctypes.Structure):
@@ -125,9 +127,11 @@ def _descs(q, k_cache, v_cache, out, cu_seqlens_q, seqused_k, block_table):
 
 
 def options(force_num_splits: int = 0, force_tile: int = 0, check_contents: bool = False,
-            decode_grid: int = 0) -> PaOptions:
+            decode_grid: int = 0, k_scale: float = 0.0, v_scale: float = 0.0) -> PaOptions:
+    """pa_options; k_scale / v_scale are the fp8 caches' dequantisation scales
+    (0 reads as 1)."""
     return PaOptions(int(force_num_splits), int(force_tile), int(bool(check_contents)),
-                     int(decode_grid))
+                     int(decode_grid), float(k_scale), float(v_scale))
 
 
 def unified_attention(q, k_cache, v_cache, out, cu_seqlens_q, seqused_k, block_table,
@@ -135,6 +139,9 @@ def unified_attention(q, k_cache, v_cache, out, cu_seqlens_q, seqused_k, block_t
                       *, opts: Optional[PaOptions] = None,
                       workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Attention of the whole varlen batch into ``out`` (bf16 [T, Hq, d]).
+
+    Caches are bf16 or ``torch.float8_e4m3fn`` (E4M3 codes; their scales go in
+    ``opts``).
 
     With ``opts`` or ``workspace`` given, calls ``pa_unified_attention_ex``
     (``workspace`` then must be a device tensor of at least ``workspace_size``

@@ -32,6 +32,7 @@ int fail(int code, const char* fmt, ...) {
 struct Shapes {
   int64_t T, Hq, D, NB, B, Hkv, S, MB, G;
   int64_t q_st, q_sh, o_st, o_sh, kv_sb, bt_stride;
+  bool kv8;          // caches hold fp8 E4M3 codes (else bf16)
 };
 
 struct Plan {
@@ -58,13 +59,13 @@ int64_t extent_elems(const pa_tensor* t) {
   return e;
 }
 
-bool overlaps(const pa_tensor* a, const pa_tensor* b, int64_t elem_bytes) {
+bool overlaps(const pa_tensor* a, int64_t a_elem_bytes, const pa_tensor* b, int64_t b_elem_bytes) {
   const int64_t ea = extent_elems(a), eb = extent_elems(b);
   if (ea == 0 || eb == 0) return false;
   const uintptr_t a0 = reinterpret_cast<uintptr_t>(a->data);
   const uintptr_t b0 = reinterpret_cast<uintptr_t>(b->data);
-  const uintptr_t a1 = a0 + static_cast<uintptr_t>(ea * elem_bytes);
-  const uintptr_t b1 = b0 + static_cast<uintptr_t>(eb * elem_bytes);
+  const uintptr_t a1 = a0 + static_cast<uintptr_t>(ea * a_elem_bytes);
+  const uintptr_t b1 = b0 + static_cast<uintptr_t>(eb * b_elem_bytes);
   return a0 < b1 && b0 < a1;
 }
 
@@ -84,6 +85,9 @@ int validate(const pa_tensor* q, const pa_tensor* k, const pa_tensor* v, const p
               {v, "v_cache", PA_BF16, 4},    {out, "out", PA_BF16, 3},
               {cu, "cu_seqlens_q", PA_INT32, 1}, {sk, "seqused_k", PA_INT32, 1},
               {bt, "block_table", PA_INT32, 2}};
+  // caches: bf16, or fp8 E4M3 codes (both caches the same)
+  const bool kv8 = k->dtype == PA_FP8_E4M3;
+  if (kv8) spec[1].dtype = spec[2].dtype = PA_FP8_E4M3;
   for (auto& e : spec) {
     if (e.t->dtype != e.dtype)
       return fail(PA_ERR_DTYPE, "%s: dtype code %d, expected %d", e.name, e.t->dtype, e.dtype);
@@ -94,6 +98,8 @@ int validate(const pa_tensor* q, const pa_tensor* k, const pa_tensor* v, const p
         return fail(PA_ERR_SHAPE, "%s: negative extent or stride in dim %d", e.name, i);
   }
   Shapes s{};
+  s.kv8 = kv8;
+  const int64_t kv_esz = kv8 ? 1 : 2;
   s.T = q->shape[0];
   s.Hq = q->shape[1];
   s.D = q->shape[2];
@@ -140,8 +146,12 @@ int validate(const pa_tensor* q, const pa_tensor* k, const pa_tensor* v, const p
     return fail(PA_ERR_UNSUPPORTED, "caches need contiguous [block_size, num_kv_heads, head_dim]");
   if (s.NB > 1 && k->stride[0] < s.B * s.Hkv * s.D)
     return fail(PA_ERR_SHAPE, "cache block stride smaller than one block");
-  if ((q->stride[0] | q->stride[1] | out->stride[0] | out->stride[1] | k->stride[0]) % 8)
-    return fail(PA_ERR_ALIGN, "q/out/cache strides must be multiples of 8 elements");
+  if ((q->stride[0] | q->stride[1] | out->stride[0] | out->stride[1]) % 8)
+    return fail(PA_ERR_ALIGN, "q/out strides must be multiples of 8 elements");
+  if ((k->stride[0] * kv_esz) % 16)
+    return fail(PA_ERR_ALIGN, "cache block stride must be a multiple of 16 bytes");
+  if ((int64_t)pa::kBlockSize * s.Hkv * s.D * kv_esz > kMaxInt32)
+    return fail(PA_ERR_UNSUPPORTED, "one cache block exceeds 2^31 bytes");
   if (cu->stride[0] != 1 && cu->shape[0] > 1) return fail(PA_ERR_UNSUPPORTED, "cu_seqlens_q not contiguous");
   if (sk->stride[0] != 1 && s.S > 1) return fail(PA_ERR_UNSUPPORTED, "seqused_k not contiguous");
   if (bt->stride[1] != 1 && s.MB > 1) return fail(PA_ERR_UNSUPPORTED, "block_table rows not contiguous");
@@ -157,7 +167,7 @@ int validate(const pa_tensor* q, const pa_tensor* k, const pa_tensor* v, const p
     return fail(PA_ERR_ALIGN, "q/out/cache data must be 16-byte aligned");
   if (!aligned(cu->data, 4) || !aligned(sk->data, 4) || !aligned(bt->data, 4))
     return fail(PA_ERR_ALIGN, "int32 metadata must be 4-byte aligned");
-  if (overlaps(out, q, 2) || overlaps(out, k, 2) || overlaps(out, v, 2))
+  if (overlaps(out, 2, q, 2) || overlaps(out, 2, k, kv_esz) || overlaps(out, 2, v, kv_esz))
     return fail(PA_ERR_ALIAS, "out overlaps q, k_cache or v_cache");
   s.q_st = q->stride[0];
   s.q_sh = q->stride[1];
@@ -316,16 +326,17 @@ int device_cu_count(bool* ok) {
   return cache[dev];
 }
 
-int decode_blocks_per_cu_cached(int head_dim, int group) {
+int decode_blocks_per_cu_cached(int head_dim, int group, bool kv8) {
   static std::mutex mu;
-  static int cache[2][17] = {};
+  static int cache[2][2][17] = {};
   const int di = head_dim == 128 ? 1 : 0;
+  const int ki = kv8 ? 1 : 0;
   std::lock_guard<std::mutex> lock(mu);
-  if (cache[di][group] == 0) {
-    const int n = pa::decode_blocks_per_cu(head_dim, group);
-    cache[di][group] = n > 0 ? n : -1;
+  if (cache[di][ki][group] == 0) {
+    const int n = pa::decode_blocks_per_cu(head_dim, group, kv8);
+    cache[di][ki][group] = n > 0 ? n : -1;
   }
-  return cache[di][group] > 0 ? cache[di][group] : 2;
+  return cache[di][ki][group] > 0 ? cache[di][ki][group] : 2;
 }
 
 int check_contents(const Shapes& s, const pa_tensor* cu, const pa_tensor* sk, const pa_tensor* bt,
@@ -409,7 +420,7 @@ int run(const pa_tensor* q, const pa_tensor* k, const pa_tensor* v, pa_tensor* o
   if (s.T == 0 || s.S == 0) return PA_OK;
   bool have_dev = false;
   const int ncu = device_cu_count(&have_dev);
-  const int dbpc = have_dev ? decode_blocks_per_cu_cached((int)s.D, (int)s.G) : 2;
+  const int dbpc = have_dev ? decode_blocks_per_cu_cached((int)s.D, (int)s.G, s.kv8) : 2;
   Plan plan;
   rc = make_plan(s, max_q, max_k, opt, ncu, dbpc, &plan);
   if (rc != PA_OK) return rc;
@@ -432,8 +443,8 @@ int run(const pa_tensor* q, const pa_tensor* k, const pa_tensor* v, pa_tensor* o
   pa::FwdParams p{};
   p.q = static_cast<const uint16_t*>(q->data);
   p.out = static_cast<uint16_t*>(out->data);
-  p.k = static_cast<const uint16_t*>(k->data);
-  p.v = static_cast<const uint16_t*>(v->data);
+  p.k = static_cast<const unsigned char*>(k->data);
+  p.v = static_cast<const unsigned char*>(v->data);
   p.cu_q = static_cast<const int32_t*>(cu->data);
   p.seq_k = static_cast<const int32_t*>(sk->data);
   p.bt = static_cast<const int32_t*>(bt->data);
@@ -467,11 +478,15 @@ int run(const pa_tensor* q, const pa_tensor* k, const pa_tensor* v, pa_tensor* o
   p.lpt = plan.lpt ? 1 : 0;
   p.causal = causal ? 1 : 0;
   p.narrow_rows = (opt && opt->force_tile == 2) ? 0 : pa::kNarrowRows;
-  p.scale_log2 = (float)((double)scale * 1.4426950408889634);
+  // fp8 caches: k_scale folds into the score scale, v_scale into the output
+  const double k_scale = s.kv8 && opt && opt->k_scale != 0.f ? opt->k_scale : 1.0;
+  const double v_scale = s.kv8 && opt && opt->v_scale != 0.f ? opt->v_scale : 1.0;
+  p.scale_log2 = (float)((double)scale * k_scale * 1.4426950408889634);
+  p.out_scale = (float)v_scale;
   if (plan.nwg > 0) {
     hipError_t e = plan.persistent
-                       ? pa::launch_decode(p, (int)s.D, (int)s.G, plan.nwg, stream)
-                       : pa::launch_fwd(p, (int)s.D, (int)s.G, plan.wide, plan.nwg, stream);
+                       ? pa::launch_decode(p, (int)s.D, (int)s.G, s.kv8, plan.nwg, stream)
+                       : pa::launch_fwd(p, (int)s.D, (int)s.G, plan.wide, s.kv8, plan.nwg, stream);
     if (e != hipSuccess) return fail(PA_ERR_HIP, "forward launch: %s", hipGetErrorString(e));
   }
   if (plan.n_split > 1) {
@@ -529,7 +544,7 @@ size_t pa_workspace_size(const pa_tensor* q, const pa_tensor* k_cache, const pa_
   if (s.T == 0 || s.S == 0) return 0;
   bool have_dev = false;
   const int ncu = device_cu_count(&have_dev);
-  const int dbpc = have_dev ? decode_blocks_per_cu_cached((int)s.D, (int)s.G) : 2;
+  const int dbpc = have_dev ? decode_blocks_per_cu_cached((int)s.D, (int)s.G, s.kv8) : 2;
   Plan plan;
   if (make_plan(s, max_seqlen_q, max_seqlen_k, opt, ncu, dbpc, &plan) != PA_OK) return (size_t)-1;
   return plan.ws_bytes;
@@ -549,7 +564,7 @@ int pa_plan_describe(const pa_tensor* q, const pa_tensor* k_cache, const pa_tens
   bool have_dev = false;
   const int ncu = num_cus > 0 ? num_cus : device_cu_count(&have_dev);
   if (num_cus > 0) (void)device_cu_count(&have_dev);
-  const int dbpc = have_dev ? decode_blocks_per_cu_cached((int)s.D, (int)s.G) : 2;
+  const int dbpc = have_dev ? decode_blocks_per_cu_cached((int)s.D, (int)s.G, s.kv8) : 2;
   Plan plan;
   rc = make_plan(s, max_seqlen_q, max_seqlen_k, opt, ncu, dbpc, &plan);
   if (rc != PA_OK) return rc;

@@ -23,8 +23,8 @@ constexpr int kLptMaxSeqs = 2048;   // longest-first order: LDS tables of 3 ints
 struct FwdParams {
   const uint16_t* q;       // bf16 [T, Hq, d]
   uint16_t* out;           // bf16 [T, Hq, d]
-  const uint16_t* k;       // bf16 [NB, B, Hkv, d]
-  const uint16_t* v;
+  const unsigned char* k;  // [NB, B, Hkv, d] cache elements: bf16, or fp8 E4M3 codes
+  const unsigned char* v;
   const int32_t* cu_q;     // [S+1]
   const int32_t* seq_k;    // [S]
   const int32_t* bt;       // [S, bt_stride]
@@ -52,7 +52,8 @@ struct FwdParams {
   int32_t causal;
   int32_t narrow_rows;     // tiles with at most this many packed rows take the narrow path
   int32_t lpt;             // grid plans: units in longest-first order (block b -> rank b / Hkv)
-  float scale_log2;        // softmax_scale * log2(e)
+  float scale_log2;        // softmax_scale * k_scale * log2(e)
+  float out_scale;         // v_scale (1 for bf16 caches): multiplies every output row
 };
 
 struct MergeParams {
@@ -75,14 +76,15 @@ struct MergeParams {
 
 // Launchers (pa_kernels.hip).  Return the hipError_t of the launch.
 // wide = false launches the narrow-only specialization (every tile <= 16 rows).
-hipError_t launch_fwd(const FwdParams& p, int head_dim, int group, bool wide,
+// kv8: the caches hold fp8 E4M3 codes (else bf16).
+hipError_t launch_fwd(const FwdParams& p, int head_dim, int group, bool wide, bool kv8,
                       int64_t num_workgroups, hipStream_t stream);
 hipError_t launch_merge(const MergeParams& p, int head_dim, hipStream_t stream);
 // Persistent decode kernel (every tile narrow, num_seqs <= kMaxDecodeSeqs).
-hipError_t launch_decode(const FwdParams& p, int head_dim, int group, int64_t num_workgroups,
-                         hipStream_t stream);
+hipError_t launch_decode(const FwdParams& p, int head_dim, int group, bool kv8,
+                         int64_t num_workgroups, hipStream_t stream);
 // Resident work-groups per CU of the decode kernel (0 if unknown).
-int decode_blocks_per_cu(int head_dim, int group);
+int decode_blocks_per_cu(int head_dim, int group, bool kv8);
 bool fwd_supported(int head_dim, int group);
 
 }  // namespace pa

@@ -82,6 +82,39 @@ __device__ __forceinline__ void scale_inplace(float& x, float s) {
   asm volatile("v_mul_f32 %0, %0, %1" : "+v"(x) : "v"(s));
 }
 
+// Cache element formats: bf16, or fp8 E4M3 codes (OCP 8-bit float, the
+// "fn" variant: no infinities, S.1111.111 is NaN) converted to bf16 right
+// after the load.  Every E4M3 value is exact in bf16, so the MFMA paths see
+// the operands a bf16 cache of the decoded codes would give; the per-tensor
+// scales are folded into the softmax scale (K) and the output (V).
+template <bool KV8>
+struct Kv {
+  static constexpr int ESZ = KV8 ? 1 : 2;                                 // bytes per element
+  using raw8 = typename std::conditional<KV8, u32x2, u32x4>::type;        // 8 elements as loaded
+};
+__device__ __forceinline__ u32x4 to_bf16x8(u32x4 v) { return v; }
+__device__ __forceinline__ u32x4 to_bf16x8(u32x2 v) {
+  // v_cvt_scalef32_pk_bf16_fp8 with scale 1: two codes -> two bf16, exact
+  u32x4 r;
+  r[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v[0], 1.0f, false));
+  r[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v[0], 1.0f, true));
+  r[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v[1], 1.0f, false));
+  r[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v[1], 1.0f, true));
+  return r;
+}
+// 8 consecutive cache elements at a byte address / a buffer byte offset
+template <bool KV8>
+__device__ __forceinline__ typename Kv<KV8>::raw8 gload8(const unsigned char* ptr) {
+  return *reinterpret_cast<const typename Kv<KV8>::raw8*>(ptr);
+}
+template <bool KV8>
+__device__ __forceinline__ typename Kv<KV8>::raw8 bload8(__amdgpu_buffer_rsrc_t r, int byte_off) {
+  if constexpr (KV8)
+    return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, byte_off, 0, 0));
+  else
+    return __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0);
+}
+
 // Round-to-nearest-even fp32 -> bf16 pair, packed low|high.
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   bf16x2 v = {(__bf16)lo, (__bf16)hi};
@@ -387,9 +420,11 @@ struct NarrowCfg {
 // ids of the wave's (at most 64) blocks are fetched once into one VGPR and
 // read per block with readlane, so no KV load waits on a block-table load.
 // ---------------------------------------------------------------------------
-template <int D, int G, int P>
+template <int D, int G, int P, bool KV8>
 __device__ __forceinline__ void attend_narrow(const FwdParams& p, const Item& it,
                                               unsigned char* smem) {
+  constexpr int ESZ = Kv<KV8>::ESZ;
+  using raw8 = typename Kv<KV8>::raw8;
   using Lay = Layout<D>;
   using Cfg = NarrowCfg<D>;
   constexpr int CPR = Lay::CPR;
@@ -416,8 +451,8 @@ __device__ __forceinline__ void attend_narrow(const FwdParams& p, const Item& it
   if (lane < nb) ids = btrow[blk0 + wave + 4 * lane];
 
   const int slot_stride = p.num_kv_heads * D;
-  const uint16_t* kbase = p.k + it.kvh * D;
-  const uint16_t* vbase = p.v + it.kvh * D;
+  const unsigned char* kbase = p.k + (int64_t)it.kvh * D * ESZ;
+  const unsigned char* vbase = p.v + (int64_t)it.kvh * D * ESZ;
   const int koff = l16 * slot_stride + 8 * h4;
   int voff[VPL], vlds[VPL];
 #pragma unroll
@@ -428,18 +463,17 @@ __device__ __forceinline__ void attend_narrow(const FwdParams& p, const Item& it
     vlds[u] = Lay::v_chunk(key, dc) * 16;
   }
 
-  u32x4 kst[P][KS];
-  u32x4 vst[P][VPL];
+  raw8 kst[P][KS];
+  raw8 vst[P][VPL];
 #pragma unroll
   for (int j = 0; j < P; ++j) {
     if (j < nb) {
       const int64_t boff = (int64_t)__builtin_amdgcn_readlane(ids, j) * p.kv_sb;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks)
-        kst[j][ks] = *reinterpret_cast<const u32x4*>(kbase + boff + koff + 32 * ks);
+        kst[j][ks] = gload8<KV8>(kbase + (boff + koff + 32 * ks) * ESZ);
 #pragma unroll
-      for (int u = 0; u < VPL; ++u)
-        vst[j][u] = *reinterpret_cast<const u32x4*>(vbase + boff + voff[u]);
+      for (int u = 0; u < VPL; ++u) vst[j][u] = gload8<KV8>(vbase + (boff + voff[u]) * ESZ);
     }
   }
 
@@ -460,21 +494,21 @@ __device__ __forceinline__ void attend_narrow(const FwdParams& p, const Item& it
         const int kb = (blk0 + wave + 4 * i) * kBlockSize;
         unsigned char* vbuf = vbuf0 + (i & 1) * BLK_BYTES;
 #pragma unroll
-        for (int u = 0; u < VPL; ++u) *reinterpret_cast<u32x4*>(vbuf + vlds[u]) = vst[j][u];
+        for (int u = 0; u < VPL; ++u)
+          *reinterpret_cast<u32x4*>(vbuf + vlds[u]) = to_bf16x8(vst[j][u]);
         f32x4 sc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks)
-          sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kst[j][ks]),
-                                                       qB[ks], sc, 0, 0, 0);
+          sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              __builtin_bit_cast(bf16x8, to_bf16x8(kst[j][ks])), qB[ks], sc, 0, 0, 0);
         // refill this ring slot with block i + P
         if (i + P < nb) {
           const int64_t boff = (int64_t)__builtin_amdgcn_readlane(ids, i + P) * p.kv_sb;
 #pragma unroll
           for (int ks = 0; ks < KS; ++ks)
-            kst[j][ks] = *reinterpret_cast<const u32x4*>(kbase + boff + koff + 32 * ks);
+            kst[j][ks] = gload8<KV8>(kbase + (boff + koff + 32 * ks) * ESZ);
 #pragma unroll
-          for (int u = 0; u < VPL; ++u)
-            vst[j][u] = *reinterpret_cast<const u32x4*>(vbase + boff + voff[u]);
+          for (int u = 0; u < VPL; ++u) vst[j][u] = gload8<KV8>(vbase + (boff + voff[u]) * ESZ);
         }
         const bool need_mask = kb + kBlockSize > it.kmin;
         float x[4];
@@ -551,7 +585,7 @@ __device__ __forceinline__ void attend_narrow(const FwdParams& p, const Item& it
     wt[w] = exp2_fast(mw[w] - M_use);
     Ls += wt[w] * red_l[w * 16 + n];
   }
-  const float inv = Ls > 0.f ? 1.f / Ls : 0.f;
+  const float inv = Ls > 0.f ? p.out_scale / Ls : 0.f;
   float o[DPER];
 #pragma unroll
   for (int e = 0; e < DPER; e += 4) {
@@ -640,10 +674,12 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 __device__ __forceinline__ float swap_halves_max(float x) { return fmaxf(x, __shfl_xor(x, 32)); }
 __device__ __forceinline__ float swap_halves_sum(float x) { return x + __shfl_xor(x, 32); }
 
-template <int D, int G>
+template <int D, int G, bool KV8>
 __device__ __forceinline__ void attend_wide(const FwdParams& p, const Item& it,
                                             unsigned char* smem) {
   using Cfg = WideCfg<D>;
+  constexpr int ESZ = Kv<KV8>::ESZ;
+  using raw8 = typename Kv<KV8>::raw8;
   constexpr int CPR = Cfg::CPR;
   constexpr int KS = D / 16;             // contraction steps of S^T = K Q^T
   constexpr int DT = D / 32;             // 32-wide d tiles of O^T
@@ -691,16 +727,23 @@ __device__ __forceinline__ void attend_wide(const FwdParams& p, const Item& it,
   for (int i = tid; i < nblk; i += kThreads) ids[i] = btrow[i];
   __syncthreads();
 
-  // ---- one stage of K and V: global -> LDS by 16-byte DMA.  Lane i of a
-  // wave's load lands at LDS base + 16 i, so each lane fetches the chunk the
-  // swizzled layout keeps at its slot: key row r, slot p holds chunk p ^ f(r).
+  // ---- one stage of K and V.  bf16: global -> LDS by 16-byte DMA; lane i of
+  // a wave's load lands at LDS base + 16 i, so each lane fetches the chunk
+  // the swizzled layout keeps at its slot (key row r, slot s holds chunk
+  // s ^ f(r)).  fp8: each lane loads its row chunk's 8 codes into registers
+  // and, after the stage's compute, writes them as bf16 to the swizzled slot.
   const int slot_elems = p.num_kv_heads * D;
   const int ld_r = wave * RPI + lane / CPR;          // key row of load u = 0
-  const int ld_p = lane % CPR;                       // slot within the row
-  const int ld_gk = ((ld_r % kBlockSize) * slot_elems + (ld_p ^ Cfg::fk(ld_r)) * 8) * 2;
-  const int ld_gv = ((ld_r % kBlockSize) * slot_elems + (ld_p ^ Cfg::fv(ld_r)) * 8) * 2;
+  const int ld_p = lane % CPR;                       // slot (bf16) or chunk (fp8) in the row
+  const int ld_gk = ((ld_r % kBlockSize) * slot_elems +
+                     (KV8 ? ld_p : (ld_p ^ Cfg::fk(ld_r))) * 8) * ESZ;
+  const int ld_gv = ((ld_r % kBlockSize) * slot_elems +
+                     (KV8 ? ld_p : (ld_p ^ Cfg::fv(ld_r))) * 8) * ESZ;
+  const int ld_sk = (ld_r * CPR + (ld_p ^ Cfg::fk(ld_r))) * 16;   // fp8: LDS slot of the chunk
+  const int ld_sv = (ld_r * CPR + (ld_p ^ Cfg::fv(ld_r))) * 16;
   const int64_t head_off = (int64_t)it.kvh * D;
   const uint32_t lds0 = uniform((int)(uint32_t)(uintptr_t)smem) + wave * RPI * CPR * 16;
+  raw8 kraw[KV8 ? CPT : 1], vraw[KV8 ? CPT : 1];
   auto load_stage = [&](int st, int buf) {
     // the stage's 4 block ids in one read (the table has 4 entries of padding,
     // so the read one stage past the end stays inside it)
@@ -716,15 +759,31 @@ __device__ __forceinline__ void attend_wide(const FwdParams& p, const Item& it,
       // keys of the block inside the item (0 past its end: no memory access,
       // the DMA writes zeros)
       const int valid = min(max(kend - (blk0 + jl) * kBlockSize, 0), kBlockSize);
-      const int nrec = uniform(valid * slot_elems * 2);
-      const int64_t boff = (int64_t)id * p.kv_sb + head_off;
+      const int nrec = uniform(valid * slot_elems * ESZ);
+      const int64_t boff = ((int64_t)id * p.kv_sb + head_off) * ESZ;
       const __amdgpu_buffer_rsrc_t rk =
           __builtin_amdgcn_make_buffer_rsrc(uniform_ptr(p.k + boff), (short)0, nrec, 0x00020000);
       const __amdgpu_buffer_rsrc_t rv =
           __builtin_amdgcn_make_buffer_rsrc(uniform_ptr(p.v + boff), (short)0, nrec, 0x00020000);
-      const uint32_t dst = lds0 + buf * SB + u * 4 * RPI * CPR * 16;
-      dma16(rk, ld_gk, dst);
-      dma16(rv, ld_gv, dst + TB);
+      if constexpr (KV8) {
+        kraw[u] = bload8<true>(rk, ld_gk);
+        vraw[u] = bload8<true>(rv, ld_gv);
+      } else {
+        const uint32_t dst = lds0 + buf * SB + u * 4 * RPI * CPR * 16;
+        dma16(rk, ld_gk, dst);
+        dma16(rv, ld_gv, dst + TB);
+      }
+    }
+  };
+  // fp8: the registers of the last load_stage, as bf16, into LDS buffer buf
+  auto store_stage = [&](int buf) {
+    if constexpr (KV8) {
+      unsigned char* base = smem + buf * SB;
+#pragma unroll
+      for (int u = 0; u < CPT; ++u) {
+        *reinterpret_cast<u32x4*>(base + u * 4 * RPI * CPR * 16 + ld_sk) = to_bf16x8(kraw[u]);
+        *reinterpret_cast<u32x4*>(base + TB + u * 4 * RPI * CPR * 16 + ld_sv) = to_bf16x8(vraw[u]);
+      }
     }
   };
 
@@ -838,11 +897,15 @@ __device__ __forceinline__ void attend_wide(const FwdParams& p, const Item& it,
     constexpr int buf = decltype(bufc)::value;
     load_stage(st + 1, buf ^ 1);
     compute(smem + buf * SB, kbeg + st * kStageKeys);
+    store_stage(buf ^ 1);
     wait_dma();
     __syncthreads();
   };
 
-  if (n_stage > 0) load_stage(0, 0);
+  if (n_stage > 0) {
+    load_stage(0, 0);
+    store_stage(0);
+  }
   wait_dma();
   __syncthreads();
   for (int st = 0; st < n_stage; st += 2) {
@@ -853,7 +916,7 @@ __device__ __forceinline__ void attend_wide(const FwdParams& p, const Item& it,
   // ---- epilogue: lanes l and l ^ 32 together hold the row
   const float lt = swap_halves_sum(l);
   if (!row_ok) return;
-  const float inv = lt > 0.f ? 1.f / lt : 0.f;
+  const float inv = lt > 0.f ? p.out_scale / lt : 0.f;
   const int64_t tok = it.q0 + it.tok0 + t_in;
   if (it.parts == 1) {
     uint16_t* op = p.out + tok * p.o_st + (int64_t)head * p.o_sh + 4 * h;
@@ -887,7 +950,8 @@ static_assert((3 * kLptMaxSeqs + 80) * 4 <= WideCfg<64>::SMEM, "LPT tables excee
 static_assert((3 * kLptMaxSeqs + 80) * 4 <= WideCfg<128>::SMEM, "LPT tables exceed LDS");
 
 // WIDE = false: every tile of the batch is narrow (the plan guarantees it).
-template <int D, int G, bool WIDE>
+// KV8: the caches hold fp8 E4M3 codes.
+template <int D, int G, bool WIDE, bool KV8>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
 void pa_fwd_kernel(FwdParams p) {
   constexpr int SMEM = WIDE ? WideCfg<D>::SMEM : NarrowCfg<D>::SMEM;
@@ -895,9 +959,9 @@ void pa_fwd_kernel(FwdParams p) {
   Item it;
   if (!decode_item<G>(p, it, smem)) return;
   if (it.rows <= p.narrow_rows) {
-    attend_narrow<D, G, kRing>(p, it, smem);
+    attend_narrow<D, G, kRing, KV8>(p, it, smem);
   } else {
-    if constexpr (WIDE) attend_wide<D, G>(p, it, smem);
+    if constexpr (WIDE) attend_wide<D, G, KV8>(p, it, smem);
   }
 }
 
@@ -995,9 +1059,11 @@ __device__ __forceinline__ DItem describe_item(const FwdParams& p, const int* pr
   return d;
 }
 
-template <int D, int G>
+template <int D, int G, bool KV8>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
 void pa_decode_kernel(FwdParams p) {
+  constexpr int ESZ = Kv<KV8>::ESZ;
+  using raw8 = typename Kv<KV8>::raw8;
   using Lay = Layout<D>;
   using Cfg = DecodeCfg<D>;
   constexpr int CPR = Lay::CPR;
@@ -1133,21 +1199,20 @@ void pa_decode_kernel(FwdParams p) {
   // fetch gets a resource of zero records, so its loads return zeros without
   // touching memory while the wait counts stay the same on every path.
   constexpr int RING = kDecodeRing;
-  u32x4 kst[RING][KS];
-  u32x4 vst[RING][VPL];
-  const int blk_extent = kBlockSize * slot_stride * 2;      // bytes of one block, all heads
+  raw8 kst[RING][KS];
+  raw8 vst[RING][VPL];
+  const int blk_extent = kBlockSize * slot_stride * ESZ;    // bytes of one block, all heads
   auto issue = [&](int kvh, int phys, bool live, int j) {
-    const int64_t boff = (int64_t)phys * p.kv_sb + (int64_t)kvh * D;
+    const int64_t boff = ((int64_t)phys * p.kv_sb + (int64_t)kvh * D) * ESZ;
     const int nrec = live ? blk_extent : 0;
     const __amdgpu_buffer_rsrc_t rk =
         __builtin_amdgcn_make_buffer_rsrc((void*)(p.k + boff), (short)0, nrec, 0x00020000);
     const __amdgpu_buffer_rsrc_t rv =
         __builtin_amdgcn_make_buffer_rsrc((void*)(p.v + boff), (short)0, nrec, 0x00020000);
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-      kst[j][ks] = __builtin_amdgcn_raw_buffer_load_b128(rk, (koff + 32 * ks) * 2, 0, 0);
+    for (int ks = 0; ks < KS; ++ks) kst[j][ks] = bload8<KV8>(rk, (koff + 32 * ks) * ESZ);
 #pragma unroll
-    for (int u = 0; u < VPL; ++u) vst[j][u] = __builtin_amdgcn_raw_buffer_load_b128(rv, voff[u] * 2, 0, 0);
+    for (int u = 0; u < VPL; ++u) vst[j][u] = bload8<KV8>(rv, voff[u] * ESZ);
   };
 
   // items m (cur), m+1 (nxt), m+2 (nx2): ids of cur and nxt live in LDS, ids of
@@ -1202,11 +1267,12 @@ void pa_decode_kernel(FwdParams p) {
         f32x4 sc = {0.f, 0.f, 0.f, 0.f};
         if (live) {
 #pragma unroll
-          for (int u = 0; u < VPL; ++u) *reinterpret_cast<u32x4*>(vbuf + vlds[u]) = vst[j][u];
+          for (int u = 0; u < VPL; ++u)
+            *reinterpret_cast<u32x4*>(vbuf + vlds[u]) = to_bf16x8(vst[j][u]);
 #pragma unroll
           for (int ks = 0; ks < KS; ++ks)
-            sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kst[j][ks]),
-                                                         qB[ks], sc, 0, 0, 0);
+            sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                __builtin_bit_cast(bf16x8, to_bf16x8(kst[j][ks])), qB[ks], sc, 0, 0, 0);
         }
         // (2) refill slot j (one call site, so the ring registers never move)
         issue(r_kvh, r_phys, r_live, j);
@@ -1257,7 +1323,7 @@ void pa_decode_kernel(FwdParams p) {
     // ---- this wave's rows of the item ----
     l = sum_across_groups(l);
     if (l16 < cur.rows) {
-      const float inv = l > 0.f ? 1.f / l : 0.f;
+      const float inv = l > 0.f ? p.out_scale / l : 0.f;
       const int64_t tok = cur.q0 + l16 / G;
       const int hn = cur.kvh * G + l16 % G;
       if (cur.units == 1) {
@@ -1394,37 +1460,28 @@ __global__ __launch_bounds__(256) void pa_merge_wide_kernel(MergeParams p) {
   merge_store(p, row, d0, o, wt);
 }
 
-template <int D, int G>
+template <int D, int G, bool KV8>
 hipError_t launch_fwd_t(const FwdParams& p, bool wide, int64_t nwg, hipStream_t stream) {
   if (wide)
-    hipLaunchKernelGGL((pa_fwd_kernel<D, G, true>), dim3((unsigned)nwg), dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL((pa_fwd_kernel<D, G, true, KV8>), dim3((unsigned)nwg), dim3(kThreads), 0,
+                       stream, p);
   else
-    hipLaunchKernelGGL((pa_fwd_kernel<D, G, false>), dim3((unsigned)nwg), dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL((pa_fwd_kernel<D, G, false, KV8>), dim3((unsigned)nwg), dim3(kThreads), 0,
+                       stream, p);
   return hipGetLastError();
 }
 
-template <int D>
-hipError_t launch_fwd_d(const FwdParams& p, int group, bool wide, int64_t nwg, hipStream_t stream) {
-  switch (group) {
-    case 1: return launch_fwd_t<D, 1>(p, wide, nwg, stream);
-    case 2: return launch_fwd_t<D, 2>(p, wide, nwg, stream);
-    case 4: return launch_fwd_t<D, 4>(p, wide, nwg, stream);
-    case 8: return launch_fwd_t<D, 8>(p, wide, nwg, stream);
-    case 16: return launch_fwd_t<D, 16>(p, wide, nwg, stream);
-    default: return hipErrorInvalidValue;
-  }
-}
-
-template <int D, int G>
+template <int D, int G, bool KV8>
 hipError_t launch_decode_t(const FwdParams& p, int64_t nwg, hipStream_t stream) {
-  hipLaunchKernelGGL((pa_decode_kernel<D, G>), dim3((unsigned)nwg), dim3(kThreads), 0, stream, p);
+  hipLaunchKernelGGL((pa_decode_kernel<D, G, KV8>), dim3((unsigned)nwg), dim3(kThreads), 0, stream,
+                     p);
   return hipGetLastError();
 }
 
-template <int D, int G>
+template <int D, int G, bool KV8>
 int decode_blocks_per_cu_t() {
   int n = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, pa_decode_kernel<D, G>, kThreads, 0) !=
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, pa_decode_kernel<D, G, KV8>, kThreads, 0) !=
       hipSuccess) {
     (void)hipGetLastError();
     return 0;
@@ -1444,16 +1501,26 @@ int decode_blocks_per_cu_t() {
     default: break;                                                    \
   }
 
-hipError_t launch_decode(const FwdParams& p, int head_dim, int group, int64_t nwg,
+// head_dim x group x cache format -> one specialization
+#define PA_DISPATCH(D_, G_, K8_, CALL)                                                 \
+  do {                                                                                 \
+    if ((D_) == 128) {                                                                 \
+      if (K8_) { constexpr int DD = 128; constexpr bool KK = true; PA_DISPATCH_DG(DD, G_, CALL); } \
+      else { constexpr int DD = 128; constexpr bool KK = false; PA_DISPATCH_DG(DD, G_, CALL); }    \
+    } else if ((D_) == 64) {                                                           \
+      if (K8_) { constexpr int DD = 64; constexpr bool KK = true; PA_DISPATCH_DG(DD, G_, CALL); }  \
+      else { constexpr int DD = 64; constexpr bool KK = false; PA_DISPATCH_DG(DD, G_, CALL); }     \
+    }                                                                                  \
+  } while (0)
+
+hipError_t launch_decode(const FwdParams& p, int head_dim, int group, bool kv8, int64_t nwg,
                          hipStream_t stream) {
-  if (head_dim == 128) { PA_DISPATCH_DG(128, group, return (launch_decode_t<128, GG>(p, nwg, stream))); }
-  if (head_dim == 64) { PA_DISPATCH_DG(64, group, return (launch_decode_t<64, GG>(p, nwg, stream))); }
+  PA_DISPATCH(head_dim, group, kv8, return (launch_decode_t<DD, GG, KK>(p, nwg, stream)));
   return hipErrorInvalidValue;
 }
 
-int decode_blocks_per_cu(int head_dim, int group) {
-  if (head_dim == 128) { PA_DISPATCH_DG(128, group, return (decode_blocks_per_cu_t<128, GG>())); }
-  if (head_dim == 64) { PA_DISPATCH_DG(64, group, return (decode_blocks_per_cu_t<64, GG>())); }
+int decode_blocks_per_cu(int head_dim, int group, bool kv8) {
+  PA_DISPATCH(head_dim, group, kv8, return (decode_blocks_per_cu_t<DD, GG, KK>()));
   return 0;
 }
 
@@ -1462,10 +1529,9 @@ bool fwd_supported(int head_dim, int group) {
          (group == 1 || group == 2 || group == 4 || group == 8 || group == 16);
 }
 
-hipError_t launch_fwd(const FwdParams& p, int head_dim, int group, bool wide, int64_t nwg,
-                      hipStream_t stream) {
-  if (head_dim == 128) return launch_fwd_d<128>(p, group, wide, nwg, stream);
-  if (head_dim == 64) return launch_fwd_d<64>(p, group, wide, nwg, stream);
+hipError_t launch_fwd(const FwdParams& p, int head_dim, int group, bool wide, bool kv8,
+                      int64_t nwg, hipStream_t stream) {
+  PA_DISPATCH(head_dim, group, kv8, return (launch_fwd_t<DD, GG, KK>(p, wide, nwg, stream)));
   return hipErrorInvalidValue;
 }
 

@@ -35,8 +35,18 @@ def require_gpu():
     return torch.device("cuda:0")
 
 
+def with_scales(b, opts):
+    """opts carrying the batch's fp8 scales (None stays None for bf16 caches)."""
+    if b.kv_format == "bf16":
+        return opts
+    o = opts if opts is not None else pa.options()
+    o.k_scale, o.v_scale = b.k_scale, b.v_scale
+    return o
+
+
 def run_pa(b, opts=None, out=None, stream=None):
     """The GPU path through the C ABI (plain entry point, or _ex with opts)."""
+    opts = with_scales(b, opts)
     if out is None:
         out = torch.full_like(b.q, float("nan"))
     ws = None
@@ -74,7 +84,7 @@ def full_parity(b, out, what=""):
     h = b.host()
     ref, _ = oracle.paged_attention(h["q"], h["k_cache"], h["v_cache"], h["cu_seqlens_q"],
                                     h["seqused_k"], h["block_table"], h["softmax_scale"],
-                                    h["causal"])
+                                    h["causal"], **b.kv_kwargs())
     return check_close(out.float().cpu().numpy(), ref, what)
 
 
@@ -83,7 +93,7 @@ def sampled_parity(b, out, seq_ids, what=""):
     sub, rows = b.host_subset(seq_ids)
     ref, _ = oracle.paged_attention(sub["q"], sub["k_cache"], sub["v_cache"],
                                     sub["cu_seqlens_q"], sub["seqused_k"], sub["block_table"],
-                                    sub["softmax_scale"], sub["causal"])
+                                    sub["softmax_scale"], sub["causal"], **b.kv_kwargs())
     g = out.index_select(0, torch.as_tensor(rows, device=out.device)).float().cpu().numpy()
     return check_close(g, ref, what)
 

@@ -350,6 +350,57 @@ def pin_brute_grid(orc, full=True):
 
 
 # cheap pins first: the mutation tests stop at the first failure
+def pin_fp8_decoder(orc):
+    """E4M3 ("fn") decoding: every one of the 256 codes against torch's own
+    float8_e4m3fn conversion (a library routine), plus values derived by hand
+    from the format's definition (bias 7, subnormals below 2^-6, no infinity,
+    S.1111.111 NaN)."""
+    codes = np.arange(256, dtype=np.uint8)
+    mine = orc.decode_e4m3fn(codes)
+    lib = torch.from_numpy(codes.copy()).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    assert np.array_equal(np.isnan(mine), np.isnan(lib))
+    assert np.array_equal(mine[~np.isnan(lib)], lib[~np.isnan(lib)])
+    hand = {0x00: 0.0, 0x38: 1.0, 0x40: 2.0, 0x3C: 1.5, 0x7E: 448.0, 0x01: 2.0 ** -9,
+            0x07: 7 * 2.0 ** -9, 0x08: 2.0 ** -6, 0xB8: -1.0, 0xFE: -448.0, 0x30: 0.5}
+    for c, v in hand.items():
+        assert orc.decode_e4m3fn(np.array([c]))[0] == v, (hex(c), v)
+    assert np.isnan(orc.decode_e4m3fn(np.array([0x7F, 0xFF]))).all()
+    assert math.copysign(1.0, orc.decode_e4m3fn(np.array([0x80]))[0]) == -1.0
+
+
+def pin_fp8_cache_path(orc):
+    """The fp8 path equals the bf16 path run on caches decoded by torch and
+    scaled (an independent decoder), and the scales act exactly as the
+    definition says: v_scale multiplies every output, k_scale multiplies the
+    scores (the same as multiplying softmax_scale)."""
+    b = build_batch("pin8", [1, 3, 5], [9, 20, 30], 8, 2, 16, True, 31, device="cpu",
+                    block_size=4, kv_dtype="fp8_e4m3fn", k_scale=0.25, v_scale=0.5)
+    h = b.host()
+    out8, lse8 = orc.paged_attention(h["q"], h["k_cache"], h["v_cache"], h["cu_seqlens_q"],
+                                     h["seqused_k"], h["block_table"], h["softmax_scale"],
+                                     h["causal"], kv_format="fp8_e4m3fn",
+                                     k_scale=b.k_scale, v_scale=b.v_scale)
+    kd = b.k_cache.to(torch.float64).numpy() * b.k_scale    # NaN codes stay NaN
+    vd = b.v_cache.to(torch.float64).numpy() * b.v_scale
+    ref, lref = orc.paged_attention(h["q"], kd, vd, h["cu_seqlens_q"], h["seqused_k"],
+                                    h["block_table"], h["softmax_scale"], h["causal"])
+    assert np.isfinite(out8).all()
+    np.testing.assert_allclose(out8, ref, rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(lse8, lref, rtol=1e-12, atol=1e-12)
+    kw = dict(kv_format="fp8_e4m3fn", k_scale=b.k_scale)
+    o1, _ = orc.paged_attention(h["q"], h["k_cache"], h["v_cache"], h["cu_seqlens_q"],
+                                h["seqused_k"], h["block_table"], h["softmax_scale"],
+                                h["causal"], v_scale=1.0, **kw)
+    o2, _ = orc.paged_attention(h["q"], h["k_cache"], h["v_cache"], h["cu_seqlens_q"],
+                                h["seqused_k"], h["block_table"], h["softmax_scale"],
+                                h["causal"], v_scale=2.0, **kw)
+    assert np.array_equal(o2, 2.0 * o1)                     # powers of two scale exactly
+    o3, _ = orc.paged_attention(h["q"], h["k_cache"], h["v_cache"], h["cu_seqlens_q"],
+                                h["seqused_k"], h["block_table"], h["softmax_scale"] * 0.25,
+                                h["causal"], kv_format="fp8_e4m3fn", k_scale=1.0, v_scale=1.0)
+    np.testing.assert_allclose(o3, o1, rtol=1e-12, atol=1e-14)
+
+
 ALL_PINS = [
     pin_golden_closed_forms,
     pin_single_key_exact,
@@ -364,4 +415,6 @@ ALL_PINS = [
     pin_rows_api,
     pin_brute_tiny_workload,
     pin_brute_grid,
+    pin_fp8_decoder,
+    pin_fp8_cache_path,
 ]

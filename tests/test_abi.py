@@ -32,7 +32,7 @@ def test_header_functions_are_exported():
 
 
 def test_version_and_status_strings():
-    assert pa.version() == 1
+    assert pa.version() == 2
     for code in range(-9, 1):
         assert pa.lib.pa_status_string(code).decode()
     assert pa.lib.pa_status_string(-100).decode() == "unknown status"
@@ -220,3 +220,33 @@ def test_workspace_size_matches_plan():
     assert n == p["workspace_bytes"] > 0
     assert pa.workspace_size(b.q, b.k_cache, b.v_cache, out, b.cu_seqlens_q, b.seqused_k,
                              b.block_table, b.max_seqlen_q, b.max_seqlen_k) == 0
+
+
+def test_fp8_cache_descriptors():
+    """fp8 E4M3 caches: both caches must share the format, the plan matches the
+    bf16 one, and byte-based alignment rules apply."""
+    b = build_batch("abi8", [1, 3, 2], [5, 17, 40], 8, 2, 128, True, seed=1,
+                    kv_dtype="fp8_e4m3fn", k_scale=0.5, v_scale=0.25)
+    base = cpu_args()
+    a = dict(base, k_cache=b.k_cache, v_cache=b.v_cache)
+    # a mixed pair is a dtype error
+    for k, v in ((b.k_cache, base["v_cache"]), (base["k_cache"], b.v_cache)):
+        rc = call(dict(base, k_cache=k, v_cache=v))
+        assert pa.STATUS[rc] == "PA_ERR_DTYPE", pa.lib.pa_last_error().decode()
+    # valid fp8 descriptors plan like bf16 ones
+    d8 = pa.plan_describe(*[a[n] for n in ("q", "k_cache", "v_cache", "out", "cu_seqlens_q",
+                                            "seqused_k", "block_table")],
+                          a["max_seqlen_q"], a["max_seqlen_k"], num_cus=256)
+    d16 = pa.plan_describe(*[base[n] for n in ("q", "k_cache", "v_cache", "out", "cu_seqlens_q",
+                                               "seqused_k", "block_table")],
+                           base["max_seqlen_q"], base["max_seqlen_k"], num_cus=256)
+    assert d8 == d16
+    # the block stride must be a multiple of 16 bytes (8 fp8 elements is not)
+    wide = torch.zeros((b.k_cache.shape[0], 16 * 2 * 128 + 8), dtype=torch.uint8)
+    kv = wide[:, :16 * 2 * 128].view(torch.float8_e4m3fn).view(-1, 16, 2, 128)
+    assert kv.stride(0) == 16 * 2 * 128 + 8
+    rc = call(dict(base, k_cache=kv, v_cache=kv))
+    assert pa.STATUS[rc] == "PA_ERR_ALIGN", pa.lib.pa_last_error().decode()
+    # the scales travel in pa_options
+    o = pa.options(k_scale=0.5, v_scale=0.25)
+    assert abs(o.k_scale - 0.5) < 1e-7 and abs(o.v_scale - 0.25) < 1e-7

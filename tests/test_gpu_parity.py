@@ -5,6 +5,8 @@ several tiles, ragged tails) and contexts in one process, so a kernel
 specialisation keyed on the wrong constants shows up.
 """
 
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -275,3 +277,61 @@ def test_many_sequences_with_wide_tiles_keep_index_order():
     out = run_pa(b)
     torch.cuda.synchronize()
     full_parity(b, out, "many sequences, wide")
+
+
+# ---------------------------------------------------------------------------
+# fp8 E4M3 caches: converted to bf16 after the load, scales folded into the
+# score scale (k_scale) and the output (v_scale)
+# ---------------------------------------------------------------------------
+
+FP8_CASES = {
+    # name: (q_lens, k_lens, Hq, Hkv, d, causal, force_tile, force_splits)
+    "decode_persistent_g4d128": ([1, 1, 2, 4, 1, 0, 1], [1, 300, 1000, 2500, 17, 5, 4100],
+                                 32, 8, 128, True, 0, 0),
+    "decode_persistent_g8d64_split3": ([1, 2, 1, 1], [700, 129, 2000, 33], 16, 2, 64, True, 0, 3),
+    "narrow_grid": ([1, 2, 1, 4], [700, 33, 2000, 64], 32, 8, 128, True, 3, 0),
+    "wide_prefill_causal": ([300, 1, 77, 5, 128], [900, 60, 77, 400, 1500], 32, 8, 128, True, 0, 0),
+    "wide_noncausal_split2": ([16, 40, 3], [3000, 700, 90], 32, 4, 128, False, 0, 2),
+    "wide_d64_g2": ([64, 17, 1], [200, 1000, 5], 8, 4, 64, True, 0, 0),
+}
+
+
+@pytest.mark.parametrize("case", sorted(FP8_CASES))
+def test_fp8_cache_parity(case):
+    require_gpu()
+    q_lens, k_lens, hq, hkv, d, causal, tile, splits = FP8_CASES[case]
+    b = build_batch("fp8", q_lens, k_lens, hq, hkv, d, causal, seed=200 + len(case), device=DEV,
+                    kv_dtype="fp8_e4m3fn", k_scale=0.25, v_scale=0.0625)
+    opts = pa.options(force_tile=tile, force_num_splits=splits) if (tile or splits) else None
+    say(f"fp8 {case}")
+    out = run_pa(b, opts=opts)
+    torch.cuda.synchronize()
+    full_parity(b, out, f"fp8 {case}")
+
+
+def test_fp8_permutation_poison_and_scale_bit_exact():
+    """Block placement and the NaN codes of unowned slots do not change a bit
+    of the output; v_scale = 2 doubles every output exactly."""
+    require_gpu()
+    args = ([1, 5, 16, 3, 40], [7, 20, 40, 300, 250], 32, 8, 128, True)
+    b = build_batch("p8", *args, seed=301, device=DEV, kv_dtype="fp8_e4m3fn", k_scale=0.5,
+                    v_scale=0.125)
+    clean = build_batch("p8", *args, seed=301, device=DEV, kv_dtype="fp8_e4m3fn", k_scale=0.5,
+                        v_scale=0.125, poison=False)
+    nan_k = b.k_cache.view(torch.uint8) == 0x7F
+    nan_v = b.v_cache.view(torch.uint8) == 0x7F
+    clean.k_cache.view(torch.uint8)[nan_k] = 0
+    clean.v_cache.view(torch.uint8)[nan_v] = 0
+    say("fp8 permutation / poison / v_scale")
+    o1 = run_pa(b)
+    o2 = run_pa(repermute_pool(b, seed=302))
+    o3 = run_pa(clean)
+    # same codes, twice the value scale (a batch regenerated with another scale
+    # would round to different codes: E4M3's subnormal grid does not scale)
+    o4 = run_pa(dataclasses.replace(b, v_scale=0.25))
+    torch.cuda.synchronize()
+    assert torch.isfinite(o1.float()).all()
+    assert torch.equal(bits(o1), bits(o2))
+    assert torch.equal(bits(o1), bits(o3))
+    assert torch.equal(o4.float(), 2.0 * o1.float())
+    full_parity(b, o1, "fp8 p/p/s")

@@ -36,6 +36,10 @@ MUTANTS = {
     "merge_unweighted": ("merged = (w[..., None] * outs).sum(axis=0)",
                          "merged = outs.sum(axis=0) * w.mean(axis=0)[..., None]"),
     "rows_api_wrong_position": ("tokens[sel] - cu[s], K[:, g, :]", "tokens[sel] - cu[s] - 1, K[:, g, :]"),
+    "fp8_bias_8": ("np.ldexp(1.0 + m / 8.0, e - 7)", "np.ldexp(1.0 + m / 8.0, e - 8)"),
+    "fp8_no_subnormals": ("np.where(e == 0, np.ldexp(m / 8.0, -6),", "np.where(e == 0, 0.0 * m,"),
+    "fp8_scale_not_applied": ("return decode_e4m3fn(codes) * float(np.float32(scale))",
+                              "return decode_e4m3fn(codes)"),
 }
 
 

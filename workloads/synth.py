@@ -21,6 +21,11 @@ kernel that reads outside a sequence's context shows it in its output.
 
 Seeds: ``numpy.random.SeedSequence(seed)`` spawns four children, used in this
 order: lengths, sequence order, block permutation, values.
+
+fp8 caches (``kv_dtype="fp8_e4m3fn"``): N(0, 1) draws clipped to [-6, 6],
+divided by the tensor's scale and rounded to the OCP E4M3 ("fn") format by
+torch; the codes are inputs like any other values, and the NaN poison is the
+code 0x7F.
 """
 
 from __future__ import annotations
@@ -54,6 +59,9 @@ class Batch:
     causal: bool
     trap_block: int
     seed: int
+    kv_format: str = "bf16"          # or "fp8_e4m3fn" (one-byte codes)
+    k_scale: float = 1.0             # fp8: a key code stands for decode(code) * k_scale
+    v_scale: float = 1.0
     extra: Dict[str, object] = field(default_factory=dict)
 
     # ---- shape helpers -------------------------------------------------
@@ -95,17 +103,29 @@ class Batch:
                 self.max_seqlen_k, self.softmax_scale, self.causal)
 
     # ---- host copies for the oracle -------------------------------------
+    def _cache_host(self, t: torch.Tensor) -> np.ndarray:
+        # bf16: values as float32 (exact); fp8: the raw one-byte codes
+        if self.kv_format == "bf16":
+            return t.float().cpu().numpy()
+        return t.view(torch.uint8).cpu().numpy()
+
+    def kv_kwargs(self) -> Dict[str, object]:
+        """Cache format arguments of the oracle."""
+        return dict(kv_format=self.kv_format, k_scale=self.k_scale, v_scale=self.v_scale)
+
     def host(self) -> Dict[str, object]:
-        """Whole batch as numpy arrays (values as float32, exact for bf16)."""
+        """Whole batch as numpy arrays (values as float32, exact for bf16;
+        fp8 caches as their uint8 codes)."""
         return dict(
             q=self.q.float().cpu().numpy(),
-            k_cache=self.k_cache.float().cpu().numpy(),
-            v_cache=self.v_cache.float().cpu().numpy(),
+            k_cache=self._cache_host(self.k_cache),
+            v_cache=self._cache_host(self.v_cache),
             cu_seqlens_q=self.cu_seqlens_q.cpu().numpy().astype(np.int64),
             seqused_k=self.seqused_k.cpu().numpy().astype(np.int64),
             block_table=self.block_table.cpu().numpy().astype(np.int64),
             softmax_scale=self.softmax_scale,
             causal=self.causal,
+            **self.kv_kwargs(),
         )
 
     def host_subset(self, seq_ids: Sequence[int]) -> Tuple[Dict[str, object], np.ndarray]:
@@ -135,13 +155,14 @@ class Batch:
         q_lens = self.q_lens[seq_ids].astype(np.int64)
         sub = dict(
             q=self.q.index_select(0, ridx).float().cpu().numpy(),
-            k_cache=self.k_cache.index_select(0, idx).float().cpu().numpy(),
-            v_cache=self.v_cache.index_select(0, idx).float().cpu().numpy(),
+            k_cache=self._cache_host(_rows(self.k_cache, idx)),
+            v_cache=self._cache_host(_rows(self.v_cache, idx)),
             cu_seqlens_q=np.concatenate([[0], np.cumsum(q_lens)]).astype(np.int64),
             seqused_k=self.k_lens[seq_ids].astype(np.int64),
             block_table=tab,
             softmax_scale=self.softmax_scale,
             causal=self.causal,
+            **self.kv_kwargs(),
         )
         return sub, rows_all
 
@@ -150,6 +171,31 @@ class Batch:
         for name in ("q", "k_cache", "v_cache", "cu_seqlens_q", "seqused_k", "block_table"):
             setattr(b, name, getattr(self, name).to(device))
         return b
+
+
+def _rows(t: torch.Tensor, idx: torch.Tensor) -> torch.Tensor:
+    """t[idx] along dim 0 (through a uint8 view for fp8 tensors)."""
+    if t.dtype == torch.float8_e4m3fn:
+        return t.view(torch.uint8).index_select(0, idx).view(torch.float8_e4m3fn)
+    return t.index_select(0, idx)
+
+
+def _fill_normal_fp8(shape, gen: torch.Generator, device, scale: float,
+                     chunk: int = 1 << 26) -> torch.Tensor:
+    """N(0,1) float32 draws clipped to [-6, 6], divided by scale and rounded
+    to E4M3 ("fn") codes by torch.  torch turns magnitudes past the format's
+    range into NaN, so scale must be at least 6 / 448."""
+    if scale < 6.0 / 448.0:
+        raise ValueError("fp8 scale below 6/448 would overflow E4M3")
+    out = torch.empty(shape, dtype=torch.float8_e4m3fn, device=device)
+    flat = out.view(-1)
+    n = flat.numel()
+    for lo in range(0, n, chunk):
+        hi = min(n, lo + chunk)
+        x = torch.randn(hi - lo, generator=gen, device=device,
+                        dtype=torch.float32).clamp_(-6.0, 6.0) / scale
+        flat[lo:hi] = x.to(torch.float8_e4m3fn)
+    return out
 
 
 def _fill_normal_bf16(shape, gen: torch.Generator, device, chunk: int = 1 << 26) -> torch.Tensor:
@@ -168,12 +214,16 @@ def build_batch(name: str, q_lens, k_lens, num_q_heads: int, num_kv_heads: int,
                 head_dim: int, causal: bool, seed: int, device="cpu",
                 block_size: int = BLOCK_SIZE, pool_blocks: Optional[int] = None,
                 poison: bool = True, softmax_scale: Optional[float] = None,
-                children=None) -> Batch:
+                children=None, kv_dtype: str = "bf16", k_scale: float = 1.0,
+                v_scale: float = 1.0) -> Batch:
     """Build a batch from explicit per-sequence query and context lengths.
 
     ``pool_blocks`` fixes the pool size; by default the pool holds exactly the
-    blocks the sequences need plus one trap block.
+    blocks the sequences need plus one trap block.  ``kv_dtype`` is "bf16" or
+    "fp8_e4m3fn" (then ``k_scale`` / ``v_scale`` are the per-tensor scales).
     """
+    if kv_dtype not in ("bf16", "fp8_e4m3fn"):
+        raise ValueError("kv_dtype must be bf16 or fp8_e4m3fn")
     q_lens = np.asarray(q_lens, dtype=np.int64)
     k_lens = np.asarray(k_lens, dtype=np.int64)
     assert q_lens.shape == k_lens.shape and q_lens.ndim == 1
@@ -210,12 +260,22 @@ def build_batch(name: str, q_lens, k_lens, num_q_heads: int, num_kv_heads: int,
     gen = torch.Generator(device=device)
     gen.manual_seed(vseed)
     q = _fill_normal_bf16((T, num_q_heads, head_dim), gen, device)
-    k_cache = _fill_normal_bf16((pool, B, num_kv_heads, head_dim), gen, device)
-    v_cache = _fill_normal_bf16((pool, B, num_kv_heads, head_dim), gen, device)
+    if kv_dtype == "bf16":
+        k_cache = _fill_normal_bf16((pool, B, num_kv_heads, head_dim), gen, device)
+        v_cache = _fill_normal_bf16((pool, B, num_kv_heads, head_dim), gen, device)
+    else:
+        k_scale = float(np.float32(k_scale))
+        v_scale = float(np.float32(v_scale))
+        k_cache = _fill_normal_fp8((pool, B, num_kv_heads, head_dim), gen, device, k_scale)
+        v_cache = _fill_normal_fp8((pool, B, num_kv_heads, head_dim), gen, device, v_scale)
     if poison:
         not_owned = torch.as_tensor(~owned, device=device)
-        k_cache[not_owned] = float("nan")
-        v_cache[not_owned] = float("nan")
+        if kv_dtype == "bf16":
+            k_cache[not_owned] = float("nan")
+            v_cache[not_owned] = float("nan")
+        else:
+            k_cache.view(torch.uint8)[not_owned] = 0x7F     # E4M3 ("fn") NaN
+            v_cache.view(torch.uint8)[not_owned] = 0x7F
 
     if softmax_scale is None:
         softmax_scale = float(np.float32(1.0 / math.sqrt(head_dim)))
@@ -227,7 +287,9 @@ def build_batch(name: str, q_lens, k_lens, num_q_heads: int, num_kv_heads: int,
         block_table=torch.as_tensor(table, **i32),
         q_lens=q_lens, k_lens=k_lens, max_seqlen_q=max_q, max_seqlen_k=max_k,
         softmax_scale=float(softmax_scale), causal=bool(causal), trap_block=trap,
-        seed=int(seed))
+        seed=int(seed), kv_format=kv_dtype,
+        k_scale=float(k_scale) if kv_dtype != "bf16" else 1.0,
+        v_scale=float(v_scale) if kv_dtype != "bf16" else 1.0)
 
 
 def repermute_pool(batch: Batch, seed: int) -> Batch:
@@ -237,8 +299,12 @@ def repermute_pool(batch: Batch, seed: int) -> Batch:
     sig = torch.as_tensor(sigma, dtype=torch.long, device=batch.k_cache.device)
     k_new = torch.empty_like(batch.k_cache)
     v_new = torch.empty_like(batch.v_cache)
-    k_new[sig] = batch.k_cache
-    v_new[sig] = batch.v_cache
+    if batch.k_cache.dtype == torch.float8_e4m3fn:
+        k_new.view(torch.uint8)[sig] = batch.k_cache.view(torch.uint8)
+        v_new.view(torch.uint8)[sig] = batch.v_cache.view(torch.uint8)
+    else:
+        k_new[sig] = batch.k_cache
+        v_new[sig] = batch.v_cache
     table = batch.block_table.cpu().numpy().astype(np.int64)
     new_table = sigma[table].astype(np.int32)
     b = Batch(**{**batch.__dict__})
@@ -265,6 +331,13 @@ WORKLOADS = {
     "decode_gqa8_64seq_ctx2k_4k": (4, 32, 4, 128, True),
     "long_decode_16seq_ctx32k_128k": (5, 32, 8, 128, True),
     "long_q16_noncausal_16seq_ctx32k_128k": (5, 32, 8, 128, False),
+    # the headline decode batch with an fp8 E4M3 cache (scales 1/64)
+    "decode_256seq_ctx1k_fp8": (2, 32, 8, 128, True),
+}
+
+# cache format and scales of the workloads that do not use bf16 caches
+WORKLOAD_KV = {
+    "decode_256seq_ctx1k_fp8": ("fp8_e4m3fn", 1.0 / 64, 1.0 / 64),
 }
 
 
@@ -274,7 +347,7 @@ def workload_lengths(name: str, children) -> Tuple[np.ndarray, np.ndarray, Optio
     rng_ord = np.random.default_rng(children[1])
     if name == "tiny_mixed_3seq":
         return np.array([1, 5, 16]), np.array([7, 20, 40]), 16
-    if name == "decode_256seq_ctx1k":
+    if name in ("decode_256seq_ctx1k", "decode_256seq_ctx1k_fp8"):
         L = rng_len.integers(1000, 1100, size=256, endpoint=True)
         return np.ones(256, np.int64), L, None
     if name in ("mixed_prefill512x8_decode248", "prefill512x8_only", "decode248_only"):
@@ -307,5 +380,7 @@ def make_workload(name: str, device="cpu", poison: bool = True) -> Batch:
     seed, hq, hkv, d, causal = WORKLOADS[name]
     children = np.random.SeedSequence(seed).spawn(4)
     q_lens, k_lens, pool = workload_lengths(name, children)
+    kv, ks, vs = WORKLOAD_KV.get(name, ("bf16", 1.0, 1.0))
     return build_batch(name, q_lens, k_lens, hq, hkv, d, causal, seed, device=device,
-                       pool_blocks=pool, poison=poison, children=children)
+                       pool_blocks=pool, poison=poison, children=children, kv_dtype=kv,
+                       k_scale=ks, v_scale=vs)
