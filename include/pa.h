@@ -213,6 +213,32 @@ int pa_plan_describe(const pa_tensor* q, const pa_tensor* k_cache,
                      int32_t max_seqlen_k, const pa_options* opt, int32_t num_cus,
                      pa_plan_info* info);
 
+/*
+ * pa_cache_write — write new tokens' keys and values into the paged caches,
+ * the step before attention reads them (same cache layout as above).
+ *
+ *  key, value   bf16 [N, Hkv, d]; stride[2] == 1; stride[0], stride[1]
+ *               multiples of 8; 16-byte aligned.
+ *  k_cache      bf16 or fp8 E4M3 [NB, 16, Hkv, d], as for pa_unified_attention;
+ *  v_cache      same dtype, shape and strides.  Written in place.
+ *  slot_mapping int32 [N], contiguous: token i goes to slot slot_mapping[i] =
+ *               physical block * 16 + position in the block; a negative slot
+ *               skips the token.  Slots must be < NB * 16 and distinct
+ *               (unchecked; a repeated slot receives one of its tokens).
+ *  k_scale, v_scale  fp8 caches: the stored code is x / scale (IEEE fp32
+ *               division) rounded to the nearest E4M3 value, ties to even,
+ *               saturated at +-448 (the format has no infinity), NaN kept;
+ *               0 reads as 1.  Ignored for bf16 caches (values copied).
+ *  stream       hipStream_t (NULL = the null stream).
+ *
+ * Errors as for pa_unified_attention (validation on the host, nothing
+ * launched on failure).  Requires NB * 16 < 2^31.  Asynchronous; the caches
+ * must not be read by other work until the write has completed on `stream`.
+ */
+int pa_cache_write(const pa_tensor* key, const pa_tensor* value, pa_tensor* k_cache,
+                   pa_tensor* v_cache, const pa_tensor* slot_mapping, float k_scale,
+                   float v_scale, void* stream);
+
 /* Static text for a status code. */
 const char* pa_status_string(int status);
 

@@ -7,7 +7,9 @@ code with the GPU library in ``paged_kv_cache_unified_amd``.
 
 from .attention import (  # noqa: F401
     attend_rows,
+    cache_write,
     decode_e4m3fn,
+    encode_e4m3fn,
     gather_context,
     merge_lse,
     paged_attention,

@@ -50,7 +50,7 @@ from __future__ import annotations
 import numpy as np
 
 __all__ = ["paged_attention", "paged_attention_rows", "gather_context",
-           "attend_rows", "merge_lse", "decode_e4m3fn"]
+           "attend_rows", "merge_lse", "decode_e4m3fn", "encode_e4m3fn", "cache_write"]
 
 KV_FORMATS = ("bf16", "fp8_e4m3fn")
 
@@ -70,6 +70,58 @@ def decode_e4m3fn(codes):
     mag = np.where(e == 0, np.ldexp(m / 8.0, -6), np.ldexp(1.0 + m / 8.0, e - 7))
     mag = np.where((e == 15) & (c & 0x7 == 7), np.nan, mag)
     return sign * mag
+
+
+def encode_e4m3fn(x):
+    """E4M3 ("fn") codes of float32 values: the nearest value of the format's
+    grid, ties to the even code (even mantissa field), magnitudes at or past
+    464 (halfway between 448 and the next step, which the format lacks)
+    saturated to 448, NaN kept as NaN (0x7F with the sign bit).
+
+    Written as a search over the 127 finite non-negative values, so it shares
+    nothing with a bit-level rounding.
+    """
+    x = np.asarray(x, dtype=np.float32)
+    grid = decode_e4m3fn(np.arange(127))                 # codes 0x00..0x7E, increasing
+    a = np.abs(x.astype(np.float64))
+    sign = np.where(np.signbit(x), 0x80, 0)
+    idx = np.searchsorted(grid, a, side="left")          # first grid value >= a
+    idx = np.clip(idx, 1, 126)
+    lo, hi = grid[idx - 1], grid[idx]
+    below = a - lo
+    above = hi - a
+    pick_hi = (above < below) | ((above == below) & (idx % 2 == 0))
+    code = np.where(pick_hi, idx, idx - 1)
+    code = np.where(a <= grid[0], 0, code)               # exact zero
+    code = np.where(a >= 464.0, 0x7E, code)
+    code = np.where(np.isnan(x), 0x7F, code)
+    return (sign | code).astype(np.uint8)
+
+
+def cache_write(key, value, k_cache, v_cache, slot_mapping, kv_format="bf16", k_scale=1.0,
+                v_scale=1.0):
+    """New caches with token i's ``[Hkv, d]`` key / value written to slot
+    ``slot_mapping[i]`` (block ``slot // B``, position ``slot % B``); negative
+    slots are skipped.  bf16: values copied (float arrays); fp8: codes of
+    ``float32(x) / float32(scale)``.  Inputs are not modified.
+    """
+    kc, vc = np.array(k_cache, copy=True), np.array(v_cache, copy=True)
+    B = kc.shape[1]
+    for i, slot in enumerate(np.asarray(slot_mapping, dtype=np.int64)):
+        if slot < 0:
+            continue
+        blk, pos = slot // B, slot % B
+        if kv_format == "bf16":
+            kc[blk, pos] = key[i]
+            vc[blk, pos] = value[i]
+        elif kv_format == "fp8_e4m3fn":
+            kq = np.asarray(key[i], dtype=np.float32) / np.float32(k_scale)
+            vq = np.asarray(value[i], dtype=np.float32) / np.float32(v_scale)
+            kc[blk, pos] = encode_e4m3fn(kq)
+            vc[blk, pos] = encode_e4m3fn(vq)
+        else:
+            raise ValueError(f"kv_format must be one of {KV_FORMATS}")
+    return kc, vc
 
 
 def _context(cache, table_row, context_len, kv_format, scale):

@@ -68,6 +68,8 @@ _SIGNATURES = {
     "pa_plan_describe": (ctypes.c_int, [_T, _T, _T, _T, _T, _T, _T, ctypes.c_int32,
                                         ctypes.c_int32, ctypes.POINTER(PaOptions),
                                         ctypes.c_int32, ctypes.POINTER(PaPlanInfo)]),
+    "pa_cache_write": (ctypes.c_int, [_T, _T, _T, _T, _T, ctypes.c_float, ctypes.c_float,
+                                      ctypes.c_void_p]),
     "pa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "pa_last_error": (ctypes.c_char_p, []),
     "pa_version": (ctypes.c_int, []),
@@ -182,6 +184,18 @@ def plan_describe(q, k_cache, v_cache, out, cu_seqlens_q, seqused_k, block_table
                                 ctypes.byref(opts) if opts is not None else None, int(num_cus),
                                 ctypes.byref(info)))
     return info.as_dict()
+
+
+def cache_write(key, value, k_cache, v_cache, slot_mapping, k_scale: float = 0.0,
+                v_scale: float = 0.0):
+    """Write new tokens (bf16 [N, Hkv, d]) into the paged caches at
+    ``slot_mapping`` (int32 [N], block * 16 + position; negative skips).  fp8
+    caches receive E4M3 codes of x / scale."""
+    ds = [describe(t) for t in (key, value, k_cache, v_cache, slot_mapping)]
+    stream = ctypes.c_void_p(_stream_handle(key.device))
+    _check(lib.pa_cache_write(*[ctypes.byref(d) for d in ds], float(k_scale), float(v_scale),
+                              stream))
+    return k_cache, v_cache
 
 
 def version() -> int:

@@ -586,6 +586,93 @@ int pa_plan_describe(const pa_tensor* q, const pa_tensor* k_cache, const pa_tens
   return PA_OK;
 }
 
+int pa_cache_write(const pa_tensor* key, const pa_tensor* value, pa_tensor* k_cache,
+                   pa_tensor* v_cache, const pa_tensor* slot_mapping, float k_scale,
+                   float v_scale, void* stream) {
+  g_last_error.clear();
+  if (!key || !value || !k_cache || !v_cache || !slot_mapping)
+    return fail(PA_ERR_NULL, "a tensor descriptor pointer is NULL");
+  const bool kv8 = k_cache->dtype == PA_FP8_E4M3;
+  const int cdt = kv8 ? PA_FP8_E4M3 : PA_BF16;
+  const int64_t esz = kv8 ? 1 : 2;
+  struct {
+    const pa_tensor* t;
+    const char* name;
+    int dtype;
+    int ndim;
+  } spec[] = {{key, "key", PA_BF16, 3},       {value, "value", PA_BF16, 3},
+              {k_cache, "k_cache", cdt, 4},   {v_cache, "v_cache", cdt, 4},
+              {slot_mapping, "slot_mapping", PA_INT32, 1}};
+  for (auto& e : spec) {
+    if (e.t->dtype != e.dtype)
+      return fail(PA_ERR_DTYPE, "%s: dtype code %d, expected %d", e.name, e.t->dtype, e.dtype);
+    if (e.t->ndim != e.ndim)
+      return fail(PA_ERR_SHAPE, "%s: ndim %d, expected %d", e.name, e.t->ndim, e.ndim);
+    for (int i = 0; i < e.ndim; ++i)
+      if (e.t->shape[i] < 0 || e.t->stride[i] < 0)
+        return fail(PA_ERR_SHAPE, "%s: negative extent or stride in dim %d", e.name, i);
+  }
+  const int64_t N = key->shape[0], Hkv = k_cache->shape[2], D = k_cache->shape[3];
+  const int64_t NB = k_cache->shape[0], B = k_cache->shape[1];
+  for (int i = 0; i < 3; ++i)
+    if (value->shape[i] != key->shape[i]) return fail(PA_ERR_SHAPE, "value shape differs from key");
+  for (int i = 0; i < 4; ++i)
+    if (v_cache->shape[i] != k_cache->shape[i] || v_cache->stride[i] != k_cache->stride[i])
+      return fail(PA_ERR_SHAPE, "v_cache shape/strides differ from k_cache in dim %d", i);
+  if (key->shape[1] != Hkv || key->shape[2] != D)
+    return fail(PA_ERR_SHAPE, "key [N, %lld, %lld] does not match the cache heads / head_dim",
+                (long long)key->shape[1], (long long)key->shape[2]);
+  if (slot_mapping->shape[0] != N)
+    return fail(PA_ERR_SHAPE, "slot_mapping has %lld entries, expected %lld",
+                (long long)slot_mapping->shape[0], (long long)N);
+  if (B != pa::kBlockSize) return fail(PA_ERR_UNSUPPORTED, "block_size %lld (supported: 16)", (long long)B);
+  if (D % 8 || D <= 0) return fail(PA_ERR_UNSUPPORTED, "head_dim must be a positive multiple of 8");
+  if (N > kMaxInt32 || NB * B > kMaxInt32 || Hkv * D > kMaxInt32 / 8)
+    return fail(PA_ERR_UNSUPPORTED, "sizes beyond the 32-bit slot range");
+  if (key->stride[2] != 1 || value->stride[2] != 1)
+    return fail(PA_ERR_UNSUPPORTED, "key/value need a unit stride along head_dim");
+  if ((key->stride[0] | key->stride[1] | value->stride[0] | value->stride[1]) % 8)
+    return fail(PA_ERR_ALIGN, "key/value strides must be multiples of 8 elements");
+  if (k_cache->stride[3] != 1 || k_cache->stride[2] != D || k_cache->stride[1] != Hkv * D)
+    return fail(PA_ERR_UNSUPPORTED, "caches need contiguous [block_size, num_kv_heads, head_dim]");
+  if (NB > 1 && k_cache->stride[0] < B * Hkv * D)
+    return fail(PA_ERR_SHAPE, "cache block stride smaller than one block");
+  if ((k_cache->stride[0] * esz) % 16)
+    return fail(PA_ERR_ALIGN, "cache block stride must be a multiple of 16 bytes");
+  if (slot_mapping->stride[0] != 1 && N > 1) return fail(PA_ERR_UNSUPPORTED, "slot_mapping not contiguous");
+  if (N == 0) return PA_OK;
+  if (!key->data || !value->data || !k_cache->data || !v_cache->data || !slot_mapping->data)
+    return fail(PA_ERR_NULL, "data pointer is NULL");
+  if (!aligned(key->data, 16) || !aligned(value->data, 16) || !aligned(k_cache->data, 16) ||
+      !aligned(v_cache->data, 16))
+    return fail(PA_ERR_ALIGN, "key/value/cache data must be 16-byte aligned");
+  if (!aligned(slot_mapping->data, 4)) return fail(PA_ERR_ALIGN, "slot_mapping must be 4-byte aligned");
+  if (overlaps(k_cache, esz, key, 2) || overlaps(k_cache, esz, value, 2) ||
+      overlaps(v_cache, esz, key, 2) || overlaps(v_cache, esz, value, 2) ||
+      overlaps(k_cache, esz, v_cache, esz))
+    return fail(PA_ERR_ALIAS, "caches overlap each other or the new keys / values");
+  pa::CacheWriteParams p{};
+  p.key = static_cast<const uint16_t*>(key->data);
+  p.value = static_cast<const uint16_t*>(value->data);
+  p.k_cache = static_cast<unsigned char*>(k_cache->data);
+  p.v_cache = static_cast<unsigned char*>(v_cache->data);
+  p.slot_mapping = static_cast<const int32_t*>(slot_mapping->data);
+  p.k_st = key->stride[0];
+  p.k_sh = key->stride[1];
+  p.v_st = value->stride[0];
+  p.v_sh = value->stride[1];
+  p.cache_sb = k_cache->stride[0];
+  p.num_tokens = (int32_t)N;
+  p.slot_elems = (int32_t)(Hkv * D);
+  p.chunks_per_token = (int32_t)(Hkv * D / 8);
+  p.chunks_per_head = (int32_t)(D / 8);
+  p.k_scale = k_scale != 0.f ? k_scale : 1.f;
+  p.v_scale = v_scale != 0.f ? v_scale : 1.f;
+  const hipError_t e = pa::launch_cache_write(p, kv8, reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(PA_ERR_HIP, "cache write launch: %s", hipGetErrorString(e));
+  return PA_OK;
+}
+
 const char* pa_status_string(int status) {
   switch (status) {
     case PA_OK: return "ok";

@@ -74,6 +74,24 @@ struct MergeParams {
   int32_t split_keys;
 };
 
+// New tokens' keys and values -> paged cache slots (pa_cache_kernels.hip).
+struct CacheWriteParams {
+  const uint16_t* key;      // bf16 [N, Hkv, d]
+  const uint16_t* value;
+  unsigned char* k_cache;   // [NB, B, Hkv, d] bf16 or fp8 E4M3 codes
+  unsigned char* v_cache;
+  const int32_t* slot_mapping;   // [N]; < 0: skip
+  int64_t k_st, k_sh, v_st, v_sh;   // source strides (elements)
+  int64_t cache_sb;         // cache stride between physical blocks (elements)
+  int32_t num_tokens;
+  int32_t slot_elems;       // Hkv * d
+  int32_t chunks_per_token; // Hkv * d / 8
+  int32_t chunks_per_head;  // d / 8
+  float k_scale, v_scale;   // fp8: codes of x / scale
+};
+
+hipError_t launch_cache_write(const CacheWriteParams& p, bool kv8, hipStream_t stream);
+
 // Launchers (pa_kernels.hip).  Return the hipError_t of the launch.
 // wide = false launches the narrow-only specialization (every tile <= 16 rows).
 // kv8: the caches hold fp8 E4M3 codes (else bf16).

@@ -401,6 +401,62 @@ def pin_fp8_cache_path(orc):
     np.testing.assert_allclose(o3, o1, rtol=1e-12, atol=1e-14)
 
 
+def pin_fp8_encoder(orc):
+    """E4M3 ("fn") encoding: in range, torch's float32 -> float8_e4m3fn
+    conversion (round to nearest even) on random and boundary values; beyond
+    it, saturation by the reading the cache write takes; ties and specials by
+    hand from the format's definition."""
+    rng = np.random.default_rng(7)
+    grid = orc.decode_e4m3fn(np.arange(127))
+    mids = (grid[:-1] + grid[1:]) / 2                     # exact ties, all of them
+    x = np.concatenate([rng.normal(0, 40, 20000), rng.normal(0, 0.005, 5000),
+                        rng.uniform(-463.99, 463.99, 5000), mids, -mids, grid, -grid,
+                        np.nextafter(mids, 0), np.nextafter(mids, 1000)]).astype(np.float32)
+    x = x[np.abs(x) < 464]
+    mine = orc.encode_e4m3fn(x)
+    lib = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(mine, lib)
+    hand = {1.0: 0x38, 1.0625: 0x38, 1.1875: 0x3A, 1.5 * 2.0 ** -9: 0x02, 0.5 * 2.0 ** -9: 0x00,
+            448.0: 0x7E, 463.99: 0x7E, 464.0: 0x7E, 1e6: 0x7E, -1e6: 0xFE, -0.0: 0x80,
+            2.0 ** -6: 0x08, 15.5 * 2.0 ** -10: 0x08}
+    for v, c in hand.items():
+        assert int(orc.encode_e4m3fn(np.float32(v))) == c, (v, hex(c))
+    assert int(orc.encode_e4m3fn(np.float32(np.nan))) & 0x7F == 0x7F
+    # decode(encode(x)) is x for every grid value
+    assert np.array_equal(orc.decode_e4m3fn(orc.encode_e4m3fn(grid.astype(np.float32))), grid)
+
+
+def pin_cache_write(orc):
+    """Writing tokens then reading them through the block table returns them
+    (bf16) or their round-trip values (fp8); untouched and skipped slots keep
+    their contents."""
+    rng = np.random.default_rng(11)
+    NB, B, Hkv, d = 5, 4, 2, 8
+    key = rng.normal(size=(6, Hkv, d)).astype(np.float32)
+    val = rng.normal(size=(6, Hkv, d)).astype(np.float32)
+    slots = np.array([3, 7, -1, 12, 0, 19])
+    kc = rng.normal(size=(NB, B, Hkv, d)).astype(np.float32)
+    vc = rng.normal(size=(NB, B, Hkv, d)).astype(np.float32)
+    k2, v2 = orc.cache_write(key, val, kc, vc, slots)
+    for i, s_ in enumerate(slots):
+        if s_ >= 0:
+            assert np.array_equal(k2[s_ // B, s_ % B], key[i])
+            assert np.array_equal(v2[s_ // B, s_ % B], val[i])
+    touched = np.zeros((NB, B), bool)
+    for s_ in slots[slots >= 0]:
+        touched[s_ // B, s_ % B] = True
+    assert np.array_equal(k2[~touched], kc[~touched]) and np.array_equal(v2[~touched], vc[~touched])
+    kc8 = rng.integers(0, 0x7F, size=(NB, B, Hkv, d)).astype(np.uint8)
+    k8, v8 = orc.cache_write(key, val, kc8, kc8.copy(), slots, kv_format="fp8_e4m3fn",
+                             k_scale=0.125, v_scale=0.25)
+    for i, s_ in enumerate(slots):
+        if s_ >= 0:
+            back = orc.decode_e4m3fn(k8[s_ // B, s_ % B]) * 0.125
+            grid_step = np.maximum(np.abs(key[i]) * 2.0 ** -3, 2.0 ** -9 * 0.125)
+            assert (np.abs(back - key[i]) <= grid_step / 2 * (1 + 1e-12)).all()
+    assert np.array_equal(k8[~touched], kc8[~touched])
+
+
 ALL_PINS = [
     pin_golden_closed_forms,
     pin_single_key_exact,
@@ -417,4 +473,6 @@ ALL_PINS = [
     pin_brute_grid,
     pin_fp8_decoder,
     pin_fp8_cache_path,
+    pin_fp8_encoder,
+    pin_cache_write,
 ]

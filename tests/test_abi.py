@@ -250,3 +250,28 @@ def test_fp8_cache_descriptors():
     # the scales travel in pa_options
     o = pa.options(k_scale=0.5, v_scale=0.25)
     assert abs(o.k_scale - 0.5) < 1e-7 and abs(o.v_scale - 0.25) < 1e-7
+
+
+def test_cache_write_validation():
+    """pa_cache_write rejects bad descriptors on the host."""
+    NB, Hkv, d = 6, 2, 64
+    key = torch.zeros(5, Hkv, d, dtype=torch.bfloat16)
+    kc = torch.zeros(NB, 16, Hkv, d, dtype=torch.bfloat16)
+    slots = torch.tensor([0, 3, -1, 17, 40], dtype=torch.int32)
+
+    def rc(**over):
+        a = dict(key=key, value=key.clone(), k_cache=kc, v_cache=kc.clone(), slots=slots)
+        a.update(over)
+        ds = [pa.describe(a[n]) for n in ("key", "value", "k_cache", "v_cache", "slots")]
+        r = pa.lib.pa_cache_write(*[ctypes.byref(x) for x in ds], 0.0, 0.0, None)
+        return pa.STATUS.get(r, r)
+
+    assert rc(slots=slots.to(torch.int64)) == "PA_ERR_DTYPE"
+    assert rc(key=key.float()) == "PA_ERR_DTYPE"
+    assert rc(v_cache=kc.to(torch.float8_e4m3fn)) == "PA_ERR_DTYPE"      # formats differ
+    assert rc(slots=slots[:4]) == "PA_ERR_SHAPE"
+    assert rc(key=torch.zeros(5, Hkv + 1, d, dtype=torch.bfloat16),
+              value=torch.zeros(5, Hkv + 1, d, dtype=torch.bfloat16)) == "PA_ERR_SHAPE"
+    assert rc(k_cache=kc, v_cache=kc) == "PA_ERR_ALIAS"
+    assert rc(key=key[:0], value=key[:0], slots=slots[:0]) == "PA_OK"      # nothing to write
+    assert "pa_cache_write" in declared_functions()

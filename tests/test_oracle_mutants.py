@@ -40,6 +40,10 @@ MUTANTS = {
     "fp8_no_subnormals": ("np.where(e == 0, np.ldexp(m / 8.0, -6),", "np.where(e == 0, 0.0 * m,"),
     "fp8_scale_not_applied": ("return decode_e4m3fn(codes) * float(np.float32(scale))",
                               "return decode_e4m3fn(codes)"),
+    "fp8_ties_away": ("(above == below) & (idx % 2 == 0)", "(above == below)"),
+    "fp8_overflow_to_nan": ("code = np.where(a >= 464.0, 0x7E, code)",
+                            "code = np.where(a >= 464.0, 0x7F, code)"),
+    "cache_write_slot_swap": ("blk, pos = slot // B, slot % B", "blk, pos = slot % B, slot // B"),
 }
 
 
