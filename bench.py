@@ -226,6 +226,52 @@ def cpu_baseline(b, unit, min_s=10.0, budget_s=20.0):
                       f"numpy oracle, {t_all:.1f} s, BLAS {blas}, {cores} host cores visible"}
 
 
+def bench_cache_write(pa, b, args, dev):
+    """pa_cache_write of every sequence's q_s new tokens (context positions
+    L_s - q_s .. L_s - 1, slots from the block table) into the batch's caches.
+    Algorithmic bytes: the new keys and values read once (bf16) and written
+    once in the cache format."""
+    import torch
+    T, hkv, d = b.total_q, b.num_kv_heads, b.head_dim
+    table = b.block_table.cpu().numpy().astype(np.int64)
+    slots = np.empty(T, np.int64)
+    cu = b.cu_seqlens_q.cpu().numpy()
+    for s in range(b.num_seqs):
+        L, q = int(b.k_lens[s]), int(b.q_lens[s])
+        pos = np.arange(L - q, L)
+        slots[cu[s]:cu[s + 1]] = table[s, pos // 16] * 16 + pos % 16
+    slot_t = torch.as_tensor(slots.astype(np.int32), device=dev)
+    g = torch.Generator(device=dev).manual_seed(5)
+    key = torch.randn(T, hkv, d, generator=g, device=dev).to(torch.bfloat16)
+    val = torch.randn(T, hkv, d, generator=g, device=dev).to(torch.bfloat16)
+    call = lambda: pa.cache_write(key, val, b.k_cache, b.v_cache, slot_t, b.k_scale, b.v_scale)
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    s0.record(stream)
+    for _ in range(args.steps):
+        call()
+    s1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    us = s0.elapsed_time(s1) * 1e3 / args.steps
+    nbytes = T * hkv * d * 2 * (2 + kv_elem_bytes(b))
+    achieved = nbytes / (us * 1e-6) / 1e9
+    print(json.dumps({
+        "metric": "KV-cache write GB/s (new tokens into the paged cache)", "value": round(achieved, 1),
+        "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3 / args.steps, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": b.kv_format, "data": "synthetic",
+        "config": {"workload": args.workload, "tokens": T, "num_kv_heads": hkv, "head_dim": d},
+        "us_per_call_events": round(us, 2), "algorithmic_bytes_per_call": nbytes,
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None},
+    }), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -242,6 +288,9 @@ def main():
                     help="pa_options.decode_grid (0 = resident work-groups)")
     ap.add_argument("--summarize", metavar="DIR",
                     help="write profiles/pa_fwd_<workload>.md from rocprofv3 output in DIR")
+    ap.add_argument("--cache-write", action="store_true",
+                    help="time pa_cache_write instead: each sequence's new tokens (its "
+                         "last q_s positions) written into the workload's caches")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a 1 GiB device-to-device copy three times (the known-size "
                          "kernel that scales rocprofv3 FETCH_SIZE / WRITE_SIZE into bytes)")
@@ -281,6 +330,9 @@ def main():
                           decode_grid=args.decode_grid, k_scale=b.k_scale, v_scale=b.v_scale)
         ws = torch.empty(max(1, pa.workspace_size(*call_args[:9], opts)), dtype=torch.uint8,
                          device=dev)
+    if args.cache_write:
+        bench_cache_write(pa, b, args, dev)
+        return
     plan = pa.plan_describe(*call_args[:9], opts=opts)
     total_bytes, kv_bytes, flops = algorithmic_work(b)
 

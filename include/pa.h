@@ -190,6 +190,41 @@ int pa_unified_attention_ex(const pa_tensor* q, const pa_tensor* k_cache,
                             size_t workspace_bytes, void* stream);
 
 /*
+ * pa_unified_attention_lse — as pa_unified_attention_ex, and also writes each
+ * row's log-sum-exp: lse[t, h] = ln sum_j exp(softmax_scale * k_scale * q . k_j)
+ * over the row's admissible keys (-inf for a row with none).  With the outputs
+ * of two calls over disjoint key sets of the same queries, pa_merge_attention
+ * gives the result over their union (the log-sum-exp export that cascade /
+ * shared-prefix attention composes, page "[Kernel] Unified Triton kernel that
+ * doesn't distinguish between prefill + decode", review discussion of the
+ * non-causal mode for cascade attention).
+ *  lse          fp32 [T, Hq]; stride[1] == 1; 4-byte aligned; must not overlap
+ *               q, out or the caches.  Fully overwritten.
+ *  workspace    as for pa_unified_attention_ex, except that NULL selects the
+ *               library workspace.
+ */
+int pa_unified_attention_lse(const pa_tensor* q, const pa_tensor* k_cache,
+                             const pa_tensor* v_cache, pa_tensor* out, pa_tensor* lse,
+                             const pa_tensor* cu_seqlens_q, const pa_tensor* seqused_k,
+                             const pa_tensor* block_table, int32_t max_seqlen_q,
+                             int32_t max_seqlen_k, float softmax_scale, int32_t causal,
+                             const pa_options* opt, void* workspace, size_t workspace_bytes,
+                             void* stream);
+
+/*
+ * pa_merge_attention — combine two attention results of the same rows over
+ * disjoint key sets: with natural-log lse a, b, out = (e^a out_a + e^b out_b) /
+ * (e^a + e^b) and lse_out = ln(e^a + e^b); a side with lse = -inf has no keys
+ * and drops out (a row with no keys on either side gives 0 and -inf).
+ *  out_a, out_b, out  bf16 [T, Hq, d], d in {64, 128}; stride[2] == 1;
+ *               stride[0], stride[1] multiples of 4; 8-byte aligned.
+ *  lse_a, lse_b fp32 [T, Hq]; stride[1] == 1.
+ *  lse_out      fp32 [T, Hq] or NULL.  Outputs must not overlap the inputs.
+ */
+int pa_merge_attention(const pa_tensor* out_a, const pa_tensor* lse_a, const pa_tensor* out_b,
+                       const pa_tensor* lse_b, pa_tensor* out, pa_tensor* lse_out, void* stream);
+
+/*
  * pa_workspace_size — bytes of workspace pa_unified_attention_ex needs for
  * these arguments and options (0 when the batch needs no key split).  Host
  * only: reads descriptors, never device memory.  Returns (size_t)-1 and sets

@@ -63,6 +63,11 @@ _SIGNATURES = {
                                                ctypes.c_int32, ctypes.c_float, ctypes.c_int32,
                                                ctypes.POINTER(PaOptions), ctypes.c_void_p,
                                                ctypes.c_size_t, ctypes.c_void_p]),
+    "pa_unified_attention_lse": (ctypes.c_int, [_T, _T, _T, _T, _T, _T, _T, _T, ctypes.c_int32,
+                                                ctypes.c_int32, ctypes.c_float, ctypes.c_int32,
+                                                ctypes.POINTER(PaOptions), ctypes.c_void_p,
+                                                ctypes.c_size_t, ctypes.c_void_p]),
+    "pa_merge_attention": (ctypes.c_int, [_T, _T, _T, _T, _T, _T, ctypes.c_void_p]),
     "pa_workspace_size": (ctypes.c_size_t, [_T, _T, _T, _T, _T, _T, _T, ctypes.c_int32,
                                             ctypes.c_int32, ctypes.POINTER(PaOptions)]),
     "pa_plan_describe": (ctypes.c_int, [_T, _T, _T, _T, _T, _T, _T, ctypes.c_int32,
@@ -163,6 +168,34 @@ def unified_attention(q, k_cache, v_cache, out, cu_seqlens_q, seqused_k, block_t
                                          ws_ptr, ws_bytes, stream)
     _check(rc)
     return out
+
+
+def unified_attention_lse(q, k_cache, v_cache, out, lse, cu_seqlens_q, seqused_k, block_table,
+                          max_seqlen_q: int, max_seqlen_k: int, softmax_scale: float,
+                          causal: bool, *, opts: Optional[PaOptions] = None,
+                          workspace: Optional[torch.Tensor] = None):
+    """As ``unified_attention``, also writing each row's natural-log
+    log-sum-exp into ``lse`` (fp32 [T, Hq])."""
+    ds = [describe(t) for t in (q, k_cache, v_cache, out, lse, cu_seqlens_q, seqused_k,
+                                block_table)]
+    stream = ctypes.c_void_p(_stream_handle(q.device))
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(lib.pa_unified_attention_lse(*[ctypes.byref(d) for d in ds], int(max_seqlen_q),
+                                        int(max_seqlen_k), float(softmax_scale), int(bool(causal)),
+                                        ctypes.byref(opts) if opts is not None else None,
+                                        ws_ptr, ws_bytes, stream))
+    return out, lse
+
+
+def merge_attention(out_a, lse_a, out_b, lse_b, out, lse_out=None):
+    """Combine two results of the same rows over disjoint key sets."""
+    ds = [describe(t) for t in (out_a, lse_a, out_b, lse_b, out)]
+    dl = describe(lse_out) if lse_out is not None else None
+    stream = ctypes.c_void_p(_stream_handle(out.device))
+    _check(lib.pa_merge_attention(*[ctypes.byref(d) for d in ds],
+                                  ctypes.byref(dl) if dl is not None else None, stream))
+    return out, lse_out
 
 
 def workspace_size(q, k_cache, v_cache, out, cu_seqlens_q, seqused_k, block_table,

@@ -409,14 +409,35 @@ int library_workspace(size_t need, hipStream_t stream, void** ptr) {
   return PA_OK;
 }
 
+// lse: optional fp32 [T, Hq] receiving each row's natural-log log-sum-exp.
+int validate_lse(const pa_tensor* lse, const Shapes& s, const pa_tensor* q, const pa_tensor* k,
+                 const pa_tensor* v, const pa_tensor* out) {
+  if (lse->dtype != PA_FP32) return fail(PA_ERR_DTYPE, "lse: dtype code %d, expected %d", lse->dtype, PA_FP32);
+  if (lse->ndim != 2 || lse->shape[0] != s.T || lse->shape[1] != s.Hq)
+    return fail(PA_ERR_SHAPE, "lse must be fp32 [total_q, num_q_heads]");
+  if (lse->stride[1] != 1 && s.Hq > 1) return fail(PA_ERR_UNSUPPORTED, "lse needs a unit head stride");
+  if (lse->stride[0] < 0) return fail(PA_ERR_SHAPE, "lse: negative stride");
+  if (s.T > 0 && !lse->data) return fail(PA_ERR_NULL, "lse data is NULL");
+  if (!aligned(lse->data, 4)) return fail(PA_ERR_ALIGN, "lse must be 4-byte aligned");
+  const int64_t kv_esz = s.kv8 ? 1 : 2;
+  if (overlaps(lse, 4, out, 2) || overlaps(lse, 4, q, 2) || overlaps(lse, 4, k, kv_esz) ||
+      overlaps(lse, 4, v, kv_esz))
+    return fail(PA_ERR_ALIAS, "lse overlaps q, out or a cache");
+  return PA_OK;
+}
+
 int run(const pa_tensor* q, const pa_tensor* k, const pa_tensor* v, pa_tensor* out,
-        const pa_tensor* cu, const pa_tensor* sk, const pa_tensor* bt, int32_t max_q,
-        int32_t max_k, float scale, int32_t causal, const pa_options* opt, bool library_ws,
-        void* ws, size_t ws_bytes, void* stream_v) {
+        const pa_tensor* lse, const pa_tensor* cu, const pa_tensor* sk, const pa_tensor* bt,
+        int32_t max_q, int32_t max_k, float scale, int32_t causal, const pa_options* opt,
+        bool library_ws, void* ws, size_t ws_bytes, void* stream_v) {
   g_last_error.clear();
   Shapes s;
   int rc = validate(q, k, v, out, cu, sk, bt, max_q, max_k, &s);
   if (rc != PA_OK) return rc;
+  if (lse) {
+    rc = validate_lse(lse, s, q, k, v, out);
+    if (rc != PA_OK) return rc;
+  }
   if (s.T == 0 || s.S == 0) return PA_OK;
   bool have_dev = false;
   const int ncu = device_cu_count(&have_dev);
@@ -483,6 +504,8 @@ int run(const pa_tensor* q, const pa_tensor* k, const pa_tensor* v, pa_tensor* o
   const double v_scale = s.kv8 && opt && opt->v_scale != 0.f ? opt->v_scale : 1.0;
   p.scale_log2 = (float)((double)scale * k_scale * 1.4426950408889634);
   p.out_scale = (float)v_scale;
+  p.lse_out = lse ? static_cast<float*>(lse->data) : nullptr;
+  p.lse_st = lse ? lse->stride[0] : 0;
   if (plan.nwg > 0) {
     hipError_t e = plan.persistent
                        ? pa::launch_decode(p, (int)s.D, (int)s.G, s.kv8, plan.nwg, stream)
@@ -504,6 +527,8 @@ int run(const pa_tensor* q, const pa_tensor* k, const pa_tensor* v, pa_tensor* o
     mp.seq_k = p.seq_k;
     mp.num_seqs = (int32_t)s.S;
     mp.split_keys = plan.split_keys;
+    mp.lse_out = p.lse_out;
+    mp.lse_st = p.lse_st;
     hipError_t e = pa::launch_merge(mp, (int)s.D, stream);
     if (e != hipSuccess) return fail(PA_ERR_HIP, "merge launch: %s", hipGetErrorString(e));
   }
@@ -518,8 +543,8 @@ int pa_unified_attention(const pa_tensor* q, const pa_tensor* k_cache, const pa_
                          pa_tensor* out, const pa_tensor* cu_seqlens_q, const pa_tensor* seqused_k,
                          const pa_tensor* block_table, int32_t max_seqlen_q, int32_t max_seqlen_k,
                          float softmax_scale, int32_t causal, void* stream) {
-  return run(q, k_cache, v_cache, out, cu_seqlens_q, seqused_k, block_table, max_seqlen_q,
-             max_seqlen_k, softmax_scale, causal, nullptr, true, nullptr, 0, stream);
+  return run(q, k_cache, v_cache, out, nullptr, cu_seqlens_q, seqused_k, block_table,
+             max_seqlen_q, max_seqlen_k, softmax_scale, causal, nullptr, true, nullptr, 0, stream);
 }
 
 int pa_unified_attention_ex(const pa_tensor* q, const pa_tensor* k_cache, const pa_tensor* v_cache,
@@ -528,8 +553,80 @@ int pa_unified_attention_ex(const pa_tensor* q, const pa_tensor* k_cache, const 
                             int32_t max_seqlen_q, int32_t max_seqlen_k, float softmax_scale,
                             int32_t causal, const pa_options* opt, void* workspace,
                             size_t workspace_bytes, void* stream) {
-  return run(q, k_cache, v_cache, out, cu_seqlens_q, seqused_k, block_table, max_seqlen_q,
-             max_seqlen_k, softmax_scale, causal, opt, false, workspace, workspace_bytes, stream);
+  return run(q, k_cache, v_cache, out, nullptr, cu_seqlens_q, seqused_k, block_table,
+             max_seqlen_q, max_seqlen_k, softmax_scale, causal, opt, false, workspace,
+             workspace_bytes, stream);
+}
+
+int pa_unified_attention_lse(const pa_tensor* q, const pa_tensor* k_cache,
+                             const pa_tensor* v_cache, pa_tensor* out, pa_tensor* lse,
+                             const pa_tensor* cu_seqlens_q, const pa_tensor* seqused_k,
+                             const pa_tensor* block_table, int32_t max_seqlen_q,
+                             int32_t max_seqlen_k, float softmax_scale, int32_t causal,
+                             const pa_options* opt, void* workspace, size_t workspace_bytes,
+                             void* stream) {
+  if (!lse) {
+    g_last_error.clear();
+    return fail(PA_ERR_NULL, "lse descriptor is NULL");
+  }
+  return run(q, k_cache, v_cache, out, lse, cu_seqlens_q, seqused_k, block_table, max_seqlen_q,
+             max_seqlen_k, softmax_scale, causal, opt, workspace == nullptr, workspace,
+             workspace_bytes, stream);
+}
+
+int pa_merge_attention(const pa_tensor* out_a, const pa_tensor* lse_a, const pa_tensor* out_b,
+                       const pa_tensor* lse_b, pa_tensor* out, pa_tensor* lse_out, void* stream) {
+  g_last_error.clear();
+  if (!out_a || !lse_a || !out_b || !lse_b || !out)
+    return fail(PA_ERR_NULL, "a tensor descriptor pointer is NULL");
+  const pa_tensor* outs[] = {out_a, out_b, out};
+  const pa_tensor* lses[] = {lse_a, lse_b, lse_out};
+  for (const pa_tensor* t : outs) {
+    if (t->dtype != PA_BF16) return fail(PA_ERR_DTYPE, "outputs must be bf16");
+    if (t->ndim != 3) return fail(PA_ERR_SHAPE, "outputs must be [total_q, num_q_heads, head_dim]");
+    for (int i = 0; i < 3; ++i)
+      if (t->shape[i] != out->shape[i]) return fail(PA_ERR_SHAPE, "output shapes differ");
+    if (t->stride[2] != 1) return fail(PA_ERR_UNSUPPORTED, "outputs need a unit head_dim stride");
+    if ((t->stride[0] | t->stride[1]) % 4) return fail(PA_ERR_ALIGN, "output strides must be multiples of 4");
+    if (!aligned(t->data, 8)) return fail(PA_ERR_ALIGN, "outputs must be 8-byte aligned");
+  }
+  const int64_t T = out->shape[0], Hq = out->shape[1], D = out->shape[2];
+  for (const pa_tensor* t : lses) {
+    if (!t) continue;
+    if (t->dtype != PA_FP32) return fail(PA_ERR_DTYPE, "lse tensors must be fp32");
+    if (t->ndim != 2 || t->shape[0] != T || t->shape[1] != Hq)
+      return fail(PA_ERR_SHAPE, "lse tensors must be [total_q, num_q_heads]");
+    if (t->stride[1] != 1 && Hq > 1) return fail(PA_ERR_UNSUPPORTED, "lse needs a unit head stride");
+    if (!aligned(t->data, 4)) return fail(PA_ERR_ALIGN, "lse must be 4-byte aligned");
+  }
+  if (D != 64 && D != 128) return fail(PA_ERR_UNSUPPORTED, "head_dim %lld (supported: 64, 128)", (long long)D);
+  if (T * Hq > kMaxInt32) return fail(PA_ERR_UNSUPPORTED, "too many rows");
+  if (overlaps(out, 2, out_a, 2) || overlaps(out, 2, out_b, 2) ||
+      (lse_out && (overlaps(lse_out, 4, lse_a, 4) || overlaps(lse_out, 4, lse_b, 4) ||
+                   overlaps(lse_out, 4, out, 2))))
+    return fail(PA_ERR_ALIAS, "merge outputs overlap its inputs");
+  if (T == 0 || Hq == 0) return PA_OK;
+  pa::Merge2Params mp{};
+  mp.oa = static_cast<const uint16_t*>(out_a->data);
+  mp.ob = static_cast<const uint16_t*>(out_b->data);
+  mp.la = static_cast<const float*>(lse_a->data);
+  mp.lb = static_cast<const float*>(lse_b->data);
+  mp.out = static_cast<uint16_t*>(out->data);
+  mp.lse = lse_out ? static_cast<float*>(lse_out->data) : nullptr;
+  mp.oa_st = out_a->stride[0];
+  mp.oa_sh = out_a->stride[1];
+  mp.ob_st = out_b->stride[0];
+  mp.ob_sh = out_b->stride[1];
+  mp.o_st = out->stride[0];
+  mp.o_sh = out->stride[1];
+  mp.la_st = lse_a->stride[0];
+  mp.lb_st = lse_b->stride[0];
+  mp.l_st = lse_out ? lse_out->stride[0] : 0;
+  mp.total_q = (int32_t)T;
+  mp.num_q_heads = (int32_t)Hq;
+  const hipError_t e = pa::launch_merge2(mp, (int)D, reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(PA_ERR_HIP, "merge launch: %s", hipGetErrorString(e));
+  return PA_OK;
 }
 
 size_t pa_workspace_size(const pa_tensor* q, const pa_tensor* k_cache, const pa_tensor* v_cache,

@@ -54,6 +54,8 @@ struct FwdParams {
   int32_t lpt;             // grid plans: units in longest-first order (block b -> rank b / Hkv)
   float scale_log2;        // softmax_scale * k_scale * log2(e)
   float out_scale;         // v_scale (1 for bf16 caches): multiplies every output row
+  float* lse_out;          // optional fp32 [T, Hq] (row stride lse_st): natural-log lse
+  int64_t lse_st;
 };
 
 struct MergeParams {
@@ -72,7 +74,22 @@ struct MergeParams {
                            // kernel and are skipped.
   int32_t num_seqs;
   int32_t split_keys;
+  float* lse_out;          // optional: merged natural-log lse [T, Hq] (row stride lse_st)
+  int64_t lse_st;
 };
+
+// Two partial results over disjoint key sets -> one (cascade composition).
+struct Merge2Params {
+  const uint16_t* oa;      // bf16 [T, Hq, d]
+  const uint16_t* ob;
+  const float* la;         // fp32 [T, Hq], natural-log lse (-inf: no key)
+  const float* lb;
+  uint16_t* out;           // bf16 [T, Hq, d]
+  float* lse;              // optional fp32 [T, Hq]
+  int64_t oa_st, oa_sh, ob_st, ob_sh, o_st, o_sh, la_st, lb_st, l_st;
+  int32_t total_q, num_q_heads;
+};
+hipError_t launch_merge2(const Merge2Params& p, int head_dim, hipStream_t stream);
 
 // New tokens' keys and values -> paged cache slots (pa_cache_kernels.hip).
 struct CacheWriteParams {

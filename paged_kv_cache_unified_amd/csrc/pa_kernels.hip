@@ -115,6 +115,14 @@ __device__ __forceinline__ typename Kv<KV8>::raw8 bload8(__amdgpu_buffer_rsrc_t 
     return __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0);
 }
 
+// Natural-log lse of a row from its log2-domain value (kept in the library's
+// kernels: scores in log2 units of softmax_scale * k_scale * q.k).
+constexpr float kLn2 = 0.6931471805599453f;
+__device__ __forceinline__ void store_lse(float* lse_out, int64_t lse_st, int64_t tok, int head,
+                                          float lse2) {
+  if (lse_out) lse_out[tok * lse_st + head] = lse2 == -__builtin_huge_valf() ? lse2 : lse2 * kLn2;
+}
+
 // Round-to-nearest-even fp32 -> bf16 pair, packed low|high.
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   bf16x2 v = {(__bf16)lo, (__bf16)hi};
@@ -599,6 +607,8 @@ __device__ __forceinline__ void attend_narrow(const FwdParams& p, const Item& it
   const int64_t tok = it.q0 + it.tok0 + n / G;
   const int hn = it.kvh * G + n % G;
   if (it.parts == 1) {
+    if ((tid & 15) == 0)
+      store_lse(p.lse_out, p.lse_st, tok, hn, Ls > 0.f ? M + __log2f(Ls) : kNegInf);
     uint16_t* op = p.out + tok * p.o_st + (int64_t)hn * p.o_sh + d0;
     if constexpr (DPER == 8) {
       u32x4 w = {pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]), pack_bf16x2(o[4], o[5]),
@@ -919,6 +929,7 @@ __device__ __forceinline__ void attend_wide(const FwdParams& p, const Item& it,
   const float inv = lt > 0.f ? p.out_scale / lt : 0.f;
   const int64_t tok = it.q0 + it.tok0 + t_in;
   if (it.parts == 1) {
+    if (h == 0) store_lse(p.lse_out, p.lse_st, tok, head, lt > 0.f ? m * c + __log2f(lt) : kNegInf);
     uint16_t* op = p.out + tok * p.o_st + (int64_t)head * p.o_sh + 4 * h;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
@@ -1327,6 +1338,7 @@ void pa_decode_kernel(FwdParams p) {
       const int64_t tok = cur.q0 + l16 / G;
       const int hn = cur.kvh * G + l16 % G;
       if (cur.units == 1) {
+        if (h4 == 0) store_lse(p.lse_out, p.lse_st, tok, hn, l > 0.f ? m + __log2f(l) : kNegInf);
         uint16_t* op = p.out + tok * p.o_st + (int64_t)hn * p.o_sh + 4 * h4;
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
@@ -1375,10 +1387,11 @@ __device__ __forceinline__ int merge_parts(const MergeParams& p, int64_t row) {
 }
 
 __device__ __forceinline__ void merge_store(const MergeParams& p, int64_t row, int d0, f32x4 o,
-                                            float wsum) {
+                                            float wsum, float M) {
   const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
   const int64_t tok = row / p.num_q_heads;
   const int hd = (int)(row % p.num_q_heads);
+  if (d0 == 0) store_lse(p.lse_out, p.lse_st, tok, hd, wsum > 0.f ? M + __log2f(wsum) : kNegInf);
   uint16_t* op = p.out + tok * p.o_st + (int64_t)hd * p.o_sh + d0;
   u32x2 w = {pack_bf16x2(o[0] * inv, o[1] * inv), pack_bf16x2(o[2] * inv, o[3] * inv)};
   *reinterpret_cast<u32x2*>(op) = w;
@@ -1408,7 +1421,7 @@ __global__ __launch_bounds__(256) void pa_merge_rows_kernel(MergeParams p) {
       a += w * *reinterpret_cast<const f32x4*>(p.ws_o + (sg * nrows + row) * D + d0);
     }
   }
-  merge_store(p, row, d0, a, ws);
+  merge_store(p, row, d0, a, ws, M);
 }
 
 // Many parts per row: one work-group per row; its threads form NG groups that
@@ -1457,7 +1470,45 @@ __global__ __launch_bounds__(256) void pa_merge_wide_kernel(MergeParams p) {
     wt += wred[k];
     o += *reinterpret_cast<const f32x4*>(&red[k][d0]);
   }
-  merge_store(p, row, d0, o, wt);
+  merge_store(p, row, d0, o, wt, M);
+}
+
+// Two partial results over disjoint key sets (natural-log lse):
+// out = (e^la oa + e^lb ob) / (e^la + e^lb), lse = ln(e^la + e^lb); a side
+// with lse = -inf (no key) drops out.  D/4 threads per row, 4 outputs each.
+template <int D>
+__global__ __launch_bounds__(256) void pa_merge2_kernel(Merge2Params p) {
+  constexpr int TPR = D / 4;
+  constexpr int RPB = 256 / TPR;
+  constexpr float kLog2e = 1.4426950408889634f;
+  const int64_t row = (int64_t)blockIdx.x * RPB + threadIdx.x / TPR;
+  if (row >= (int64_t)p.total_q * p.num_q_heads) return;
+  const int64_t tok = row / p.num_q_heads;
+  const int hd = (int)(row % p.num_q_heads);
+  const int d0 = (threadIdx.x % TPR) * 4;
+  const float la = p.la[tok * p.la_st + hd], lb = p.lb[tok * p.lb_st + hd];
+  const float M = fmaxf(la, lb);
+  float wa = 0.f, wb = 0.f;
+  if (M != kNegInf) {
+    wa = la == kNegInf ? 0.f : exp2_fast((la - M) * kLog2e);
+    wb = lb == kNegInf ? 0.f : exp2_fast((lb - M) * kLog2e);
+  }
+  const float ws = wa + wb;
+  const float inv = ws > 0.f ? 1.f / ws : 0.f;
+  const u32x2 xa = *reinterpret_cast<const u32x2*>(p.oa + tok * p.oa_st + (int64_t)hd * p.oa_sh + d0);
+  const u32x2 xb = *reinterpret_cast<const u32x2*>(p.ob + tok * p.ob_st + (int64_t)hd * p.ob_sh + d0);
+  float o[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const uint32_t ua = (xa[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
+    const uint32_t ub = (xb[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
+    const float fa = __builtin_bit_cast(float, ua << 16), fb = __builtin_bit_cast(float, ub << 16);
+    // a side with no weight is not read into the sum (its value may be anything)
+    o[e] = ((wa > 0.f ? wa * fa : 0.f) + (wb > 0.f ? wb * fb : 0.f)) * inv;
+  }
+  const u32x2 w = {pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
+  *reinterpret_cast<u32x2*>(p.out + tok * p.o_st + (int64_t)hd * p.o_sh + d0) = w;
+  if (p.lse && d0 == 0) p.lse[tok * p.l_st + hd] = ws > 0.f ? M + __logf(ws) : kNegInf;
 }
 
 template <int D, int G, bool KV8>
@@ -1533,6 +1584,18 @@ hipError_t launch_fwd(const FwdParams& p, int head_dim, int group, bool wide, bo
                       int64_t nwg, hipStream_t stream) {
   PA_DISPATCH(head_dim, group, kv8, return (launch_fwd_t<DD, GG, KK>(p, wide, nwg, stream)));
   return hipErrorInvalidValue;
+}
+
+hipError_t launch_merge2(const Merge2Params& p, int head_dim, hipStream_t stream) {
+  const int64_t rows = (int64_t)p.total_q * p.num_q_heads;
+  if (rows <= 0) return hipSuccess;
+  if (head_dim == 128)
+    hipLaunchKernelGGL(pa_merge2_kernel<128>, dim3((unsigned)((rows + 7) / 8)), dim3(256), 0, stream, p);
+  else if (head_dim == 64)
+    hipLaunchKernelGGL(pa_merge2_kernel<64>, dim3((unsigned)((rows + 15) / 16)), dim3(256), 0, stream, p);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
 }
 
 hipError_t launch_merge(const MergeParams& p, int head_dim, hipStream_t stream) {

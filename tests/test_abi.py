@@ -275,3 +275,41 @@ def test_cache_write_validation():
     assert rc(k_cache=kc, v_cache=kc) == "PA_ERR_ALIAS"
     assert rc(key=key[:0], value=key[:0], slots=slots[:0]) == "PA_OK"      # nothing to write
     assert "pa_cache_write" in declared_functions()
+
+
+def test_lse_and_merge_validation():
+    a = cpu_args()
+    T, Hq = a["q"].shape[0], a["q"].shape[1]
+    lse = torch.zeros(T, Hq, dtype=torch.float32)
+    ds = [pa.describe(a[n]) for n in ("q", "k_cache", "v_cache", "out")]
+    meta = [pa.describe(a[n]) for n in ("cu_seqlens_q", "seqused_k", "block_table")]
+
+    def rc_lse(l):
+        dl = pa.describe(l) if l is not None else None
+        r = pa.lib.pa_unified_attention_lse(*[ctypes.byref(d) for d in ds],
+                                            ctypes.byref(dl) if dl is not None else None,
+                                            *[ctypes.byref(d) for d in meta], a["max_seqlen_q"],
+                                            a["max_seqlen_k"], a["softmax_scale"], 1, None, None,
+                                            0, None)
+        return pa.STATUS.get(r, r)
+
+    assert rc_lse(None) == "PA_ERR_NULL"
+    assert rc_lse(lse.double()) == "PA_ERR_DTYPE"
+    assert rc_lse(torch.zeros(T, Hq + 1, dtype=torch.float32)) == "PA_ERR_SHAPE"
+    out = a["out"]
+
+    def rc_merge(**over):
+        m = dict(oa=out.clone(), la=lse.clone(), ob=out.clone(), lb=lse.clone(), o=out, lo=None)
+        m.update(over)
+        dd = [pa.describe(m[n]) for n in ("oa", "la", "ob", "lb", "o")]
+        dlo = pa.describe(m["lo"]) if m["lo"] is not None else None
+        r = pa.lib.pa_merge_attention(*[ctypes.byref(d) for d in dd],
+                                      ctypes.byref(dlo) if dlo is not None else None, None)
+        return pa.STATUS.get(r, r)
+
+    assert rc_merge(la=lse.double()) == "PA_ERR_DTYPE"
+    assert rc_merge(ob=torch.zeros(T, Hq, 64, dtype=torch.bfloat16)) == "PA_ERR_SHAPE"
+    assert rc_merge(oa=out) == "PA_ERR_ALIAS"
+    assert rc_merge(o=torch.zeros(T, Hq, 32, dtype=torch.bfloat16),
+                    oa=torch.zeros(T, Hq, 32, dtype=torch.bfloat16),
+                    ob=torch.zeros(T, Hq, 32, dtype=torch.bfloat16)) == "PA_ERR_UNSUPPORTED"
