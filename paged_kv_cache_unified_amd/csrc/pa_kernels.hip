@@ -678,11 +678,24 @@ struct WideCfg {
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-// Lanes l and l ^ 32 hold halves of one row.  (ds_bpermute through
-// __shfl_xor; the permlane32 swap builtin is not used because the compiler
-// folds its two results into one when both inputs are the same value.)
-__device__ __forceinline__ float swap_halves_max(float x) { return fmaxf(x, __shfl_xor(x, 32)); }
-__device__ __forceinline__ float swap_halves_sum(float x) { return x + __shfl_xor(x, 32); }
+// Lanes l and l ^ 32 hold halves of one row.  v_permlane32_swap exchanges
+// the upper half-wave of its first operand with the lower half-wave of its
+// second: with both holding x, the results are x of lanes 0..31 and x of
+// lanes 32..63 in every lane, so one max / add combines a row's halves.
+// Written as asm: the compiler's builtin folds the two results into one.
+__device__ __forceinline__ void swap_halves(float& a, float& b) {
+  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+}
+__device__ __forceinline__ float swap_halves_max(float x) {
+  float a = x, b = x;
+  swap_halves(a, b);
+  return fmaxf(a, b);
+}
+__device__ __forceinline__ float swap_halves_sum(float x) {
+  float a = x, b = x;
+  swap_halves(a, b);
+  return a + b;
+}
 
 template <int D, int G, bool KV8>
 __device__ __forceinline__ void attend_wide(const FwdParams& p, const Item& it,
@@ -820,8 +833,10 @@ __device__ __forceinline__ void attend_wide(const FwdParams& p, const Item& it,
   const float thr = kThr / c;
 
   // One stage: S^T for 64 keys, mask (only where a row limit falls inside the
-  // stage), online softmax, O^T += V^T P^T.  Written without branches that
-  // touch the accumulators, so they stay in place across stages.
+  // stage), then per 32-key half: row max, (rare) rescale, exp, O^T += V^T
+  // P^T.  The half-0 softmax overlaps the half-1 score MFMAs and the
+  // half-0 P V MFMAs overlap the half-1 softmax.  No branch touches the
+  // accumulators except the in-place rescale.
   auto compute = [&](const unsigned char* Kb, int kst) {
     const unsigned char* Vb = Kb + TB;
     f32x16 s[2];
@@ -830,9 +845,9 @@ __device__ __forceinline__ void attend_wide(const FwdParams& p, const Item& it,
 #pragma unroll
       for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {     // two independent accumulation chains
+      for (int ks = 0; ks < KS; ++ks) {
         const bf16x8 a = *reinterpret_cast<const bf16x8*>(Kb + kb * 32 * CPR * 16 + koff[ks]);
         s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qB[ks], s[kb], 0, 0, 0);
       }
@@ -852,49 +867,49 @@ __device__ __forceinline__ void attend_wide(const FwdParams& p, const Item& it,
         for (int r = 0; r < 16; ++r)
           if (32 * kb + 8 * (r >> 2) + (r & 3) >= rel) s[kb][r] = kNegInf;
     }
-    float mx = s[0][0];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < 2; ++kb) {
+      float mx = s[kb][0];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-    mx = swap_halves_max(mx);
-    const float mnew = fmaxf(m, mx);
-    if (__builtin_amdgcn_ballot_w64(mnew > m + thr)) {
-      const float alpha = m == kNegInf ? 0.f : exp2_fast((m - mnew) * c);
-      m = mnew;
-      l *= alpha;
+      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+      mx = swap_halves_max(mx);
+      const float mnew = fmaxf(m, mx);
+      if (__builtin_amdgcn_ballot_w64(mnew > m + thr)) {
+        const float alpha = m == kNegInf ? 0.f : exp2_fast((m - mnew) * c);
+        m = mnew;
+        l *= alpha;
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt)
+        for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float x = acc[dt][r];
-          scale_inplace(x, alpha);
-          acc[dt][r] = x;
-        }
-    }
-    const float mc = m == kNegInf ? 0.f : m * c;
-    bf16x8 pb[4];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+          for (int r = 0; r < 16; ++r) {
+            float x = acc[dt][r];
+            scale_inplace(x, alpha);
+            acc[dt][r] = x;
+          }
+      }
+      const float mc = m == kNegInf ? 0.f : m * c;
+      bf16x8 pb[2];
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const float pr = exp2_fast(__builtin_fmaf(s[kb][r], c, -mc));
         l += pr;
-        pb[2 * kb + (r >> 3)][r & 7] = (__bf16)pr;
+        pb[r >> 3][r & 7] = (__bf16)pr;
       }
 #pragma unroll
-    for (int sl = 0; sl < 4; ++sl) {
+      for (int hs = 0; hs < 2; ++hs) {
+        const int sl = 2 * kb + hs;                // 16-key slice of the stage
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        const unsigned char* a = Vb + sl * 16 * CPR * 16 + voff[dt];
-        const i16x4 a0 = __builtin_bit_cast(
-            i16x4, __builtin_amdgcn_ds_read_tr16_b64_v4bf16((PA_LDS bf16x4*)(a)));
-        const i16x4 a1 = __builtin_bit_cast(
-            i16x4, __builtin_amdgcn_ds_read_tr16_b64_v4bf16((PA_LDS bf16x4*)(a + 8 * CPR * 16)));
-        const u32x4 packed = {__builtin_bit_cast(u32x2, a0)[0], __builtin_bit_cast(u32x2, a0)[1],
-                              __builtin_bit_cast(u32x2, a1)[0], __builtin_bit_cast(u32x2, a1)[1]};
-        acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, packed),
-                                                          pb[sl], acc[dt], 0, 0, 0);
+        for (int dt = 0; dt < DT; ++dt) {
+          const unsigned char* a = Vb + sl * 16 * CPR * 16 + voff[dt];
+          const i16x4 a0 = __builtin_bit_cast(
+              i16x4, __builtin_amdgcn_ds_read_tr16_b64_v4bf16((PA_LDS bf16x4*)(a)));
+          const i16x4 a1 = __builtin_bit_cast(
+              i16x4, __builtin_amdgcn_ds_read_tr16_b64_v4bf16((PA_LDS bf16x4*)(a + 8 * CPR * 16)));
+          const u32x4 packed = {__builtin_bit_cast(u32x2, a0)[0], __builtin_bit_cast(u32x2, a0)[1],
+                                __builtin_bit_cast(u32x2, a1)[0], __builtin_bit_cast(u32x2, a1)[1]};
+          acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, packed),
+                                                            pb[hs], acc[dt], 0, 0, 0);
+        }
       }
     }
   };
