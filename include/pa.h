@@ -112,10 +112,14 @@ typedef struct {
   int32_t persistent;    /* 1: persistent decode kernel; items (sequence, key
                             split, kv-head) are enumerated on the device, and
                             num_splits bounds a row's split count            */
-  int32_t balanced;      /* 1 (persistent only): split sizes are chosen on the
-                            device from the batch's total context so every
-                            work-group streams about the same bytes; at least
-                            split_keys keys per split                        */
+  int32_t balanced;      /* 1 (persistent only): even split.  The device lays
+                            the rows (sequence, kv-head) end to end as one
+                            stream of cache blocks and cuts it into equal
+                            chunks, one or more per wave, so every wave
+                            streams the same bytes however ragged the
+                            lengths; a chunk has at least split_keys / 16
+                            blocks and a row's parts are the chunks it
+                            touches (at most num_splits)                     */
   int32_t longest_first; /* 1 (grid plans with wide tiles, at most 2048
                             sequences): work-group b takes the (b / Hkv)-th
                             (sequence, query tile, key split) in order of

@@ -224,27 +224,39 @@ int make_plan(const Shapes& s, int32_t max_q, int32_t max_k, const pa_options* o
     const int64_t grid = std::max<int64_t>(8, resident / 8 * 8);
     int64_t split_keys;
     p.balanced = false;
-    if (force_split > 0) {
-      split_keys = (mk + force_split - 1) / force_split;        // fixed-size parts
-    } else if (mk <= pa::kMaxSplitKeys && s.S * s.Hkv >= 4 * grid) {
-      split_keys = mk;                       // a whole (sequence, kv-head) for every wave
+    if (force_split > 0 || (mk <= pa::kMaxSplitKeys && s.S * s.Hkv >= 4 * grid) ||
+        mk <= pa::kEvenMinContext) {
+      // fixed-size parts; without a forced count a whole (sequence, kv-head)
+      // for every wave: the batch fills every wave, or its rows are so short
+      // that a merge pass would cost more than the imbalance
+      split_keys = force_split > 0 ? (mk + force_split - 1) / force_split : mk;
+      split_keys = (split_keys + pa::kStageKeys - 1) / pa::kStageKeys * pa::kStageKeys;
+      split_keys = std::min<int64_t>(split_keys, pa::kMaxSplitKeys);
+      p.n_split = (int32_t)((mk + split_keys - 1) / split_keys);
     } else {
-      // balanced parts: the device sizes them from the total context so each
-      // wave gets ~kDecodeItemsPerWave equal items; at least kMinSplitKeys
+      // even split: the device cuts the stream of (sequence, kv-head, block)
+      // into equal chunks, so every wave streams the same bytes however ragged
+      // the batch.  A chunk has at least cmin blocks, cmin chosen so a row has
+      // at most ~kEvenMaxParts parts; a row's parts are the chunks it touches.
       p.balanced = true;
-      split_keys = pa::kMinSplitKeys;
+      const int64_t mkb = (mk + pa::kBlockSize - 1) / pa::kBlockSize;
+      const int64_t cmin = std::min<int64_t>(
+          std::max<int64_t>(pa::kEvenMinBlocks, (mkb + pa::kEvenMaxParts - 1) / pa::kEvenMaxParts),
+          pa::kMaxSplitKeys / pa::kBlockSize);
+      split_keys = cmin * pa::kBlockSize;
+      p.n_split = (int32_t)((mkb + cmin - 1) / cmin + 1);
+      // stream positions stay in int32 on the device
+      if ((int64_t)s.S * (mkb + 1) * s.Hkv * 2 > kMaxInt32)
+        return fail(PA_ERR_UNSUPPORTED, "decode batch too large for the even split");
     }
-    split_keys = (split_keys + pa::kStageKeys - 1) / pa::kStageKeys * pa::kStageKeys;
-    split_keys = std::min<int64_t>(split_keys, pa::kMaxSplitKeys);
     p.split_keys = (int32_t)split_keys;
-    p.n_split = (int32_t)((mk + split_keys - 1) / split_keys);   // bound on parts per row
     p.num_items = 0;                         // known on the device only
     p.nwg = grid;
     if (p.n_split > 1) {
       const size_t rows = (size_t)s.T * (size_t)s.Hq * (size_t)p.n_split;
       p.ws_lse_offset = align256(rows * (size_t)s.D * sizeof(float));
       p.ws_parts_offset = p.ws_lse_offset + align256(rows * sizeof(float));
-      p.ws_bytes = p.ws_parts_offset + align256((size_t)s.S * sizeof(int32_t));
+      p.ws_bytes = p.ws_parts_offset + align256((size_t)s.S * (size_t)s.Hkv * sizeof(int32_t));
     }
     *out = p;
     return PA_OK;
@@ -489,7 +501,6 @@ int run(const pa_tensor* q, const pa_tensor* k, const pa_tensor* v, pa_tensor* o
   p.n_split = plan.n_split;
   p.split_keys = plan.split_keys;
   p.balanced = plan.balanced ? 1 : 0;
-  p.items_per_wg = pa::kDecodeItemsPerWave;
   p.ws_parts = plan.persistent && plan.n_split > 1
                    ? reinterpret_cast<int32_t*>(static_cast<char*>(ws) + plan.ws_parts_offset)
                    : nullptr;
@@ -526,6 +537,7 @@ int run(const pa_tensor* q, const pa_tensor* k, const pa_tensor* v, pa_tensor* o
     mp.cu_q = p.cu_q;
     mp.seq_k = p.seq_k;
     mp.num_seqs = (int32_t)s.S;
+    mp.num_kv_heads = (int32_t)s.Hkv;
     mp.split_keys = plan.split_keys;
     mp.lse_out = p.lse_out;
     mp.lse_st = p.lse_st;

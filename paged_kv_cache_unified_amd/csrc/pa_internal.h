@@ -14,8 +14,9 @@ constexpr int kTileRows = 128;    // packed rows of a wide query tile (32 per wa
 constexpr int kNarrowRows = 16;   // rows of a narrow (decode) tile
 constexpr int kMaxSplitKeys = 4096;  // keys per split: at most 64 blocks per wave (narrow)
 constexpr int kMaxDecodeSeqs = 2048; // sequences the persistent decode kernel can enumerate
-constexpr int kMinSplitKeys = 512;   // smallest balanced split of the persistent decode kernel
-constexpr int kDecodeItemsPerWave = 2; // balanced decode: items per resident wave
+constexpr int kEvenMinBlocks = 16;   // even split: smallest chunk (cache blocks per wave)
+constexpr int kEvenMinContext = 1024; // decode batches with shorter rows keep one part per row
+constexpr int kEvenMaxParts = 256;   // even split: chunks grow so a row has at most ~this many parts
 constexpr int kDecodeRing = 2;        // cache blocks in flight per wave (persistent decode; 3 measured no faster)
 constexpr int kLptMaxSeqs = 2048;   // longest-first order: LDS tables of 3 ints per sequence
 
@@ -43,9 +44,11 @@ struct FwdParams {
   int32_t slots_direct;    // 1: slot index is the sequence index
   int32_t n_split;
   int32_t split_keys;      // multiple of kStageKeys
-  int32_t balanced;        // persistent decode: parts per sequence chosen on the device
-  int32_t items_per_wg;    // balanced decode: target items per wave
-  int32_t* ws_parts;       // persistent decode with n_split > 1: parts of each sequence [S]
+  int32_t balanced;        // persistent decode, even split: the batch's (sequence, kv-head,
+                           // block) stream is cut into equal chunks of at least
+                           // split_keys / 16 blocks, one or more per wave
+  int32_t* ws_parts;       // persistent decode with n_split > 1: parts of each
+                           // (sequence, kv-head) row [S * Hkv]
   int32_t num_items;       // num_slots * num_kv_heads * n_split
   int32_t items_per_xcd;   // ceil(num_items / 8): contiguous item range per XCD
   int32_t kv_major;        // item order: 1 = (kv-head, slot, split), 0 = (slot, kv-head, split)
@@ -68,11 +71,12 @@ struct MergeParams {
   int32_t total_q;
   int32_t num_q_heads;
   int32_t n_split;         // upper bound on parts per row
-  const int32_t* parts;    // persistent decode: parts of each sequence [S]; null:
+  const int32_t* parts;    // persistent decode: parts of each (sequence, kv-head) [S * Hkv]; null:
                            // ceil(seq_k / split_keys) clamped to [1, n_split].
                            // Rows with one part were written by the forward
                            // kernel and are skipped.
   int32_t num_seqs;
+  int32_t num_kv_heads;
   int32_t split_keys;
   float* lse_out;          // optional: merged natural-log lse [T, Hq] (row stride lse_st)
   int64_t lse_st;

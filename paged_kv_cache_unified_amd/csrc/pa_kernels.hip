@@ -994,13 +994,22 @@ void pa_fwd_kernel(FwdParams p) {
 // ---------------------------------------------------------------------------
 // Persistent decode kernel (batches whose every sequence is one narrow tile).
 //
-// Work list: sequence s contributes n_s key parts (one if L_s = 0, none if it
-// has no query) and every (s, part, kv-head) is one item, streamed by ONE
-// wave from start to end: no cross-wave merge and no work-group barrier after
-// the set-up.  Each work-group builds the prefix sums of n_s in LDS once and
-// stages the per-sequence metadata there; items are dealt to XCDs in
-// contiguous ranges and the waves of one XCD stride through its range, so the
-// kv-heads of a sequence (which share its cache blocks) stream together.
+// Work list, two modes.  Fixed parts: sequence s contributes n_s key parts of
+// split_keys keys (one if L_s = 0, none if it has no query) and every (s,
+// part, kv-head) is one item; items are dealt to XCDs in contiguous ranges
+// and the waves of one XCD stride through its range, so the kv-heads of a
+// sequence (which share its cache blocks) stream together.  Even split (for
+// ragged batches): the sequences, each ceil(L_s / 16) blocks long (at least
+// one), are laid end to end as one stream of blocks, cut into equal chunks;
+// every (chunk, kv-head) pair is one wave's work (one or more pairs per wave),
+// an item is the piece of one sequence inside a chunk for that kv-head, and a
+// row's parts are the chunks its sequence touches.  Every wave then streams
+// the same number of blocks however skewed the lengths (stream-K), and the
+// waves of a work-group read the same blocks for different kv-heads.
+// Either way one item is streamed by ONE wave from start to end: no
+// cross-wave merge and no work-group barrier after the set-up.  Each
+// work-group builds the prefix sums of the per-sequence units in LDS once and
+// stages the per-sequence metadata there.
 //
 // A wave's block stream continues across items: the last refills of an item
 // already fetch the next item's first blocks (its block ids and Q were loaded
@@ -1023,26 +1032,11 @@ struct DecodeCfg {
 };
 
 
-// Key parts of a sequence with `ql` queries and context L.  Fixed mode: parts
-// of `target` keys.  Balanced mode: round(L / target) equal parts (at least
-// one, each at most kMaxSplitKeys keys), where target ~ total context * Hkv /
-// (waves * items per wave), so waves stream similar byte counts.
+// Key parts of a sequence with `ql` queries and context L (fixed-size parts
+// of `target` keys, at most n_split).
 __device__ __forceinline__ int seq_parts(const FwdParams& p, int ql, int L, int target) {
   if (ql <= 0) return 0;
-  int n;
-  if (p.balanced) {
-    n = (L + target / 2) / target;
-    n = max(n, (L + kMaxSplitKeys - 1) / kMaxSplitKeys);
-  } else {
-    n = (L + target - 1) / target;
-  }
-  return min(max(n, 1), p.n_split);
-}
-// keys per part (a multiple of the block size)
-__device__ __forceinline__ int part_keys(const FwdParams& p, int L, int parts, int target) {
-  if (!p.balanced) return target;
-  const int k = (L + parts - 1) / parts;
-  return max(kBlockSize, (k + kBlockSize - 1) / kBlockSize * kBlockSize);
+  return min(max((L + target - 1) / target, 1), p.n_split);
 }
 
 struct DItem {
@@ -1051,6 +1045,8 @@ struct DItem {
   int q0, q_len, rows, L, diag;
   int kbeg, kend, kmin;
   int blk0, nb;          // first block and number of blocks of the item
+  int c, next;           // even split: (chunk, kv-head) pair and stream position after the item;
+                         // fixed parts: the wave's next item ordinal
 };
 
 // Item -> (sequence, part, kv-head) from the LDS tables only.
@@ -1076,9 +1072,8 @@ __device__ __forceinline__ DItem describe_item(const FwdParams& p, const int* pr
   d.rows = d.q_len * G;
   d.L = uniform(lent[lo]);
   d.diag = d.L - d.q_len;
-  const int pk = part_keys(p, d.L, d.units, target);
-  d.kbeg = d.sigma * pk;
-  d.kend = max(0, min(d.L, d.kbeg + pk));
+  d.kbeg = d.sigma * target;
+  d.kend = max(0, min(d.L, d.kbeg + target));
   d.kmin = p.causal ? min(d.kend, d.diag + 1) : d.kend;
   d.blk0 = d.kbeg / kBlockSize;
   d.nb = d.kend > d.kbeg ? (d.kend + kBlockSize - 1) / kBlockSize - d.blk0 : 0;
@@ -1111,38 +1106,30 @@ void pa_decode_kernel(FwdParams p) {
   int* wsum = reinterpret_cast<int*>(smem + Cfg::SCAN_OFFSET);
   int* idsw = reinterpret_cast<int*>(smem + Cfg::IDS_OFFSET) + wave * 2 * kMaxItemBlocks;
 
-  // ---- stage per-sequence metadata; part size; prefix sums of part counts ----
+  // ---- stage per-sequence metadata; prefix sums of per-sequence units ----
   const int S = p.num_seqs;
+  const int Hkv = p.num_kv_heads;
   const int C = (S + kThreads - 1) / kThreads;
   const int s0 = min(S, tid * C), s1 = min(S, s0 + C);
-  long long ctx = 0;
   for (int s = s0; s < s1; ++s) {
-    const int a = p.cu_q[s], L = p.seq_k[s];
-    q0t[s] = a;
-    lent[s] = L;
-    if (p.cu_q[s + 1] > a) ctx += L;
+    q0t[s] = p.cu_q[s];
+    lent[s] = p.seq_k[s];
   }
   if (tid == 0) q0t[S] = p.cu_q[S];
   const int workers = (int)gridDim.x * 4;
-  int target = p.split_keys;
-  if (p.balanced) {
-    // total context of sequences with queries (64-bit: can exceed 2^31)
-#pragma unroll
-    for (int d = 32; d >= 1; d >>= 1) ctx += __shfl_xor(ctx, d);
-    long long* tot = reinterpret_cast<long long*>(wsum);
-    if (lane == 0) tot[wave] = ctx;
-    __syncthreads();
-    // items are (sequence, part, kv-head): aim for items_per_wg items per wave
-    const long long all = (tot[0] + tot[1] + tot[2] + tot[3]) * p.num_kv_heads;
-    const long long denom = (long long)workers * p.items_per_wg;
-    long long t = (all + denom - 1) / denom;
-    t = (t + kBlockSize - 1) / kBlockSize * kBlockSize;
-    target = (int)min((long long)kMaxSplitKeys, max((long long)p.split_keys, t));
-  }
-  __syncthreads();                                  // tables written, tot read
+  const int target = p.split_keys;                   // fixed parts: keys per part
+  __syncthreads();
+  // units of a sequence per kv-head: its parts (fixed), or its blocks in the
+  // stream (even split; a row with no key still takes one position, so its
+  // zero output gets written)
+  auto seq_units = [&](int s) -> int {
+    const int ql = q0t[s + 1] - q0t[s];
+    if (p.balanced) return ql > 0 ? max((lent[s] + kBlockSize - 1) / kBlockSize, 1) : 0;
+    return seq_parts(p, ql, lent[s], target);
+  };
   {
     int local = 0;
-    for (int s = s0; s < s1; ++s) local += seq_parts(p, q0t[s + 1] - q0t[s], lent[s], target);
+    for (int s = s0; s < s1; ++s) local += seq_units(s);
     int incl = local;
 #pragma unroll
     for (int d = 1; d < 64; d <<= 1) {
@@ -1155,31 +1142,110 @@ void pa_decode_kernel(FwdParams p) {
     for (int w = 0; w < wave; ++w) base += wsum[w];
     int run = base + incl - local;
     for (int s = s0; s < s1; ++s) {
-      const int n = seq_parts(p, q0t[s + 1] - q0t[s], lent[s], target);
       pref[s] = run;
-      run += n;
-      if (p.n_split > 1 && blockIdx.x == 0) p.ws_parts[s] = n;   // for pa_merge
+      run += seq_units(s);
     }
     if (tid == kThreads - 1) pref[S] = base + incl;
     __syncthreads();
   }
-  const int n_items = uniform(pref[S]) * p.num_kv_heads;
+  // fixed parts: items, kv-heads included; even split: the blocks of the
+  // per-sequence stream (one kv-head's worth)
+  const int n_units = uniform(pref[S]) * (p.balanced ? 1 : Hkv);
+  // Even split: the stream is cut into n_chunks chunks of `chunk` blocks, and
+  // every (chunk, kv-head) pair is one wave's work: kpw pairs per wave, each at
+  // most kMaxItemBlocks blocks (one item's block-id table) and at least
+  // split_keys / 16.
+  int chunk = 1, n_pairs = 0;
+  if (p.balanced) {
+    const int all = n_units * Hkv;                     // blocks over all kv-heads
+    const int cap = workers * kMaxItemBlocks;
+    const int kpw = max(1, (all + cap - 1) / cap);
+    chunk = max((all + workers * kpw - 1) / (workers * kpw), target / kBlockSize);
+    n_pairs = (n_units + chunk - 1) / chunk * Hkv;
+  }
+  // parts of every (sequence, kv-head) row, for pa_merge
+  if (p.n_split > 1 && blockIdx.x == 0) {
+    for (int s = s0; s < s1; ++s) {
+      const int u = seq_units(s);
+      int n = u;
+      if (p.balanced) n = u > 0 ? (pref[s] + u - 1) / chunk - pref[s] / chunk + 1 : 0;
+      for (int g = 0; g < Hkv; ++g) p.ws_parts[s * Hkv + g] = n;
+    }
+  }
 
-  // Items are dealt to XCDs in contiguous ranges (work-group w runs on XCD
-  // w % 8); the waves of one XCD stride through its range.
+  // Fixed parts: items are dealt to XCDs in contiguous ranges (work-group w
+  // runs on XCD w % 8); the waves of one XCD stride through its range, and
+  // consecutive items (the kv-heads of one sequence, which read the same cache
+  // blocks) go to the waves of one work-group, i.e. one CU.  Even split: wave
+  // gw (numbered XCD-major) takes pairs gw, gw + workers, ...; pair q is chunk
+  // q / Hkv for kv-head q % Hkv, so the waves of a work-group read the same
+  // blocks for different kv-heads.
   const int xcd = blockIdx.x & 7;
   const int wpx = (int)(gridDim.x >> 3) * 4;           // waves per XCD (grid % 8 == 0)
+  const int n_items = p.balanced ? 0 : n_units;
   const int per_xcd = (n_items + 7) >> 3;
   const int range_end = min(n_items, (xcd + 1) * per_xcd);
-  // consecutive items (the kv-heads of one sequence, which read the same cache
-  // blocks) go to the waves of one work-group, i.e. one CU
   const int item0 = xcd * per_xcd + (int)(blockIdx.x >> 3) * 4 + wave;
+  const int gw = xcd * wpx + (int)(blockIdx.x >> 3) * 4 + wave;
   auto item_at = [&](int m) -> int {                   // m-th item of this wave
     const int it = item0 + m * wpx;
     return it < range_end ? it : n_items;              // n_items marks "none"
   };
-  int mi = 0;
-  if (item_at(0) >= n_items) return;                   // whole wave idle
+  if (p.balanced ? gw >= n_pairs : item_at(0) >= n_items) return;   // whole wave idle
+
+  // Fixed parts: pos is the wave's item ordinal.  Even split: the item is the
+  // piece of pair q's chunk from stream position pos to the end of its
+  // sequence or of the chunk, for the pair's kv-head.
+  auto describe = [&](int q, int pos) -> DItem {
+    if (!p.balanced) {
+      DItem d = describe_item<G>(p, pref, q0t, lent, n_items, item_at(pos), target);
+      d.next = pos + 1;
+      return d;
+    }
+    DItem d = {};
+    d.valid = q < n_pairs;
+    if (!d.valid) return d;
+    const int c = q / Hkv;
+    const int xe = min((c + 1) * chunk, n_units);
+    int lo = 0, hi = S - 1;                            // largest s with its first block <= pos
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (uniform(pref[mid]) <= pos) lo = mid; else hi = mid - 1;
+    }
+    const int L = uniform(lent[lo]);
+    const int nbe = max((L + kBlockSize - 1) / kBlockSize, 1);
+    const int x0 = uniform(pref[lo]);                  // the sequence's first position
+    const int b0 = pos - x0;
+    const int b1 = min(nbe, b0 + (xe - pos));
+    d.s = lo;
+    d.kvh = q - c * Hkv;
+    d.sigma = c - x0 / chunk;
+    d.units = (x0 + nbe - 1) / chunk - x0 / chunk + 1;
+    d.q0 = uniform(q0t[lo]);
+    d.q_len = uniform(q0t[lo + 1]) - d.q0;
+    d.rows = d.q_len * G;
+    d.L = L;
+    d.diag = L - d.q_len;
+    d.kbeg = b0 * kBlockSize;
+    d.kend = max(0, min(L, b1 * kBlockSize));
+    d.kmin = p.causal ? min(d.kend, d.diag + 1) : d.kend;
+    d.blk0 = b0;
+    d.nb = d.kend > d.kbeg ? (d.kend + kBlockSize - 1) / kBlockSize - b0 : 0;
+    d.c = q;
+    d.next = pos + (b1 - b0);
+    return d;
+  };
+  auto after = [&](const DItem& d) -> DItem {
+    if (!d.valid) return d;
+    if (!p.balanced) return describe(0, d.next);
+    int q = d.c, pos = d.next;
+    if (pos >= min((q / Hkv + 1) * chunk, n_units)) {
+      q += workers;
+      if (q >= n_pairs) return describe(q, 0);         // invalid: no pair left
+      pos = q / Hkv * chunk;
+    }
+    return describe(q, pos);
+  };
 
   const int slot_stride = p.num_kv_heads * D;
   const int koff = l16 * slot_stride + 8 * h4;
@@ -1243,8 +1309,8 @@ void pa_decode_kernel(FwdParams p) {
 
   // items m (cur), m+1 (nxt), m+2 (nx2): ids of cur and nxt live in LDS, ids of
   // nx2 in VGPRs until cur finishes; Q of nxt is prefetched.
-  DItem cur = describe_item<G>(p, pref, q0t, lent, n_items, item_at(0), target);
-  DItem nxt = describe_item<G>(p, pref, q0t, lent, n_items, item_at(1), target);
+  DItem cur = p.balanced ? describe(gw, gw / Hkv * chunk) : describe(0, 0);
+  DItem nxt = after(cur);
   int cb = 0;
   {
     int v[IDL];
@@ -1253,7 +1319,7 @@ void pa_decode_kernel(FwdParams p) {
     load_ids(nxt, v);
     store_ids(1, v);
   }
-  DItem nx2 = describe_item<G>(p, pref, q0t, lent, n_items, item_at(2), target);
+  DItem nx2 = after(nxt);
   int ids_v2[IDL];
   load_ids(nx2, ids_v2);
   bf16x8 qB[KS], qB_n[KS];
@@ -1371,12 +1437,11 @@ void pa_decode_kernel(FwdParams p) {
     }
     if (!nxt.valid) break;
     // advance: nxt becomes current; nx2's ids move to LDS; fetch the one after
-    ++mi;
     cur = nxt;
     nxt = nx2;
     cb ^= 1;
     store_ids(cb ^ 1, ids_v2);
-    nx2 = describe_item<G>(p, pref, q0t, lent, n_items, item_at(mi + 2), target);
+    nx2 = after(nxt);
     load_ids(nx2, ids_v2);
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) qB[ks] = qB_n[ks];
@@ -1388,16 +1453,19 @@ void pa_decode_kernel(FwdParams p) {
 // w_sigma = 2^(lse_sigma - max lse), out = sum w O_sigma / sum w.  Parts with no
 // key carry lse = -inf and are skipped (their O is never read).
 __device__ __forceinline__ int merge_parts(const MergeParams& p, int64_t row) {
-  // sequence s has parts[s] parts (persistent decode) or ceil(L_s / split)
-  // parts (grid plans); a single part was written straight to out by the
-  // forward kernel
+  // row (sequence s, kv-head g) has parts[s * Hkv + g] parts (persistent
+  // decode) or ceil(L_s / split) parts (grid plans); a single part was
+  // written straight to out by the forward kernel
   const int tok = (int)(row / p.num_q_heads);
   int lo = 0, hi = p.num_seqs - 1;
   while (lo < hi) {
     const int mid = (lo + hi + 1) >> 1;
     if (p.cu_q[mid] <= tok) lo = mid; else hi = mid - 1;
   }
-  if (p.parts) return p.parts[lo];
+  if (p.parts) {
+    const int head = (int)(row - (int64_t)tok * p.num_q_heads);
+    return p.parts[lo * p.num_kv_heads + head / (p.num_q_heads / p.num_kv_heads)];
+  }
   return min(max((p.seq_k[lo] + p.split_keys - 1) / p.split_keys, 1), p.n_split);
 }
 
@@ -1616,7 +1684,10 @@ hipError_t launch_merge2(const Merge2Params& p, int head_dim, hipStream_t stream
 hipError_t launch_merge(const MergeParams& p, int head_dim, hipStream_t stream) {
   const int64_t rows = (int64_t)p.total_q * p.num_q_heads;
   if (rows <= 0) return hipSuccess;
-  const bool wide = p.n_split > 4;           // many parts: a work-group per row
+  // many parts per row: a work-group per row; otherwise D/4 threads per row,
+  // looping over the row's parts.  An even decode split bounds a row's parts
+  // loosely (most rows have one or two): there many rows take the loop form.
+  const bool wide = p.n_split > 4 && (p.parts == nullptr || rows <= 4096);
   if (head_dim == 128) {
     if (wide)
       hipLaunchKernelGGL(pa_merge_wide_kernel<128>, dim3((unsigned)rows), dim3(256), 0, stream, p);

@@ -172,12 +172,17 @@ def test_plan_heuristic_on_workload_shapes():
     p = plan_of(b)
     assert p["persistent"] == 1 and p["tile_tokens"] == 1 and p["num_splits"] == 1
     assert p["num_workgroups"] == 256 * 2 and p["workspace_bytes"] == 0
-    # few long sequences: balanced splits sized on the device, >= 512 keys each;
-    # num_splits bounds the parts of any row
+    # few long sequences: even split on the device, chunks of >= 16 blocks;
+    # num_splits bounds the parts of any row (128 blocks: 128 / 16 + 1)
     b = build_batch("l", np.ones(16, int), np.full(16, 2048), 32, 8, 128, True, 5)
     p = plan_of(b)
     assert p["persistent"] == 1 and p["balanced"] == 1
-    assert p["split_keys"] == 512 and p["num_splits"] == 4
+    assert p["split_keys"] == 256 and p["num_splits"] == 9
+    assert p["workspace_bytes"] >= 9 * 16 * 32 * 129 * 4 + 16 * 8 * 4
+    # very long rows: the smallest chunk grows so a row has at most ~256 parts
+    bl = build_batch("l", np.ones(2, int), np.array([131072, 40]), 32, 8, 128, True, 5)
+    pl = plan_of(bl)
+    assert pl["balanced"] == 1 and pl["split_keys"] == 32 * 16 and pl["num_splits"] == 8192 // 32 + 1
     # a forced split count gives fixed-size parts
     p = plan_of(b, force_num_splits=3)
     assert p["balanced"] == 0 and p["num_splits"] == 3 and p["split_keys"] == 704

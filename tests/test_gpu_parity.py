@@ -211,6 +211,37 @@ def test_persistent_decode_ragged(splits, shape):
     full_parity(b, out, f"persistent splits={splits}")
 
 
+def even_split_lengths(grid):
+    """Ragged decode batch for the even split: long and empty rows, a sequence
+    without queries, two query tokens (rows with no key under the causal mask)."""
+    rng = np.random.default_rng(97 + grid)
+    S = 24
+    q_lens = rng.integers(1, 3, size=S)
+    k_lens = rng.integers(0, 6000, size=S)
+    q_lens[3] = 0
+    k_lens[5] = 0
+    k_lens[7] = 1
+    k_lens[0] = 9000
+    return q_lens, k_lens
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("grid", [8, 64])
+def test_even_split_few_waves(grid):
+    """Even split on a small decode grid: several chunks per wave, rows cut
+    across chunks and waves, rows with no key, a sequence with no query."""
+    require_gpu()
+    q_lens, k_lens = even_split_lengths(grid)
+    b = build_batch("even", q_lens, k_lens, 32, 8, 128, True, seed=97 + grid, device=DEV)
+    opts = pa.options(decode_grid=grid)
+    plan = pa.plan_describe(*b.args(torch.empty_like(b.q))[:9], opts=opts)
+    assert plan["persistent"] == 1 and plan["balanced"] == 1
+    say(f"even split grid={grid} plan={plan['num_splits']}x{plan['split_keys']}")
+    out = run_pa(b, opts=opts)
+    torch.cuda.synchronize()
+    full_parity(b, out, f"even split grid={grid}")
+
+
 def test_narrow_grid_path():
     """The one-work-group-per-item narrow path (force_tile=3)."""
     require_gpu()
