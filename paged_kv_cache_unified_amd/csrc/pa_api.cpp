@@ -45,7 +45,7 @@ struct Plan {
   int64_t nwg;
   size_t ws_bytes;
   size_t ws_lse_offset;
-  size_t ws_parts_offset;
+  size_t ws_parts_offset;   // row part counts [T * Hq] int32
 };
 
 constexpr int64_t kMaxInt32 = 0x7fffffff;
@@ -256,7 +256,7 @@ int make_plan(const Shapes& s, int32_t max_q, int32_t max_k, const pa_options* o
       const size_t rows = (size_t)s.T * (size_t)s.Hq * (size_t)p.n_split;
       p.ws_lse_offset = align256(rows * (size_t)s.D * sizeof(float));
       p.ws_parts_offset = p.ws_lse_offset + align256(rows * sizeof(float));
-      p.ws_bytes = p.ws_parts_offset + align256((size_t)s.S * (size_t)s.Hkv * sizeof(int32_t));
+      p.ws_bytes = p.ws_parts_offset + align256((size_t)s.T * (size_t)s.Hq * sizeof(int32_t));
     }
     *out = p;
     return PA_OK;
@@ -307,7 +307,8 @@ int make_plan(const Shapes& s, int32_t max_q, int32_t max_k, const pa_options* o
   if (n_split > 1) {
     const size_t rows = (size_t)s.T * (size_t)s.Hq * (size_t)n_split;
     p.ws_lse_offset = align256(rows * (size_t)s.D * sizeof(float));
-    p.ws_bytes = p.ws_lse_offset + align256(rows * sizeof(float));
+    p.ws_parts_offset = p.ws_lse_offset + align256(rows * sizeof(float));
+    p.ws_bytes = p.ws_parts_offset + align256((size_t)s.T * (size_t)s.Hq * sizeof(int32_t));
   }
   *out = p;
   return PA_OK;
@@ -501,7 +502,7 @@ int run(const pa_tensor* q, const pa_tensor* k, const pa_tensor* v, pa_tensor* o
   p.n_split = plan.n_split;
   p.split_keys = plan.split_keys;
   p.balanced = plan.balanced ? 1 : 0;
-  p.ws_parts = plan.persistent && plan.n_split > 1
+  p.ws_rparts = plan.n_split > 1
                    ? reinterpret_cast<int32_t*>(static_cast<char*>(ws) + plan.ws_parts_offset)
                    : nullptr;
   p.num_items = (int32_t)plan.num_items;
@@ -533,12 +534,8 @@ int run(const pa_tensor* q, const pa_tensor* k, const pa_tensor* v, pa_tensor* o
     mp.total_q = (int32_t)s.T;
     mp.num_q_heads = (int32_t)s.Hq;
     mp.n_split = plan.n_split;
-    mp.parts = plan.persistent ? p.ws_parts : nullptr;
-    mp.cu_q = p.cu_q;
-    mp.seq_k = p.seq_k;
-    mp.num_seqs = (int32_t)s.S;
-    mp.num_kv_heads = (int32_t)s.Hkv;
-    mp.split_keys = plan.split_keys;
+    mp.row_parts = p.ws_rparts;
+    mp.even = plan.balanced ? 1 : 0;
     mp.lse_out = p.lse_out;
     mp.lse_st = p.lse_st;
     hipError_t e = pa::launch_merge(mp, (int)s.D, stream);

@@ -47,8 +47,8 @@ struct FwdParams {
   int32_t balanced;        // persistent decode, even split: the batch's (sequence, kv-head,
                            // block) stream is cut into equal chunks of at least
                            // split_keys / 16 blocks, one or more per wave
-  int32_t* ws_parts;       // persistent decode with n_split > 1: parts of each
-                           // (sequence, kv-head) row [S * Hkv]
+  int32_t* ws_rparts;      // n_split > 1: parts of each row (token, q-head) [T * Hq],
+                           // written by the row's first part
   int32_t num_items;       // num_slots * num_kv_heads * n_split
   int32_t items_per_xcd;   // ceil(num_items / 8): contiguous item range per XCD
   int32_t kv_major;        // item order: 1 = (kv-head, slot, split), 0 = (slot, kv-head, split)
@@ -64,21 +64,15 @@ struct FwdParams {
 struct MergeParams {
   const float* ws_o;
   const float* ws_lse;
+  const int32_t* row_parts;  // [T * Hq]: parts of each row; rows with one part were
+                             // written by the forward kernel and are skipped
   uint16_t* out;
-  const int32_t* cu_q;     // [S+1]: row -> sequence
-  const int32_t* seq_k;    // [S]: parts of a grid plan, ceil(L_s / split_keys)
   int64_t o_st, o_sh;
   int32_t total_q;
   int32_t num_q_heads;
-  int32_t n_split;         // upper bound on parts per row
-  const int32_t* parts;    // persistent decode: parts of each (sequence, kv-head) [S * Hkv]; null:
-                           // ceil(seq_k / split_keys) clamped to [1, n_split].
-                           // Rows with one part were written by the forward
-                           // kernel and are skipped.
-  int32_t num_seqs;
-  int32_t num_kv_heads;
-  int32_t split_keys;
-  float* lse_out;          // optional: merged natural-log lse [T, Hq] (row stride lse_st)
+  int32_t n_split;           // upper bound on parts per row
+  int32_t even;              // the bound is loose (even decode split): most rows have 1-2
+  float* lse_out;            // optional: merged natural-log lse [T, Hq] (row stride lse_st)
   int64_t lse_st;
 };
 

@@ -606,6 +606,8 @@ __device__ __forceinline__ void attend_narrow(const FwdParams& p, const Item& it
   }
   const int64_t tok = it.q0 + it.tok0 + n / G;
   const int hn = it.kvh * G + n % G;
+  if (p.ws_rparts && it.sigma == 0 && (tid & 15) == 0)
+    p.ws_rparts[tok * p.num_q_heads + hn] = it.parts;     // the row's part count, for pa_merge
   if (it.parts == 1) {
     if ((tid & 15) == 0)
       store_lse(p.lse_out, p.lse_st, tok, hn, Ls > 0.f ? M + __log2f(Ls) : kNegInf);
@@ -943,6 +945,8 @@ __device__ __forceinline__ void attend_wide(const FwdParams& p, const Item& it,
   if (!row_ok) return;
   const float inv = lt > 0.f ? p.out_scale / lt : 0.f;
   const int64_t tok = it.q0 + it.tok0 + t_in;
+  if (p.ws_rparts && it.sigma == 0 && h == 0)
+    p.ws_rparts[tok * p.num_q_heads + head] = it.parts;   // the row's part count, for pa_merge
   if (it.parts == 1) {
     if (h == 0) store_lse(p.lse_out, p.lse_st, tok, head, lt > 0.f ? m * c + __log2f(lt) : kNegInf);
     uint16_t* op = p.out + tok * p.o_st + (int64_t)head * p.o_sh + 4 * h;
@@ -1163,16 +1167,6 @@ void pa_decode_kernel(FwdParams p) {
     chunk = max((all + workers * kpw - 1) / (workers * kpw), target / kBlockSize);
     n_pairs = (n_units + chunk - 1) / chunk * Hkv;
   }
-  // parts of every (sequence, kv-head) row, for pa_merge
-  if (p.n_split > 1 && blockIdx.x == 0) {
-    for (int s = s0; s < s1; ++s) {
-      const int u = seq_units(s);
-      int n = u;
-      if (p.balanced) n = u > 0 ? (pref[s] + u - 1) / chunk - pref[s] / chunk + 1 : 0;
-      for (int g = 0; g < Hkv; ++g) p.ws_parts[s * Hkv + g] = n;
-    }
-  }
-
   // Fixed parts: items are dealt to XCDs in contiguous ranges (work-group w
   // runs on XCD w % 8); the waves of one XCD stride through its range, and
   // consecutive items (the kv-heads of one sequence, which read the same cache
@@ -1418,6 +1412,8 @@ void pa_decode_kernel(FwdParams p) {
       const float inv = l > 0.f ? p.out_scale / l : 0.f;
       const int64_t tok = cur.q0 + l16 / G;
       const int hn = cur.kvh * G + l16 % G;
+      if (p.ws_rparts && cur.sigma == 0 && h4 == 0)
+        p.ws_rparts[tok * p.num_q_heads + hn] = cur.units;  // the row's part count, for pa_merge
       if (cur.units == 1) {
         if (h4 == 0) store_lse(p.lse_out, p.lse_st, tok, hn, l > 0.f ? m + __log2f(l) : kNegInf);
         uint16_t* op = p.out + tok * p.o_st + (int64_t)hn * p.o_sh + 4 * h4;
@@ -1452,21 +1448,10 @@ void pa_decode_kernel(FwdParams p) {
 // Log-sum-exp merge of key-split partials (all lse in the log2 domain):
 // w_sigma = 2^(lse_sigma - max lse), out = sum w O_sigma / sum w.  Parts with no
 // key carry lse = -inf and are skipped (their O is never read).
+// Parts of a row, written by the forward kernel's first part (1: the row was
+// written straight to out and is skipped).
 __device__ __forceinline__ int merge_parts(const MergeParams& p, int64_t row) {
-  // row (sequence s, kv-head g) has parts[s * Hkv + g] parts (persistent
-  // decode) or ceil(L_s / split) parts (grid plans); a single part was
-  // written straight to out by the forward kernel
-  const int tok = (int)(row / p.num_q_heads);
-  int lo = 0, hi = p.num_seqs - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (p.cu_q[mid] <= tok) lo = mid; else hi = mid - 1;
-  }
-  if (p.parts) {
-    const int head = (int)(row - (int64_t)tok * p.num_q_heads);
-    return p.parts[lo * p.num_kv_heads + head / (p.num_q_heads / p.num_kv_heads)];
-  }
-  return min(max((p.seq_k[lo] + p.split_keys - 1) / p.split_keys, 1), p.n_split);
+  return p.row_parts[row];
 }
 
 __device__ __forceinline__ void merge_store(const MergeParams& p, int64_t row, int d0, f32x4 o,
@@ -1687,7 +1672,7 @@ hipError_t launch_merge(const MergeParams& p, int head_dim, hipStream_t stream) 
   // many parts per row: a work-group per row; otherwise D/4 threads per row,
   // looping over the row's parts.  An even decode split bounds a row's parts
   // loosely (most rows have one or two): there many rows take the loop form.
-  const bool wide = p.n_split > 4 && (p.parts == nullptr || rows <= 4096);
+  const bool wide = p.n_split > 4 && (!p.even || rows <= 4096);
   if (head_dim == 128) {
     if (wide)
       hipLaunchKernelGGL(pa_merge_wide_kernel<128>, dim3((unsigned)rows), dim3(256), 0, stream, p);
