@@ -153,7 +153,7 @@ typedef struct {
  *               causal mask (see above).
  *  stream       hipStream_t to launch on (NULL = the null stream).
  *
- * Supported: d in {64, 128}; B == 16; Hq % Hkv == 0 with G = Hq/Hkv in
+ * Supported: d in {64, 128}; B in {16, 32, 64}; Hq % Hkv == 0 with G = Hq/Hkv in
  * {1, 2, 4, 8, 16}.  Unsupported values return PA_ERR_UNSUPPORTED.
  *
  * Preconditions on device contents (unchecked unless check_contents is set;
@@ -258,11 +258,12 @@ int pa_plan_describe(const pa_tensor* q, const pa_tensor* k_cache,
  *
  *  key, value   bf16 [N, Hkv, d]; stride[2] == 1; stride[0], stride[1]
  *               multiples of 8; 16-byte aligned.
- *  k_cache      bf16 or fp8 E4M3 [NB, 16, Hkv, d], as for pa_unified_attention;
+ *  k_cache      bf16 or fp8 E4M3 [NB, B, Hkv, d], B in {16, 32, 64}, as for
+ *               pa_unified_attention;
  *  v_cache      same dtype, shape and strides.  Written in place.
  *  slot_mapping int32 [N], contiguous: token i goes to slot slot_mapping[i] =
- *               physical block * 16 + position in the block; a negative slot
- *               skips the token.  Slots must be < NB * 16 and distinct
+ *               physical block * B + position in the block; a negative slot
+ *               skips the token.  Slots must be < NB * B and distinct
  *               (unchecked; a repeated slot receives one of its tokens).
  *  k_scale, v_scale  fp8 caches: the stored code is x / scale (IEEE fp32
  *               division) rounded to the nearest E4M3 value, ties to even,

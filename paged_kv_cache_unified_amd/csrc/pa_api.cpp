@@ -130,8 +130,11 @@ int validate(const pa_tensor* q, const pa_tensor* k, const pa_tensor* v, const p
   s.G = s.Hq / s.Hkv;
   if (s.D != 64 && s.D != 128)
     return fail(PA_ERR_UNSUPPORTED, "head_dim %lld (supported: 64, 128)", (long long)s.D);
-  if (s.B != pa::kBlockSize)
-    return fail(PA_ERR_UNSUPPORTED, "block_size %lld (supported: 16)", (long long)s.B);
+  if (s.B != 16 && s.B != 32 && s.B != 64)
+    return fail(PA_ERR_UNSUPPORTED, "block_size %lld (supported: 16, 32, 64)", (long long)s.B);
+  // the kernels address 16-key sub-blocks: physical block * (B / 16) + part
+  if (s.NB * (s.B / pa::kBlockSize) > kMaxInt32)
+    return fail(PA_ERR_UNSUPPORTED, "num_blocks * block_size / 16 beyond the 32-bit range");
   if (!pa::fwd_supported((int)s.D, (int)s.G))
     return fail(PA_ERR_UNSUPPORTED, "GQA group %lld (supported: 1, 2, 4, 8, 16)", (long long)s.G);
   if (s.S > 0 && (int64_t)max_k > s.MB * s.B)
@@ -150,7 +153,7 @@ int validate(const pa_tensor* q, const pa_tensor* k, const pa_tensor* v, const p
     return fail(PA_ERR_ALIGN, "q/out strides must be multiples of 8 elements");
   if ((k->stride[0] * kv_esz) % 16)
     return fail(PA_ERR_ALIGN, "cache block stride must be a multiple of 16 bytes");
-  if ((int64_t)pa::kBlockSize * s.Hkv * s.D * kv_esz > kMaxInt32)
+  if (s.B * s.Hkv * s.D * kv_esz > kMaxInt32)
     return fail(PA_ERR_UNSUPPORTED, "one cache block exceeds 2^31 bytes");
   if (cu->stride[0] != 1 && cu->shape[0] > 1) return fail(PA_ERR_UNSUPPORTED, "cu_seqlens_q not contiguous");
   if (sk->stride[0] != 1 && s.S > 1) return fail(PA_ERR_UNSUPPORTED, "seqused_k not contiguous");
@@ -508,6 +511,8 @@ int run(const pa_tensor* q, const pa_tensor* k, const pa_tensor* v, pa_tensor* o
   p.num_items = (int32_t)plan.num_items;
   p.items_per_xcd = (int32_t)(plan.nwg / 8);
   p.kv_major = plan.wide ? 1 : 0;
+  p.sub_sb = (int64_t)pa::kBlockSize * s.Hkv * s.D;
+  p.bshift = s.B == 64 ? 2 : (s.B == 32 ? 1 : 0);
   p.lpt = plan.lpt ? 1 : 0;
   p.causal = causal ? 1 : 0;
   p.narrow_rows = (opt && opt->force_tile == 2) ? 0 : pa::kNarrowRows;
@@ -731,7 +736,8 @@ int pa_cache_write(const pa_tensor* key, const pa_tensor* value, pa_tensor* k_ca
   if (slot_mapping->shape[0] != N)
     return fail(PA_ERR_SHAPE, "slot_mapping has %lld entries, expected %lld",
                 (long long)slot_mapping->shape[0], (long long)N);
-  if (B != pa::kBlockSize) return fail(PA_ERR_UNSUPPORTED, "block_size %lld (supported: 16)", (long long)B);
+  if (B != 16 && B != 32 && B != 64)
+    return fail(PA_ERR_UNSUPPORTED, "block_size %lld (supported: 16, 32, 64)", (long long)B);
   if (D % 8 || D <= 0) return fail(PA_ERR_UNSUPPORTED, "head_dim must be a positive multiple of 8");
   if (N > kMaxInt32 || NB * B > kMaxInt32 || Hkv * D > kMaxInt32 / 8)
     return fail(PA_ERR_UNSUPPORTED, "sizes beyond the 32-bit slot range");
@@ -768,6 +774,7 @@ int pa_cache_write(const pa_tensor* key, const pa_tensor* value, pa_tensor* k_ca
   p.v_st = value->stride[0];
   p.v_sh = value->stride[1];
   p.cache_sb = k_cache->stride[0];
+  p.block_size = (int32_t)B;
   p.num_tokens = (int32_t)N;
   p.slot_elems = (int32_t)(Hkv * D);
   p.chunks_per_token = (int32_t)(Hkv * D / 8);

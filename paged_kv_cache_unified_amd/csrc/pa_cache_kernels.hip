@@ -1,8 +1,8 @@
 // gfx950 kernel of libpa: writing new tokens' keys and values into the paged
-// KV cache [num_blocks, 16, Hkv, d] (the cache layout of the unified kernel,
+// KV cache [num_blocks, block_size, Hkv, d] (the cache layout of the unified kernel,
 // page "[Kernel] Unified Triton kernel that doesn't distinguish between
 // prefill + decode", PR description).  Token i goes to cache slot
-// slot_mapping[i] = physical block * 16 + position in the block; a negative
+// slot_mapping[i] = physical block * block_size + position in the block; a negative
 // slot is skipped.  bf16 caches receive the bf16 values unchanged; fp8 caches
 // (OCP E4M3 "fn", the KV-cache format discussed in the review of page
 // "[Kernel] [V1] Improved performance for V1 Triton (ROCm) backend") receive
@@ -63,8 +63,8 @@ __global__ __launch_bounds__(256) void pa_cache_write_kernel(CacheWriteParams p)
                           (int64_t)head * (is_v ? p.v_sh : p.k_sh) + dc * 8;
     const u32x4 w = *reinterpret_cast<const u32x4*>(src);
     // element offset of the chunk in the cache
-    const int64_t dst = (int64_t)(slot / kBlockSize) * p.cache_sb +
-                        (int64_t)(slot % kBlockSize) * p.slot_elems + (int64_t)ch * 8;
+    const int64_t dst = (int64_t)(slot / p.block_size) * p.cache_sb +
+                        (int64_t)(slot % p.block_size) * p.slot_elems + (int64_t)ch * 8;
     unsigned char* cache = is_v ? p.v_cache : p.k_cache;
     if constexpr (!KV8) {
       *reinterpret_cast<u32x4*>(cache + dst * 2) = w;

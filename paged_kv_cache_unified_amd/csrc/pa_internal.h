@@ -34,6 +34,8 @@ struct FwdParams {
   int64_t q_st, q_sh;      // q strides (token, head)
   int64_t o_st, o_sh;      // out strides
   int64_t kv_sb;           // cache stride between physical blocks
+  int64_t sub_sb;          // cache stride between 16-key sub-blocks of a block (16 * Hkv * d)
+  int32_t bshift;          // block size = 16 << bshift (16, 32 or 64 keys)
   int32_t bt_stride;
   int32_t num_seqs;
   int32_t total_q;
@@ -98,6 +100,7 @@ struct CacheWriteParams {
   const int32_t* slot_mapping;   // [N]; < 0: skip
   int64_t k_st, k_sh, v_st, v_sh;   // source strides (elements)
   int64_t cache_sb;         // cache stride between physical blocks (elements)
+  int32_t block_size;       // slots per block (16, 32 or 64)
   int32_t num_tokens;
   int32_t slot_elems;       // Hkv * d
   int32_t chunks_per_token; // Hkv * d / 8

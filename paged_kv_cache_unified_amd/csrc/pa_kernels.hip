@@ -124,6 +124,17 @@ __device__ __forceinline__ void store_lse(float* lse_out, int64_t lse_st, int64_
 }
 
 // Round-to-nearest-even fp32 -> bf16 pair, packed low|high.
+// Cache blocks of B = 16 * 2^bshift keys are read as 2^bshift sub-blocks of 16
+// keys.  Sub-block j of a sequence is part j % 2^bshift of block-table entry
+// j >> bshift; its id packs (physical block, part) into one int.
+__device__ __forceinline__ int sub_block_id(const int32_t* row, int j, int bshift) {
+  return (row[j >> bshift] << bshift) | (j & ((1 << bshift) - 1));
+}
+// element offset of a sub-block in the cache
+__device__ __forceinline__ int64_t sub_block_base(const FwdParams& p, int id) {
+  return (int64_t)(id >> p.bshift) * p.kv_sb + (int64_t)(id & ((1 << p.bshift) - 1)) * p.sub_sb;
+}
+
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   bf16x2 v = {(__bf16)lo, (__bf16)hi};
   return __builtin_bit_cast(uint32_t, v);
@@ -456,7 +467,7 @@ __device__ __forceinline__ void attend_narrow(const FwdParams& p, const Item& it
   const int nb = nblk > wave ? (nblk - wave + 3) / 4 : 0;     // <= 64: split_keys <= 4096
   const int32_t* btrow = p.bt + (int64_t)it.s * p.bt_stride;
   int ids = 0;
-  if (lane < nb) ids = btrow[blk0 + wave + 4 * lane];
+  if (lane < nb) ids = sub_block_id(btrow, blk0 + wave + 4 * lane, p.bshift);
 
   const int slot_stride = p.num_kv_heads * D;
   const unsigned char* kbase = p.k + (int64_t)it.kvh * D * ESZ;
@@ -476,7 +487,7 @@ __device__ __forceinline__ void attend_narrow(const FwdParams& p, const Item& it
 #pragma unroll
   for (int j = 0; j < P; ++j) {
     if (j < nb) {
-      const int64_t boff = (int64_t)__builtin_amdgcn_readlane(ids, j) * p.kv_sb;
+      const int64_t boff = sub_block_base(p, __builtin_amdgcn_readlane(ids, j));
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks)
         kst[j][ks] = gload8<KV8>(kbase + (boff + koff + 32 * ks) * ESZ);
@@ -511,7 +522,7 @@ __device__ __forceinline__ void attend_narrow(const FwdParams& p, const Item& it
               __builtin_bit_cast(bf16x8, to_bf16x8(kst[j][ks])), qB[ks], sc, 0, 0, 0);
         // refill this ring slot with block i + P
         if (i + P < nb) {
-          const int64_t boff = (int64_t)__builtin_amdgcn_readlane(ids, i + P) * p.kv_sb;
+          const int64_t boff = sub_block_base(p, __builtin_amdgcn_readlane(ids, i + P));
 #pragma unroll
           for (int ks = 0; ks < KS; ++ks)
             kst[j][ks] = gload8<KV8>(kbase + (boff + koff + 32 * ks) * ESZ);
@@ -747,9 +758,9 @@ __device__ __forceinline__ void attend_wide(const FwdParams& p, const Item& it,
   const int blk0 = kbeg / kBlockSize;
   const int nblk = kend > kbeg ? (kend + kBlockSize - 1) / kBlockSize - blk0 : 0;
   const int n_stage = kend > kbeg ? (kend - kbeg + kStageKeys - 1) / kStageKeys : 0;
-  const int32_t* btrow = p.bt + (int64_t)it.s * p.bt_stride + blk0;
+  const int32_t* btrow = p.bt + (int64_t)it.s * p.bt_stride;
   int32_t* ids = reinterpret_cast<int32_t*>(smem + Cfg::IDS_OFFSET);
-  for (int i = tid; i < nblk; i += kThreads) ids[i] = btrow[i];
+  for (int i = tid; i < nblk; i += kThreads) ids[i] = sub_block_id(btrow, blk0 + i, p.bshift);
   __syncthreads();
 
   // ---- one stage of K and V.  bf16: global -> LDS by 16-byte DMA; lane i of
@@ -785,7 +796,7 @@ __device__ __forceinline__ void attend_wide(const FwdParams& p, const Item& it,
       // the DMA writes zeros)
       const int valid = min(max(kend - (blk0 + jl) * kBlockSize, 0), kBlockSize);
       const int nrec = uniform(valid * slot_elems * ESZ);
-      const int64_t boff = ((int64_t)id * p.kv_sb + head_off) * ESZ;
+      const int64_t boff = (sub_block_base(p, id) + head_off) * ESZ;
       const __amdgpu_buffer_rsrc_t rk =
           __builtin_amdgcn_make_buffer_rsrc(uniform_ptr(p.k + boff), (short)0, nrec, 0x00020000);
       const __amdgpu_buffer_rsrc_t rv =
@@ -1261,7 +1272,7 @@ void pa_decode_kernel(FwdParams p) {
     for (int k = 0; k < IDL; ++k) {
       v[k] = 0;
       if (d.valid && lane + 64 * k < d.nb)
-        v[k] = p.bt[(int64_t)d.s * p.bt_stride + d.blk0 + lane + 64 * k];
+        v[k] = sub_block_id(p.bt + (int64_t)d.s * p.bt_stride, d.blk0 + lane + 64 * k, p.bshift);
     }
   };
   auto store_ids = [&](int buf, const int (&v)[IDL]) {
@@ -1289,7 +1300,7 @@ void pa_decode_kernel(FwdParams p) {
   raw8 vst[RING][VPL];
   const int blk_extent = kBlockSize * slot_stride * ESZ;    // bytes of one block, all heads
   auto issue = [&](int kvh, int phys, bool live, int j) {
-    const int64_t boff = ((int64_t)phys * p.kv_sb + (int64_t)kvh * D) * ESZ;
+    const int64_t boff = (sub_block_base(p, phys) + (int64_t)kvh * D) * ESZ;
     const int nrec = live ? blk_extent : 0;
     const __amdgpu_buffer_rsrc_t rk =
         __builtin_amdgcn_make_buffer_rsrc((void*)(p.k + boff), (short)0, nrec, 0x00020000);

@@ -105,9 +105,13 @@ def test_head_ratio_and_unsupported():
     q = torch.zeros(6, 8, 96, dtype=torch.bfloat16)
     k = torch.zeros(b["k_cache"].shape[0], 16, 2, 96, dtype=torch.bfloat16)
     assert status_of(q=q, out=torch.zeros_like(q), k_cache=k, v_cache=k.clone())[0] == "PA_ERR_UNSUPPORTED"
-    # block size 32
-    k = torch.zeros(4, 32, 2, 128, dtype=torch.bfloat16)
-    assert status_of(k_cache=k, v_cache=k.clone())[0] == "PA_ERR_UNSUPPORTED"
+    # block sizes 16, 32 and 64 are built (the host plan accepts them), others are not
+    for B in (32, 64):
+        bb = build_batch("abi", [1, 3, 2], [5, 17, 40], 8, 2, 128, True, seed=1, block_size=B)
+        assert pa.plan_describe(*bb.args(torch.empty_like(bb.q))[:9])["persistent"] == 1
+    for B in (8, 48, 128):
+        k = torch.zeros(4, B, 2, 128, dtype=torch.bfloat16)
+        assert status_of(k_cache=k, v_cache=k.clone())[0] == "PA_ERR_UNSUPPORTED", B
 
 
 def test_strides_alignment_alias():

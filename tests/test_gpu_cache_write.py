@@ -29,32 +29,33 @@ def special_values(n, scale):
 
 
 @pytest.mark.parametrize("fmt", ["bf16", "fp8_e4m3fn"])
-@pytest.mark.parametrize("shape", [(8, 128), (2, 64)], ids=["hkv8d128", "hkv2d64"])
+@pytest.mark.parametrize("shape", [(8, 128, 16), (2, 64, 16), (8, 128, 32), (2, 64, 64)],
+                         ids=["hkv8d128", "hkv2d64", "hkv8d128b32", "hkv2d64b64"])
 def test_cache_write_bit_exact(fmt, shape):
     require_gpu()
-    hkv, d = shape
-    g = torch.Generator(device="cpu").manual_seed(hkv * 1000 + d)
-    NB, N = 40, 300
+    hkv, d, bs = shape
+    g = torch.Generator(device="cpu").manual_seed(hkv * 1000 + d + bs)
+    NB, N = 640 // bs, 300
     key = torch.randn(N, hkv, d, generator=g).to(torch.bfloat16)
     value = torch.randn(N, hkv, d, generator=g).to(torch.bfloat16)
     ks, vs = 0.125, 0.5
     if fmt == "fp8_e4m3fn":
         key.view(-1)[: 4000] = special_values(4000, ks)
         value.view(-1)[: 4000] = special_values(4000, vs)
-    perm = torch.randperm(NB * 16, generator=g)[:N].to(torch.int32)
+    perm = torch.randperm(NB * bs, generator=g)[:N].to(torch.int32)
     perm[::7] = -1                                            # skipped tokens
     if fmt == "bf16":
-        kc = torch.randn(NB, 16, hkv, d, generator=g).to(torch.bfloat16)
-        vc = torch.randn(NB, 16, hkv, d, generator=g).to(torch.bfloat16)
+        kc = torch.randn(NB, bs, hkv, d, generator=g).to(torch.bfloat16)
+        vc = torch.randn(NB, bs, hkv, d, generator=g).to(torch.bfloat16)
         host = lambda t: t.float().numpy()
     else:
-        kc = torch.randint(0, 256, (NB, 16, hkv, d), generator=g, dtype=torch.uint8).view(torch.float8_e4m3fn)
-        vc = torch.randint(0, 256, (NB, 16, hkv, d), generator=g, dtype=torch.uint8).view(torch.float8_e4m3fn)
+        kc = torch.randint(0, 256, (NB, bs, hkv, d), generator=g, dtype=torch.uint8).view(torch.float8_e4m3fn)
+        vc = torch.randint(0, 256, (NB, bs, hkv, d), generator=g, dtype=torch.uint8).view(torch.float8_e4m3fn)
         host = lambda t: t.view(torch.uint8).numpy()
     ek, ev = oracle.cache_write(key.float().numpy(), value.float().numpy(), host(kc), host(vc),
                                 perm.numpy(), kv_format=fmt, k_scale=ks, v_scale=vs)
     dk, dv = kc.to(DEV), vc.to(DEV)
-    say(f"cache write {fmt} hkv={hkv} d={d}")
+    say(f"cache write {fmt} hkv={hkv} d={d} block={bs}")
     pa.cache_write(key.to(DEV), value.to(DEV), dk, dv, perm.to(DEV), k_scale=ks, v_scale=vs)
     torch.cuda.synchronize()
     gk, gv = host(dk.cpu()), host(dv.cpu())
