@@ -63,7 +63,9 @@ typedef enum {
  * performance for V1 Triton (ROCm) backend", review discussion of the
  * fp8_e4m3fn KV cache).  Element (b, t, h, i) of a cache then stands for
  * decode(code) * k_scale (keys) or * v_scale (values); see pa_options. */
-typedef enum { PA_BF16 = 1, PA_INT32 = 2, PA_FP32 = 3, PA_FP8_E4M3 = 4 } pa_dtype;
+/* PA_F16: IEEE binary16.  q, out and 16-bit caches are all bf16 or all fp16
+ * (the element type is the caller's; the kernels compute in fp32 either way). */
+typedef enum { PA_BF16 = 1, PA_INT32 = 2, PA_FP32 = 3, PA_FP8_E4M3 = 4, PA_F16 = 5 } pa_dtype;
 
 /* A strided view of device memory.  shape/stride entries beyond ndim are
  * ignored; strides are in ELEMENTS. */

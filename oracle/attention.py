@@ -36,7 +36,9 @@ What it computes is the plain definition of the operation:
 All arithmetic is float64.  ``softmax_scale`` is first rounded to float32 so
 the oracle uses exactly the value a float32 kernel argument carries.
 
-fp8 caches (``kv_format="fp8_e4m3fn"``): the cache holds one-byte codes of the
+16-bit caches (``kv_format`` "bf16" or "f16") are given as their values, which
+float64 holds exactly.  fp8 caches (``kv_format="fp8_e4m3fn"``): the cache
+holds one-byte codes of the
 OCP 8-bit floating point format E4M3 in its "fn" variant (finite only; the
 KV-cache format discussed in the review of page "[Kernel] [V1] Improved
 performance for V1 Triton (ROCm) backend").  A code stands for
@@ -52,7 +54,7 @@ import numpy as np
 __all__ = ["paged_attention", "paged_attention_rows", "gather_context",
            "attend_rows", "merge_lse", "decode_e4m3fn", "encode_e4m3fn", "cache_write"]
 
-KV_FORMATS = ("bf16", "fp8_e4m3fn")
+KV_FORMATS = ("bf16", "f16", "fp8_e4m3fn")
 
 
 def decode_e4m3fn(codes):
@@ -102,7 +104,7 @@ def cache_write(key, value, k_cache, v_cache, slot_mapping, kv_format="bf16", k_
                 v_scale=1.0):
     """New caches with token i's ``[Hkv, d]`` key / value written to slot
     ``slot_mapping[i]`` (block ``slot // B``, position ``slot % B``); negative
-    slots are skipped.  bf16: values copied (float arrays); fp8: codes of
+    slots are skipped.  bf16 / f16: values copied (float arrays); fp8: codes of
     ``float32(x) / float32(scale)``.  Inputs are not modified.
     """
     kc, vc = np.array(k_cache, copy=True), np.array(v_cache, copy=True)
@@ -111,7 +113,7 @@ def cache_write(key, value, k_cache, v_cache, slot_mapping, kv_format="bf16", k_
         if slot < 0:
             continue
         blk, pos = slot // B, slot % B
-        if kv_format == "bf16":
+        if kv_format in ("bf16", "f16"):
             kc[blk, pos] = key[i]
             vc[blk, pos] = value[i]
         elif kv_format == "fp8_e4m3fn":
@@ -126,7 +128,7 @@ def cache_write(key, value, k_cache, v_cache, slot_mapping, kv_format="bf16", k_
 
 def _context(cache, table_row, context_len, kv_format, scale):
     """Gathered ``[L, Hkv, d]`` float64 values of one sequence's cache."""
-    if kv_format == "bf16":
+    if kv_format in ("bf16", "f16"):
         return gather_context(cache, table_row, context_len)
     if kv_format == "fp8_e4m3fn":
         codes = gather_context(cache, table_row, context_len).astype(np.int64)

@@ -21,9 +21,9 @@ import torch
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libpa.so")
 
-PA_BF16, PA_INT32, PA_FP32, PA_FP8_E4M3 = 1, 2, 3, 4
+PA_BF16, PA_INT32, PA_FP32, PA_FP8_E4M3, PA_F16 = 1, 2, 3, 4, 5
 _DTYPES = {torch.bfloat16: PA_BF16, torch.int32: PA_INT32, torch.float32: PA_FP32,
-           torch.float8_e4m3fn: PA_FP8_E4M3}
+           torch.float8_e4m3fn: PA_FP8_E4M3, torch.float16: PA_F16}
 
 
 class PaTensor(ctypes.Structure):
@@ -145,10 +145,10 @@ def unified_attention(q, k_cache, v_cache, out, cu_seqlens_q, seqused_k, block_t
                       max_seqlen_q: int, max_seqlen_k: int, softmax_scale: float, causal: bool,
                       *, opts: Optional[PaOptions] = None,
                       workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """Attention of the whole varlen batch into ``out`` (bf16 [T, Hq, d]).
+    """Attention of the whole varlen batch into ``out`` ([T, Hq, d], q's dtype).
 
-    Caches are bf16 or ``torch.float8_e4m3fn`` (E4M3 codes; their scales go in
-    ``opts``).
+    q and out are bf16 or fp16; caches are of q's dtype or
+    ``torch.float8_e4m3fn`` (E4M3 codes; their scales go in ``opts``).
 
     With ``opts`` or ``workspace`` given, calls ``pa_unified_attention_ex``
     (``workspace`` then must be a device tensor of at least ``workspace_size``
@@ -221,9 +221,10 @@ def plan_describe(q, k_cache, v_cache, out, cu_seqlens_q, seqused_k, block_table
 
 def cache_write(key, value, k_cache, v_cache, slot_mapping, k_scale: float = 0.0,
                 v_scale: float = 0.0):
-    """Write new tokens (bf16 [N, Hkv, d]) into the paged caches at
-    ``slot_mapping`` (int32 [N], block * 16 + position; negative skips).  fp8
-    caches receive E4M3 codes of x / scale."""
+    """Write new tokens (bf16 or fp16 [N, Hkv, d]) into the paged caches at
+    ``slot_mapping`` (int32 [N], block * block_size + position; negative
+    skips).  Caches of the tokens' dtype receive the values; fp8 caches receive
+    E4M3 codes of x / scale."""
     ds = [describe(t) for t in (key, value, k_cache, v_cache, slot_mapping)]
     stream = ctypes.c_void_p(_stream_handle(key.device))
     _check(lib.pa_cache_write(*[ctypes.byref(d) for d in ds], float(k_scale), float(v_scale),

@@ -32,7 +32,8 @@ int fail(int code, const char* fmt, ...) {
 struct Shapes {
   int64_t T, Hq, D, NB, B, Hkv, S, MB, G;
   int64_t q_st, q_sh, o_st, o_sh, kv_sb, bt_stride;
-  bool kv8;          // caches hold fp8 E4M3 codes (else bf16)
+  bool kv8;          // caches hold fp8 E4M3 codes (else 16-bit elements)
+  bool f16;          // q, out and 16-bit caches are fp16 (else bf16)
 };
 
 struct Plan {
@@ -85,7 +86,10 @@ int validate(const pa_tensor* q, const pa_tensor* k, const pa_tensor* v, const p
               {v, "v_cache", PA_BF16, 4},    {out, "out", PA_BF16, 3},
               {cu, "cu_seqlens_q", PA_INT32, 1}, {sk, "seqused_k", PA_INT32, 1},
               {bt, "block_table", PA_INT32, 2}};
-  // caches: bf16, or fp8 E4M3 codes (both caches the same)
+  // q and out: bf16 or fp16; caches: the same 16-bit type, or fp8 E4M3 codes
+  // (both caches the same)
+  const bool f16 = q->dtype == PA_F16;
+  if (f16) spec[0].dtype = spec[1].dtype = spec[2].dtype = spec[3].dtype = PA_F16;
   const bool kv8 = k->dtype == PA_FP8_E4M3;
   if (kv8) spec[1].dtype = spec[2].dtype = PA_FP8_E4M3;
   for (auto& e : spec) {
@@ -99,6 +103,7 @@ int validate(const pa_tensor* q, const pa_tensor* k, const pa_tensor* v, const p
   }
   Shapes s{};
   s.kv8 = kv8;
+  s.f16 = f16;
   const int64_t kv_esz = kv8 ? 1 : 2;
   s.T = q->shape[0];
   s.Hq = q->shape[1];
@@ -342,17 +347,19 @@ int device_cu_count(bool* ok) {
   return cache[dev];
 }
 
-int decode_blocks_per_cu_cached(int head_dim, int group, bool kv8) {
+int decode_blocks_per_cu_cached(int head_dim, int group, bool kv8, bool f16) {
   static std::mutex mu;
-  static int cache[2][2][17] = {};
+  static int cache[2][2][2][17] = {};
   const int di = head_dim == 128 ? 1 : 0;
   const int ki = kv8 ? 1 : 0;
+  const int fi = f16 ? 1 : 0;
   std::lock_guard<std::mutex> lock(mu);
-  if (cache[di][ki][group] == 0) {
-    const int n = pa::decode_blocks_per_cu(head_dim, group, kv8);
-    cache[di][ki][group] = n > 0 ? n : -1;
+  int& c = cache[di][ki][fi][group];
+  if (c == 0) {
+    const int n = pa::decode_blocks_per_cu(head_dim, group, kv8, f16);
+    c = n > 0 ? n : -1;
   }
-  return cache[di][ki][group] > 0 ? cache[di][ki][group] : 2;
+  return c > 0 ? c : 2;
 }
 
 int check_contents(const Shapes& s, const pa_tensor* cu, const pa_tensor* sk, const pa_tensor* bt,
@@ -457,7 +464,7 @@ int run(const pa_tensor* q, const pa_tensor* k, const pa_tensor* v, pa_tensor* o
   if (s.T == 0 || s.S == 0) return PA_OK;
   bool have_dev = false;
   const int ncu = device_cu_count(&have_dev);
-  const int dbpc = have_dev ? decode_blocks_per_cu_cached((int)s.D, (int)s.G, s.kv8) : 2;
+  const int dbpc = have_dev ? decode_blocks_per_cu_cached((int)s.D, (int)s.G, s.kv8, s.f16) : 2;
   Plan plan;
   rc = make_plan(s, max_q, max_k, opt, ncu, dbpc, &plan);
   if (rc != PA_OK) return rc;
@@ -525,8 +532,9 @@ int run(const pa_tensor* q, const pa_tensor* k, const pa_tensor* v, pa_tensor* o
   p.lse_st = lse ? lse->stride[0] : 0;
   if (plan.nwg > 0) {
     hipError_t e = plan.persistent
-                       ? pa::launch_decode(p, (int)s.D, (int)s.G, s.kv8, plan.nwg, stream)
-                       : pa::launch_fwd(p, (int)s.D, (int)s.G, plan.wide, s.kv8, plan.nwg, stream);
+                       ? pa::launch_decode(p, (int)s.D, (int)s.G, s.kv8, s.f16, plan.nwg, stream)
+                       : pa::launch_fwd(p, (int)s.D, (int)s.G, plan.wide, s.kv8, s.f16, plan.nwg,
+                                        stream);
     if (e != hipSuccess) return fail(PA_ERR_HIP, "forward launch: %s", hipGetErrorString(e));
   }
   if (plan.n_split > 1) {
@@ -543,7 +551,7 @@ int run(const pa_tensor* q, const pa_tensor* k, const pa_tensor* v, pa_tensor* o
     mp.even = plan.balanced ? 1 : 0;
     mp.lse_out = p.lse_out;
     mp.lse_st = p.lse_st;
-    hipError_t e = pa::launch_merge(mp, (int)s.D, stream);
+    hipError_t e = pa::launch_merge(mp, (int)s.D, s.f16, stream);
     if (e != hipSuccess) return fail(PA_ERR_HIP, "merge launch: %s", hipGetErrorString(e));
   }
   return PA_OK;
@@ -595,8 +603,10 @@ int pa_merge_attention(const pa_tensor* out_a, const pa_tensor* lse_a, const pa_
     return fail(PA_ERR_NULL, "a tensor descriptor pointer is NULL");
   const pa_tensor* outs[] = {out_a, out_b, out};
   const pa_tensor* lses[] = {lse_a, lse_b, lse_out};
+  const bool f16 = out->dtype == PA_F16;
   for (const pa_tensor* t : outs) {
-    if (t->dtype != PA_BF16) return fail(PA_ERR_DTYPE, "outputs must be bf16");
+    if (t->dtype != (f16 ? PA_F16 : PA_BF16))
+      return fail(PA_ERR_DTYPE, "outputs must all be bf16 or all fp16");
     if (t->ndim != 3) return fail(PA_ERR_SHAPE, "outputs must be [total_q, num_q_heads, head_dim]");
     for (int i = 0; i < 3; ++i)
       if (t->shape[i] != out->shape[i]) return fail(PA_ERR_SHAPE, "output shapes differ");
@@ -638,7 +648,7 @@ int pa_merge_attention(const pa_tensor* out_a, const pa_tensor* lse_a, const pa_
   mp.l_st = lse_out ? lse_out->stride[0] : 0;
   mp.total_q = (int32_t)T;
   mp.num_q_heads = (int32_t)Hq;
-  const hipError_t e = pa::launch_merge2(mp, (int)D, reinterpret_cast<hipStream_t>(stream));
+  const hipError_t e = pa::launch_merge2(mp, (int)D, f16, reinterpret_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(PA_ERR_HIP, "merge launch: %s", hipGetErrorString(e));
   return PA_OK;
 }
@@ -655,7 +665,7 @@ size_t pa_workspace_size(const pa_tensor* q, const pa_tensor* k_cache, const pa_
   if (s.T == 0 || s.S == 0) return 0;
   bool have_dev = false;
   const int ncu = device_cu_count(&have_dev);
-  const int dbpc = have_dev ? decode_blocks_per_cu_cached((int)s.D, (int)s.G, s.kv8) : 2;
+  const int dbpc = have_dev ? decode_blocks_per_cu_cached((int)s.D, (int)s.G, s.kv8, s.f16) : 2;
   Plan plan;
   if (make_plan(s, max_seqlen_q, max_seqlen_k, opt, ncu, dbpc, &plan) != PA_OK) return (size_t)-1;
   return plan.ws_bytes;
@@ -675,7 +685,7 @@ int pa_plan_describe(const pa_tensor* q, const pa_tensor* k_cache, const pa_tens
   bool have_dev = false;
   const int ncu = num_cus > 0 ? num_cus : device_cu_count(&have_dev);
   if (num_cus > 0) (void)device_cu_count(&have_dev);
-  const int dbpc = have_dev ? decode_blocks_per_cu_cached((int)s.D, (int)s.G, s.kv8) : 2;
+  const int dbpc = have_dev ? decode_blocks_per_cu_cached((int)s.D, (int)s.G, s.kv8, s.f16) : 2;
   Plan plan;
   rc = make_plan(s, max_seqlen_q, max_seqlen_k, opt, ncu, dbpc, &plan);
   if (rc != PA_OK) return rc;
@@ -704,14 +714,16 @@ int pa_cache_write(const pa_tensor* key, const pa_tensor* value, pa_tensor* k_ca
   if (!key || !value || !k_cache || !v_cache || !slot_mapping)
     return fail(PA_ERR_NULL, "a tensor descriptor pointer is NULL");
   const bool kv8 = k_cache->dtype == PA_FP8_E4M3;
-  const int cdt = kv8 ? PA_FP8_E4M3 : PA_BF16;
+  const bool f16 = key->dtype == PA_F16;
+  const int sdt = f16 ? PA_F16 : PA_BF16;
+  const int cdt = kv8 ? PA_FP8_E4M3 : sdt;
   const int64_t esz = kv8 ? 1 : 2;
   struct {
     const pa_tensor* t;
     const char* name;
     int dtype;
     int ndim;
-  } spec[] = {{key, "key", PA_BF16, 3},       {value, "value", PA_BF16, 3},
+  } spec[] = {{key, "key", sdt, 3},           {value, "value", sdt, 3},
               {k_cache, "k_cache", cdt, 4},   {v_cache, "v_cache", cdt, 4},
               {slot_mapping, "slot_mapping", PA_INT32, 1}};
   for (auto& e : spec) {
@@ -781,7 +793,7 @@ int pa_cache_write(const pa_tensor* key, const pa_tensor* value, pa_tensor* k_ca
   p.chunks_per_head = (int32_t)(D / 8);
   p.k_scale = k_scale != 0.f ? k_scale : 1.f;
   p.v_scale = v_scale != 0.f ? v_scale : 1.f;
-  const hipError_t e = pa::launch_cache_write(p, kv8, reinterpret_cast<hipStream_t>(stream));
+  const hipError_t e = pa::launch_cache_write(p, kv8, f16, reinterpret_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(PA_ERR_HIP, "cache write launch: %s", hipGetErrorString(e));
   return PA_OK;
 }

@@ -3,7 +3,7 @@
 // page "[Kernel] Unified Triton kernel that doesn't distinguish between
 // prefill + decode", PR description).  Token i goes to cache slot
 // slot_mapping[i] = physical block * block_size + position in the block; a negative
-// slot is skipped.  bf16 caches receive the bf16 values unchanged; fp8 caches
+// slot is skipped.  16-bit caches receive the bf16 / fp16 values unchanged; fp8 caches
 // (OCP E4M3 "fn", the KV-cache format discussed in the review of page
 // "[Kernel] [V1] Improved performance for V1 Triton (ROCm) backend") receive
 // the code of x / scale rounded to nearest, ties to even, saturated at +-448
@@ -42,10 +42,21 @@ __device__ __forceinline__ uint32_t e4m3_code(float x) {
   return sign | ((uint32_t)(e + 7) << 3) | (uint32_t)(m - 8);
 }
 
-__device__ __forceinline__ float bf16_lo(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
-__device__ __forceinline__ float bf16_hi(uint32_t w) { return __builtin_bit_cast(float, w & 0xFFFF0000u); }
+// the two 16-bit source elements of w (low, high) as fp32, exactly
+template <bool F16>
+__device__ __forceinline__ float src_lo(uint32_t w) {
+  if constexpr (F16) return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xFFFFu));
+  return __builtin_bit_cast(float, w << 16);
+}
+template <bool F16>
+__device__ __forceinline__ float src_hi(uint32_t w) {
+  if constexpr (F16) return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
+  return __builtin_bit_cast(float, w & 0xFFFF0000u);
+}
 
-template <bool KV8>
+// KV8: fp8 caches (else the source's 16-bit type, copied); F16: fp16 sources
+// (else bf16)
+template <bool KV8, bool F16>
 __global__ __launch_bounds__(256) void pa_cache_write_kernel(CacheWriteParams p) {
   const int64_t per_tensor = (int64_t)p.num_tokens * p.chunks_per_token;
   const int64_t total = 2 * per_tensor;
@@ -73,8 +84,8 @@ __global__ __launch_bounds__(256) void pa_cache_write_kernel(CacheWriteParams p)
       uint32_t lo = 0, hi = 0;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const uint32_t a = e4m3_code(__fdiv_rn(bf16_lo(w[e]), s));
-        const uint32_t b = e4m3_code(__fdiv_rn(bf16_hi(w[e]), s));
+        const uint32_t a = e4m3_code(__fdiv_rn(src_lo<F16>(w[e]), s));
+        const uint32_t b = e4m3_code(__fdiv_rn(src_hi<F16>(w[e]), s));
         const uint32_t pair = a | (b << 8);
         if (e < 2) lo |= pair << (16 * e);
         else hi |= pair << (16 * (e - 2));
@@ -86,15 +97,18 @@ __global__ __launch_bounds__(256) void pa_cache_write_kernel(CacheWriteParams p)
 
 }  // namespace
 
-hipError_t launch_cache_write(const CacheWriteParams& p, bool kv8, hipStream_t stream) {
+hipError_t launch_cache_write(const CacheWriteParams& p, bool kv8, bool f16, hipStream_t stream) {
   const int64_t total = 2 * (int64_t)p.num_tokens * p.chunks_per_token;
   if (total <= 0) return hipSuccess;
   const int64_t want = (total + 255) / 256;
   const unsigned grid = (unsigned)(want < 65536 ? want : 65536);
-  if (kv8)
-    hipLaunchKernelGGL(pa_cache_write_kernel<true>, dim3(grid), dim3(256), 0, stream, p);
+  if (kv8 && f16)
+    hipLaunchKernelGGL((pa_cache_write_kernel<true, true>), dim3(grid), dim3(256), 0, stream, p);
+  else if (kv8)
+    hipLaunchKernelGGL((pa_cache_write_kernel<true, false>), dim3(grid), dim3(256), 0, stream, p);
   else
-    hipLaunchKernelGGL(pa_cache_write_kernel<false>, dim3(grid), dim3(256), 0, stream, p);
+    // a 16-bit copy does not depend on the element type
+    hipLaunchKernelGGL((pa_cache_write_kernel<false, false>), dim3(grid), dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 

@@ -89,13 +89,14 @@ struct Merge2Params {
   int64_t oa_st, oa_sh, ob_st, ob_sh, o_st, o_sh, la_st, lb_st, l_st;
   int32_t total_q, num_q_heads;
 };
-hipError_t launch_merge2(const Merge2Params& p, int head_dim, hipStream_t stream);
+// f16: the outputs are fp16 (else bf16)
+hipError_t launch_merge2(const Merge2Params& p, int head_dim, bool f16, hipStream_t stream);
 
 // New tokens' keys and values -> paged cache slots (pa_cache_kernels.hip).
 struct CacheWriteParams {
-  const uint16_t* key;      // bf16 [N, Hkv, d]
+  const uint16_t* key;      // bf16 or fp16 [N, Hkv, d]
   const uint16_t* value;
-  unsigned char* k_cache;   // [NB, B, Hkv, d] bf16 or fp8 E4M3 codes
+  unsigned char* k_cache;   // [NB, B, Hkv, d] of the key's 16-bit type, or fp8 E4M3 codes
   unsigned char* v_cache;
   const int32_t* slot_mapping;   // [N]; < 0: skip
   int64_t k_st, k_sh, v_st, v_sh;   // source strides (elements)
@@ -108,19 +109,20 @@ struct CacheWriteParams {
   float k_scale, v_scale;   // fp8: codes of x / scale
 };
 
-hipError_t launch_cache_write(const CacheWriteParams& p, bool kv8, hipStream_t stream);
+hipError_t launch_cache_write(const CacheWriteParams& p, bool kv8, bool f16, hipStream_t stream);
 
 // Launchers (pa_kernels.hip).  Return the hipError_t of the launch.
 // wide = false launches the narrow-only specialization (every tile <= 16 rows).
-// kv8: the caches hold fp8 E4M3 codes (else bf16).
-hipError_t launch_fwd(const FwdParams& p, int head_dim, int group, bool wide, bool kv8,
+// kv8: the caches hold fp8 E4M3 codes (else 16-bit elements); f16: q, out and
+// 16-bit caches are fp16 (else bf16).
+hipError_t launch_fwd(const FwdParams& p, int head_dim, int group, bool wide, bool kv8, bool f16,
                       int64_t num_workgroups, hipStream_t stream);
-hipError_t launch_merge(const MergeParams& p, int head_dim, hipStream_t stream);
+hipError_t launch_merge(const MergeParams& p, int head_dim, bool f16, hipStream_t stream);
 // Persistent decode kernel (every tile narrow, num_seqs <= kMaxDecodeSeqs).
-hipError_t launch_decode(const FwdParams& p, int head_dim, int group, bool kv8,
+hipError_t launch_decode(const FwdParams& p, int head_dim, int group, bool kv8, bool f16,
                          int64_t num_workgroups, hipStream_t stream);
 // Resident work-groups per CU of the decode kernel (0 if unknown).
-int decode_blocks_per_cu(int head_dim, int group, bool kv8);
+int decode_blocks_per_cu(int head_dim, int group, bool kv8, bool f16);
 bool fwd_supported(int head_dim, int group);
 
 }  // namespace pa

@@ -50,12 +50,78 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 #define PA_LDS __attribute__((address_space(3)))
+
+// The 16-bit element type of q, out and unquantised caches: bf16 (F16 =
+// false) or IEEE fp16 (F16 = true).  Operands travel as raw 16-bit lanes (u32x4
+// = 8 elements, u32x2 = 4) and meet their type only in these wrappers: the
+// MFMAs of that type, round-to-nearest-even packing of fp32 pairs, and the
+// exact fp8 E4M3 -> element conversion (every E4M3 value is exact in both).
+template <bool F16>
+struct Elem;
+template <>
+struct Elem<false> {
+  static __device__ __forceinline__ f32x16 mma32(u32x4 a, u32x4 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ f32x4 mma16(u32x4 a, u32x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ f32x4 mma16k16(u32x2 a, u32x2 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4, a),
+                                                     __builtin_bit_cast(i16x4, b), c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
+    bf16x2 v = {(__bf16)lo, (__bf16)hi};
+    return __builtin_bit_cast(uint32_t, v);
+  }
+  // v_cvt_scalef32_pk_bf16_fp8 with scale 1: codes (byte 2*SEL, 2*SEL+1) of w
+  template <bool SEL>
+  static __device__ __forceinline__ uint32_t fp8x2(uint32_t w) {
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, SEL));
+  }
+  // the element in the low 16 bits of u, as fp32 (exact)
+  static __device__ __forceinline__ float unpack(uint32_t u) {
+    return __builtin_bit_cast(float, u << 16);
+  }
+};
+template <>
+struct Elem<true> {
+  static __device__ __forceinline__ f32x16 mma32(u32x4 a, u32x4 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ f32x4 mma16(u32x4 a, u32x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ f32x4 mma16k16(u32x2 a, u32x2 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4, a),
+                                                 __builtin_bit_cast(f16x4, b), c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
+    f16x2 v = {(_Float16)lo, (_Float16)hi};
+    return __builtin_bit_cast(uint32_t, v);
+  }
+  template <bool SEL>
+  static __device__ __forceinline__ uint32_t fp8x2(uint32_t w) {
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, SEL));
+  }
+  static __device__ __forceinline__ float unpack(uint32_t u) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)(u & 0xFFFFu));
+  }
+};
 
 constexpr float kNegInf = -__builtin_huge_valf();
 
@@ -82,25 +148,25 @@ __device__ __forceinline__ void scale_inplace(float& x, float s) {
   asm volatile("v_mul_f32 %0, %0, %1" : "+v"(x) : "v"(s));
 }
 
-// Cache element formats: bf16, or fp8 E4M3 codes (OCP 8-bit float, the
-// "fn" variant: no infinities, S.1111.111 is NaN) converted to bf16 right
-// after the load.  Every E4M3 value is exact in bf16, so the MFMA paths see
-// the operands a bf16 cache of the decoded codes would give; the per-tensor
-// scales are folded into the softmax scale (K) and the output (V).
+// Cache element formats: the 16-bit element type, or fp8 E4M3 codes (OCP
+// 8-bit float, the "fn" variant: no infinities, S.1111.111 is NaN) converted
+// to the element type right after the load.  Every E4M3 value is exact in
+// bf16 and fp16, so the MFMA paths see the operands a 16-bit cache of the
+// decoded codes would give; the per-tensor scales are folded into the
+// softmax scale (K) and the output (V).
 template <bool KV8>
 struct Kv {
   static constexpr int ESZ = KV8 ? 1 : 2;                                 // bytes per element
   using raw8 = typename std::conditional<KV8, u32x2, u32x4>::type;        // 8 elements as loaded
 };
-__device__ __forceinline__ u32x4 to_bf16x8(u32x4 v) { return v; }
-__device__ __forceinline__ u32x4 to_bf16x8(u32x2 v) {
-  // v_cvt_scalef32_pk_bf16_fp8 with scale 1: two codes -> two bf16, exact
-  u32x4 r;
-  r[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v[0], 1.0f, false));
-  r[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v[0], 1.0f, true));
-  r[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v[1], 1.0f, false));
-  r[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v[1], 1.0f, true));
-  return r;
+// 8 loaded cache elements as 8 elements of the 16-bit type
+template <bool F16>
+__device__ __forceinline__ u32x4 to_elem8(u32x4 v) { return v; }
+template <bool F16>
+__device__ __forceinline__ u32x4 to_elem8(u32x2 v) {
+  using E = Elem<F16>;
+  return u32x4{E::template fp8x2<false>(v[0]), E::template fp8x2<true>(v[0]),
+               E::template fp8x2<false>(v[1]), E::template fp8x2<true>(v[1])};
 }
 // 8 consecutive cache elements at a byte address / a buffer byte offset
 template <bool KV8>
@@ -123,7 +189,6 @@ __device__ __forceinline__ void store_lse(float* lse_out, int64_t lse_st, int64_
   if (lse_out) lse_out[tok * lse_st + head] = lse2 == -__builtin_huge_valf() ? lse2 : lse2 * kLn2;
 }
 
-// Round-to-nearest-even fp32 -> bf16 pair, packed low|high.
 // Cache blocks of B = 16 * 2^bshift keys are read as 2^bshift sub-blocks of 16
 // keys.  Sub-block j of a sequence is part j % 2^bshift of block-table entry
 // j >> bshift; its id packs (physical block, part) into one int.
@@ -133,11 +198,6 @@ __device__ __forceinline__ int sub_block_id(const int32_t* row, int j, int bshif
 // element offset of a sub-block in the cache
 __device__ __forceinline__ int64_t sub_block_base(const FwdParams& p, int id) {
   return (int64_t)(id >> p.bshift) * p.kv_sb + (int64_t)(id & ((1 << p.bshift) - 1)) * p.sub_sb;
-}
-
-__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  bf16x2 v = {(__bf16)lo, (__bf16)hi};
-  return __builtin_bit_cast(uint32_t, v);
 }
 
 __device__ __forceinline__ float max_across_groups(float x) {
@@ -403,7 +463,7 @@ __device__ __forceinline__ bool decode_item(const FwdParams& p, Item& it, unsign
 // h4 holds d = 32 ks + 8 h4 .. +7 for each contraction step ks.
 template <int D, int G>
 __device__ __forceinline__ void load_q(const FwdParams& p, const Item& it, int row, int h4,
-                                       bf16x8 (&qB)[D / 32]) {
+                                       u32x4 (&qB)[D / 32]) {
   const bool ok = row < it.rows;
   const int t_in = row / G;
   const int head = it.kvh * G + row % G;
@@ -413,7 +473,7 @@ __device__ __forceinline__ void load_q(const FwdParams& p, const Item& it, int r
   for (int ks = 0; ks < D / 32; ++ks) {
     u32x4 v = {0u, 0u, 0u, 0u};
     if (ok) v = *reinterpret_cast<const u32x4*>(qp + 32 * ks);
-    qB[ks] = __builtin_bit_cast(bf16x8, v);
+    qB[ks] = v;
   }
 }
 
@@ -439,9 +499,10 @@ struct NarrowCfg {
 // ids of the wave's (at most 64) blocks are fetched once into one VGPR and
 // read per block with readlane, so no KV load waits on a block-table load.
 // ---------------------------------------------------------------------------
-template <int D, int G, int P, bool KV8>
+template <int D, int G, int P, bool KV8, bool F16>
 __device__ __forceinline__ void attend_narrow(const FwdParams& p, const Item& it,
                                               unsigned char* smem) {
+  using E = Elem<F16>;
   constexpr int ESZ = Kv<KV8>::ESZ;
   using raw8 = typename Kv<KV8>::raw8;
   using Lay = Layout<D>;
@@ -457,7 +518,7 @@ __device__ __forceinline__ void attend_narrow(const FwdParams& p, const Item& it
   const int h4 = lane >> 4;
   const int l16 = lane & 15;
 
-  bf16x8 qB[KS];
+  u32x4 qB[KS];
   load_q<D, G>(p, it, l16, h4, qB);
   const int t_in = l16 / G;
   const int klim = p.causal ? min(it.kend, it.diag + it.tok0 + t_in + 1) : it.kend;
@@ -514,12 +575,10 @@ __device__ __forceinline__ void attend_narrow(const FwdParams& p, const Item& it
         unsigned char* vbuf = vbuf0 + (i & 1) * BLK_BYTES;
 #pragma unroll
         for (int u = 0; u < VPL; ++u)
-          *reinterpret_cast<u32x4*>(vbuf + vlds[u]) = to_bf16x8(vst[j][u]);
+          *reinterpret_cast<u32x4*>(vbuf + vlds[u]) = to_elem8<F16>(vst[j][u]);
         f32x4 sc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-          sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-              __builtin_bit_cast(bf16x8, to_bf16x8(kst[j][ks])), qB[ks], sc, 0, 0, 0);
+        for (int ks = 0; ks < KS; ++ks) sc = E::mma16(to_elem8<F16>(kst[j][ks]), qB[ks], sc);
         // refill this ring slot with block i + P
         if (i + P < nb) {
           const int64_t boff = sub_block_base(p, __builtin_amdgcn_readlane(ids, i + P));
@@ -550,8 +609,7 @@ __device__ __forceinline__ void attend_narrow(const FwdParams& p, const Item& it
         }
         l = l * alpha + rs;
         m = m_new;
-        u32x2 pk = {pack_bf16x2(pr[0], pr[1]), pack_bf16x2(pr[2], pr[3])};
-        const i16x4 pB = __builtin_bit_cast(i16x4, pk);
+        const u32x2 pB = {E::pack2(pr[0], pr[1]), E::pack2(pr[2], pr[3])};
         const bool vmask = kb + kBlockSize > it.kend;
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
@@ -565,7 +623,7 @@ __device__ __forceinline__ void attend_narrow(const FwdParams& p, const Item& it
               if (kb + 4 * h4 + e >= it.kend) va[e] = 0;
           }
           acc[dt] *= alpha;
-          acc[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pB, acc[dt], 0, 0, 0);
+          acc[dt] = E::mma16k16(__builtin_bit_cast(u32x2, va), pB, acc[dt]);
         }
       }
     }
@@ -624,11 +682,11 @@ __device__ __forceinline__ void attend_narrow(const FwdParams& p, const Item& it
       store_lse(p.lse_out, p.lse_st, tok, hn, Ls > 0.f ? M + __log2f(Ls) : kNegInf);
     uint16_t* op = p.out + tok * p.o_st + (int64_t)hn * p.o_sh + d0;
     if constexpr (DPER == 8) {
-      u32x4 w = {pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]), pack_bf16x2(o[4], o[5]),
-                 pack_bf16x2(o[6], o[7])};
+      u32x4 w = {E::pack2(o[0], o[1]), E::pack2(o[2], o[3]), E::pack2(o[4], o[5]),
+                 E::pack2(o[6], o[7])};
       *reinterpret_cast<u32x4*>(op) = w;
     } else {
-      u32x2 w = {pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
+      u32x2 w = {E::pack2(o[0], o[1]), E::pack2(o[2], o[3])};
       *reinterpret_cast<u32x2*>(op) = w;
     }
   } else {
@@ -689,8 +747,6 @@ struct WideCfg {
   }
 };
 
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-
 // Lanes l and l ^ 32 hold halves of one row.  v_permlane32_swap exchanges
 // the upper half-wave of its first operand with the lower half-wave of its
 // second: with both holding x, the results are x of lanes 0..31 and x of
@@ -710,9 +766,10 @@ __device__ __forceinline__ float swap_halves_sum(float x) {
   return a + b;
 }
 
-template <int D, int G, bool KV8>
+template <int D, int G, bool KV8, bool F16>
 __device__ __forceinline__ void attend_wide(const FwdParams& p, const Item& it,
                                             unsigned char* smem) {
+  using E = Elem<F16>;
   using Cfg = WideCfg<D>;
   constexpr int ESZ = Kv<KV8>::ESZ;
   using raw8 = typename Kv<KV8>::raw8;
@@ -738,7 +795,7 @@ __device__ __forceinline__ void attend_wide(const FwdParams& p, const Item& it,
   const int head = it.kvh * G + row % G;
   const float c = fmaxf(fabsf(p.scale_log2), 1e-30f);
   const uint32_t qflip = p.scale_log2 < 0.f ? 0x80008000u : 0u;
-  bf16x8 qB[KS];                          // B operand of S^T: d = 16 ks + 8 h + e
+  u32x4 qB[KS];                           // B operand of S^T: d = 16 ks + 8 h + e
   {
     const uint16_t* qp = p.q + (int64_t)(it.q0 + it.tok0 + (row_ok ? t_in : 0)) * p.q_st +
                          (int64_t)head * p.q_sh + 8 * h;
@@ -747,7 +804,7 @@ __device__ __forceinline__ void attend_wide(const FwdParams& p, const Item& it,
       u32x4 v = {0u, 0u, 0u, 0u};
       if (row_ok) v = *reinterpret_cast<const u32x4*>(qp + 16 * ks);
       v ^= qflip;
-      qB[ks] = __builtin_bit_cast(bf16x8, v);
+      qB[ks] = v;
     }
   }
   const int kbeg = it.kbeg, kend = it.kend;
@@ -817,8 +874,8 @@ __device__ __forceinline__ void attend_wide(const FwdParams& p, const Item& it,
       unsigned char* base = smem + buf * SB;
 #pragma unroll
       for (int u = 0; u < CPT; ++u) {
-        *reinterpret_cast<u32x4*>(base + u * 4 * RPI * CPR * 16 + ld_sk) = to_bf16x8(kraw[u]);
-        *reinterpret_cast<u32x4*>(base + TB + u * 4 * RPI * CPR * 16 + ld_sv) = to_bf16x8(vraw[u]);
+        *reinterpret_cast<u32x4*>(base + u * 4 * RPI * CPR * 16 + ld_sk) = to_elem8<F16>(kraw[u]);
+        *reinterpret_cast<u32x4*>(base + TB + u * 4 * RPI * CPR * 16 + ld_sv) = to_elem8<F16>(vraw[u]);
       }
     }
   };
@@ -861,8 +918,8 @@ __device__ __forceinline__ void attend_wide(const FwdParams& p, const Item& it,
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(Kb + kb * 32 * CPR * 16 + koff[ks]);
-        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qB[ks], s[kb], 0, 0, 0);
+        const u32x4 a = *reinterpret_cast<const u32x4*>(Kb + kb * 32 * CPR * 16 + koff[ks]);
+        s[kb] = E::mma32(a, qB[ks], s[kb]);
       }
     // operand reads run 4 ahead of the MFMAs: latency hidden, 16 registers
     __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
@@ -901,13 +958,15 @@ __device__ __forceinline__ void attend_wide(const FwdParams& p, const Item& it,
           }
       }
       const float mc = m == kNegInf ? 0.f : m * c;
-      bf16x8 pb[2];
+      float pr[16];
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float pr = exp2_fast(__builtin_fmaf(s[kb][r], c, -mc));
-        l += pr;
-        pb[r >> 3][r & 7] = (__bf16)pr;
+        pr[r] = exp2_fast(__builtin_fmaf(s[kb][r], c, -mc));
+        l += pr[r];
       }
+      u32x4 pb[2];                               // P^T operand of slice 2 kb + hs
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) pb[r >> 3][(r & 7) >> 1] = E::pack2(pr[r], pr[r + 1]);
 #pragma unroll
       for (int hs = 0; hs < 2; ++hs) {
         const int sl = 2 * kb + hs;                // 16-key slice of the stage
@@ -920,8 +979,7 @@ __device__ __forceinline__ void attend_wide(const FwdParams& p, const Item& it,
               i16x4, __builtin_amdgcn_ds_read_tr16_b64_v4bf16((PA_LDS bf16x4*)(a + 8 * CPR * 16)));
           const u32x4 packed = {__builtin_bit_cast(u32x2, a0)[0], __builtin_bit_cast(u32x2, a0)[1],
                                 __builtin_bit_cast(u32x2, a1)[0], __builtin_bit_cast(u32x2, a1)[1]};
-          acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, packed),
-                                                            pb[hs], acc[dt], 0, 0, 0);
+          acc[dt] = E::mma32(packed, pb[hs], acc[dt]);
         }
       }
     }
@@ -965,8 +1023,8 @@ __device__ __forceinline__ void attend_wide(const FwdParams& p, const Item& it,
     for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const u32x2 w = {pack_bf16x2(acc[dt][4 * j] * inv, acc[dt][4 * j + 1] * inv),
-                         pack_bf16x2(acc[dt][4 * j + 2] * inv, acc[dt][4 * j + 3] * inv)};
+        const u32x2 w = {E::pack2(acc[dt][4 * j] * inv, acc[dt][4 * j + 1] * inv),
+                         E::pack2(acc[dt][4 * j + 2] * inv, acc[dt][4 * j + 3] * inv)};
         *reinterpret_cast<u32x2*>(op + 32 * dt + 8 * j) = w;
       }
   } else {
@@ -991,8 +1049,9 @@ static_assert((3 * kLptMaxSeqs + 80) * 4 <= WideCfg<64>::SMEM, "LPT tables excee
 static_assert((3 * kLptMaxSeqs + 80) * 4 <= WideCfg<128>::SMEM, "LPT tables exceed LDS");
 
 // WIDE = false: every tile of the batch is narrow (the plan guarantees it).
-// KV8: the caches hold fp8 E4M3 codes.
-template <int D, int G, bool WIDE, bool KV8>
+// KV8: the caches hold fp8 E4M3 codes.  F16: q, out (and 16-bit caches) are
+// fp16, else bf16.
+template <int D, int G, bool WIDE, bool KV8, bool F16>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
 void pa_fwd_kernel(FwdParams p) {
   constexpr int SMEM = WIDE ? WideCfg<D>::SMEM : NarrowCfg<D>::SMEM;
@@ -1000,9 +1059,9 @@ void pa_fwd_kernel(FwdParams p) {
   Item it;
   if (!decode_item<G>(p, it, smem)) return;
   if (it.rows <= p.narrow_rows) {
-    attend_narrow<D, G, kRing, KV8>(p, it, smem);
+    attend_narrow<D, G, kRing, KV8, F16>(p, it, smem);
   } else {
-    if constexpr (WIDE) attend_wide<D, G, KV8>(p, it, smem);
+    if constexpr (WIDE) attend_wide<D, G, KV8, F16>(p, it, smem);
   }
 }
 
@@ -1095,9 +1154,10 @@ __device__ __forceinline__ DItem describe_item(const FwdParams& p, const int* pr
   return d;
 }
 
-template <int D, int G, bool KV8>
+template <int D, int G, bool KV8, bool F16>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
 void pa_decode_kernel(FwdParams p) {
+  using E = Elem<F16>;
   constexpr int ESZ = Kv<KV8>::ESZ;
   using raw8 = typename Kv<KV8>::raw8;
   using Lay = Layout<D>;
@@ -1279,7 +1339,7 @@ void pa_decode_kernel(FwdParams p) {
 #pragma unroll
     for (int k = 0; k < IDL; ++k) idsw[buf * kMaxItemBlocks + lane + 64 * k] = v[k];
   };
-  auto load_qb = [&](const DItem& d, bf16x8 (&qB)[KS]) {
+  auto load_qb = [&](const DItem& d, u32x4 (&qB)[KS]) {
     const bool ok = d.valid && l16 < d.rows;
     const uint16_t* qp = p.q + (int64_t)(d.q0 + (ok ? l16 / G : 0)) * p.q_st +
                          (int64_t)(d.kvh * G + l16 % G) * p.q_sh + 8 * h4;
@@ -1287,7 +1347,7 @@ void pa_decode_kernel(FwdParams p) {
     for (int ks = 0; ks < KS; ++ks) {
       u32x4 v = {0u, 0u, 0u, 0u};
       if (ok) v = *reinterpret_cast<const u32x4*>(qp + 32 * ks);
-      qB[ks] = __builtin_bit_cast(bf16x8, v);
+      qB[ks] = v;
     }
   };
 
@@ -1327,7 +1387,7 @@ void pa_decode_kernel(FwdParams p) {
   DItem nx2 = after(nxt);
   int ids_v2[IDL];
   load_ids(nx2, ids_v2);
-  bf16x8 qB[KS], qB_n[KS];
+  u32x4 qB[KS], qB_n[KS];
   load_qb(cur, qB);
   load_qb(nxt, qB_n);
   // the first RING blocks of the first item (idle slots load nothing)
@@ -1365,11 +1425,9 @@ void pa_decode_kernel(FwdParams p) {
         if (live) {
 #pragma unroll
           for (int u = 0; u < VPL; ++u)
-            *reinterpret_cast<u32x4*>(vbuf + vlds[u]) = to_bf16x8(vst[j][u]);
+            *reinterpret_cast<u32x4*>(vbuf + vlds[u]) = to_elem8<F16>(vst[j][u]);
 #pragma unroll
-          for (int ks = 0; ks < KS; ++ks)
-            sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                __builtin_bit_cast(bf16x8, to_bf16x8(kst[j][ks])), qB[ks], sc, 0, 0, 0);
+          for (int ks = 0; ks < KS; ++ks) sc = E::mma16(to_elem8<F16>(kst[j][ks]), qB[ks], sc);
         }
         // (2) refill slot j (one call site, so the ring registers never move)
         issue(r_kvh, r_phys, r_live, j);
@@ -1396,8 +1454,7 @@ void pa_decode_kernel(FwdParams p) {
           }
           l = l * alpha + rs;
           m = m_new;
-          u32x2 pk = {pack_bf16x2(pr[0], pr[1]), pack_bf16x2(pr[2], pr[3])};
-          const i16x4 pB = __builtin_bit_cast(i16x4, pk);
+          const u32x2 pB = {E::pack2(pr[0], pr[1]), E::pack2(pr[2], pr[3])};
           const bool vmask = kb + kBlockSize > cur.kend;
 #pragma unroll
           for (int dt = 0; dt < DT; ++dt) {
@@ -1411,7 +1468,7 @@ void pa_decode_kernel(FwdParams p) {
                 if (kb + 4 * h4 + e >= cur.kend) va[e] = 0;
             }
             acc[dt] *= alpha;
-            acc[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pB, acc[dt], 0, 0, 0);
+            acc[dt] = E::mma16k16(__builtin_bit_cast(u32x2, va), pB, acc[dt]);
           }
         }
       }
@@ -1430,8 +1487,8 @@ void pa_decode_kernel(FwdParams p) {
         uint16_t* op = p.out + tok * p.o_st + (int64_t)hn * p.o_sh + 4 * h4;
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
-          u32x2 w = {pack_bf16x2(acc[dt][0] * inv, acc[dt][1] * inv),
-                     pack_bf16x2(acc[dt][2] * inv, acc[dt][3] * inv)};
+          u32x2 w = {E::pack2(acc[dt][0] * inv, acc[dt][1] * inv),
+                     E::pack2(acc[dt][2] * inv, acc[dt][3] * inv)};
           *reinterpret_cast<u32x2*>(op + 16 * dt) = w;
         }
       } else {
@@ -1465,6 +1522,7 @@ __device__ __forceinline__ int merge_parts(const MergeParams& p, int64_t row) {
   return p.row_parts[row];
 }
 
+template <bool F16>
 __device__ __forceinline__ void merge_store(const MergeParams& p, int64_t row, int d0, f32x4 o,
                                             float wsum, float M) {
   const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
@@ -1472,12 +1530,12 @@ __device__ __forceinline__ void merge_store(const MergeParams& p, int64_t row, i
   const int hd = (int)(row % p.num_q_heads);
   if (d0 == 0) store_lse(p.lse_out, p.lse_st, tok, hd, wsum > 0.f ? M + __log2f(wsum) : kNegInf);
   uint16_t* op = p.out + tok * p.o_st + (int64_t)hd * p.o_sh + d0;
-  u32x2 w = {pack_bf16x2(o[0] * inv, o[1] * inv), pack_bf16x2(o[2] * inv, o[3] * inv)};
+  u32x2 w = {Elem<F16>::pack2(o[0] * inv, o[1] * inv), Elem<F16>::pack2(o[2] * inv, o[3] * inv)};
   *reinterpret_cast<u32x2*>(op) = w;
 }
 
 // Few parts per row: D/4 threads per row, each loops over the parts.
-template <int D>
+template <int D, bool F16>
 __global__ __launch_bounds__(256) void pa_merge_rows_kernel(MergeParams p) {
   constexpr int TPR = D / 4;
   constexpr int RPB = 256 / TPR;
@@ -1500,12 +1558,12 @@ __global__ __launch_bounds__(256) void pa_merge_rows_kernel(MergeParams p) {
       a += w * *reinterpret_cast<const f32x4*>(p.ws_o + (sg * nrows + row) * D + d0);
     }
   }
-  merge_store(p, row, d0, a, ws, M);
+  merge_store<F16>(p, row, d0, a, ws, M);
 }
 
 // Many parts per row: one work-group per row; its threads form NG groups that
 // take every NG-th part (several loads in flight each), then reduce in LDS.
-template <int D>
+template <int D, bool F16>
 __global__ __launch_bounds__(256) void pa_merge_wide_kernel(MergeParams p) {
   constexpr int TPG = D / 4;                 // threads per group (4 outputs each)
   constexpr int NG = 256 / TPG;              // groups
@@ -1549,13 +1607,13 @@ __global__ __launch_bounds__(256) void pa_merge_wide_kernel(MergeParams p) {
     wt += wred[k];
     o += *reinterpret_cast<const f32x4*>(&red[k][d0]);
   }
-  merge_store(p, row, d0, o, wt, M);
+  merge_store<F16>(p, row, d0, o, wt, M);
 }
 
 // Two partial results over disjoint key sets (natural-log lse):
 // out = (e^la oa + e^lb ob) / (e^la + e^lb), lse = ln(e^la + e^lb); a side
 // with lse = -inf (no key) drops out.  D/4 threads per row, 4 outputs each.
-template <int D>
+template <int D, bool F16>
 __global__ __launch_bounds__(256) void pa_merge2_kernel(Merge2Params p) {
   constexpr int TPR = D / 4;
   constexpr int RPB = 256 / TPR;
@@ -1579,44 +1637,60 @@ __global__ __launch_bounds__(256) void pa_merge2_kernel(Merge2Params p) {
   float o[4];
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
-    const uint32_t ua = (xa[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
-    const uint32_t ub = (xb[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
-    const float fa = __builtin_bit_cast(float, ua << 16), fb = __builtin_bit_cast(float, ub << 16);
+    const float fa = Elem<F16>::unpack(xa[e >> 1] >> (16 * (e & 1)));
+    const float fb = Elem<F16>::unpack(xb[e >> 1] >> (16 * (e & 1)));
     // a side with no weight is not read into the sum (its value may be anything)
     o[e] = ((wa > 0.f ? wa * fa : 0.f) + (wb > 0.f ? wb * fb : 0.f)) * inv;
   }
-  const u32x2 w = {pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
+  const u32x2 w = {Elem<F16>::pack2(o[0], o[1]), Elem<F16>::pack2(o[2], o[3])};
   *reinterpret_cast<u32x2*>(p.out + tok * p.o_st + (int64_t)hd * p.o_sh + d0) = w;
   if (p.lse && d0 == 0) p.lse[tok * p.l_st + hd] = ws > 0.f ? M + __logf(ws) : kNegInf;
 }
 
-template <int D, int G, bool KV8>
+template <int D, int G, bool KV8, bool F16>
 hipError_t launch_fwd_t(const FwdParams& p, bool wide, int64_t nwg, hipStream_t stream) {
   if (wide)
-    hipLaunchKernelGGL((pa_fwd_kernel<D, G, true, KV8>), dim3((unsigned)nwg), dim3(kThreads), 0,
-                       stream, p);
+    hipLaunchKernelGGL((pa_fwd_kernel<D, G, true, KV8, F16>), dim3((unsigned)nwg), dim3(kThreads),
+                       0, stream, p);
   else
-    hipLaunchKernelGGL((pa_fwd_kernel<D, G, false, KV8>), dim3((unsigned)nwg), dim3(kThreads), 0,
-                       stream, p);
+    hipLaunchKernelGGL((pa_fwd_kernel<D, G, false, KV8, F16>), dim3((unsigned)nwg), dim3(kThreads),
+                       0, stream, p);
   return hipGetLastError();
 }
 
-template <int D, int G, bool KV8>
+template <int D, int G, bool KV8, bool F16>
 hipError_t launch_decode_t(const FwdParams& p, int64_t nwg, hipStream_t stream) {
-  hipLaunchKernelGGL((pa_decode_kernel<D, G, KV8>), dim3((unsigned)nwg), dim3(kThreads), 0, stream,
-                     p);
+  hipLaunchKernelGGL((pa_decode_kernel<D, G, KV8, F16>), dim3((unsigned)nwg), dim3(kThreads), 0,
+                     stream, p);
   return hipGetLastError();
 }
 
-template <int D, int G, bool KV8>
+template <int D, int G, bool KV8, bool F16>
 int decode_blocks_per_cu_t() {
   int n = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, pa_decode_kernel<D, G, KV8>, kThreads, 0) !=
-      hipSuccess) {
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, pa_decode_kernel<D, G, KV8, F16>, kThreads,
+                                                   0) != hipSuccess) {
     (void)hipGetLastError();
     return 0;
   }
   return n;
+}
+
+template <int D, bool F16>
+hipError_t launch_merge_t(const MergeParams& p, bool wide, int64_t rows, hipStream_t stream) {
+  if (wide)
+    hipLaunchKernelGGL((pa_merge_wide_kernel<D, F16>), dim3((unsigned)rows), dim3(256), 0, stream, p);
+  else
+    hipLaunchKernelGGL((pa_merge_rows_kernel<D, F16>), dim3((unsigned)((rows + 1024 / D - 1) / (1024 / D))),
+                       dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
+
+template <int D, bool F16>
+hipError_t launch_merge2_t(const Merge2Params& p, int64_t rows, hipStream_t stream) {
+  hipLaunchKernelGGL((pa_merge2_kernel<D, F16>), dim3((unsigned)((rows + 1024 / D - 1) / (1024 / D))),
+                     dim3(256), 0, stream, p);
+  return hipGetLastError();
 }
 
 }  // namespace
@@ -1631,26 +1705,32 @@ int decode_blocks_per_cu_t() {
     default: break;                                                    \
   }
 
-// head_dim x group x cache format -> one specialization
-#define PA_DISPATCH(D_, G_, K8_, CALL)                                                 \
-  do {                                                                                 \
-    if ((D_) == 128) {                                                                 \
-      if (K8_) { constexpr int DD = 128; constexpr bool KK = true; PA_DISPATCH_DG(DD, G_, CALL); } \
-      else { constexpr int DD = 128; constexpr bool KK = false; PA_DISPATCH_DG(DD, G_, CALL); }    \
-    } else if ((D_) == 64) {                                                           \
-      if (K8_) { constexpr int DD = 64; constexpr bool KK = true; PA_DISPATCH_DG(DD, G_, CALL); }  \
-      else { constexpr int DD = 64; constexpr bool KK = false; PA_DISPATCH_DG(DD, G_, CALL); }     \
-    }                                                                                  \
+#define PA_DISPATCH_F(D_, G_, K8_, CALL)                                                        \
+  do {                                                                                          \
+    if (f16) { constexpr bool FF = true; PA_DISPATCH_DG(D_, G_, CALL); }                        \
+    else { constexpr bool FF = false; PA_DISPATCH_DG(D_, G_, CALL); }                           \
   } while (0)
 
-hipError_t launch_decode(const FwdParams& p, int head_dim, int group, bool kv8, int64_t nwg,
-                         hipStream_t stream) {
-  PA_DISPATCH(head_dim, group, kv8, return (launch_decode_t<DD, GG, KK>(p, nwg, stream)));
+// head_dim x cache format x element type x group -> one specialization
+#define PA_DISPATCH(D_, G_, K8_, CALL)                                                          \
+  do {                                                                                          \
+    if ((D_) == 128) {                                                                          \
+      if (K8_) { constexpr int DD = 128; constexpr bool KK = true; PA_DISPATCH_F(DD, G_, KK, CALL); }  \
+      else { constexpr int DD = 128; constexpr bool KK = false; PA_DISPATCH_F(DD, G_, KK, CALL); }     \
+    } else if ((D_) == 64) {                                                                    \
+      if (K8_) { constexpr int DD = 64; constexpr bool KK = true; PA_DISPATCH_F(DD, G_, KK, CALL); }   \
+      else { constexpr int DD = 64; constexpr bool KK = false; PA_DISPATCH_F(DD, G_, KK, CALL); }      \
+    }                                                                                           \
+  } while (0)
+
+hipError_t launch_decode(const FwdParams& p, int head_dim, int group, bool kv8, bool f16,
+                         int64_t nwg, hipStream_t stream) {
+  PA_DISPATCH(head_dim, group, kv8, return (launch_decode_t<DD, GG, KK, FF>(p, nwg, stream)));
   return hipErrorInvalidValue;
 }
 
-int decode_blocks_per_cu(int head_dim, int group, bool kv8) {
-  PA_DISPATCH(head_dim, group, kv8, return (decode_blocks_per_cu_t<DD, GG, KK>()));
+int decode_blocks_per_cu(int head_dim, int group, bool kv8, bool f16) {
+  PA_DISPATCH(head_dim, group, kv8, return (decode_blocks_per_cu_t<DD, GG, KK, FF>()));
   return 0;
 }
 
@@ -1659,47 +1739,36 @@ bool fwd_supported(int head_dim, int group) {
          (group == 1 || group == 2 || group == 4 || group == 8 || group == 16);
 }
 
-hipError_t launch_fwd(const FwdParams& p, int head_dim, int group, bool wide, bool kv8,
+hipError_t launch_fwd(const FwdParams& p, int head_dim, int group, bool wide, bool kv8, bool f16,
                       int64_t nwg, hipStream_t stream) {
-  PA_DISPATCH(head_dim, group, kv8, return (launch_fwd_t<DD, GG, KK>(p, wide, nwg, stream)));
+  PA_DISPATCH(head_dim, group, kv8, return (launch_fwd_t<DD, GG, KK, FF>(p, wide, nwg, stream)));
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_merge2(const Merge2Params& p, int head_dim, hipStream_t stream) {
+hipError_t launch_merge2(const Merge2Params& p, int head_dim, bool f16, hipStream_t stream) {
   const int64_t rows = (int64_t)p.total_q * p.num_q_heads;
   if (rows <= 0) return hipSuccess;
   if (head_dim == 128)
-    hipLaunchKernelGGL(pa_merge2_kernel<128>, dim3((unsigned)((rows + 7) / 8)), dim3(256), 0, stream, p);
-  else if (head_dim == 64)
-    hipLaunchKernelGGL(pa_merge2_kernel<64>, dim3((unsigned)((rows + 15) / 16)), dim3(256), 0, stream, p);
-  else
-    return hipErrorInvalidValue;
-  return hipGetLastError();
+    return f16 ? launch_merge2_t<128, true>(p, rows, stream) : launch_merge2_t<128, false>(p, rows, stream);
+  if (head_dim == 64)
+    return f16 ? launch_merge2_t<64, true>(p, rows, stream) : launch_merge2_t<64, false>(p, rows, stream);
+  return hipErrorInvalidValue;
 }
 
-hipError_t launch_merge(const MergeParams& p, int head_dim, hipStream_t stream) {
+hipError_t launch_merge(const MergeParams& p, int head_dim, bool f16, hipStream_t stream) {
   const int64_t rows = (int64_t)p.total_q * p.num_q_heads;
   if (rows <= 0) return hipSuccess;
   // many parts per row: a work-group per row; otherwise D/4 threads per row,
   // looping over the row's parts.  An even decode split bounds a row's parts
   // loosely (most rows have one or two): there many rows take the loop form.
   const bool wide = p.n_split > 4 && (!p.even || rows <= 4096);
-  if (head_dim == 128) {
-    if (wide)
-      hipLaunchKernelGGL(pa_merge_wide_kernel<128>, dim3((unsigned)rows), dim3(256), 0, stream, p);
-    else
-      hipLaunchKernelGGL(pa_merge_rows_kernel<128>, dim3((unsigned)((rows + 7) / 8)), dim3(256), 0,
-                         stream, p);
-  } else if (head_dim == 64) {
-    if (wide)
-      hipLaunchKernelGGL(pa_merge_wide_kernel<64>, dim3((unsigned)rows), dim3(256), 0, stream, p);
-    else
-      hipLaunchKernelGGL(pa_merge_rows_kernel<64>, dim3((unsigned)((rows + 15) / 16)), dim3(256), 0,
-                         stream, p);
-  } else {
-    return hipErrorInvalidValue;
-  }
-  return hipGetLastError();
+  if (head_dim == 128)
+    return f16 ? launch_merge_t<128, true>(p, wide, rows, stream)
+               : launch_merge_t<128, false>(p, wide, rows, stream);
+  if (head_dim == 64)
+    return f16 ? launch_merge_t<64, true>(p, wide, rows, stream)
+               : launch_merge_t<64, false>(p, wide, rows, stream);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace pa

@@ -37,7 +37,7 @@ def require_gpu():
 
 def with_scales(b, opts):
     """opts carrying the batch's fp8 scales (None stays None for bf16 caches)."""
-    if b.kv_format == "bf16":
+    if b.kv_format != "fp8_e4m3fn":
         return opts
     o = opts if opts is not None else pa.options()
     o.k_scale, o.v_scale = b.k_scale, b.v_scale

@@ -114,6 +114,23 @@ def test_head_ratio_and_unsupported():
         assert status_of(k_cache=k, v_cache=k.clone())[0] == "PA_ERR_UNSUPPORTED", B
 
 
+def test_element_types():
+    """q, out and 16-bit caches are all bf16 or all fp16 (fp8 caches go with either)."""
+    a = cpu_args()
+    h = {n: a[n].half() for n in ("q", "k_cache", "v_cache")}
+    # fp16 q with bf16 caches, or fp16 everything but out
+    assert status_of(q=h["q"], out=torch.empty_like(h["q"]))[0] == "PA_ERR_DTYPE"
+    assert status_of(q=h["q"], k_cache=h["k_cache"], v_cache=h["v_cache"])[0] == "PA_ERR_DTYPE"
+    # all fp16 passes validation (the host plan accepts it)
+    bb = build_batch("abi", [1, 3, 2], [5, 17, 40], 8, 2, 128, True, seed=1, kv_dtype="f16")
+    assert bb.q.dtype == torch.float16
+    assert pa.plan_describe(*bb.args(torch.empty_like(bb.q))[:9])["persistent"] == 1
+    # fp16 q next to an fp8 cache
+    b8 = build_batch("abi", [1, 3, 2], [5, 17, 40], 8, 2, 128, True, seed=1,
+                     kv_dtype="fp8_e4m3fn", k_scale=0.5, v_scale=0.5, q_dtype="f16")
+    assert pa.plan_describe(*b8.args(torch.empty_like(b8.q))[:9])["persistent"] == 1
+
+
 def test_strides_alignment_alias():
     a = cpu_args()
     # q with a non-unit innermost stride

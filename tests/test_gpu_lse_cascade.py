@@ -42,6 +42,8 @@ CASES = {
     "wide_causal": ([200, 1, 33, 5], [700, 40, 33, 2], 32, 8, 128, True, None, "bf16"),
     "wide_noncausal_split": ([16, 40], [3000, 90], 32, 4, 128, False, dict(force_num_splits=3), "bf16"),
     "fp8_wide_and_decode": ([1, 100, 1], [500, 400, 3000], 32, 8, 128, True, None, "fp8_e4m3fn"),
+    "f16_decode_persistent": ([1, 1, 1, 2, 0, 1], [300, 1, 9000, 64, 5, 0], 32, 8, 128, True, None, "f16"),
+    "f16_wide_split": ([200, 1, 33], [2500, 40, 90], 32, 4, 128, True, dict(force_num_splits=3), "f16"),
 }
 
 
@@ -62,7 +64,8 @@ def test_lse_export(case):
     check_lse(lse, lref, f"lse {case}")
 
 
-def test_cascade_shared_prefix():
+@pytest.mark.parametrize("elem", ["bf16", "f16"])
+def test_cascade_shared_prefix(elem):
     """Sequences share a 64-key prefix (the same four physical blocks)."""
     require_gpu()
     P = 64
@@ -70,14 +73,14 @@ def test_cascade_shared_prefix():
     suf = [50, 7, 300, 40, 2]
     L = [P + s for s in suf]
     hq, hkv, d = 32, 8, 128
-    b = build_batch("casc", q_lens, L, hq, hkv, d, True, seed=501, device=DEV)
+    b = build_batch("casc", q_lens, L, hq, hkv, d, True, seed=501, device=DEV, kv_dtype=elem)
     table = b.block_table.clone()
     table[:, : P // 16] = table[0, : P // 16]                 # one shared prefix
     b.block_table = table
-    say("cascade: one pass")
+    say(f"cascade {elem}: one pass")
     one, lse_one = run_lse(b)
     # prefix pass: every query sees the whole prefix (non-causal over P keys)
-    bp = build_batch("casc", q_lens, L, hq, hkv, d, True, seed=501, device=DEV)
+    bp = build_batch("casc", q_lens, L, hq, hkv, d, True, seed=501, device=DEV, kv_dtype=elem)
     bp.k_cache, bp.v_cache, bp.q = b.k_cache, b.v_cache, b.q
     bp.block_table = table[:, : P // 16].contiguous()
     bp.seqused_k = torch.full_like(b.seqused_k, P)
@@ -87,7 +90,7 @@ def test_cascade_shared_prefix():
     say("cascade: prefix pass")
     o_pre, l_pre = run_lse(bp)
     # suffix pass: causal over each sequence's own blocks
-    bs = build_batch("casc", q_lens, L, hq, hkv, d, True, seed=501, device=DEV)
+    bs = build_batch("casc", q_lens, L, hq, hkv, d, True, seed=501, device=DEV, kv_dtype=elem)
     bs.k_cache, bs.v_cache, bs.q = b.k_cache, b.v_cache, b.q
     bs.block_table = table[:, P // 16:].contiguous()
     bs.seqused_k = b.seqused_k - P
@@ -102,7 +105,7 @@ def test_cascade_shared_prefix():
     h = b.host()
     ref, lref = oracle.paged_attention(h["q"], h["k_cache"], h["v_cache"], h["cu_seqlens_q"],
                                        h["seqused_k"], h["block_table"], h["softmax_scale"],
-                                       h["causal"])
+                                       h["causal"], **b.kv_kwargs())
     check_close(merged.float().cpu().numpy(), ref, "cascade merged vs oracle")
     check_close(one.float().cpu().numpy(), ref, "one pass vs oracle")
     check_lse(l_m, lref, "cascade lse")

@@ -59,7 +59,7 @@ class Batch:
     causal: bool
     trap_block: int
     seed: int
-    kv_format: str = "bf16"          # or "fp8_e4m3fn" (one-byte codes)
+    kv_format: str = "bf16"          # "f16", or "fp8_e4m3fn" (one-byte codes)
     k_scale: float = 1.0             # fp8: a key code stands for decode(code) * k_scale
     v_scale: float = 1.0
     extra: Dict[str, object] = field(default_factory=dict)
@@ -104,8 +104,8 @@ class Batch:
 
     # ---- host copies for the oracle -------------------------------------
     def _cache_host(self, t: torch.Tensor) -> np.ndarray:
-        # bf16: values as float32 (exact); fp8: the raw one-byte codes
-        if self.kv_format == "bf16":
+        # 16-bit: values as float32 (exact); fp8: the raw one-byte codes
+        if self.kv_format != "fp8_e4m3fn":
             return t.float().cpu().numpy()
         return t.view(torch.uint8).cpu().numpy()
 
@@ -198,15 +198,21 @@ def _fill_normal_fp8(shape, gen: torch.Generator, device, scale: float,
     return out
 
 
-def _fill_normal_bf16(shape, gen: torch.Generator, device, chunk: int = 1 << 26) -> torch.Tensor:
-    """N(0,1) float32 draws rounded to bf16, produced in chunks to bound memory."""
-    out = torch.empty(shape, dtype=torch.bfloat16, device=device)
+_TORCH16 = {"bf16": torch.bfloat16, "f16": torch.float16}
+
+
+def _fill_normal_bf16(shape, gen: torch.Generator, device, chunk: int = 1 << 26,
+                      dtype: str = "bf16") -> torch.Tensor:
+    """N(0,1) float32 draws rounded (to nearest even) to bf16 or fp16,
+    produced in chunks to bound memory."""
+    tdt = _TORCH16[dtype]
+    out = torch.empty(shape, dtype=tdt, device=device)
     flat = out.view(-1)
     n = flat.numel()
     for lo in range(0, n, chunk):
         hi = min(n, lo + chunk)
         flat[lo:hi] = torch.randn(hi - lo, generator=gen, device=device,
-                                  dtype=torch.float32).to(torch.bfloat16)
+                                  dtype=torch.float32).to(tdt)
     return out
 
 
@@ -215,15 +221,21 @@ def build_batch(name: str, q_lens, k_lens, num_q_heads: int, num_kv_heads: int,
                 block_size: int = BLOCK_SIZE, pool_blocks: Optional[int] = None,
                 poison: bool = True, softmax_scale: Optional[float] = None,
                 children=None, kv_dtype: str = "bf16", k_scale: float = 1.0,
-                v_scale: float = 1.0) -> Batch:
+                v_scale: float = 1.0, q_dtype: Optional[str] = None) -> Batch:
     """Build a batch from explicit per-sequence query and context lengths.
 
     ``pool_blocks`` fixes the pool size; by default the pool holds exactly the
-    blocks the sequences need plus one trap block.  ``kv_dtype`` is "bf16" or
-    "fp8_e4m3fn" (then ``k_scale`` / ``v_scale`` are the per-tensor scales).
+    blocks the sequences need plus one trap block.  ``kv_dtype`` is "bf16",
+    "f16" or "fp8_e4m3fn" (then ``k_scale`` / ``v_scale`` are the per-tensor
+    scales).  ``q_dtype`` ("bf16" or "f16") defaults to the cache's 16-bit
+    type, or bf16 next to an fp8 cache; q and a 16-bit cache share one type.
     """
-    if kv_dtype not in ("bf16", "fp8_e4m3fn"):
-        raise ValueError("kv_dtype must be bf16 or fp8_e4m3fn")
+    if kv_dtype not in ("bf16", "f16", "fp8_e4m3fn"):
+        raise ValueError("kv_dtype must be bf16, f16 or fp8_e4m3fn")
+    if q_dtype is None:
+        q_dtype = kv_dtype if kv_dtype != "fp8_e4m3fn" else "bf16"
+    if q_dtype not in _TORCH16 or (kv_dtype != "fp8_e4m3fn" and q_dtype != kv_dtype):
+        raise ValueError("q_dtype must be bf16 or f16, the same as a 16-bit cache")
     q_lens = np.asarray(q_lens, dtype=np.int64)
     k_lens = np.asarray(k_lens, dtype=np.int64)
     assert q_lens.shape == k_lens.shape and q_lens.ndim == 1
@@ -259,10 +271,10 @@ def build_batch(name: str, q_lens, k_lens, num_q_heads: int, num_kv_heads: int,
     vseed = int(np.random.default_rng(children[3]).integers(0, 2**62))
     gen = torch.Generator(device=device)
     gen.manual_seed(vseed)
-    q = _fill_normal_bf16((T, num_q_heads, head_dim), gen, device)
-    if kv_dtype == "bf16":
-        k_cache = _fill_normal_bf16((pool, B, num_kv_heads, head_dim), gen, device)
-        v_cache = _fill_normal_bf16((pool, B, num_kv_heads, head_dim), gen, device)
+    q = _fill_normal_bf16((T, num_q_heads, head_dim), gen, device, dtype=q_dtype)
+    if kv_dtype != "fp8_e4m3fn":
+        k_cache = _fill_normal_bf16((pool, B, num_kv_heads, head_dim), gen, device, dtype=kv_dtype)
+        v_cache = _fill_normal_bf16((pool, B, num_kv_heads, head_dim), gen, device, dtype=kv_dtype)
     else:
         k_scale = float(np.float32(k_scale))
         v_scale = float(np.float32(v_scale))
@@ -270,7 +282,7 @@ def build_batch(name: str, q_lens, k_lens, num_q_heads: int, num_kv_heads: int,
         v_cache = _fill_normal_fp8((pool, B, num_kv_heads, head_dim), gen, device, v_scale)
     if poison:
         not_owned = torch.as_tensor(~owned, device=device)
-        if kv_dtype == "bf16":
+        if kv_dtype != "fp8_e4m3fn":
             k_cache[not_owned] = float("nan")
             v_cache[not_owned] = float("nan")
         else:
@@ -288,8 +300,8 @@ def build_batch(name: str, q_lens, k_lens, num_q_heads: int, num_kv_heads: int,
         q_lens=q_lens, k_lens=k_lens, max_seqlen_q=max_q, max_seqlen_k=max_k,
         softmax_scale=float(softmax_scale), causal=bool(causal), trap_block=trap,
         seed=int(seed), kv_format=kv_dtype,
-        k_scale=float(k_scale) if kv_dtype != "bf16" else 1.0,
-        v_scale=float(v_scale) if kv_dtype != "bf16" else 1.0)
+        k_scale=float(k_scale) if kv_dtype == "fp8_e4m3fn" else 1.0,
+        v_scale=float(v_scale) if kv_dtype == "fp8_e4m3fn" else 1.0)
 
 
 def repermute_pool(batch: Batch, seed: int) -> Batch:
