@@ -41,7 +41,7 @@
 extern "C" {
 #endif
 
-#define PA_VERSION 2
+#define PA_VERSION 3   /* 3: fp16 (PA_F16) and block sizes 32, 64 */
 
 /* Return codes.  Every failure is reported before anything is launched, with
  * one exception: PA_ERR_HIP, which may also come from the launch itself. */
