@@ -47,6 +47,8 @@ struct Plan {
   size_t ws_bytes;
   size_t ws_lse_offset;
   size_t ws_parts_offset;   // row part counts [T * Hq] int32
+  size_t ws_lpt_offset;     // longest-first unit order [lpt_units] int4
+  int64_t lpt_units;
 };
 
 constexpr int64_t kMaxInt32 = 0x7fffffff;
@@ -308,16 +310,24 @@ int make_plan(const Shapes& s, int32_t max_q, int32_t max_k, const pa_options* o
   p.split_keys = (int32_t)split_keys;
   p.num_items = items * n_split;
   p.nwg = (p.num_items + 7) / 8 * 8;
-  // wide plans rank their units longest-first on the device (LDS tables of
-  // the sequence lengths); larger batches keep the index order
+  // wide plans rank their units longest-first on the device (one work-group
+  // sorts the units by stage count into the workspace before the grid runs);
+  // larger batches keep the index order
   p.lpt = p.wide && s.S <= pa::kLptMaxSeqs;
   if (p.num_items > kMaxInt32) return fail(PA_ERR_UNSUPPORTED, "grid too large");
+  size_t off = 0;
   if (n_split > 1) {
     const size_t rows = (size_t)s.T * (size_t)s.Hq * (size_t)n_split;
     p.ws_lse_offset = align256(rows * (size_t)s.D * sizeof(float));
     p.ws_parts_offset = p.ws_lse_offset + align256(rows * sizeof(float));
-    p.ws_bytes = p.ws_parts_offset + align256((size_t)s.T * (size_t)s.Hq * sizeof(int32_t));
+    off = p.ws_parts_offset + align256((size_t)s.T * (size_t)s.Hq * sizeof(int32_t));
   }
+  if (p.lpt) {
+    p.lpt_units = (int64_t)p.num_slots * n_split;     // units the grid can hold
+    p.ws_lpt_offset = off;
+    off += align256((size_t)p.lpt_units * 4 * sizeof(int32_t));
+  }
+  p.ws_bytes = off;
   *out = p;
   return PA_OK;
 }
@@ -521,6 +531,9 @@ int run(const pa_tensor* q, const pa_tensor* k, const pa_tensor* v, pa_tensor* o
   p.sub_sb = (int64_t)pa::kBlockSize * s.Hkv * s.D;
   p.bshift = s.B == 64 ? 2 : (s.B == 32 ? 1 : 0);
   p.lpt = plan.lpt ? 1 : 0;
+  p.lpt_units = (int32_t)plan.lpt_units;
+  p.lpt_order = plan.lpt ? reinterpret_cast<int4*>(static_cast<char*>(ws) + plan.ws_lpt_offset)
+                         : nullptr;
   p.causal = causal ? 1 : 0;
   p.narrow_rows = (opt && opt->force_tile == 2) ? 0 : pa::kNarrowRows;
   // fp8 caches: k_scale folds into the score scale, v_scale into the output
@@ -530,6 +543,10 @@ int run(const pa_tensor* q, const pa_tensor* k, const pa_tensor* v, pa_tensor* o
   p.out_scale = (float)v_scale;
   p.lse_out = lse ? static_cast<float*>(lse->data) : nullptr;
   p.lse_st = lse ? lse->stride[0] : 0;
+  if (plan.nwg > 0 && plan.lpt) {
+    const hipError_t e = pa::launch_rank(p, stream);
+    if (e != hipSuccess) return fail(PA_ERR_HIP, "rank launch: %s", hipGetErrorString(e));
+  }
   if (plan.nwg > 0) {
     hipError_t e = plan.persistent
                        ? pa::launch_decode(p, (int)s.D, (int)s.G, s.kv8, s.f16, plan.nwg, stream)

@@ -57,6 +57,8 @@ struct FwdParams {
   int32_t causal;
   int32_t narrow_rows;     // tiles with at most this many packed rows take the narrow path
   int32_t lpt;             // grid plans: units in longest-first order (block b -> rank b / Hkv)
+  int32_t lpt_units;       // entries of lpt_order (the grid's unit capacity)
+  int4* lpt_order;         // [lpt_units] (s, tile, split, -) of each rank, from pa_rank_kernel
   float scale_log2;        // softmax_scale * k_scale * log2(e)
   float out_scale;         // v_scale (1 for bf16 caches): multiplies every output row
   float* lse_out;          // optional fp32 [T, Hq] (row stride lse_st): natural-log lse
@@ -118,6 +120,8 @@ hipError_t launch_cache_write(const CacheWriteParams& p, bool kv8, bool f16, hip
 hipError_t launch_fwd(const FwdParams& p, int head_dim, int group, bool wide, bool kv8, bool f16,
                       int64_t num_workgroups, hipStream_t stream);
 hipError_t launch_merge(const MergeParams& p, int head_dim, bool f16, hipStream_t stream);
+// Longest-first unit order of a grid plan into p.lpt_order (one work-group).
+hipError_t launch_rank(const FwdParams& p, hipStream_t stream);
 // Persistent decode kernel (every tile narrow, num_seqs <= kMaxDecodeSeqs).
 hipError_t launch_decode(const FwdParams& p, int head_dim, int group, bool kv8, bool f16,
                          int64_t num_workgroups, hipStream_t stream);

@@ -305,20 +305,22 @@ __device__ __forceinline__ int unit_stages(const FwdParams& p, int q_len, int L,
 // Longest-first order of the batch's units (sequence, query tile, key split),
 // so the work-group scheduler starts the most expensive tiles first and the
 // grid drains with short ones (list scheduling, longest processing time
-// first).  Unit rank r is decoded by every work-group from the lengths alone:
-// units are ranked by (stages descending, unit index ascending), where sequence
-// s owns unit indices [P[s], P[s] + tiles_s * parts_s) and index j within it is
-// (tile j % tiles_s, split j / tiles_s).  Uses LDS `tab` (3 S + 80 ints) and
-// barriers: call from every thread.  Returns false if there is no unit r.
-__device__ bool lpt_unit(const FwdParams& p, int r, int* tab, int* s_out, int* t_out,
-                         int* sg_out) {
+// first).  One work-group computes the order once per call from the lengths
+// and writes order[r] = (s, tile, split) for rank r, ranks running over the
+// 64-key stage counts descending; ranks past the last unit get s = -1.
+// Sequence s owns unit indices [P[s], P[s] + tiles_s * parts_s), index j
+// within it being (tile j % tiles_s, split j / tiles_s).  Units of equal stage
+// count take their ranks in any order (LDS atomics): the order decides only
+// which work-group computes a unit, never its result.
+__global__ __launch_bounds__(kThreads) void pa_rank_kernel(FwdParams p) {
+  extern __shared__ int tab[];     // 3 S + 1 + 65 + 65 + 8 ints
   const int S = p.num_seqs;
   int* qlen = tab;                 // [S]
   int* klen = tab + S;             // [S]
   int* pre = tab + 2 * S;          // [S + 1] first unit index of each sequence
   int* hist = tab + 3 * S + 1;     // [65] units per stage count (0..64)
-  int* scr = hist + 65;            // [8] scan scratch
-  int* res = scr + 8;              // [4] the chosen unit
+  int* next = hist + 65;           // [65] next free rank of each stage count
+  int* scr = next + 65;            // [8] scan scratch
   const int tid = threadIdx.x;
   const int Tq = p.tile_tokens;
   // per-sequence tables; threads own contiguous runs of sequences
@@ -344,7 +346,6 @@ __device__ bool lpt_unit(const FwdParams& p, int r, int* tab, int* s_out, int* t
   }
   if (tid == 0) pre[S] = U;
   __syncthreads();
-  if (r >= U) return false;                         // uniform: r is per work-group
   // each thread walks a contiguous run of unit indices
   const int cu = (U + kThreads - 1) / kThreads;
   const int u0 = min(U, tid * cu), u1 = min(U, u0 + cu);
@@ -365,54 +366,24 @@ __device__ bool lpt_unit(const FwdParams& p, int r, int* tab, int* s_out, int* t
       const int nt = (q + Tq - 1) / Tq;
       const int j = u - pre[s];
       const int tile = j % nt, sg = j / nt;
-      if (!visit(s, tile, sg, unit_stages(p, q, klen[s], tile, sg))) return;
+      visit(s, tile, sg, unit_stages(p, q, klen[s], tile, sg));
     }
   };
-  walk([&](int, int, int, int w) { atomicAdd(&hist[w], 1); return true; });
+  walk([&](int, int, int, int w) { atomicAdd(&hist[w], 1); });
   __syncthreads();
-  // stage count W of rank r: ranks run over W = 64, 63, ..., 0
-  int Wsel = 0, before = 0;
-  {
-    const int lane = tid & 63;
-    const int h = hist[64 - lane];                   // lane l <-> W = 64 - l (W = 1..64)
-    int x = h;
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-      const int y = __shfl_up(x, d);
-      if (lane >= d) x += y;
-    }
-    const unsigned long long hit = __builtin_amdgcn_ballot_w64(r < x);
-    if (hit) {
-      const int l = __builtin_ctzll(hit);
-      Wsel = 64 - l;
-      before = __shfl(x - h, l);
-    } else {
-      Wsel = 0;                                      // units without keys come last
-      before = __shfl(x, 63);
+  if (tid == 0) {                                    // first rank of each stage count
+    int r = 0;
+    for (int w = 64; w >= 0; --w) {
+      next[w] = r;
+      r += hist[w];
     }
   }
-  const int rr = r - before;                         // rank among units with Wsel stages
-  int cnt = 0;
-  walk([&](int, int, int, int w) { cnt += w == Wsel; return true; });
-  int dummy;
-  const int ex = block_exclusive_scan(cnt, scr, &dummy);
-  if (ex <= rr && rr < ex + cnt) {
-    int k = rr - ex;
-    walk([&](int s, int tile, int sg, int w) {
-      if (w != Wsel) return true;
-      if (k-- > 0) return true;
-      res[0] = s;
-      res[1] = tile;
-      res[2] = sg;
-      return false;
-    });
-  }
   __syncthreads();
-  *s_out = res[0];
-  *t_out = res[1];
-  *sg_out = res[2];
-  __syncthreads();                                   // tables may be overwritten next
-  return true;
+  walk([&](int s, int tile, int sg, int w) {
+    const int r = atomicAdd(&next[w], 1);
+    p.lpt_order[r] = int4{s, tile, sg, 0};
+  });
+  for (int r = U + tid; r < p.lpt_units; r += kThreads) p.lpt_order[r] = int4{-1, 0, 0, 0};
 }
 
 template <int G>
@@ -422,9 +393,10 @@ __device__ __forceinline__ bool decode_item(const FwdParams& p, Item& it, unsign
     // XCD (b % 8) serves one kv-head, so K/V of its sequences stay in its L2
     const int r = blockIdx.x / p.num_kv_heads;
     const int kvh = blockIdx.x % p.num_kv_heads;
-    int s, tile, sg;
-    if (!lpt_unit(p, r, reinterpret_cast<int*>(smem), &s, &tile, &sg)) return false;
-    return fill_item<G>(p, s, tile, sg, kvh, it);
+    if (r >= p.lpt_units) return false;              // the grid is rounded up to 8 blocks
+    const int4 u = p.lpt_order[r];                   // written by pa_rank_kernel
+    if (u.x < 0) return false;
+    return fill_item<G>(p, u.x, u.y, u.z, kvh, it);
   }
   // Work-groups are dispatched round-robin over the 8 XCDs (XCD = id % 8);
   // give each XCD a contiguous range of items so items that share data
@@ -1043,10 +1015,6 @@ __device__ __forceinline__ void attend_wide(const FwdParams& p, const Item& it,
 }
 
 constexpr int kRing = 2;   // cache blocks in flight per wave on the narrow path
-
-// the longest-first tables (3 ints per sequence + 80) fit the wide kernel's LDS
-static_assert((3 * kLptMaxSeqs + 80) * 4 <= WideCfg<64>::SMEM, "LPT tables exceed LDS");
-static_assert((3 * kLptMaxSeqs + 80) * 4 <= WideCfg<128>::SMEM, "LPT tables exceed LDS");
 
 // WIDE = false: every tile of the batch is narrow (the plan guarantees it).
 // KV8: the caches hold fp8 E4M3 codes.  F16: q, out (and 16-bit caches) are
@@ -1743,6 +1711,12 @@ hipError_t launch_fwd(const FwdParams& p, int head_dim, int group, bool wide, bo
                       int64_t nwg, hipStream_t stream) {
   PA_DISPATCH(head_dim, group, kv8, return (launch_fwd_t<DD, GG, KK, FF>(p, wide, nwg, stream)));
   return hipErrorInvalidValue;
+}
+
+hipError_t launch_rank(const FwdParams& p, hipStream_t stream) {
+  const size_t lds = (size_t)(3 * p.num_seqs + 1 + 65 + 65 + 8) * sizeof(int);
+  hipLaunchKernelGGL(pa_rank_kernel, dim3(1), dim3(kThreads), lds, stream, p);
+  return hipGetLastError();
 }
 
 hipError_t launch_merge2(const Merge2Params& p, int head_dim, bool f16, hipStream_t stream) {

@@ -220,7 +220,8 @@ def test_plan_heuristic_on_workload_shapes():
     # a full prefill batch does not split: 8 x 512 queries over 2048 keys
     bf = build_batch("f", np.full(8, 512), np.full(8, 2048), 32, 8, 128, True, 4)
     pf = plan_of(bf)
-    assert pf["num_splits"] == 1 and pf["workspace_bytes"] == 0
+    # no split: the workspace holds only the longest-first unit order (16 B a unit)
+    assert pf["num_splits"] == 1 and pf["workspace_bytes"] == -(-pf["num_slots"] * 16 // 256) * 256
     assert pf["num_slots"] * 8 >= 4 * 256 and pf["longest_first"] == 1
     # decode plans and batches of more than 2048 sequences keep the index order
     assert plan_of(build_batch("d", np.ones(8, int), np.full(8, 100), 32, 8, 128, True, 2))[
@@ -244,8 +245,13 @@ def test_workspace_size_matches_plan():
     p = pa.plan_describe(b.q, b.k_cache, b.v_cache, out, b.cu_seqlens_q, b.seqused_k,
                          b.block_table, b.max_seqlen_q, b.max_seqlen_k, o)
     assert n == p["workspace_bytes"] > 0
-    assert pa.workspace_size(b.q, b.k_cache, b.v_cache, out, b.cu_seqlens_q, b.seqused_k,
-                             b.block_table, b.max_seqlen_q, b.max_seqlen_k) == 0
+    # without a split only the longest-first unit order (16 B a unit) remains
+    p0 = pa.plan_describe(b.q, b.k_cache, b.v_cache, out, b.cu_seqlens_q, b.seqused_k,
+                          b.block_table, b.max_seqlen_q, b.max_seqlen_k)
+    n0 = pa.workspace_size(b.q, b.k_cache, b.v_cache, out, b.cu_seqlens_q, b.seqused_k,
+                           b.block_table, b.max_seqlen_q, b.max_seqlen_k)
+    assert p0["num_splits"] == 1 and p0["longest_first"] == 1
+    assert n0 == p0["workspace_bytes"] == -(-p0["num_slots"] * 16 // 256) * 256
 
 
 def test_fp8_cache_descriptors():
