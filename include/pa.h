@@ -41,7 +41,7 @@
 extern "C" {
 #endif
 
-#define PA_VERSION 3   /* 3: fp16 (PA_F16) and block sizes 32, 64 */
+#define PA_VERSION 3   /* 3: fp16 (PA_F16), block sizes 32 and 64, head sizes 96 and 256 */
 
 /* Return codes.  Every failure is reported before anything is launched, with
  * one exception: PA_ERR_HIP, which may also come from the launch itself. */
@@ -155,7 +155,7 @@ typedef struct {
  *               causal mask (see above).
  *  stream       hipStream_t to launch on (NULL = the null stream).
  *
- * Supported: d in {64, 128}; B in {16, 32, 64}; Hq % Hkv == 0 with G = Hq/Hkv in
+ * Supported: d in {64, 96, 128, 256}; B in {16, 32, 64}; Hq % Hkv == 0 with G = Hq/Hkv in
  * {1, 2, 4, 8, 16}.  Unsupported values return PA_ERR_UNSUPPORTED.
  *
  * Preconditions on device contents (unchecked unless check_contents is set;
@@ -222,7 +222,8 @@ int pa_unified_attention_lse(const pa_tensor* q, const pa_tensor* k_cache,
  * disjoint key sets: with natural-log lse a, b, out = (e^a out_a + e^b out_b) /
  * (e^a + e^b) and lse_out = ln(e^a + e^b); a side with lse = -inf has no keys
  * and drops out (a row with no keys on either side gives 0 and -inf).
- *  out_a, out_b, out  bf16 [T, Hq, d], d in {64, 128}; stride[2] == 1;
+ *  out_a, out_b, out  bf16, or all three fp16, [T, Hq, d], d in {64, 96, 128,
+ *               256}; stride[2] == 1;
  *               stride[0], stride[1] multiples of 4; 8-byte aligned.
  *  lse_a, lse_b fp32 [T, Hq]; stride[1] == 1.
  *  lse_out      fp32 [T, Hq] or NULL.  Outputs must not overlap the inputs.

@@ -48,17 +48,38 @@ def _run(cmd, verbose):
         print("\n".join(rest), file=sys.stderr)
 
 
+# (source, extra flags, object): the kernels are compiled once per head size
+HEAD_DIMS = (64, 96, 128, 256)
+
+
+def _units():
+    units = []
+    for src in SOURCES:
+        stem = os.path.splitext(src)[0]
+        if src == "pa_kernels.hip":
+            for d in HEAD_DIMS:
+                units.append((src, [f"-DPA_TU_HEAD_DIM={d}"], f"{stem}_d{d}.o"))
+        else:
+            units.append((src, [], stem + ".o"))
+    return units
+
+
 def build(verbose: bool = False) -> str:
-    """Compile every source and link libpa.so; always rebuilds."""
+    """Compile every source (in parallel) and link libpa.so; always rebuilds."""
+    from concurrent.futures import ThreadPoolExecutor
+
     os.makedirs(BUILD, exist_ok=True)
     cc = hipcc()
-    objs = []
-    for src in SOURCES:
-        obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
+    jobs = []
+    for src, extra, objname in _units():
+        obj = os.path.join(BUILD, objname)
         lang = ["-x", "hip"] if src.endswith(".hip") else []
-        _run([cc, *HIP_FLAGS, "-I", os.path.join(ROOT, "include"), "-I", CSRC, *lang, "-c",
-              os.path.join(CSRC, src), "-o", obj], verbose)
-        objs.append(obj)
+        jobs.append(([cc, *HIP_FLAGS, *extra, "-I", os.path.join(ROOT, "include"), "-I", CSRC,
+                      *lang, "-c", os.path.join(CSRC, src), "-o", obj], obj))
+    workers = max(1, min(len(jobs), os.cpu_count() or 1, 8))
+    with ThreadPoolExecutor(max_workers=workers) as pool:
+        list(pool.map(lambda j: _run(j[0], verbose), jobs))
+    objs = [obj for _, obj in jobs]
     tmp = LIB + ".tmp"
     _run([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp], verbose)
     os.replace(tmp, LIB)

@@ -135,8 +135,8 @@ int validate(const pa_tensor* q, const pa_tensor* k, const pa_tensor* v, const p
   if (s.S == 0 && s.T != 0) return fail(PA_ERR_SHAPE, "total_q > 0 with no sequences");
   if (max_q < 0 || max_k < 0) return fail(PA_ERR_SHAPE, "negative max_seqlen");
   s.G = s.Hq / s.Hkv;
-  if (s.D != 64 && s.D != 128)
-    return fail(PA_ERR_UNSUPPORTED, "head_dim %lld (supported: 64, 128)", (long long)s.D);
+  if (s.D != 64 && s.D != 96 && s.D != 128 && s.D != 256)
+    return fail(PA_ERR_UNSUPPORTED, "head_dim %lld (supported: 64, 96, 128, 256)", (long long)s.D);
   if (s.B != 16 && s.B != 32 && s.B != 64)
     return fail(PA_ERR_UNSUPPORTED, "block_size %lld (supported: 16, 32, 64)", (long long)s.B);
   // the kernels address 16-key sub-blocks: physical block * (B / 16) + part
@@ -216,6 +216,11 @@ int make_plan(const Shapes& s, int32_t max_q, int32_t max_k, const pa_options* o
     return fail(PA_ERR_UNSUPPORTED, "force_tile=%d needs max_seqlen_q * G <= 16", force_tile);
   if (force_tile < 0 || force_tile > 3)
     return fail(PA_ERR_UNSUPPORTED, "force_tile must be 0, 1, 2 or 3");
+  // wide tiles (32 rows per wave, fp32 accumulators of the whole d) exist for
+  // d = 64 and 128; other head sizes run every tile on the narrow path
+  const bool wide_ok = s.D == 64 || s.D == 128;
+  if (force_tile == 2 && !wide_ok)
+    return fail(PA_ERR_UNSUPPORTED, "force_tile=2 (wide tiles) needs head_dim 64 or 128");
   const bool narrow = force_tile == 1 || force_tile == 3 || (force_tile == 0 && narrow_fits);
   // (the decode kernel's idle ring slots re-read pool block 0, so the pool
   // must hold at least one block)
@@ -276,6 +281,12 @@ int make_plan(const Shapes& s, int32_t max_q, int32_t max_k, const pa_options* o
     p.slots_direct = 1;
     p.num_slots = (int32_t)s.S;
     p.wide = false;
+  } else if (!wide_ok) {
+    // narrow tiles of 16 / G tokens; a sequence spans several of them
+    p.wide = false;
+    p.tile_tokens = (int32_t)std::max<int64_t>(1, pa::kNarrowRows / G);
+    p.slots_direct = 0;
+    p.num_slots = (int32_t)(s.T / p.tile_tokens + s.S);
   } else {
     p.wide = true;
     p.tile_tokens = (int32_t)(pa::kTileRows / G);
@@ -359,8 +370,8 @@ int device_cu_count(bool* ok) {
 
 int decode_blocks_per_cu_cached(int head_dim, int group, bool kv8, bool f16) {
   static std::mutex mu;
-  static int cache[2][2][2][17] = {};
-  const int di = head_dim == 128 ? 1 : 0;
+  static int cache[4][2][2][17] = {};
+  const int di = head_dim == 64 ? 0 : (head_dim == 96 ? 1 : (head_dim == 128 ? 2 : 3));
   const int ki = kv8 ? 1 : 0;
   const int fi = f16 ? 1 : 0;
   std::lock_guard<std::mutex> lock(mu);
@@ -640,7 +651,8 @@ int pa_merge_attention(const pa_tensor* out_a, const pa_tensor* lse_a, const pa_
     if (t->stride[1] != 1 && Hq > 1) return fail(PA_ERR_UNSUPPORTED, "lse needs a unit head stride");
     if (!aligned(t->data, 4)) return fail(PA_ERR_ALIGN, "lse must be 4-byte aligned");
   }
-  if (D != 64 && D != 128) return fail(PA_ERR_UNSUPPORTED, "head_dim %lld (supported: 64, 128)", (long long)D);
+  if (D != 64 && D != 96 && D != 128 && D != 256)
+    return fail(PA_ERR_UNSUPPORTED, "head_dim %lld (supported: 64, 96, 128, 256)", (long long)D);
   if (T * Hq > kMaxInt32) return fail(PA_ERR_UNSUPPORTED, "too many rows");
   if (overlaps(out, 2, out_a, 2) || overlaps(out, 2, out_b, 2) ||
       (lse_out && (overlaps(lse_out, 4, lse_a, 4) || overlaps(lse_out, 4, lse_b, 4) ||

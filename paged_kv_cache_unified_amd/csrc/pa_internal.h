@@ -91,8 +91,6 @@ struct Merge2Params {
   int64_t oa_st, oa_sh, ob_st, ob_sh, o_st, o_sh, la_st, lb_st, l_st;
   int32_t total_q, num_q_heads;
 };
-// f16: the outputs are fp16 (else bf16)
-hipError_t launch_merge2(const Merge2Params& p, int head_dim, bool f16, hipStream_t stream);
 
 // New tokens' keys and values -> paged cache slots (pa_cache_kernels.hip).
 struct CacheWriteParams {
@@ -113,20 +111,65 @@ struct CacheWriteParams {
 
 hipError_t launch_cache_write(const CacheWriteParams& p, bool kv8, bool f16, hipStream_t stream);
 
-// Launchers (pa_kernels.hip).  Return the hipError_t of the launch.
+// Launchers (pa_kernels.hip, one object per head size d).  Return the
+// hipError_t of the launch.
 // wide = false launches the narrow-only specialization (every tile <= 16 rows).
 // kv8: the caches hold fp8 E4M3 codes (else 16-bit elements); f16: q, out and
 // 16-bit caches are fp16 (else bf16).
-hipError_t launch_fwd(const FwdParams& p, int head_dim, int group, bool wide, bool kv8, bool f16,
-                      int64_t num_workgroups, hipStream_t stream);
-hipError_t launch_merge(const MergeParams& p, int head_dim, bool f16, hipStream_t stream);
+#define PA_DECLARE_HEAD_DIM(DV)                                                                  \
+  hipError_t launch_fwd_d##DV(const FwdParams& p, int group, bool wide, bool kv8, bool f16,     \
+                              int64_t num_workgroups, hipStream_t stream);                     \
+  hipError_t launch_decode_d##DV(const FwdParams& p, int group, bool kv8, bool f16,             \
+                                 int64_t num_workgroups, hipStream_t stream);                  \
+  int decode_blocks_per_cu_d##DV(int group, bool kv8, bool f16);                                \
+  hipError_t launch_merge_d##DV(const MergeParams& p, bool f16, hipStream_t stream);            \
+  hipError_t launch_merge2_d##DV(const Merge2Params& p, bool f16, hipStream_t stream);
+PA_DECLARE_HEAD_DIM(64)
+PA_DECLARE_HEAD_DIM(96)
+PA_DECLARE_HEAD_DIM(128)
+PA_DECLARE_HEAD_DIM(256)
+#undef PA_DECLARE_HEAD_DIM
+
+#define PA_BY_HEAD_DIM(D_, FN, ...)                     \
+  switch (D_) {                                         \
+    case 64: return FN##_d64(__VA_ARGS__);              \
+    case 96: return FN##_d96(__VA_ARGS__);              \
+    case 128: return FN##_d128(__VA_ARGS__);            \
+    case 256: return FN##_d256(__VA_ARGS__);            \
+    default: break;                                     \
+  }
+
+inline hipError_t launch_fwd(const FwdParams& p, int head_dim, int group, bool wide, bool kv8,
+                             bool f16, int64_t num_workgroups, hipStream_t stream) {
+  PA_BY_HEAD_DIM(head_dim, launch_fwd, p, group, wide, kv8, f16, num_workgroups, stream)
+  return hipErrorInvalidValue;
+}
+inline hipError_t launch_merge(const MergeParams& p, int head_dim, bool f16, hipStream_t stream) {
+  PA_BY_HEAD_DIM(head_dim, launch_merge, p, f16, stream)
+  return hipErrorInvalidValue;
+}
+// f16: the outputs are fp16 (else bf16)
+inline hipError_t launch_merge2(const Merge2Params& p, int head_dim, bool f16, hipStream_t stream) {
+  PA_BY_HEAD_DIM(head_dim, launch_merge2, p, f16, stream)
+  return hipErrorInvalidValue;
+}
 // Longest-first unit order of a grid plan into p.lpt_order (one work-group).
 hipError_t launch_rank(const FwdParams& p, hipStream_t stream);
 // Persistent decode kernel (every tile narrow, num_seqs <= kMaxDecodeSeqs).
-hipError_t launch_decode(const FwdParams& p, int head_dim, int group, bool kv8, bool f16,
-                         int64_t num_workgroups, hipStream_t stream);
+inline hipError_t launch_decode(const FwdParams& p, int head_dim, int group, bool kv8, bool f16,
+                                int64_t num_workgroups, hipStream_t stream) {
+  PA_BY_HEAD_DIM(head_dim, launch_decode, p, group, kv8, f16, num_workgroups, stream)
+  return hipErrorInvalidValue;
+}
 // Resident work-groups per CU of the decode kernel (0 if unknown).
-int decode_blocks_per_cu(int head_dim, int group, bool kv8, bool f16);
-bool fwd_supported(int head_dim, int group);
+inline int decode_blocks_per_cu(int head_dim, int group, bool kv8, bool f16) {
+  PA_BY_HEAD_DIM(head_dim, decode_blocks_per_cu, group, kv8, f16)
+  return 0;
+}
+inline bool fwd_supported(int head_dim, int group) {
+  return (head_dim == 64 || head_dim == 96 || head_dim == 128 || head_dim == 256) &&
+         (group == 1 || group == 2 || group == 4 || group == 8 || group == 16);
+}
+#undef PA_BY_HEAD_DIM
 
 }  // namespace pa

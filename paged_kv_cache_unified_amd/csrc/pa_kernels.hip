@@ -54,6 +54,7 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -224,9 +225,11 @@ template <int D>
 struct Layout {
   static constexpr int CPR = D / 8;                  // chunks per key row
   static constexpr int BLK_BYTES = kBlockSize * D * 2;
-  static __device__ __forceinline__ int k_chunk(int key, int dc) { return dc * 16 + (key ^ dc); }
+  // XOR swizzle of a V row's chunks; d = 96 (12 chunks, not closed under
+  // XOR) keeps the plain order
   static __device__ __forceinline__ int v_swz(int key) {
-    return D == 128 ? 2 * (key & 7) : 2 * ((key >> 1) & 3);
+    if constexpr (D == 96) return 0;
+    return D >= 128 ? 2 * (key & 7) : 2 * ((key >> 1) & 3);
   }
   static __device__ __forceinline__ int v_chunk(int key, int c) { return key * CPR + (c ^ v_swz(key)); }
 };
@@ -312,6 +315,7 @@ __device__ __forceinline__ int unit_stages(const FwdParams& p, int q_len, int L,
 // within it being (tile j % tiles_s, split j / tiles_s).  Units of equal stage
 // count take their ranks in any order (LDS atomics): the order decides only
 // which work-group computes a unit, never its result.
+#if PA_TU_HEAD_DIM == 64
 __global__ __launch_bounds__(kThreads) void pa_rank_kernel(FwdParams p) {
   extern __shared__ int tab[];     // 3 S + 1 + 65 + 65 + 8 ints
   const int S = p.num_seqs;
@@ -385,9 +389,10 @@ __global__ __launch_bounds__(kThreads) void pa_rank_kernel(FwdParams p) {
   });
   for (int r = U + tid; r < p.lpt_units; r += kThreads) p.lpt_order[r] = int4{-1, 0, 0, 0};
 }
+#endif
 
 template <int G>
-__device__ __forceinline__ bool decode_item(const FwdParams& p, Item& it, unsigned char* smem) {
+__device__ __forceinline__ bool decode_item(const FwdParams& p, Item& it) {
   if (p.lpt) {
     // block b -> unit rank b / Hkv, kv-head b % Hkv: with 8 kv-heads every
     // XCD (b % 8) serves one kv-head, so K/V of its sequences stay in its L2
@@ -635,15 +640,16 @@ __device__ __forceinline__ void attend_narrow(const FwdParams& p, const Item& it
     Ls += wt[w] * red_l[w * 16 + n];
   }
   const float inv = Ls > 0.f ? p.out_scale / Ls : 0.f;
+  // DPER = 4, 6, 8 or 16 values per thread: pairs (8-byte aligned: d0 is even)
   float o[DPER];
 #pragma unroll
-  for (int e = 0; e < DPER; e += 4) {
-    f32x4 a = {0.f, 0.f, 0.f, 0.f};
+  for (int e = 0; e < DPER; e += 2) {
+    f32x2 a = {0.f, 0.f};
 #pragma unroll
     for (int w = 0; w < 4; ++w)
-      a += wt[w] * *reinterpret_cast<const f32x4*>(red_o + (w * 16 + n) * RS + d0 + e);
-#pragma unroll
-    for (int k = 0; k < 4; ++k) o[e + k] = a[k] * inv;
+      a += wt[w] * *reinterpret_cast<const f32x2*>(red_o + (w * 16 + n) * RS + d0 + e);
+    o[e] = a[0] * inv;
+    o[e + 1] = a[1] * inv;
   }
   const int64_t tok = it.q0 + it.tok0 + n / G;
   const int hn = it.kvh * G + n % G;
@@ -653,20 +659,25 @@ __device__ __forceinline__ void attend_narrow(const FwdParams& p, const Item& it
     if ((tid & 15) == 0)
       store_lse(p.lse_out, p.lse_st, tok, hn, Ls > 0.f ? M + __log2f(Ls) : kNegInf);
     uint16_t* op = p.out + tok * p.o_st + (int64_t)hn * p.o_sh + d0;
-    if constexpr (DPER == 8) {
-      u32x4 w = {E::pack2(o[0], o[1]), E::pack2(o[2], o[3]), E::pack2(o[4], o[5]),
-                 E::pack2(o[6], o[7])};
-      *reinterpret_cast<u32x4*>(op) = w;
-    } else {
-      u32x2 w = {E::pack2(o[0], o[1]), E::pack2(o[2], o[3])};
-      *reinterpret_cast<u32x2*>(op) = w;
+    if constexpr (DPER % 8 == 0) {               // 16-byte stores
+#pragma unroll
+      for (int e = 0; e < DPER; e += 8)
+        *reinterpret_cast<u32x4*>(op + e) = u32x4{E::pack2(o[e], o[e + 1]), E::pack2(o[e + 2], o[e + 3]),
+                                                  E::pack2(o[e + 4], o[e + 5]), E::pack2(o[e + 6], o[e + 7])};
+    } else if constexpr (DPER % 4 == 0) {        // 8-byte stores
+#pragma unroll
+      for (int e = 0; e < DPER; e += 4)
+        *reinterpret_cast<u32x2*>(op + e) = u32x2{E::pack2(o[e], o[e + 1]), E::pack2(o[e + 2], o[e + 3])};
+    } else {                                     // d = 96: 4-byte stores (d0 = 6 j)
+#pragma unroll
+      for (int e = 0; e < DPER; e += 2)
+        *reinterpret_cast<uint32_t*>(op + e) = E::pack2(o[e], o[e + 1]);
     }
   } else {
     const int64_t r = ((int64_t)it.sigma * p.total_q + tok) * p.num_q_heads + hn;
     float* wp = p.ws_o + r * D + d0;
 #pragma unroll
-    for (int e = 0; e < DPER; e += 4)
-      *reinterpret_cast<f32x4*>(wp + e) = f32x4{o[e], o[e + 1], o[e + 2], o[e + 3]};
+    for (int e = 0; e < DPER; e += 2) *reinterpret_cast<f32x2*>(wp + e) = f32x2{o[e], o[e + 1]};
     if ((tid & 15) == 0) p.ws_lse[r] = Ls > 0.f ? M + __log2f(Ls) : kNegInf;
   }
 }
@@ -1014,7 +1025,9 @@ __device__ __forceinline__ void attend_wide(const FwdParams& p, const Item& it,
   }
 }
 
-constexpr int kRing = 2;   // cache blocks in flight per wave on the narrow path
+// cache blocks in flight per wave on the narrow path (d = 256: one, for registers)
+template <int D>
+constexpr int narrow_ring() { return D == 256 ? 1 : 2; }
 
 // WIDE = false: every tile of the batch is narrow (the plan guarantees it).
 // KV8: the caches hold fp8 E4M3 codes.  F16: q, out (and 16-bit caches) are
@@ -1022,14 +1035,16 @@ constexpr int kRing = 2;   // cache blocks in flight per wave on the narrow path
 template <int D, int G, bool WIDE, bool KV8, bool F16>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
 void pa_fwd_kernel(FwdParams p) {
-  constexpr int SMEM = WIDE ? WideCfg<D>::SMEM : NarrowCfg<D>::SMEM;
+  // wide tiles exist for d = 64 and 128 only (the plan gives other sizes narrow tiles)
+  constexpr bool HAS_WIDE = WIDE && (D == 64 || D == 128);
+  constexpr int SMEM = HAS_WIDE ? WideCfg<D>::SMEM : NarrowCfg<D>::SMEM;
   __shared__ __attribute__((aligned(16))) unsigned char smem[SMEM];
   Item it;
-  if (!decode_item<G>(p, it, smem)) return;
+  if (!decode_item<G>(p, it)) return;
   if (it.rows <= p.narrow_rows) {
-    attend_narrow<D, G, kRing, KV8, F16>(p, it, smem);
+    attend_narrow<D, G, narrow_ring<D>(), KV8, F16>(p, it, smem);
   } else {
-    if constexpr (WIDE) attend_wide<D, G, KV8, F16>(p, it, smem);
+    if constexpr (HAS_WIDE) attend_wide<D, G, KV8, F16>(p, it, smem);
   }
 }
 
@@ -1063,8 +1078,10 @@ constexpr int kMaxItemBlocks = kMaxSplitKeys / kBlockSize;   // 256 blocks per i
 
 template <int D>
 struct DecodeCfg {
+  // cache blocks in flight per wave (d = 256: one, for registers and LDS)
+  static constexpr int RING = D == 256 ? 1 : kDecodeRing;
   static constexpr int BLK_BYTES = kBlockSize * D * 2;
-  static constexpr int VBUF_BYTES = 4 * 2 * BLK_BYTES;            // 2 V buffers per wave
+  static constexpr int VBUF_BYTES = 4 * RING * BLK_BYTES;         // a V buffer per ring slot
   static constexpr int IDS_OFFSET = VBUF_BYTES;                   // int [4 waves][2][256]
   static constexpr int PREF_OFFSET = IDS_OFFSET + 4 * 2 * kMaxItemBlocks * 4;  // int [S + 1]
   static constexpr int Q0_OFFSET = PREF_OFFSET + (kMaxDecodeSeqs + 1) * 4;   // int [S + 1]
@@ -1293,7 +1310,7 @@ void pa_decode_kernel(FwdParams p) {
   const int tr_key = 4 * h4 + (l16 >> 2);
   const int tr_c_lo = (l16 & 3) >> 1;
   const int tr_half = (l16 & 1) * 8;
-  unsigned char* vbuf0 = smem + wave * 2 * BLK_BYTES;
+  unsigned char* vbuf0 = smem + wave * Cfg::RING * BLK_BYTES;
 
   auto load_ids = [&](const DItem& d, int (&v)[IDL]) {
 #pragma unroll
@@ -1323,7 +1340,7 @@ void pa_decode_kernel(FwdParams p) {
   // buffer loads through a per-block resource; a slot with nothing left to
   // fetch gets a resource of zero records, so its loads return zeros without
   // touching memory while the wait counts stay the same on every path.
-  constexpr int RING = kDecodeRing;
+  constexpr int RING = Cfg::RING;
   raw8 kst[RING][KS];
   raw8 vst[RING][VPL];
   const int blk_extent = kBlockSize * slot_stride * ESZ;    // bytes of one block, all heads
@@ -1355,9 +1372,12 @@ void pa_decode_kernel(FwdParams p) {
   DItem nx2 = after(nxt);
   int ids_v2[IDL];
   load_ids(nx2, ids_v2);
+  // Q of the next item is loaded one item ahead (d = 256: at the switch, for
+  // registers)
+  constexpr bool QPRE = D <= 128;
   u32x4 qB[KS], qB_n[KS];
   load_qb(cur, qB);
-  load_qb(nxt, qB_n);
+  if constexpr (QPRE) load_qb(nxt, qB_n);
   // the first RING blocks of the first item (idle slots load nothing)
 #pragma unroll
   for (int j = 0; j < RING; ++j) issue(cur.kvh, cur.nb > j ? uniform(idsw[j]) : 0, cur.nb > j, j);
@@ -1388,7 +1408,7 @@ void pa_decode_kernel(FwdParams p) {
         // (1) consume slot j: V rows to LDS, scores S^T = K Q^T
         const bool live = b < cur.nb;
         const int kb = (cur.blk0 + b) * kBlockSize;
-        unsigned char* vbuf = vbuf0 + (j & 1) * BLK_BYTES;   // two V buffers per wave
+        unsigned char* vbuf = vbuf0 + j * BLK_BYTES;         // the slot's V buffer
         f32x4 sc = {0.f, 0.f, 0.f, 0.f};
         if (live) {
 #pragma unroll
@@ -1475,9 +1495,13 @@ void pa_decode_kernel(FwdParams p) {
     store_ids(cb ^ 1, ids_v2);
     nx2 = after(nxt);
     load_ids(nx2, ids_v2);
+    if constexpr (QPRE) {
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) qB[ks] = qB_n[ks];
-    load_qb(nxt, qB_n);
+      for (int ks = 0; ks < KS; ++ks) qB[ks] = qB_n[ks];
+      load_qb(nxt, qB_n);
+    } else {
+      load_qb(cur, qB);
+    }
   }
 }
 
@@ -1506,7 +1530,8 @@ __device__ __forceinline__ void merge_store(const MergeParams& p, int64_t row, i
 template <int D, bool F16>
 __global__ __launch_bounds__(256) void pa_merge_rows_kernel(MergeParams p) {
   constexpr int TPR = D / 4;
-  constexpr int RPB = 256 / TPR;
+  constexpr int RPB = 256 / TPR;                     // d = 96: 10 rows, 16 threads idle
+  if ((int)threadIdx.x >= RPB * TPR) return;
   const int64_t row = (int64_t)blockIdx.x * RPB + threadIdx.x / TPR;
   const int64_t nrows = (int64_t)p.total_q * p.num_q_heads;
   if (row >= nrows) return;
@@ -1534,7 +1559,7 @@ __global__ __launch_bounds__(256) void pa_merge_rows_kernel(MergeParams p) {
 template <int D, bool F16>
 __global__ __launch_bounds__(256) void pa_merge_wide_kernel(MergeParams p) {
   constexpr int TPG = D / 4;                 // threads per group (4 outputs each)
-  constexpr int NG = 256 / TPG;              // groups
+  constexpr int NG = 256 / TPG;              // groups (d = 96: 10, 16 threads in none)
   __shared__ float red[NG][D + 4];
   __shared__ float wred[NG];
   __shared__ float mred[4];
@@ -1554,7 +1579,7 @@ __global__ __launch_bounds__(256) void pa_merge_wide_kernel(MergeParams p) {
   M = fmaxf(fmaxf(mred[0], mred[1]), fmaxf(mred[2], mred[3]));
   f32x4 a = {0.f, 0.f, 0.f, 0.f};
   float ws = 0.f;
-  if (M != kNegInf) {
+  if (M != kNegInf && g < NG) {
 #pragma unroll 4
     for (int sg = g; sg < n_part; sg += NG) {
       const float ls = p.ws_lse[sg * nrows + row];
@@ -1564,8 +1589,10 @@ __global__ __launch_bounds__(256) void pa_merge_wide_kernel(MergeParams p) {
       a += w * *reinterpret_cast<const f32x4*>(p.ws_o + (sg * nrows + row) * D + d0);
     }
   }
-  *reinterpret_cast<f32x4*>(&red[g][d0]) = a;
-  if (t % TPG == 0) wred[g] = ws;
+  if (g < NG) {
+    *reinterpret_cast<f32x4*>(&red[g][d0]) = a;
+    if (t % TPG == 0) wred[g] = ws;
+  }
   __syncthreads();
   if (g != 0) return;
   float wt = 0.f;
@@ -1584,7 +1611,8 @@ __global__ __launch_bounds__(256) void pa_merge_wide_kernel(MergeParams p) {
 template <int D, bool F16>
 __global__ __launch_bounds__(256) void pa_merge2_kernel(Merge2Params p) {
   constexpr int TPR = D / 4;
-  constexpr int RPB = 256 / TPR;
+  constexpr int RPB = 256 / TPR;                     // d = 96: 10 rows, 16 threads idle
+  if ((int)threadIdx.x >= RPB * TPR) return;
   constexpr float kLog2e = 1.4426950408889634f;
   const int64_t row = (int64_t)blockIdx.x * RPB + threadIdx.x / TPR;
   if (row >= (int64_t)p.total_q * p.num_q_heads) return;
@@ -1617,10 +1645,15 @@ __global__ __launch_bounds__(256) void pa_merge2_kernel(Merge2Params p) {
 
 template <int D, int G, bool KV8, bool F16>
 hipError_t launch_fwd_t(const FwdParams& p, bool wide, int64_t nwg, hipStream_t stream) {
-  if (wide)
-    hipLaunchKernelGGL((pa_fwd_kernel<D, G, true, KV8, F16>), dim3((unsigned)nwg), dim3(kThreads),
-                       0, stream, p);
-  else
+  if constexpr (D == 64 || D == 128) {
+    if (wide) {
+      hipLaunchKernelGGL((pa_fwd_kernel<D, G, true, KV8, F16>), dim3((unsigned)nwg),
+                         dim3(kThreads), 0, stream, p);
+      return hipGetLastError();
+    }
+  } else if (wide) {
+    return hipErrorInvalidValue;                     // no wide tiles for this head size
+  }
     hipLaunchKernelGGL((pa_fwd_kernel<D, G, false, KV8, F16>), dim3((unsigned)nwg), dim3(kThreads),
                        0, stream, p);
   return hipGetLastError();
@@ -1663,7 +1696,17 @@ hipError_t launch_merge2_t(const Merge2Params& p, int64_t rows, hipStream_t stre
 
 }  // namespace
 
-#define PA_DISPATCH_DG(D_, G_, CALL)                                   \
+// This file is compiled once per head size (-DPA_TU_HEAD_DIM=64, 96, 128 or
+// 256, in parallel); each object defines the launchers of its head size, and
+// the D = 64 object also the head-size independent kernels.
+#ifndef PA_TU_HEAD_DIM
+#error "compile with -DPA_TU_HEAD_DIM=64, 96, 128 or 256"
+#endif
+#define PA_CAT2(a, b) a##b
+#define PA_CAT(a, b) PA_CAT2(a, b)
+#define PA_SFX(name) PA_CAT(name, PA_TU_HEAD_DIM)
+
+#define PA_DISPATCH_G(G_, CALL)                                        \
   switch (G_) {                                                        \
     case 1: { constexpr int GG = 1; CALL; }                            \
     case 2: { constexpr int GG = 2; CALL; }                            \
@@ -1673,76 +1716,62 @@ hipError_t launch_merge2_t(const Merge2Params& p, int64_t rows, hipStream_t stre
     default: break;                                                    \
   }
 
-#define PA_DISPATCH_F(D_, G_, K8_, CALL)                                                        \
-  do {                                                                                          \
-    if (f16) { constexpr bool FF = true; PA_DISPATCH_DG(D_, G_, CALL); }                        \
-    else { constexpr bool FF = false; PA_DISPATCH_DG(D_, G_, CALL); }                           \
+// cache format x element type x group -> one specialization of this head size
+#define PA_DISPATCH(G_, K8_, F16_, CALL)                                              \
+  do {                                                                                \
+    constexpr int DD = PA_TU_HEAD_DIM;                                                \
+    if (K8_) {                                                                        \
+      constexpr bool KK = true;                                                       \
+      if (F16_) { constexpr bool FF = true; PA_DISPATCH_G(G_, CALL); }                \
+      else { constexpr bool FF = false; PA_DISPATCH_G(G_, CALL); }                    \
+    } else {                                                                          \
+      constexpr bool KK = false;                                                      \
+      if (F16_) { constexpr bool FF = true; PA_DISPATCH_G(G_, CALL); }                \
+      else { constexpr bool FF = false; PA_DISPATCH_G(G_, CALL); }                    \
+    }                                                                                 \
   } while (0)
 
-// head_dim x cache format x element type x group -> one specialization
-#define PA_DISPATCH(D_, G_, K8_, CALL)                                                          \
-  do {                                                                                          \
-    if ((D_) == 128) {                                                                          \
-      if (K8_) { constexpr int DD = 128; constexpr bool KK = true; PA_DISPATCH_F(DD, G_, KK, CALL); }  \
-      else { constexpr int DD = 128; constexpr bool KK = false; PA_DISPATCH_F(DD, G_, KK, CALL); }     \
-    } else if ((D_) == 64) {                                                                    \
-      if (K8_) { constexpr int DD = 64; constexpr bool KK = true; PA_DISPATCH_F(DD, G_, KK, CALL); }   \
-      else { constexpr int DD = 64; constexpr bool KK = false; PA_DISPATCH_F(DD, G_, KK, CALL); }      \
-    }                                                                                           \
-  } while (0)
-
-hipError_t launch_decode(const FwdParams& p, int head_dim, int group, bool kv8, bool f16,
-                         int64_t nwg, hipStream_t stream) {
-  PA_DISPATCH(head_dim, group, kv8, return (launch_decode_t<DD, GG, KK, FF>(p, nwg, stream)));
+hipError_t PA_SFX(launch_decode_d)(const FwdParams& p, int group, bool kv8, bool f16, int64_t nwg,
+                                  hipStream_t stream) {
+  PA_DISPATCH(group, kv8, f16, return (launch_decode_t<DD, GG, KK, FF>(p, nwg, stream)));
   return hipErrorInvalidValue;
 }
 
-int decode_blocks_per_cu(int head_dim, int group, bool kv8, bool f16) {
-  PA_DISPATCH(head_dim, group, kv8, return (decode_blocks_per_cu_t<DD, GG, KK, FF>()));
+int PA_SFX(decode_blocks_per_cu_d)(int group, bool kv8, bool f16) {
+  PA_DISPATCH(group, kv8, f16, return (decode_blocks_per_cu_t<DD, GG, KK, FF>()));
   return 0;
 }
 
-bool fwd_supported(int head_dim, int group) {
-  return (head_dim == 64 || head_dim == 128) &&
-         (group == 1 || group == 2 || group == 4 || group == 8 || group == 16);
-}
-
-hipError_t launch_fwd(const FwdParams& p, int head_dim, int group, bool wide, bool kv8, bool f16,
-                      int64_t nwg, hipStream_t stream) {
-  PA_DISPATCH(head_dim, group, kv8, return (launch_fwd_t<DD, GG, KK, FF>(p, wide, nwg, stream)));
+hipError_t PA_SFX(launch_fwd_d)(const FwdParams& p, int group, bool wide, bool kv8, bool f16,
+                               int64_t nwg, hipStream_t stream) {
+  PA_DISPATCH(group, kv8, f16, return (launch_fwd_t<DD, GG, KK, FF>(p, wide, nwg, stream)));
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_rank(const FwdParams& p, hipStream_t stream) {
-  const size_t lds = (size_t)(3 * p.num_seqs + 1 + 65 + 65 + 8) * sizeof(int);
-  hipLaunchKernelGGL(pa_rank_kernel, dim3(1), dim3(kThreads), lds, stream, p);
-  return hipGetLastError();
-}
-
-hipError_t launch_merge2(const Merge2Params& p, int head_dim, bool f16, hipStream_t stream) {
+hipError_t PA_SFX(launch_merge2_d)(const Merge2Params& p, bool f16, hipStream_t stream) {
   const int64_t rows = (int64_t)p.total_q * p.num_q_heads;
   if (rows <= 0) return hipSuccess;
-  if (head_dim == 128)
-    return f16 ? launch_merge2_t<128, true>(p, rows, stream) : launch_merge2_t<128, false>(p, rows, stream);
-  if (head_dim == 64)
-    return f16 ? launch_merge2_t<64, true>(p, rows, stream) : launch_merge2_t<64, false>(p, rows, stream);
-  return hipErrorInvalidValue;
+  return f16 ? launch_merge2_t<PA_TU_HEAD_DIM, true>(p, rows, stream)
+             : launch_merge2_t<PA_TU_HEAD_DIM, false>(p, rows, stream);
 }
 
-hipError_t launch_merge(const MergeParams& p, int head_dim, bool f16, hipStream_t stream) {
+hipError_t PA_SFX(launch_merge_d)(const MergeParams& p, bool f16, hipStream_t stream) {
   const int64_t rows = (int64_t)p.total_q * p.num_q_heads;
   if (rows <= 0) return hipSuccess;
   // many parts per row: a work-group per row; otherwise D/4 threads per row,
   // looping over the row's parts.  An even decode split bounds a row's parts
   // loosely (most rows have one or two): there many rows take the loop form.
   const bool wide = p.n_split > 4 && (!p.even || rows <= 4096);
-  if (head_dim == 128)
-    return f16 ? launch_merge_t<128, true>(p, wide, rows, stream)
-               : launch_merge_t<128, false>(p, wide, rows, stream);
-  if (head_dim == 64)
-    return f16 ? launch_merge_t<64, true>(p, wide, rows, stream)
-               : launch_merge_t<64, false>(p, wide, rows, stream);
-  return hipErrorInvalidValue;
+  return f16 ? launch_merge_t<PA_TU_HEAD_DIM, true>(p, wide, rows, stream)
+             : launch_merge_t<PA_TU_HEAD_DIM, false>(p, wide, rows, stream);
 }
+
+#if PA_TU_HEAD_DIM == 64
+hipError_t launch_rank(const FwdParams& p, hipStream_t stream) {
+  const size_t lds = (size_t)(3 * p.num_seqs + 1 + 65 + 65 + 8) * sizeof(int);
+  hipLaunchKernelGGL(pa_rank_kernel, dim3(1), dim3(kThreads), lds, stream, p);
+  return hipGetLastError();
+}
+#endif
 
 }  // namespace pa
