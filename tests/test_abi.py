@@ -32,7 +32,8 @@ def test_header_functions_are_exported():
 
 
 def test_version_and_status_strings():
-    assert pa.version() == 3
+    import __graft_entry__
+    assert pa.version() == __graft_entry__.header_version() == 3
     for code in range(-9, 1):
         assert pa.lib.pa_status_string(code).decode()
     assert pa.lib.pa_status_string(-100).decode() == "unknown status"
