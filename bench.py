@@ -5,9 +5,10 @@
 
 A step is one call of pa_unified_attention over one synthetic batch (inputs
 resident in HBM).  Prints one JSON line: whole-job throughput in the metric's
-unit, plus the roofline of the forward kernel (algorithmic bytes or flops per
-launch over its average launch duration, from HIP events on the launch stream)
-and the fp64 CPU oracle timed on a bounded sample of the same workload.
+unit, plus the roofline of one call (algorithmic bytes or flops per call over
+the mean GPU time of a call: a pair of HIP events on the launch stream around
+the K back-to-back calls of the timed region) and the fp64 CPU oracle timed on
+a bounded sample of the same workload.
 
 Algorithmic bytes per launch: every valid context token's K and V read once
 (sum_s L_s * Hkv * d * e * 2, e = 2 B for bf16 caches and 1 B for fp8) plus q
@@ -347,20 +348,21 @@ def main():
         call()
     torch.cuda.synchronize()
 
-    # timed region: exactly K steps, per-launch events on the launch stream
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    # timed region: exactly K steps back to back, bracketed by synchronisation
+    # (wall clock: the step rate) and by a pair of HIP events on the launch
+    # stream (GPU time: the mean duration of one call's kernels, without the
+    # host's per-call overhead, which the queue of calls hides)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(args.steps):
-        starts[i].record(stream)
+    ev0.record(stream)
+    for _ in range(args.steps):
         call()
-        ends[i].record(stream)
+    ev1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    per_launch_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
     ms_per_step = wall * 1e3 / args.steps
-    launch_ms = float(np.mean(per_launch_ms))
+    launch_ms = ev0.elapsed_time(ev1) / args.steps
 
     # cold calls: reading 1 GiB between calls evicts the 256 MB Infinity Cache
     # (a read, so no dirty lines are written back during the timed call)
