@@ -41,7 +41,7 @@ struct Plan {
   bool wide;        // launch the specialization with the wide-tile path
   bool lpt;         // grid plan with longest-first unit order
   bool persistent;  // persistent decode kernel with per-sequence split counts
-  bool balanced;    // persistent: part sizes chosen on the device from the total context
+  bool balanced;    // persistent: even split of the block stream, chunks sized on the device
   int64_t num_items;
   int64_t nwg;
   size_t ws_bytes;

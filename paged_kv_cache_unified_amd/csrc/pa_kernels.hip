@@ -3,8 +3,8 @@
 //
 // Operation: softmax(scale * q k^T + mask) v for a varlen batch whose sequences
 // have arbitrary query lengths (decode, chunked prefill, prefill in one grid),
-// keys and values read from a paged cache [num_blocks, 16, Hkv, d] through a
-// block table (page "[Kernel] Unified Triton kernel that doesn't distinguish
+// keys and values read from a paged cache [num_blocks, B, Hkv, d] (B = 16, 32
+// or 64, read as 16-key sub-blocks) through a block table (page "[Kernel] Unified Triton kernel that doesn't distinguish
 // between prefill + decode", PR description; the causal mask is end-aligned so
 // decode queries and prefill chunks share one kernel, page "[Kernel] [V1]
 // Improved performance for V1 Triton (ROCm) backend", section "How is this
@@ -19,22 +19,28 @@
 //    serves G heads (the packing of a kv-head's query heads into the query
 //    dimension that the unified-kernel page adopts).  Tiles of at most 16
 //    packed rows take the narrow path (four waves split the keys), larger ones
-//    the wide path (each wave owns 32 rows, 32x32x16 MFMA).  Wide plans run
-//    their units longest-first.
+//    the wide path (each wave owns 32 rows, 32x32x16 MFMA; d = 64 and 128).
+//    Wide plans run their units longest-first, in the order pa_rank_kernel
+//    sorts them into.
 //  * pa_decode_kernel: persistent decode for batches whose every sequence is
-//    one narrow tile; each wave streams (sequence, key part, kv-head) items.
+//    one narrow tile; each wave streams items of fixed-size key parts, or of
+//    the even split of the batch's block stream.
 //  * pa_merge_*: log-sum-exp merge of key-split partial results.
+//
+// Element types: bf16 or fp16 q / out / caches, or fp8 E4M3 caches; head
+// sizes 64, 96, 128 and 256.
 //
 // Scores are computed transposed, S^T = K Q^T, so each lane holds one packed
 // row's scores and softmax row reductions stay within a lane plus cross-lane
-// steps; P^T (bf16) feeds O^T += V^T P^T straight from the score accumulators,
+// steps; P^T (16-bit) feeds O^T += V^T P^T straight from the score accumulators,
 // with V^T operands from the gfx950 LDS transpose read (ds_read_b64_tr_b16) of
 // row-major V.  Softmax runs online in fp32 in the log2 domain.
 //
-// Key splits: a sequence of L keys has ceil(L / split) parts (balanced on the
-// device in the persistent decode kernel); a part writes its normalised fp32
-// output and log2-domain lse to the workspace and pa_merge combines them.
-// Split boundaries depend on lengths only, so results are deterministic.
+// Key splits: a sequence of L keys has ceil(L / split) parts (or the parts of
+// the even split in the persistent decode kernel); a part writes its
+// normalised fp32 output and log2-domain lse to the workspace and pa_merge
+// combines them.  Split boundaries depend on lengths only, so results are
+// deterministic.
 //
 // Address math for the cache is 64-bit (physical block * block stride), since
 // one cache tensor can exceed 2^31 elements (the int64 cast discussed in the
