@@ -7,7 +7,8 @@
 
 namespace pa {
 
-constexpr int kBlockSize = 16;    // cache block size (tokens) the kernels are built for
+constexpr int kBlockSize = 16;    // keys of a sub-block, the unit the kernels address (cache blocks
+                                  // of 32 or 64 keys are read as 2 or 4 sub-blocks)
 constexpr int kStageKeys = 64;    // keys staged in LDS per pipeline step
 constexpr int kThreads = 256;     // 4 wave64s per work-group
 constexpr int kTileRows = 128;    // packed rows of a wide query tile (32 per wave)
@@ -22,9 +23,9 @@ constexpr int kLptMaxSeqs = 2048;   // longest-first order: LDS tables of 3 ints
 
 // Everything the forward kernel needs, by value.  Strides in elements.
 struct FwdParams {
-  const uint16_t* q;       // bf16 [T, Hq, d]
-  uint16_t* out;           // bf16 [T, Hq, d]
-  const unsigned char* k;  // [NB, B, Hkv, d] cache elements: bf16, or fp8 E4M3 codes
+  const uint16_t* q;       // bf16 or fp16 [T, Hq, d]
+  uint16_t* out;           // q's type [T, Hq, d]
+  const unsigned char* k;  // [NB, B, Hkv, d] cache elements: q's type, or fp8 E4M3 codes
   const unsigned char* v;
   const int32_t* cu_q;     // [S+1]
   const int32_t* seq_k;    // [S]
@@ -60,7 +61,7 @@ struct FwdParams {
   int32_t lpt_units;       // entries of lpt_order (the grid's unit capacity)
   int4* lpt_order;         // [lpt_units] (s, tile, split, -) of each rank, from pa_rank_kernel
   float scale_log2;        // softmax_scale * k_scale * log2(e)
-  float out_scale;         // v_scale (1 for bf16 caches): multiplies every output row
+  float out_scale;         // v_scale (1 for 16-bit caches): multiplies every output row
   float* lse_out;          // optional fp32 [T, Hq] (row stride lse_st): natural-log lse
   int64_t lse_st;
 };
@@ -82,11 +83,11 @@ struct MergeParams {
 
 // Two partial results over disjoint key sets -> one (cascade composition).
 struct Merge2Params {
-  const uint16_t* oa;      // bf16 [T, Hq, d]
+  const uint16_t* oa;      // bf16 or fp16 [T, Hq, d]
   const uint16_t* ob;
   const float* la;         // fp32 [T, Hq], natural-log lse (-inf: no key)
   const float* lb;
-  uint16_t* out;           // bf16 [T, Hq, d]
+  uint16_t* out;           // oa's type [T, Hq, d]
   float* lse;              // optional fp32 [T, Hq]
   int64_t oa_st, oa_sh, ob_st, ob_sh, o_st, o_sh, la_st, lb_st, l_st;
   int32_t total_q, num_q_heads;
