@@ -136,6 +136,11 @@ __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_ex
 
 // A wave-uniform value as a scalar (lets the compiler keep branches scalar).
 __device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+__device__ __forceinline__ int64_t uniform64(int64_t x) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)x);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)x >> 32));
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
 __device__ __forceinline__ void* uniform_ptr(const void* ptr) {
   const uint64_t a = reinterpret_cast<uint64_t>(ptr);
   const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
@@ -721,8 +726,11 @@ struct WideCfg {
   static constexpr int CPR = D / 8;                        // 16-byte chunks per key row
   static constexpr int TENSOR_BYTES = kStageKeys * D * 2;  // K (or V) of one stage
   static constexpr int STAGE_BYTES = 2 * TENSOR_BYTES;
-  static constexpr int IDS_OFFSET = 2 * STAGE_BYTES;
-  static constexpr int SMEM_RAW = IDS_OFFSET + (kMaxSplitKeys / kBlockSize + 4) * 4;
+  static constexpr int OFFS_OFFSET = 2 * STAGE_BYTES;
+  // byte offsets of the unit's sub-blocks, with 4 entries of padding (the
+  // loads of the stage past the end read them, and touch no memory)
+  static constexpr int OFFS_ENTRIES = kMaxSplitKeys / kBlockSize + 4;
+  static constexpr int SMEM_RAW = OFFS_OFFSET + OFFS_ENTRIES * 8;
   static constexpr int SMEM = SMEM_RAW > NarrowCfg<D>::SMEM ? SMEM_RAW : NarrowCfg<D>::SMEM;
   static constexpr int RPI = 64 / CPR;                     // key rows per wave-wide 1 KB load
   static constexpr int CPT = kStageKeys / (4 * RPI);       // loads per thread per tensor
@@ -753,6 +761,14 @@ __device__ __forceinline__ float swap_halves_sum(float x) {
   float a = x, b = x;
   swap_halves(a, b);
   return a + b;
+}
+
+// Transpose read through a restrict pointer.  Inlined, the access carries
+// alias metadata, so the compiler orders it against LDS DMA by the explicit
+// waits and barriers of the caller (as it does the plain LDS reads) instead
+// of waiting for every DMA in flight.
+__device__ __forceinline__ i16x4 lds_read_tr(const PA_LDS bf16x4* __restrict__ a) {
+  return __builtin_bit_cast(i16x4, __builtin_amdgcn_ds_read_tr16_b64_v4bf16((PA_LDS bf16x4*)a));
 }
 
 template <int D, int G, bool KV8, bool F16>
@@ -805,8 +821,13 @@ __device__ __forceinline__ void attend_wide(const FwdParams& p, const Item& it,
   const int nblk = kend > kbeg ? (kend + kBlockSize - 1) / kBlockSize - blk0 : 0;
   const int n_stage = kend > kbeg ? (kend - kbeg + kStageKeys - 1) / kStageKeys : 0;
   const int32_t* btrow = p.bt + (int64_t)it.s * p.bt_stride;
-  int32_t* ids = reinterpret_cast<int32_t*>(smem + Cfg::IDS_OFFSET);
-  for (int i = tid; i < nblk; i += kThreads) ids[i] = sub_block_id(btrow, blk0 + i, p.bshift);
+  const int64_t head_off = (int64_t)it.kvh * D;
+  // byte offset of each sub-block's (kv-head) tile; entries past nblk are
+  // padding (loads past the end have zero records and read nothing)
+  int64_t* offs = reinterpret_cast<int64_t*>(smem + Cfg::OFFS_OFFSET);
+  for (int i = tid; i < 4 * n_stage + 4; i += kThreads)
+    offs[i] = i < nblk ? (sub_block_base(p, sub_block_id(btrow, blk0 + i, p.bshift)) + head_off) * ESZ
+                       : 0;
   __syncthreads();
 
   // ---- one stage of K and V.  bf16: global -> LDS by 16-byte DMA; lane i of
@@ -823,26 +844,22 @@ __device__ __forceinline__ void attend_wide(const FwdParams& p, const Item& it,
                      (KV8 ? ld_p : (ld_p ^ Cfg::fv(ld_r))) * 8) * ESZ;
   const int ld_sk = (ld_r * CPR + (ld_p ^ Cfg::fk(ld_r))) * 16;   // fp8: LDS slot of the chunk
   const int ld_sv = (ld_r * CPR + (ld_p ^ Cfg::fv(ld_r))) * 16;
-  const int64_t head_off = (int64_t)it.kvh * D;
   const uint32_t lds0 = uniform((int)(uint32_t)(uintptr_t)smem) + wave * RPI * CPR * 16;
   raw8 kraw[KV8 ? CPT : 1], vraw[KV8 ? CPT : 1];
+  // wave-uniform copies: the per-block address and bound arithmetic is scalar
+  const int kend_u = uniform(kend), blk0_u = uniform(blk0);
   auto load_stage = [&](int st, int buf) {
-    // the stage's 4 block ids in one read (the table has 4 entries of padding,
-    // so the read one stage past the end stays inside it)
-    const int4 ids4 = *reinterpret_cast<const int4*>(ids + 4 * st);
 #pragma unroll
     for (int u = 0; u < CPT; ++u) {
       // block within the stage: u (d = 128: 4 key rows per load) or 2u + wave/2
       // (d = 64: 8 key rows per load)
-      const bool hi = D == 64 && (wave & 2);
-      const int bi = D == 128 ? u : 2 * u + (hi ? 1 : 0);
-      const int id = uniform(D == 128 ? ids4[u] : (hi ? ids4[(2 * u + 1) & 3] : ids4[(2 * u) & 3]));
+      const int bi = D == 128 ? u : 2 * u + ((wave & 2) ? 1 : 0);
       const int jl = st * (kStageKeys / kBlockSize) + bi;
+      const int64_t boff = uniform64(offs[jl]);
       // keys of the block inside the item (0 past its end: no memory access,
       // the DMA writes zeros)
-      const int valid = min(max(kend - (blk0 + jl) * kBlockSize, 0), kBlockSize);
-      const int nrec = uniform(valid * slot_elems * ESZ);
-      const int64_t boff = (sub_block_base(p, id) + head_off) * ESZ;
+      const int valid = min(max(kend_u - (blk0_u + jl) * kBlockSize, 0), kBlockSize);
+      const int nrec = uniform(valid * p.num_kv_heads * D * ESZ);
       const __amdgpu_buffer_rsrc_t rk =
           __builtin_amdgcn_make_buffer_rsrc(uniform_ptr(p.k + boff), (short)0, nrec, 0x00020000);
       const __amdgpu_buffer_rsrc_t rv =
@@ -962,10 +979,8 @@ __device__ __forceinline__ void attend_wide(const FwdParams& p, const Item& it,
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
           const unsigned char* a = Vb + sl * 16 * CPR * 16 + voff[dt];
-          const i16x4 a0 = __builtin_bit_cast(
-              i16x4, __builtin_amdgcn_ds_read_tr16_b64_v4bf16((PA_LDS bf16x4*)(a)));
-          const i16x4 a1 = __builtin_bit_cast(
-              i16x4, __builtin_amdgcn_ds_read_tr16_b64_v4bf16((PA_LDS bf16x4*)(a + 8 * CPR * 16)));
+          const i16x4 a0 = lds_read_tr((PA_LDS bf16x4*)(a));
+          const i16x4 a1 = lds_read_tr((PA_LDS bf16x4*)(a + 8 * CPR * 16));
           const u32x4 packed = {__builtin_bit_cast(u32x2, a0)[0], __builtin_bit_cast(u32x2, a0)[1],
                                 __builtin_bit_cast(u32x2, a1)[0], __builtin_bit_cast(u32x2, a1)[1]};
           acc[dt] = E::mma32(packed, pb[hs], acc[dt]);
@@ -1532,6 +1547,16 @@ __device__ __forceinline__ void merge_store(const MergeParams& p, int64_t row, i
   *reinterpret_cast<u32x2*>(op) = w;
 }
 
+// One part into the running sums; a part with no key (lse = -inf) adds
+// nothing, whatever its O slot holds (selects, not multiplies by 0).
+__device__ __forceinline__ void merge_add(float ls, f32x4 o, float M, f32x4& a, float& ws) {
+  const bool live = ls != kNegInf;
+  const float w = live ? exp2_fast(ls - M) : 0.f;
+  ws += w;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) a[e] += live ? w * o[e] : 0.f;
+}
+
 // Few parts per row: D/4 threads per row, each loops over the parts.
 template <int D, bool F16>
 __global__ __launch_bounds__(256) void pa_merge_rows_kernel(MergeParams p) {
@@ -1545,17 +1570,17 @@ __global__ __launch_bounds__(256) void pa_merge_rows_kernel(MergeParams p) {
   if (n_part <= 1) return;
   const int d0 = (threadIdx.x % TPR) * 4;
   float M = kNegInf;
+#pragma unroll 4
   for (int sg = 0; sg < n_part; ++sg) M = fmaxf(M, p.ws_lse[sg * nrows + row]);
   f32x4 a = {0.f, 0.f, 0.f, 0.f};
   float ws = 0.f;
   if (M != kNegInf) {
-    for (int sg = 0; sg < n_part; ++sg) {
-      const float ls = p.ws_lse[sg * nrows + row];
-      if (ls == kNegInf) continue;
-      const float w = exp2_fast(ls - M);
-      ws += w;
-      a += w * *reinterpret_cast<const f32x4*>(p.ws_o + (sg * nrows + row) * D + d0);
-    }
+    // loads do not wait on the weights (a part's slot exists for every
+    // sg < n_part), so the parts' loads overlap
+#pragma unroll 4
+    for (int sg = 0; sg < n_part; ++sg)
+      merge_add(p.ws_lse[sg * nrows + row],
+                *reinterpret_cast<const f32x4*>(p.ws_o + (sg * nrows + row) * D + d0), M, a, ws);
   }
   merge_store<F16>(p, row, d0, a, ws, M);
 }
@@ -1587,13 +1612,9 @@ __global__ __launch_bounds__(256) void pa_merge_wide_kernel(MergeParams p) {
   float ws = 0.f;
   if (M != kNegInf && g < NG) {
 #pragma unroll 4
-    for (int sg = g; sg < n_part; sg += NG) {
-      const float ls = p.ws_lse[sg * nrows + row];
-      if (ls == kNegInf) continue;
-      const float w = exp2_fast(ls - M);
-      ws += w;
-      a += w * *reinterpret_cast<const f32x4*>(p.ws_o + (sg * nrows + row) * D + d0);
-    }
+    for (int sg = g; sg < n_part; sg += NG)
+      merge_add(p.ws_lse[sg * nrows + row],
+                *reinterpret_cast<const f32x4*>(p.ws_o + (sg * nrows + row) * D + d0), M, a, ws);
   }
   if (g < NG) {
     *reinterpret_cast<f32x4*>(&red[g][d0]) = a;
