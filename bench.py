@@ -72,9 +72,10 @@ def profile_path(workload, kernel):
     return os.path.join(ROOT, "profiles", f"{kernel}_{workload}.md")
 
 
-def traffic_record(workload):
-    """HBM bytes per launch of the dominant kernel from the committed rocprofv3
-    summary, if its counters were taken on the current kernel sources; else None."""
+def profile_record(workload):
+    """The counter record of the committed rocprofv3 summary for the workload's
+    dominant kernel, if its counters were taken on the current kernel sources;
+    else None."""
     import glob
     for path in sorted(glob.glob(os.path.join(ROOT, "profiles", f"*_{workload}.md"))):
         text = open(path).read()
@@ -83,14 +84,21 @@ def traffic_record(workload):
             continue
         rec = json.loads(text.split(marker, 1)[1].split(" -->", 1)[0])
         if rec.get("workload") == workload and rec.get("source_hash") == source_hash():
-            return rec.get("traffic_bytes_per_launch")
+            return rec
     return None
+
+
+def traffic_record(workload):
+    """HBM bytes per launch of the dominant kernel (profile_record), or None."""
+    rec = profile_record(workload)
+    return rec.get("traffic_bytes_per_launch") if rec else None
 
 
 PROF_COMMANDS = """cd /tmp && export TMPDIR=/tmp
 rocprofv3 --kernel-trace --stats -d $OUT/trace_{w} -o run -- python3 $REPO/bench.py --workload {w} --steps 20 --warmup 5 --no-cpu-baseline --cold 0
 rocprofv3 --pmc FETCH_SIZE -d $OUT/pmc_FETCH_SIZE_{w} -o run -- python3 $REPO/bench.py --workload {w} --steps 3 --warmup 1 --no-cpu-baseline --cold 0
 rocprofv3 --pmc WRITE_SIZE -d $OUT/pmc_WRITE_SIZE_{w} -o run -- python3 $REPO/bench.py --workload {w} --steps 3 --warmup 1 --no-cpu-baseline --cold 0
+rocprofv3 --pmc MfmaUtil MfmaFlopsBF16 LdsBankConflict -d $OUT/pmc_MFMA_{w} -o run -- python3 $REPO/bench.py --workload {w} --steps 3 --warmup 1 --no-cpu-baseline --cold 0
 rocprofv3 --pmc FETCH_SIZE -d $OUT/pmc_FETCH_SIZE_copy -o run -- python3 $REPO/bench.py --calibrate-copy
 rocprofv3 --pmc WRITE_SIZE -d $OUT/pmc_WRITE_SIZE_copy -o run -- python3 $REPO/bench.py --calibrate-copy
 python3 $REPO/bench.py --summarize $OUT --workload {w}"""
@@ -154,11 +162,25 @@ def summarize_profiles(out_dir, workload):
               f"factors {f_scale:.4f} (fetch) and {w_scale:.4f} (write)",
               f"- Scaled: fetched {fetch_bytes / 1e9:.4f} GB, written {write_bytes / 1e9:.4f} GB, "
               f"total {(fetch_bytes + write_bytes) / 1e9:.4f} GB per launch", ""]
+    mfma = {}
+    if glob.glob(os.path.join(out_dir, f"pmc_MFMA_{workload}", "**", "*.db"), recursive=True):
+        for name in ("MfmaUtil", "MfmaFlopsBF16", "LdsBankConflict"):
+            mfma[name] = counter(f"pmc_MFMA_{workload}", name, like)[0]
+        lines += [f"## Matrix cores and LDS of `{kernel}` (--pmc, derived metrics of the box)", "",
+                  f"- MfmaUtil (SQ_VALU_MFMA_BUSY_CYCLES over GRBM_GUI_ACTIVE x SIMDs): "
+                  f"{mfma['MfmaUtil']:.2f} %",
+                  f"- MfmaFlopsBF16 (SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512): "
+                  f"{mfma['MfmaFlopsBF16'] / 1e9:.3f} GFLOP per dispatch (matrix-core work "
+                  f"issued, padding and masked pairs included)",
+                  f"- LdsBankConflict (SQ_LDS_BANK_CONFLICT over conflict-free LDS cycles): "
+                  f"{mfma['LdsBankConflict']:.4f}", ""]
     rec = {"workload": workload, "kernel": kernel, "source_hash": source_hash(),
            "kernel_avg_us": top[3],
            "traffic_bytes_per_launch": int(fetch_bytes + write_bytes),
            "fetch_kib": fetch_k, "write_kib": write_k,
-           "fetch_scale": f_scale, "write_scale": w_scale}
+           "fetch_scale": f_scale, "write_scale": w_scale,
+           "mfma_util_pct": mfma.get("MfmaUtil"), "mfma_flops_bf16": mfma.get("MfmaFlopsBF16"),
+           "lds_bank_conflict": mfma.get("LdsBankConflict")}
     lines.append("<!-- traffic " + json.dumps(rec) + " -->")
     os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
     path = profile_path(workload, kernel)
@@ -426,6 +448,12 @@ def main():
         "roofline": roof,
         "cpu_baseline": None,
     }
+    prof = profile_record(args.workload)
+    if prof and prof.get("mfma_util_pct") is not None:
+        # matrix-core and LDS counters of the same kernel (committed rocprofv3 summary)
+        res["counters"] = {"kernel": prof["kernel"], "mfma_util_pct": round(prof["mfma_util_pct"], 2),
+                           "mfma_flops_bf16_per_launch": prof["mfma_flops_bf16"],
+                           "lds_bank_conflict": prof["lds_bank_conflict"]}
     if not args.no_cpu_baseline:
         print("bench: timing the CPU oracle on a sample", file=sys.stderr, flush=True)
         res["cpu_baseline"] = cpu_baseline(b, unit)
