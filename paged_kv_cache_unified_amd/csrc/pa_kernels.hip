@@ -993,10 +993,13 @@ __device__ __forceinline__ void attend_wide(const FwdParams& p, const Item& it,
   // The other buffer was released by the previous step's barrier; its DMA
   // completes (vmcnt) before this step's barrier.  The loads of the step after
   // the last one have zero records (no memory access) and are never read.
+  // a wave whose 32 rows all lie past the tile's rows (a short tile) only
+  // loads and synchronises: its scores and weights would go nowhere
+  const bool wave_rows = uniform(wave * 32 < it.rows ? 1 : 0) != 0;
   auto step = [&](int st, auto bufc) {
     constexpr int buf = decltype(bufc)::value;
     load_stage(st + 1, buf ^ 1);
-    compute(smem + buf * SB, kbeg + st * kStageKeys);
+    if (wave_rows) compute(smem + buf * SB, kbeg + st * kStageKeys);
     store_stage(buf ^ 1);
     wait_dma();
     __syncthreads();
