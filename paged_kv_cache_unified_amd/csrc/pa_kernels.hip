@@ -794,7 +794,13 @@ __device__ __forceinline__ void attend_wide(const FwdParams& p, const Item& it,
   const int h = lane >> 5;
 
   // ---- rows of this lane
-  const int row = wave * 32 + l32;
+  // A tile of at most 64 rows splits every stage's keys instead: waves w and
+  // w + 2 own the same 32 rows, wave w the first 32 keys of each stage and
+  // wave w + 2 the last 32; the two halves' (m, l, O) merge after the loop.
+  const bool ksplit = it.rows <= 64;
+  const int rw = ksplit ? (wave & 1) : wave;          // 32-row block of this wave
+  const int kh = ksplit ? (wave >> 1) : 0;            // key half (ksplit)
+  const int row = rw * 32 + l32;
   const bool row_ok = row < it.rows;
   const int t_in = row / G;
   const int head = it.kvh * G + row % G;
@@ -815,7 +821,7 @@ __device__ __forceinline__ void attend_wide(const FwdParams& p, const Item& it,
   const int kbeg = it.kbeg, kend = it.kend;
   const int klim = p.causal ? min(kend, it.diag + it.tok0 + t_in + 1) : kend;
   // keys below w_kmin are admissible for every row of this wave (no mask)
-  const int w_kmin = p.causal ? min(kend, it.diag + it.tok0 + (wave * 32) / G + 1) : kend;
+  const int w_kmin = p.causal ? min(kend, it.diag + it.tok0 + (rw * 32) / G + 1) : kend;
 
   const int blk0 = kbeg / kBlockSize;
   const int nblk = kend > kbeg ? (kend + kBlockSize - 1) / kBlockSize - blk0 : 0;
@@ -913,41 +919,52 @@ __device__ __forceinline__ void attend_wide(const FwdParams& p, const Item& it,
   // P^T.  The half-0 softmax overlaps the half-1 score MFMAs and the
   // half-0 P V MFMAs overlap the half-1 softmax.  No branch touches the
   // accumulators except the in-place rescale.
-  auto compute = [&](const unsigned char* Kb, int kst) {
+  // One stage (HALF: only key half kh of it).  S^T for the stage's keys, mask
+  // (only where a row limit falls inside the stage), then per 32-key half:
+  // row max, (rare) rescale, exp, O^T += V^T P^T.  The half-0 softmax
+  // overlaps the half-1 score MFMAs and the half-0 P V MFMAs overlap the
+  // half-1 softmax.  No branch touches the accumulators except the in-place
+  // rescale.
+  auto compute = [&](const unsigned char* Kb, int kst, auto halfc) {
+    constexpr bool HALF = decltype(halfc)::value;
+    constexpr int NKB = HALF ? 1 : 2;                // 32-key halves computed
+    const int kb0 = HALF ? kh : 0;
     const unsigned char* Vb = Kb + TB;
-    f32x16 s[2];
+    f32x16 s[NKB];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int i = 0; i < NKB; ++i)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
+      for (int r = 0; r < 16; ++r) s[i][r] = 0.f;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int i = 0; i < NKB; ++i)
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        const u32x4 a = *reinterpret_cast<const u32x4*>(Kb + kb * 32 * CPR * 16 + koff[ks]);
-        s[kb] = E::mma32(a, qB[ks], s[kb]);
+        const u32x4 a = *reinterpret_cast<const u32x4*>(Kb + (kb0 + i) * 32 * CPR * 16 + koff[ks]);
+        s[i] = E::mma32(a, qB[ks], s[i]);
       }
     // operand reads run 4 ahead of the MFMAs: latency hidden, 16 registers
     __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
 #pragma unroll
-    for (int i = 0; i < 2 * KS - 4; ++i) {
+    for (int i = 0; i < NKB * KS - 4; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one LDS read
     }
     __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
     if (kst + kStageKeys > w_kmin) {
-      const int rel = klim - kst - 4 * h;     // element (kb, r) is key 32kb + 8(r/4) + r%4 + 4h
+      // element (i, r) is key 32 (kb0 + i) + 8(r/4) + r%4 + 4h of the stage
+      const int rel = klim - kst - 4 * h - 32 * kb0;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int i = 0; i < NKB; ++i)
 #pragma unroll
         for (int r = 0; r < 16; ++r)
-          if (32 * kb + 8 * (r >> 2) + (r & 3) >= rel) s[kb][r] = kNegInf;
+          if (32 * i + 8 * (r >> 2) + (r & 3) >= rel) s[i][r] = kNegInf;
     }
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      float mx = s[kb][0];
+    for (int i = 0; i < NKB; ++i) {
+      const int kb = kb0 + i;
+      float mx = s[i][0];
 #pragma unroll
-      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[i][r]);
       mx = swap_halves_max(mx);
       const float mnew = fmaxf(m, mx);
       if (__builtin_amdgcn_ballot_w64(mnew > m + thr)) {
@@ -967,7 +984,7 @@ __device__ __forceinline__ void attend_wide(const FwdParams& p, const Item& it,
       float pr[16];
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        pr[r] = exp2_fast(__builtin_fmaf(s[kb][r], c, -mc));
+        pr[r] = exp2_fast(__builtin_fmaf(s[i][r], c, -mc));
         l += pr[r];
       }
       u32x4 pb[2];                               // P^T operand of slice 2 kb + hs
@@ -995,14 +1012,20 @@ __device__ __forceinline__ void attend_wide(const FwdParams& p, const Item& it,
   // the last one have zero records (no memory access) and are never read.
   // a wave whose 32 rows all lie past the tile's rows (a short tile) only
   // loads and synchronises: its scores and weights would go nowhere
-  const bool wave_rows = uniform(wave * 32 < it.rows ? 1 : 0) != 0;
-  auto step = [&](int st, auto bufc) {
-    constexpr int buf = decltype(bufc)::value;
-    load_stage(st + 1, buf ^ 1);
-    if (wave_rows) compute(smem + buf * SB, kbeg + st * kStageKeys);
-    store_stage(buf ^ 1);
-    wait_dma();
-    __syncthreads();
+  const bool wave_rows = uniform(rw * 32 < it.rows ? 1 : 0) != 0;
+  auto run = [&](auto halfc) {
+    auto step = [&](int st, auto bufc) {
+      constexpr int buf = decltype(bufc)::value;
+      load_stage(st + 1, buf ^ 1);
+      if (wave_rows) compute(smem + buf * SB, kbeg + st * kStageKeys, halfc);
+      store_stage(buf ^ 1);
+      wait_dma();
+      __syncthreads();
+    };
+    for (int st = 0; st < n_stage; st += 2) {
+      step(st, std::integral_constant<int, 0>());
+      if (st + 1 < n_stage) step(st + 1, std::integral_constant<int, 1>());
+    }
   };
 
   if (n_stage > 0) {
@@ -1011,9 +1034,41 @@ __device__ __forceinline__ void attend_wide(const FwdParams& p, const Item& it,
   }
   wait_dma();
   __syncthreads();
-  for (int st = 0; st < n_stage; st += 2) {
-    step(st, std::integral_constant<int, 0>());
-    if (st + 1 < n_stage) step(st + 1, std::integral_constant<int, 1>());
+  if (ksplit) run(std::true_type());
+  else run(std::false_type());
+
+  // ---- key halves: wave w + 2 hands its (m, l, O) to wave w (same rows and
+  // lane layout) through the now idle stage buffers
+  if (ksplit) {
+    constexpr int RS = 16 * DT + 4;                   // floats per lane (16-byte aligned)
+    float* red = reinterpret_cast<float*>(smem) + (wave & 1) * 64 * RS;
+    float* mine = red + lane * RS;
+    if (kh == 1) {
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; r += 4)
+          *reinterpret_cast<f32x4*>(mine + 16 * dt + r) =
+              f32x4{acc[dt][r], acc[dt][r + 1], acc[dt][r + 2], acc[dt][r + 3]};
+      mine[16 * DT] = m;
+      mine[16 * DT + 1] = l;
+    }
+    __syncthreads();
+    if (kh == 1) return;
+    const float m1 = mine[16 * DT], l1 = mine[16 * DT + 1];
+    const float mm = fmaxf(m, m1);
+    const float a0 = m == kNegInf ? 0.f : exp2_fast((m - mm) * c);
+    const float a1 = m1 == kNegInf ? 0.f : exp2_fast((m1 - mm) * c);
+    l = a0 * l + a1 * l1;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int r = 0; r < 16; r += 4) {
+        const f32x4 o = *reinterpret_cast<const f32x4*>(mine + 16 * dt + r);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[dt][r + e] = a0 * acc[dt][r + e] + a1 * o[e];
+      }
+    m = mm;
   }
 
   // ---- epilogue: lanes l and l ^ 32 together hold the row
