@@ -14,6 +14,7 @@ from __future__ import annotations
 
 import ctypes
 import os
+import struct
 from typing import Optional
 
 import torch
@@ -101,25 +102,32 @@ class PaError(RuntimeError):
         super().__init__(f"{STATUS.get(status, status)}: {detail}")
 
 
+# pa_tensor's bytes: data pointer, dtype code, ndim, shape[4], stride[4]
+_PA_TENSOR = struct.Struct("=Qii4q4q")
+_PAD = [(0,) * (4 - n) for n in range(5)]
+
+
 def describe(t: Optional[torch.Tensor]) -> PaTensor:
     """Descriptor of a tensor (data pointer, dtype code, shape, strides)."""
-    d = PaTensor()
     if t is None:
-        return d
-    if t.dim() > 4:
+        return PaTensor()
+    nd = t.dim()
+    if nd > 4:
         raise ValueError("at most 4 dimensions")
-    d.data = t.data_ptr() if t.numel() else (t.data_ptr() or None)
-    d.dtype = _DTYPES.get(t.dtype, 0)
-    d.ndim = t.dim()
-    for i in range(t.dim()):
-        d.shape[i] = t.shape[i]
-        d.stride[i] = t.stride(i)
-    return d
+    pad = _PAD[nd]
+    return PaTensor.from_buffer_copy(_PA_TENSOR.pack(t.data_ptr(), _DTYPES.get(t.dtype, 0), nd,
+                                                     *t.shape, *pad, *t.stride(), *pad))
+
+
+_raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
 
 
 def _stream_handle(device) -> int:
+    """The current HIP stream of the tensor's device (0 for host tensors)."""
     if device.type != "cuda":
         return 0
+    if _raw_stream is not None:
+        return _raw_stream(device.index if device.index is not None else torch.cuda.current_device())
     return torch.cuda.current_stream(device).cuda_stream
 
 
