@@ -98,7 +98,7 @@ PROF_COMMANDS = """cd /tmp && export TMPDIR=/tmp
 rocprofv3 --kernel-trace --stats -d $OUT/trace_{w} -o run -- python3 $REPO/bench.py --workload {w} --steps 20 --warmup 5 --no-cpu-baseline --cold 0
 rocprofv3 --pmc FETCH_SIZE -d $OUT/pmc_FETCH_SIZE_{w} -o run -- python3 $REPO/bench.py --workload {w} --steps 3 --warmup 1 --no-cpu-baseline --cold 0
 rocprofv3 --pmc WRITE_SIZE -d $OUT/pmc_WRITE_SIZE_{w} -o run -- python3 $REPO/bench.py --workload {w} --steps 3 --warmup 1 --no-cpu-baseline --cold 0
-rocprofv3 --pmc MfmaUtil MfmaFlopsBF16 LdsBankConflict -d $OUT/pmc_MFMA_{w} -o run -- python3 $REPO/bench.py --workload {w} --steps 3 --warmup 1 --no-cpu-baseline --cold 0
+rocprofv3 --pmc MfmaUtil MfmaFlopsBF16 LdsBankConflict LdsUtil VALUBusy VmemLatency -d $OUT/pmc_MFMA_{w} -o run -- python3 $REPO/bench.py --workload {w} --steps 3 --warmup 1 --no-cpu-baseline --cold 0
 rocprofv3 --pmc FETCH_SIZE -d $OUT/pmc_FETCH_SIZE_copy -o run -- python3 $REPO/bench.py --calibrate-copy
 rocprofv3 --pmc WRITE_SIZE -d $OUT/pmc_WRITE_SIZE_copy -o run -- python3 $REPO/bench.py --calibrate-copy
 python3 $REPO/bench.py --summarize $OUT --workload {w}"""
@@ -164,7 +164,8 @@ def summarize_profiles(out_dir, workload):
               f"total {(fetch_bytes + write_bytes) / 1e9:.4f} GB per launch", ""]
     mfma = {}
     if glob.glob(os.path.join(out_dir, f"pmc_MFMA_{workload}", "**", "*.db"), recursive=True):
-        for name in ("MfmaUtil", "MfmaFlopsBF16", "LdsBankConflict"):
+        for name in ("MfmaUtil", "MfmaFlopsBF16", "LdsBankConflict", "LdsUtil", "VALUBusy",
+                     "VmemLatency"):
             mfma[name] = counter(f"pmc_MFMA_{workload}", name, like)[0]
         lines += [f"## Matrix cores and LDS of `{kernel}` (--pmc, derived metrics of the box)", "",
                   f"- MfmaUtil (SQ_VALU_MFMA_BUSY_CYCLES over GRBM_GUI_ACTIVE x SIMDs): "
@@ -173,14 +174,22 @@ def summarize_profiles(out_dir, workload):
                   f"{mfma['MfmaFlopsBF16'] / 1e9:.3f} GFLOP per dispatch (matrix-core work "
                   f"issued, padding and masked pairs included)",
                   f"- LdsBankConflict (SQ_LDS_BANK_CONFLICT over conflict-free LDS cycles): "
-                  f"{mfma['LdsBankConflict']:.4f}", ""]
+                  f"{mfma['LdsBankConflict']:.4f}"]
+        if mfma.get("LdsUtil") is not None:
+            lines += [f"- LdsUtil (SQ_LDS_IDX_ACTIVE over busy cycles x CUs): {mfma['LdsUtil']:.2f} %",
+                      f"- VALUBusy (SQ_ACTIVE_INST_VALU over busy cycles x CUs): "
+                      f"{mfma['VALUBusy']:.2f} %",
+                      f"- VmemLatency (in-flight vector memory instructions per issued one, "
+                      f"cycles): {mfma['VmemLatency']:.0f}"]
+        lines.append("")
     rec = {"workload": workload, "kernel": kernel, "source_hash": source_hash(),
            "kernel_avg_us": top[3],
            "traffic_bytes_per_launch": int(fetch_bytes + write_bytes),
            "fetch_kib": fetch_k, "write_kib": write_k,
            "fetch_scale": f_scale, "write_scale": w_scale,
            "mfma_util_pct": mfma.get("MfmaUtil"), "mfma_flops_bf16": mfma.get("MfmaFlopsBF16"),
-           "lds_bank_conflict": mfma.get("LdsBankConflict")}
+           "lds_bank_conflict": mfma.get("LdsBankConflict"), "lds_util_pct": mfma.get("LdsUtil"),
+           "valu_busy_pct": mfma.get("VALUBusy"), "vmem_latency_cycles": mfma.get("VmemLatency")}
     lines.append("<!-- traffic " + json.dumps(rec) + " -->")
     os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
     path = profile_path(workload, kernel)
@@ -454,6 +463,9 @@ def main():
         res["counters"] = {"kernel": prof["kernel"], "mfma_util_pct": round(prof["mfma_util_pct"], 2),
                            "mfma_flops_bf16_per_launch": prof["mfma_flops_bf16"],
                            "lds_bank_conflict": prof["lds_bank_conflict"]}
+        for key in ("lds_util_pct", "valu_busy_pct", "vmem_latency_cycles"):
+            if prof.get(key) is not None:
+                res["counters"][key] = round(prof[key], 2)
     if not args.no_cpu_baseline:
         print("bench: timing the CPU oracle on a sample", file=sys.stderr, flush=True)
         res["cpu_baseline"] = cpu_baseline(b, unit)
