@@ -914,11 +914,6 @@ __device__ __forceinline__ void attend_wide(const FwdParams& p, const Item& it,
   float l = 0.f;                         // this lane's half of the row sum
   const float thr = kThr / c;
 
-  // One stage: S^T for 64 keys, mask (only where a row limit falls inside the
-  // stage), then per 32-key half: row max, (rare) rescale, exp, O^T += V^T
-  // P^T.  The half-0 softmax overlaps the half-1 score MFMAs and the
-  // half-0 P V MFMAs overlap the half-1 softmax.  No branch touches the
-  // accumulators except the in-place rescale.
   // One stage (HALF: only key half kh of it).  S^T for the stage's keys, mask
   // (only where a row limit falls inside the stage), then per 32-key half:
   // row max, (rare) rescale, exp, O^T += V^T P^T.  The half-0 softmax
@@ -1009,9 +1004,9 @@ __device__ __forceinline__ void attend_wide(const FwdParams& p, const Item& it,
   // One pipeline step; `buf` is a constant so LDS offsets fold into the reads.
   // The other buffer was released by the previous step's barrier; its DMA
   // completes (vmcnt) before this step's barrier.  The loads of the step after
-  // the last one have zero records (no memory access) and are never read.
-  // a wave whose 32 rows all lie past the tile's rows (a short tile) only
-  // loads and synchronises: its scores and weights would go nowhere
+  // the last one have zero records (no memory access) and are never read.  A
+  // wave whose 32 rows all lie past the tile's rows (a short tile) only loads
+  // and synchronises: its scores and weights would go nowhere.
   const bool wave_rows = uniform(rw * 32 < it.rows ? 1 : 0) != 0;
   auto run = [&](auto halfc) {
     auto step = [&](int st, auto bufc) {
