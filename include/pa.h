@@ -85,16 +85,18 @@ typedef struct {
                                range holds at least one 64-key stage)          */
   int32_t force_tile;       /* 0: heuristic; 1: one query tile per sequence of
                                at most 16/G tokens (requires max_seqlen_q*G <=
-                               16), persistent decode kernel; 2: 64-row query
-                               tiles, and the per-wave-rows code path even for
-                               tiles of <= 16 rows; 3: as 1 but one work-group
-                               per item on the unified kernel                 */
+                               16), persistent decode kernel; 2: wide query
+                               tiles (128 rows, 32 per wave), and the wide
+                               code path even for tiles of <= 16 rows; 3: as 1
+                               but one work-group per item on the unified
+                               kernel                                         */
   int32_t check_contents;   /* !=0: copy the metadata to the host (synchronous)
                                and return PA_ERR_CONTENT if it breaks the
                                preconditions listed below                      */
   int32_t decode_grid;      /* >0: work-groups of the persistent decode kernel
                                (rounded down to a multiple of 8; default: the
-                               resident work-groups of the device)             */
+                               resident work-groups of the device, or one per
+                               CU when an even split streams 16-bit caches)   */
   float k_scale;            /* fp8 caches: dequantisation scale of k_cache
                                (0 reads as 1; ignored for bf16 caches)        */
   float v_scale;            /* fp8 caches: dequantisation scale of v_cache
