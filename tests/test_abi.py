@@ -194,6 +194,27 @@ def plan_of(b, **opt):
                             opts=pa.options(**opt) if opt else None, num_cus=256)
 
 
+def test_plan_even_split_work_groups():
+    # an even decode split over 16-bit caches launches one work-group per CU
+    # (each wave streams a longer chunk); fp8 caches keep every resident
+    # work-group (two per CU here), and a requested grid is kept
+    b = build_batch("l", np.ones(16, int), np.full(16, 2048), 32, 8, 128, True, 5)
+    p = plan_of(b)
+    assert p["persistent"] == 1 and p["balanced"] == 1 and p["num_workgroups"] == 256
+    b16 = build_batch("l", np.ones(16, int), np.full(16, 2048), 32, 8, 128, True, 5,
+                      kv_dtype="f16", q_dtype="f16")
+    assert plan_of(b16)["num_workgroups"] == 256
+    b8 = build_batch("l", np.ones(16, int), np.full(16, 2048), 32, 8, 128, True, 5,
+                     kv_dtype="fp8_e4m3fn", k_scale=1.0 / 64, v_scale=1.0 / 64)
+    p8 = plan_of(b8)
+    assert p8["balanced"] == 1 and p8["num_workgroups"] == 512
+    assert plan_of(b, decode_grid=384)["num_workgroups"] == 384
+    # fixed parts (a batch that fills every wave) keep the resident grid
+    bd = build_batch("d", np.ones(256, int), np.full(256, 1050), 32, 8, 128, True, 2)
+    pd = plan_of(bd)
+    assert pd["balanced"] == 0 and pd["num_workgroups"] == 512
+
+
 def test_plan_heuristic_on_workload_shapes():
     # decode: persistent kernel, one narrow tile per sequence, no split (2048
     # (sequence, kv-head) items are 4x the 512 resident work-groups)
