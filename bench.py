@@ -1,7 +1,8 @@
 """Benchmark of unified paged attention on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                    [--no-cpu-baseline] [--all]
+                    [--no-cpu-baseline] [--cold N] [--force-tile T] [--force-splits S]
+                    [--decode-grid G] [--cache-write] [--summarize DIR] [--calibrate-copy]
 
 A step is one call of pa_unified_attention over one synthetic batch (inputs
 resident in HBM).  Prints one JSON line: whole-job throughput in the metric's
