@@ -41,7 +41,8 @@
 extern "C" {
 #endif
 
-#define PA_VERSION 3   /* 3: fp16 (PA_F16), block sizes 32 and 64, head sizes 96 and 256 */
+#define PA_VERSION 4   /* 4: pa_workspace_bytes; 3: fp16 (PA_F16), block sizes 32 and 64, head
+                          sizes 96 and 256 */
 
 /* Return codes.  Every failure is reported before anything is launched, with
  * one exception: PA_ERR_HIP, which may also come from the launch itself. */
@@ -163,7 +164,10 @@ typedef struct {
  * Preconditions on device contents (unchecked unless check_contents is set;
  * breaking them is undefined behaviour): cu_seqlens_q[0] == 0, non-decreasing,
  * cu_seqlens_q[S] == T; q_s <= max_seqlen_q; 0 <= L_s <= max_seqlen_k; block
- * ids in range.
+ * ids in range.  The kernels read every context length as
+ * min(max(seqused_k[s], 0), max_seqlen_k), so an overstated seqused_k gives
+ * wrong values for that sequence but never reads the block table past
+ * max_seqlen_k / B entries or writes past the workspace.
  *
  * Ownership: the caller owns every buffer; the library keeps no pointer after
  * return.  This entry point uses a library-owned split workspace (device
@@ -234,11 +238,18 @@ int pa_merge_attention(const pa_tensor* out_a, const pa_tensor* lse_a, const pa_
                        const pa_tensor* lse_b, pa_tensor* out, pa_tensor* lse_out, void* stream);
 
 /*
- * pa_workspace_size — bytes of workspace pa_unified_attention_ex needs for
+ * pa_workspace_bytes — bytes of workspace pa_unified_attention_ex needs for
  * these arguments and options (0 when the batch needs no key split).  Host
  * only: reads descriptors, never device memory.  Returns (size_t)-1 and sets
  * pa_last_error when the arguments are invalid.
  */
+size_t pa_workspace_bytes(const pa_tensor* q, const pa_tensor* k_cache,
+                          const pa_tensor* v_cache, const pa_tensor* out,
+                          const pa_tensor* cu_seqlens_q, const pa_tensor* seqused_k,
+                          const pa_tensor* block_table, int32_t max_seqlen_q,
+                          int32_t max_seqlen_k, const pa_options* opt);
+
+/* pa_workspace_size — the same function under its earlier name. */
 size_t pa_workspace_size(const pa_tensor* q, const pa_tensor* k_cache,
                          const pa_tensor* v_cache, const pa_tensor* out,
                          const pa_tensor* cu_seqlens_q, const pa_tensor* seqused_k,
@@ -267,9 +278,10 @@ int pa_plan_describe(const pa_tensor* q, const pa_tensor* k_cache,
  *               pa_unified_attention;
  *  v_cache      same dtype, shape and strides.  Written in place.
  *  slot_mapping int32 [N], contiguous: token i goes to slot slot_mapping[i] =
- *               physical block * B + position in the block; a negative slot
- *               skips the token.  Slots must be < NB * B and distinct
- *               (unchecked; a repeated slot receives one of its tokens).
+ *               physical block * B + position in the block; a negative slot,
+ *               or one at or past NB * B (outside the cache), skips the token
+ *               (checked on the device).  Slots should be distinct (unchecked;
+ *               a repeated slot receives one of its tokens).
  *  k_scale, v_scale  fp8 caches: the stored code is x / scale (IEEE fp32
  *               division) rounded to the nearest E4M3 value, ties to even,
  *               saturated at +-448 (the format has no infinity), NaN kept;

@@ -69,6 +69,8 @@ _SIGNATURES = {
                                                 ctypes.POINTER(PaOptions), ctypes.c_void_p,
                                                 ctypes.c_size_t, ctypes.c_void_p]),
     "pa_merge_attention": (ctypes.c_int, [_T, _T, _T, _T, _T, _T, ctypes.c_void_p]),
+    "pa_workspace_bytes": (ctypes.c_size_t, [_T, _T, _T, _T, _T, _T, _T, ctypes.c_int32,
+                                             ctypes.c_int32, ctypes.POINTER(PaOptions)]),
     "pa_workspace_size": (ctypes.c_size_t, [_T, _T, _T, _T, _T, _T, _T, ctypes.c_int32,
                                             ctypes.c_int32, ctypes.POINTER(PaOptions)]),
     "pa_plan_describe": (ctypes.c_int, [_T, _T, _T, _T, _T, _T, _T, ctypes.c_int32,
@@ -206,14 +208,18 @@ def merge_attention(out_a, lse_a, out_b, lse_b, out, lse_out=None):
     return out, lse_out
 
 
-def workspace_size(q, k_cache, v_cache, out, cu_seqlens_q, seqused_k, block_table,
-                   max_seqlen_q: int, max_seqlen_k: int, opts: Optional[PaOptions] = None) -> int:
+def workspace_bytes(q, k_cache, v_cache, out, cu_seqlens_q, seqused_k, block_table,
+                    max_seqlen_q: int, max_seqlen_k: int, opts: Optional[PaOptions] = None) -> int:
+    """Bytes of caller workspace ``pa_unified_attention_ex`` needs (0: none)."""
     ds, refs = _descs(q, k_cache, v_cache, out, cu_seqlens_q, seqused_k, block_table)
-    n = lib.pa_workspace_size(*refs, int(max_seqlen_q), int(max_seqlen_k),
-                              ctypes.byref(opts) if opts is not None else None)
+    n = lib.pa_workspace_bytes(*refs, int(max_seqlen_q), int(max_seqlen_k),
+                               ctypes.byref(opts) if opts is not None else None)
     if n == ctypes.c_size_t(-1).value:
         raise PaError(-3, lib.pa_last_error().decode())
     return int(n)
+
+
+workspace_size = workspace_bytes
 
 
 def plan_describe(q, k_cache, v_cache, out, cu_seqlens_q, seqused_k, block_table,

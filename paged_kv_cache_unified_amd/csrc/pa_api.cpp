@@ -8,6 +8,7 @@
 #include <cstdio>
 #include <cstring>
 #include <map>
+#include <memory>
 #include <mutex>
 #include <string>
 #include <vector>
@@ -420,43 +421,58 @@ int check_contents(const Shapes& s, const pa_tensor* cu, const pa_tensor* sk, co
   return PA_OK;
 }
 
+// One workspace per (device, stream): calls on different streams never share
+// split partials; calls on one stream are ordered by the stream.  Each entry
+// has its own lock, which a call holds from the lookup until its kernels are
+// enqueued: a second thread on the same stream that needs a larger buffer
+// waits, and then frees the old one only after the stream has drained, so no
+// enqueued kernel can see its workspace freed.
 struct DeviceWorkspace {
+  std::mutex mu;
   void* ptr = nullptr;
   size_t bytes = 0;
 };
 
-// One workspace per (device, stream): calls on different streams never share
-// split partials; calls on one stream are ordered by the stream.
-int library_workspace(size_t need, hipStream_t stream, void** ptr) {
+DeviceWorkspace* workspace_entry(hipStream_t stream, int* rc) {
   static std::mutex mu;
-  static std::map<std::pair<int, hipStream_t>, DeviceWorkspace> pool;
+  static std::map<std::pair<int, hipStream_t>, std::unique_ptr<DeviceWorkspace>> pool;
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
-  if (e != hipSuccess) return fail(PA_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
-  std::lock_guard<std::mutex> lock(mu);
-  DeviceWorkspace& w = pool[std::make_pair(dev, stream)];
-  if (w.bytes < need) {
-    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
-    if (hipStreamIsCapturing(stream, &cs) == hipSuccess && cs != hipStreamCaptureStatusNone)
-      return fail(PA_ERR_WORKSPACE,
-                  "library workspace must grow to %zu bytes during stream capture; use "
-                  "pa_unified_attention_ex with a caller workspace", need);
-    if (w.ptr) {
-      e = hipDeviceSynchronize();
-      if (e == hipSuccess) e = hipFree(w.ptr);
-      if (e != hipSuccess) return fail(PA_ERR_HIP, "workspace release: %s", hipGetErrorString(e));
-      w.ptr = nullptr;
-      w.bytes = 0;
-    }
-    const size_t grow = std::max(need, w.bytes + w.bytes / 2);
-    e = hipMalloc(&w.ptr, grow);
-    if (e != hipSuccess) {
-      w.ptr = nullptr;
-      return fail(PA_ERR_HIP, "workspace hipMalloc(%zu): %s", grow, hipGetErrorString(e));
-    }
-    w.bytes = grow;
+  if (e != hipSuccess) {
+    *rc = fail(PA_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+    return nullptr;
   }
-  *ptr = w.ptr;
+  std::lock_guard<std::mutex> lock(mu);
+  std::unique_ptr<DeviceWorkspace>& w = pool[std::make_pair(dev, stream)];
+  if (!w) w.reset(new DeviceWorkspace());
+  *rc = PA_OK;
+  return w.get();
+}
+
+// Grows the entry to `need` bytes; the caller holds w->mu.
+int grow_workspace(DeviceWorkspace* w, size_t need, hipStream_t stream) {
+  if (w->bytes >= need) return PA_OK;
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(stream, &cs) == hipSuccess && cs != hipStreamCaptureStatusNone)
+    return fail(PA_ERR_WORKSPACE,
+                "library workspace must grow to %zu bytes during stream capture; use "
+                "pa_unified_attention_ex with a caller workspace", need);
+  hipError_t e;
+  if (w->ptr) {
+    // every kernel that used the old buffer was enqueued on this stream
+    e = hipStreamSynchronize(stream);
+    if (e == hipSuccess) e = hipFree(w->ptr);
+    if (e != hipSuccess) return fail(PA_ERR_HIP, "workspace release: %s", hipGetErrorString(e));
+    w->ptr = nullptr;
+    w->bytes = 0;
+  }
+  const size_t grow = std::max(need, w->bytes + w->bytes / 2);
+  e = hipMalloc(&w->ptr, grow);
+  if (e != hipSuccess) {
+    w->ptr = nullptr;
+    return fail(PA_ERR_HIP, "workspace hipMalloc(%zu): %s", grow, hipGetErrorString(e));
+  }
+  w->bytes = grow;
   return PA_OK;
 }
 
@@ -477,10 +493,13 @@ int validate_lse(const pa_tensor* lse, const Shapes& s, const pa_tensor* q, cons
   return PA_OK;
 }
 
+// Where a call's split workspace comes from.
+enum class WsMode { kLibrary, kCaller };
+
 int run(const pa_tensor* q, const pa_tensor* k, const pa_tensor* v, pa_tensor* out,
         const pa_tensor* lse, const pa_tensor* cu, const pa_tensor* sk, const pa_tensor* bt,
         int32_t max_q, int32_t max_k, float scale, int32_t causal, const pa_options* opt,
-        bool library_ws, void* ws, size_t ws_bytes, void* stream_v) {
+        WsMode ws_mode, void* ws, size_t ws_bytes, void* stream_v) {
   g_last_error.clear();
   Shapes s;
   int rc = validate(q, k, v, out, cu, sk, bt, max_q, max_k, &s);
@@ -497,10 +516,15 @@ int run(const pa_tensor* q, const pa_tensor* k, const pa_tensor* v, pa_tensor* o
   rc = make_plan(s, max_q, max_k, opt, ncu, dbpc, &plan);
   if (rc != PA_OK) return rc;
   hipStream_t stream = reinterpret_cast<hipStream_t>(stream_v);
-  if (library_ws) {
+  std::unique_lock<std::mutex> ws_lock;   // held until the kernels are enqueued
+  if (ws_mode == WsMode::kLibrary) {
     if (plan.ws_bytes) {
-      rc = library_workspace(plan.ws_bytes, stream, &ws);
+      DeviceWorkspace* w = workspace_entry(stream, &rc);
       if (rc != PA_OK) return rc;
+      ws_lock = std::unique_lock<std::mutex>(w->mu);
+      rc = grow_workspace(w, plan.ws_bytes, stream);
+      if (rc != PA_OK) return rc;
+      ws = w->ptr;
     }
   } else if (plan.ws_bytes) {
     if (!ws) return fail(PA_ERR_WORKSPACE, "workspace of %zu bytes required", plan.ws_bytes);
@@ -534,6 +558,7 @@ int run(const pa_tensor* q, const pa_tensor* k, const pa_tensor* v, pa_tensor* o
   p.total_q = (int32_t)s.T;
   p.num_q_heads = (int32_t)s.Hq;
   p.num_kv_heads = (int32_t)s.Hkv;
+  p.max_k = max_k;
   p.tile_tokens = plan.tile_tokens;
   p.num_slots = plan.num_slots;
   p.slots_direct = plan.slots_direct;
@@ -601,7 +626,8 @@ int pa_unified_attention(const pa_tensor* q, const pa_tensor* k_cache, const pa_
                          const pa_tensor* block_table, int32_t max_seqlen_q, int32_t max_seqlen_k,
                          float softmax_scale, int32_t causal, void* stream) {
   return run(q, k_cache, v_cache, out, nullptr, cu_seqlens_q, seqused_k, block_table,
-             max_seqlen_q, max_seqlen_k, softmax_scale, causal, nullptr, true, nullptr, 0, stream);
+             max_seqlen_q, max_seqlen_k, softmax_scale, causal, nullptr, WsMode::kLibrary, nullptr,
+             0, stream);
 }
 
 int pa_unified_attention_ex(const pa_tensor* q, const pa_tensor* k_cache, const pa_tensor* v_cache,
@@ -611,7 +637,7 @@ int pa_unified_attention_ex(const pa_tensor* q, const pa_tensor* k_cache, const 
                             int32_t causal, const pa_options* opt, void* workspace,
                             size_t workspace_bytes, void* stream) {
   return run(q, k_cache, v_cache, out, nullptr, cu_seqlens_q, seqused_k, block_table,
-             max_seqlen_q, max_seqlen_k, softmax_scale, causal, opt, false, workspace,
+             max_seqlen_q, max_seqlen_k, softmax_scale, causal, opt, WsMode::kCaller, workspace,
              workspace_bytes, stream);
 }
 
@@ -627,7 +653,8 @@ int pa_unified_attention_lse(const pa_tensor* q, const pa_tensor* k_cache,
     return fail(PA_ERR_NULL, "lse descriptor is NULL");
   }
   return run(q, k_cache, v_cache, out, lse, cu_seqlens_q, seqused_k, block_table, max_seqlen_q,
-             max_seqlen_k, softmax_scale, causal, opt, workspace == nullptr, workspace,
+             max_seqlen_k, softmax_scale, causal, opt,
+             workspace == nullptr ? WsMode::kLibrary : WsMode::kCaller, workspace,
              workspace_bytes, stream);
 }
 
@@ -705,6 +732,14 @@ size_t pa_workspace_size(const pa_tensor* q, const pa_tensor* k_cache, const pa_
   Plan plan;
   if (make_plan(s, max_seqlen_q, max_seqlen_k, opt, ncu, dbpc, &plan) != PA_OK) return (size_t)-1;
   return plan.ws_bytes;
+}
+
+size_t pa_workspace_bytes(const pa_tensor* q, const pa_tensor* k_cache, const pa_tensor* v_cache,
+                          const pa_tensor* out, const pa_tensor* cu_seqlens_q,
+                          const pa_tensor* seqused_k, const pa_tensor* block_table,
+                          int32_t max_seqlen_q, int32_t max_seqlen_k, const pa_options* opt) {
+  return pa_workspace_size(q, k_cache, v_cache, out, cu_seqlens_q, seqused_k, block_table,
+                           max_seqlen_q, max_seqlen_k, opt);
 }
 
 int pa_plan_describe(const pa_tensor* q, const pa_tensor* k_cache, const pa_tensor* v_cache,
@@ -823,6 +858,7 @@ int pa_cache_write(const pa_tensor* key, const pa_tensor* value, pa_tensor* k_ca
   p.v_sh = value->stride[1];
   p.cache_sb = k_cache->stride[0];
   p.block_size = (int32_t)B;
+  p.num_slots = (int32_t)(NB * B);
   p.num_tokens = (int32_t)N;
   p.slot_elems = (int32_t)(Hkv * D);
   p.chunks_per_token = (int32_t)(Hkv * D / 8);

@@ -67,7 +67,7 @@ __global__ __launch_bounds__(256) void pa_cache_write_kernel(CacheWriteParams p)
     const int tok = (int)(r / p.chunks_per_token);
     const int ch = (int)(r - (int64_t)tok * p.chunks_per_token);
     const int slot = p.slot_mapping[tok];
-    if (slot < 0) continue;
+    if (slot < 0 || slot >= p.num_slots) continue;   // padding token, or a slot outside the cache
     const int head = ch / p.chunks_per_head;
     const int dc = ch - head * p.chunks_per_head;
     const uint16_t* src = (is_v ? p.value : p.key) + (int64_t)tok * (is_v ? p.v_st : p.k_st) +

@@ -42,6 +42,8 @@ struct FwdParams {
   int32_t total_q;
   int32_t num_q_heads;
   int32_t num_kv_heads;
+  int32_t max_k;           // max_seqlen_k: every context length is read as min(seq_k[s], max_k)
+                           // (the plan sizes splits and the workspace from it)
   int32_t tile_tokens;     // tokens per query tile
   int32_t num_slots;       // query-tile slots
   int32_t slots_direct;    // 1: slot index is the sequence index
@@ -103,6 +105,7 @@ struct CacheWriteParams {
   int64_t k_st, k_sh, v_st, v_sh;   // source strides (elements)
   int64_t cache_sb;         // cache stride between physical blocks (elements)
   int32_t block_size;       // slots per block (16, 32 or 64)
+  int32_t num_slots;        // NB * block_size: slots at or past it are skipped like negative ones
   int32_t num_tokens;
   int32_t slot_elems;       // Hkv * d
   int32_t chunks_per_token; // Hkv * d / 8

@@ -212,6 +212,13 @@ __device__ __forceinline__ int64_t sub_block_base(const FwdParams& p, int id) {
   return (int64_t)(id >> p.bshift) * p.kv_sb + (int64_t)(id & ((1 << p.bshift) - 1)) * p.sub_sb;
 }
 
+// Context length of sequence s, clamped to [0, max_seqlen_k]: the plan sized
+// the key splits, the workspace and the block-table reads from max_seqlen_k, so
+// a larger seqused_k (a broken precondition) cannot take a kernel past them.
+__device__ __forceinline__ int context_len(const FwdParams& p, int s) {
+  return min(max(p.seq_k[s], 0), p.max_k);
+}
+
 __device__ __forceinline__ float max_across_groups(float x) {
   // lanes l, l^16, l^32, l^48 hold the same packed row
   x = fmaxf(x, __shfl_xor(x, 16));
@@ -269,7 +276,7 @@ __device__ __forceinline__ bool fill_item(const FwdParams& p, int s, int tile, i
   if (it.tok0 >= it.q_len) return false;            // empty slot (whole work-group)
   it.n_tok = min(p.tile_tokens, it.q_len - it.tok0);
   it.rows = it.n_tok * G;
-  it.L = p.seq_k[s];
+  it.L = context_len(p, s);
   // a sequence has ceil(L / split) parts (at least one): items past them idle
   it.parts = min(max((it.L + p.split_keys - 1) / p.split_keys, 1), p.n_split);
   if (it.sigma >= it.parts) return false;
@@ -344,7 +351,7 @@ __global__ __launch_bounds__(kThreads) void pa_rank_kernel(FwdParams p) {
   int mine = 0;
   for (int s = s0; s < s1; ++s) {
     const int q = p.cu_q[s + 1] - p.cu_q[s];
-    const int L = p.seq_k[s];
+    const int L = context_len(p, s);
     qlen[s] = q;
     klen[s] = L;
     const int parts = min(max((L + p.split_keys - 1) / p.split_keys, 1), p.n_split);
@@ -1247,7 +1254,7 @@ void pa_decode_kernel(FwdParams p) {
   const int s0 = min(S, tid * C), s1 = min(S, s0 + C);
   for (int s = s0; s < s1; ++s) {
     q0t[s] = p.cu_q[s];
-    lent[s] = p.seq_k[s];
+    lent[s] = context_len(p, s);
   }
   if (tid == 0) q0t[S] = p.cu_q[S];
   const int workers = (int)gridDim.x * 4;

@@ -366,3 +366,92 @@ def test_fp8_permutation_poison_and_scale_bit_exact():
     assert torch.equal(bits(o1), bits(o3))
     assert torch.equal(o4.float(), 2.0 * o1.float())
     full_parity(b, o1, "fp8 p/p/s")
+
+
+@pytest.mark.parametrize("causal", [True, False], ids=["causal", "noncausal"])
+def test_wide_tile_sequence_without_keys(causal):
+    """A sequence with queries and no context (L = 0) on a wide tile (40 tokens
+    x G = 4 = 160 packed rows): every row is exactly 0; its neighbour is
+    checked against the oracle."""
+    require_gpu()
+    b = build_batch("nokeys", [40, 33, 1], [0, 33, 70], 16, 4, 128, causal, seed=91, device=DEV)
+    plan = pa.plan_describe(*b.args(b.new_out())[:9])
+    assert plan["tile_rows"] > 16 and plan["persistent"] == 0
+    say(f"wide tile without keys causal={causal}")
+    out = run_pa(b)
+    torch.cuda.synchronize()
+    assert torch.equal(bits(out[:40]), torch.zeros_like(bits(out[:40])))
+    full_parity(b, out, f"no keys causal={causal}")
+
+
+@pytest.mark.parametrize("tile", [0, 2, 3], ids=["plan", "wide", "grid_narrow"])
+def test_context_longer_than_max_seqlen_k_is_clamped(tile):
+    """seqused_k above max_seqlen_k (a broken precondition) is read as
+    max_seqlen_k: the result equals the call with the lengths clamped, bit for
+    bit, and no split partial lands outside the workspace the plan sized."""
+    require_gpu()
+    q_lens = [1, 1, 1, 1] if tile in (0, 3) else [1, 20, 3, 40]
+    b = build_batch("clamp", q_lens, [900, 2500, 3000, 60], 32, 8, 128, True, seed=92,
+                    device=DEV)
+    max_k = 2048
+    clamped = b.seqused_k.clamp(max=max_k)
+    outs = []
+    for sk in (b.seqused_k, clamped):
+        out = torch.full_like(b.q, float("nan"))
+        args = list(b.args(out))
+        args[5] = sk
+        args[8] = max_k
+        opts = pa.options(force_tile=tile)
+        n = pa.workspace_bytes(*args[:9], opts)
+        ws = torch.full((max(n, 1) + 4096,), 0x7F, dtype=torch.uint8, device=DEV)
+        pa.unified_attention(*args, opts=opts, workspace=ws[:max(n, 1)])
+        torch.cuda.synchronize()
+        assert torch.all(ws[max(n, 1):] == 0x7F), "a partial landed past the workspace"
+        outs.append(out)
+    say(f"clamp tile={tile}")
+    assert torch.equal(bits(outs[0]), bits(outs[1]))
+    b.seqused_k = clamped
+    b.k_lens = np.minimum(b.k_lens, max_k)
+    full_parity(b, outs[1], f"clamped tile={tile}")
+
+
+def test_library_workspace_grows_under_two_threads():
+    """Two host threads on one stream call the plain entry point (library
+    workspace) with batches whose split workspaces keep growing; every output
+    equals the single-thread result of the same batch bit for bit."""
+    import threading
+    require_gpu()
+    batches = [build_batch(f"grow{i}", [1] * (4 + 4 * i), [3000 + 700 * i] * (4 + 4 * i), 32, 8,
+                           128, True, seed=93 + i, device=DEV) for i in range(6)]
+    expect = []
+    for b in batches:
+        o = torch.full_like(b.q, float("nan"))
+        n = pa.workspace_bytes(*b.args(o)[:9], pa.options())
+        ws = torch.empty(max(n, 1), dtype=torch.uint8, device=DEV)
+        pa.unified_attention(*b.args(o), opts=pa.options(), workspace=ws)
+        torch.cuda.synchronize()
+        expect.append(o)
+    outs = [[None] * len(batches) for _ in range(2)]
+    errors = []
+
+    def worker(w):
+        try:
+            for rep in range(3):
+                for i in (range(len(batches)) if w == 0 else reversed(range(len(batches)))):
+                    o = torch.full_like(batches[i].q, float("nan"))
+                    pa.unified_attention(*batches[i].args(o))
+                    outs[w][i] = o
+        except Exception as e:   # reported in the main thread
+            errors.append(e)
+
+    say("two threads growing the library workspace")
+    ts = [threading.Thread(target=worker, args=(w,)) for w in range(2)]
+    for t in ts:
+        t.start()
+    for t in ts:
+        t.join()
+    torch.cuda.synchronize()
+    assert not errors, errors
+    for w in range(2):
+        for i, e in enumerate(expect):
+            assert torch.equal(bits(outs[w][i]), bits(e)), (w, i)

@@ -2,8 +2,10 @@
 times (default plan, library workspace).
 
 * Sampled parity: the oracle computes whole sequences picked from the batch
-  (shortest, longest, first, last, prefill chunks and decodes); the GPU output
-  rows of those sequences must meet the tolerance bar.
+  (longest and shortest context first, then the first and last sequence, then
+  prefill chunks and decodes); the GPU output rows of those sequences must
+  meet the tolerance bar.  The long-context batches compare four sequences,
+  the longest (about 250 merged key parts) and the shortest among them.
 * Block-histogram closed form: with q = 0 every admissible key gets weight
   exactly 1, so each output row is the plain mean of V over its admissible
   keys.  Filling V so that key j holds a one-hot vector at position
@@ -41,7 +43,7 @@ PARITY_ONLY = ["decode_256seq_ctx1k_fp8"]
 
 def pick_sequences(b, limit):
     q, k = b.q_lens, b.k_lens
-    picks = [0, len(q) - 1, int(np.argmax(k)), int(np.argmin(k))]
+    picks = [int(np.argmax(k)), int(np.argmin(k)), 0, len(q) - 1]
     if (q > 1).any() and (q == 1).any():
         picks += list(np.nonzero(q > 1)[0][:2]) + list(np.nonzero(q == 1)[0][:2])
     seen = []
@@ -60,7 +62,7 @@ def test_workload_sampled_parity(name):
     out = run_pa(b)
     torch.cuda.synchronize()
     assert torch.isfinite(out.float()).all(), "non-finite output"
-    limit = 2 if name.startswith("long_") else 6
+    limit = 4 if name.startswith("long_") else 6
     seqs = pick_sequences(b, limit)
     say(f"workload {name}: oracle on sequences {seqs}")
     err, frob = sampled_parity(b, out, seqs, name)
