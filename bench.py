@@ -1,15 +1,20 @@
 """Benchmark of unified paged attention on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                    [--no-cpu-baseline] [--cold N] [--force-tile T] [--force-splits S]
-                    [--decode-grid G] [--cache-write] [--summarize DIR] [--calibrate-copy]
+                    [--no-cpu-baseline] [--cold N] [--no-configs] [--config-steps K]
+                    [--config-warmup W] [--config-cold N] [--force-tile T]
+                    [--force-splits S] [--decode-grid G] [--cache-write]
+                    [--summarize DIR] [--calibrate-copy]
 
 A step is one call of pa_unified_attention over one synthetic batch (inputs
 resident in HBM).  Prints one JSON line: whole-job throughput in the metric's
 unit, plus the roofline of one call (algorithmic bytes or flops per call over
 the mean GPU time of a call: a pair of HIP events on the launch stream around
 the K back-to-back calls of the timed region) and the fp64 CPU oracle timed on
-a bounded sample of the same workload.
+a bounded sample of the same workload.  The default run (the headline decode
+workload) also times every other workload of the metric the same way and
+reports each in a "configs" map (µs per call from events and cold calls,
+algorithmic work, bound, achieved rate, roofline fraction, traffic).
 
 Algorithmic bytes per launch: every valid context token's K and V read once
 (sum_s L_s * Hkv * d * e * 2, e = 2 B for bf16 caches and 1 B for fp8) plus q
@@ -96,10 +101,10 @@ def traffic_record(workload):
 
 
 PROF_COMMANDS = """cd /tmp && export TMPDIR=/tmp
-rocprofv3 --kernel-trace --stats -d $OUT/trace_{w} -o run -- python3 $REPO/bench.py --workload {w} --steps 20 --warmup 5 --no-cpu-baseline --cold 0
-rocprofv3 --pmc FETCH_SIZE -d $OUT/pmc_FETCH_SIZE_{w} -o run -- python3 $REPO/bench.py --workload {w} --steps 3 --warmup 1 --no-cpu-baseline --cold 0
-rocprofv3 --pmc WRITE_SIZE -d $OUT/pmc_WRITE_SIZE_{w} -o run -- python3 $REPO/bench.py --workload {w} --steps 3 --warmup 1 --no-cpu-baseline --cold 0
-rocprofv3 --pmc MfmaUtil MfmaFlopsBF16 LdsBankConflict LdsUtil VALUBusy VmemLatency -d $OUT/pmc_MFMA_{w} -o run -- python3 $REPO/bench.py --workload {w} --steps 3 --warmup 1 --no-cpu-baseline --cold 0
+rocprofv3 --kernel-trace --stats -d $OUT/trace_{w} -o run -- python3 $REPO/bench.py --workload {w} --steps 20 --warmup 5 --no-cpu-baseline --no-configs --cold 0
+rocprofv3 --pmc FETCH_SIZE -d $OUT/pmc_FETCH_SIZE_{w} -o run -- python3 $REPO/bench.py --workload {w} --steps 3 --warmup 1 --no-cpu-baseline --no-configs --cold 0
+rocprofv3 --pmc WRITE_SIZE -d $OUT/pmc_WRITE_SIZE_{w} -o run -- python3 $REPO/bench.py --workload {w} --steps 3 --warmup 1 --no-cpu-baseline --no-configs --cold 0
+rocprofv3 --pmc MfmaUtil MfmaFlopsBF16 LdsBankConflict LdsUtil VALUBusy VmemLatency -d $OUT/pmc_MFMA_{w} -o run -- python3 $REPO/bench.py --workload {w} --steps 3 --warmup 1 --no-cpu-baseline --no-configs --cold 0
 rocprofv3 --pmc FETCH_SIZE -d $OUT/pmc_FETCH_SIZE_copy -o run -- python3 $REPO/bench.py --calibrate-copy
 rocprofv3 --pmc WRITE_SIZE -d $OUT/pmc_WRITE_SIZE_copy -o run -- python3 $REPO/bench.py --calibrate-copy
 python3 $REPO/bench.py --summarize $OUT --workload {w}"""
@@ -312,7 +317,14 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cold", type=int, default=20, help="extra cold-cache timed calls")
+    ap.add_argument("--cold", type=int, default=100, help="extra cold-cache timed calls")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="time the headline workload only (no configs map)")
+    ap.add_argument("--config-steps", type=int, default=20,
+                    help="back-to-back calls timed per config workload")
+    ap.add_argument("--config-warmup", type=int, default=5)
+    ap.add_argument("--config-cold", type=int, default=20,
+                    help="cold-cache calls per config workload")
     ap.add_argument("--force-tile", type=int, default=0,
                     help="pa_options.force_tile (0 = heuristic plan)")
     ap.add_argument("--force-splits", type=int, default=0,
@@ -355,17 +367,85 @@ def main():
     torch.cuda.set_device(dev)
     print(f"bench: generating {args.workload}", file=sys.stderr, flush=True)
     b = make_workload(args.workload, device=dev)
+    if args.cache_write:
+        bench_cache_write(pa, b, args, dev)
+        return
+    m = measure(pa, b, args, args.steps, args.warmup, args.cold)
+
+    res = {
+        "metric": METRIC,
+        "value": m["value"],
+        "unit": m["unit"],
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": m["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": m["dtype"],
+        "data": "synthetic",
+        "config": m["config"],
+        "us_per_batch": m["us_per_batch"],
+        "us_per_launch_events": m["us_per_launch_events"],
+        "us_per_launch_cold_p10_p50_p90": m["us_per_launch_cold_p10_p50_p90"],
+        "algorithmic_bytes_per_launch": m["algorithmic_bytes_per_launch"],
+        "algorithmic_flops_per_launch": m["algorithmic_flops_per_launch"],
+        "plan": m["plan"],
+        "roofline": m["roofline"],
+        "cpu_baseline": None,
+    }
+    if m.get("counters"):
+        res["counters"] = m["counters"]
+    if not args.no_cpu_baseline:
+        print("bench: timing the CPU oracle on a sample", file=sys.stderr, flush=True)
+        res["cpu_baseline"] = cpu_baseline(b, m["unit"])
+    del b
+    torch.cuda.empty_cache()
+    if not args.no_configs and args.workload == DEFAULT_WORKLOAD:
+        # every other workload of the metric, timed the same way in this run
+        res["configs"] = {}
+        for name in CONFIG_WORKLOADS:
+            print(f"bench: config {name}", file=sys.stderr, flush=True)
+            cb = make_workload(name, device=dev)
+            cm = measure(pa, cb, args, args.config_steps, args.config_warmup, args.config_cold)
+            res["configs"][name] = {k: cm[k] for k in (
+                "us_per_launch_events", "us_per_launch_cold_p10_p50_p90", "us_per_batch",
+                "algorithmic_bytes_per_launch", "algorithmic_flops_per_launch", "roofline",
+                "dtype", "plan", "counters") if k in cm}
+            del cb
+            torch.cuda.empty_cache()
+    print(json.dumps(res), flush=True)
+
+
+# The workloads timed beside the headline in the default run (the metric's
+# other configurations: the mixed batch, its prefill and decode parts, the 70B
+# TP=2 share, the two long-context batches, and the headline with an fp8 cache)
+CONFIG_WORKLOADS = [
+    "mixed_prefill512x8_decode248",
+    "prefill512x8_only",
+    "decode248_only",
+    "decode_gqa8_64seq_ctx2k_4k",
+    "long_decode_16seq_ctx32k_128k",
+    "long_q16_noncausal_16seq_ctx32k_128k",
+    "decode_256seq_ctx1k_fp8",
+]
+
+
+def measure(pa, b, args, steps, warmup, n_cold):
+    """Times one workload: `steps` back-to-back calls (wall clock and a pair of
+    HIP events on the launch stream), then `n_cold` calls each after a 1 GiB
+    read that evicts the Infinity Cache; returns the bench fields of it."""
+    import torch
+    dev = b.q.device
     out = torch.empty_like(b.q)
     call_args = b.args(out)
     opts, ws = None, None
     if args.force_tile or args.force_splits or args.decode_grid or b.kv_format != "bf16":
         opts = pa.options(force_num_splits=args.force_splits, force_tile=args.force_tile,
                           decode_grid=args.decode_grid, k_scale=b.k_scale, v_scale=b.v_scale)
-        ws = torch.empty(max(1, pa.workspace_size(*call_args[:9], opts)), dtype=torch.uint8,
+        ws = torch.empty(max(1, pa.workspace_bytes(*call_args[:9], opts)), dtype=torch.uint8,
                          device=dev)
-    if args.cache_write:
-        bench_cache_write(pa, b, args, dev)
-        return
     plan = pa.plan_describe(*call_args[:9], opts=opts)
     total_bytes, kv_bytes, flops = algorithmic_work(b)
 
@@ -376,7 +456,7 @@ def main():
             pa.unified_attention(*call_args, opts=opts, workspace=ws)
 
     stream = torch.cuda.current_stream(dev)
-    for _ in range(args.warmup):
+    for _ in range(warmup):
         call()
     torch.cuda.synchronize()
 
@@ -388,20 +468,20 @@ def main():
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     ev0.record(stream)
-    for _ in range(args.steps):
+    for _ in range(steps):
         call()
     ev1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    ms_per_step = wall * 1e3 / args.steps
-    launch_ms = ev0.elapsed_time(ev1) / args.steps
+    ms_per_step = wall * 1e3 / steps
+    launch_ms = ev0.elapsed_time(ev1) / steps
 
     # cold calls: reading 1 GiB between calls evicts the 256 MB Infinity Cache
     # (a read, so no dirty lines are written back during the timed call)
     cold = []
-    if args.cold:
+    if n_cold:
         flush = torch.ones(1 << 28, dtype=torch.float32, device=dev)
-        for _ in range(args.cold):
+        for _ in range(n_cold):
             flush.sum()
             s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             s.record(stream)
@@ -416,32 +496,23 @@ def main():
         achieved = total_bytes / (launch_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                "traffic": traffic_record(args.workload)}
+                "traffic": traffic_record(b.name)}
         value = kv_bytes / (ms_per_step * 1e-3) / 1e12
         unit = "TB/s"
     else:
         achieved = flops / (launch_ms * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": BF16_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4),
-                "traffic": traffic_record(args.workload)}
+                "traffic": traffic_record(b.name)}
         value = flops / (ms_per_step * 1e-3) / 1e12
         unit = "TFLOP/s"
-
     res = {
-        "metric": METRIC,
         "value": round(value, 4),
         "unit": unit,
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 5),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
         "dtype": "bf16" if b.kv_format == "bf16" else "bf16 q/out, fp8 e4m3 KV",
-        "data": "synthetic",
         "config": {
-            "workload": args.workload,
+            "workload": b.name,
             "num_seqs": b.num_seqs, "total_q": b.total_q,
             "context_tokens": int(b.k_lens.sum()), "max_seqlen_q": b.max_seqlen_q,
             "max_seqlen_k": b.max_seqlen_k, "num_q_heads": b.num_q_heads,
@@ -456,9 +527,8 @@ def main():
         "algorithmic_flops_per_launch": flops,
         "plan": plan,
         "roofline": roof,
-        "cpu_baseline": None,
     }
-    prof = profile_record(args.workload)
+    prof = profile_record(b.name)
     if prof and prof.get("mfma_util_pct") is not None:
         # matrix-core and LDS counters of the same kernel (committed rocprofv3 summary)
         res["counters"] = {"kernel": prof["kernel"], "mfma_util_pct": round(prof["mfma_util_pct"], 2),
@@ -467,10 +537,7 @@ def main():
         for key in ("lds_util_pct", "valu_busy_pct", "vmem_latency_cycles"):
             if prof.get(key) is not None:
                 res["counters"][key] = round(prof[key], 2)
-    if not args.no_cpu_baseline:
-        print("bench: timing the CPU oracle on a sample", file=sys.stderr, flush=True)
-        res["cpu_baseline"] = cpu_baseline(b, unit)
-    print(json.dumps(res), flush=True)
+    return res
 
 
 if __name__ == "__main__":
