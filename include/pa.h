@@ -201,6 +201,38 @@ int pa_unified_attention_ex(const pa_tensor* q, const pa_tensor* k_cache,
                             const pa_options* opt, void* workspace,
                             size_t workspace_bytes, void* stream);
 
+/* Bytes of the static device scratch behind pa_unified_attention_noalloc
+ * (one copy per GPU, held until the process ends). */
+#define PA_NOALLOC_SCRATCH_BYTES (64u << 20)
+
+/*
+ * pa_unified_attention_noalloc — pa_unified_attention_ex without any device
+ * allocation, for callers that cannot allocate: code under stream capture,
+ * tight serving loops, harnesses that forbid hipMalloc.  The split workspace
+ * (partial outputs, per-row part counts, the longest-first unit order) lives in
+ * a static device array of PA_NOALLOC_SCRATCH_BYTES per GPU instead of a
+ * caller or library buffer; the launches, kernels and results are those of
+ * pa_unified_attention_ex with the same options.
+ *
+ *  Arguments as for pa_unified_attention_ex (opt may be NULL); there is no
+ *  workspace argument.
+ *  Errors: a batch whose plan needs more workspace than
+ *  PA_NOALLOC_SCRATCH_BYTES (pa_workspace_bytes tells) returns
+ *  PA_ERR_WORKSPACE and launches nothing; opt->check_contents (which copies
+ *  to the host and synchronises) returns PA_ERR_UNSUPPORTED.
+ *  Calls no hipMalloc / hipFree.  The first call on a device looks up that
+ *  device's copy of the array.
+ *  Concurrency: every call on one GPU uses the same array, which keeps the last
+ *  call's contents; calls whose work overlaps on one GPU (other streams or
+ *  threads) race and must be ordered by the caller.
+ */
+int pa_unified_attention_noalloc(const pa_tensor* q, const pa_tensor* k_cache,
+                                 const pa_tensor* v_cache, pa_tensor* out,
+                                 const pa_tensor* cu_seqlens_q, const pa_tensor* seqused_k,
+                                 const pa_tensor* block_table, int32_t max_seqlen_q,
+                                 int32_t max_seqlen_k, float softmax_scale, int32_t causal,
+                                 const pa_options* opt, void* stream);
+
 /*
  * pa_unified_attention_lse — as pa_unified_attention_ex, and also writes each
  * row's log-sum-exp: lse[t, h] = ln sum_j exp(softmax_scale * k_scale * q . k_j)

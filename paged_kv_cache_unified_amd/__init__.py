@@ -23,6 +23,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libpa.so")
 
 PA_BF16, PA_INT32, PA_FP32, PA_FP8_E4M3, PA_F16 = 1, 2, 3, 4, 5
+NOALLOC_SCRATCH_BYTES = 64 << 20    # PA_NOALLOC_SCRATCH_BYTES of include/pa.h
 _DTYPES = {torch.bfloat16: PA_BF16, torch.int32: PA_INT32, torch.float32: PA_FP32,
            torch.float8_e4m3fn: PA_FP8_E4M3, torch.float16: PA_F16}
 
@@ -64,6 +65,10 @@ _SIGNATURES = {
                                                ctypes.c_int32, ctypes.c_float, ctypes.c_int32,
                                                ctypes.POINTER(PaOptions), ctypes.c_void_p,
                                                ctypes.c_size_t, ctypes.c_void_p]),
+    "pa_unified_attention_noalloc": (ctypes.c_int, [_T, _T, _T, _T, _T, _T, _T, ctypes.c_int32,
+                                                    ctypes.c_int32, ctypes.c_float,
+                                                    ctypes.c_int32, ctypes.POINTER(PaOptions),
+                                                    ctypes.c_void_p]),
     "pa_unified_attention_lse": (ctypes.c_int, [_T, _T, _T, _T, _T, _T, _T, _T, ctypes.c_int32,
                                                 ctypes.c_int32, ctypes.c_float, ctypes.c_int32,
                                                 ctypes.POINTER(PaOptions), ctypes.c_void_p,
@@ -177,6 +182,21 @@ def unified_attention(q, k_cache, v_cache, out, cu_seqlens_q, seqused_k, block_t
                                          ctypes.byref(opts) if opts is not None else None,
                                          ws_ptr, ws_bytes, stream)
     _check(rc)
+    return out
+
+
+def unified_attention_noalloc(q, k_cache, v_cache, out, cu_seqlens_q, seqused_k, block_table,
+                              max_seqlen_q: int, max_seqlen_k: int, softmax_scale: float,
+                              causal: bool, *, opts: Optional[PaOptions] = None) -> torch.Tensor:
+    """As ``unified_attention`` through ``pa_unified_attention_noalloc``: the
+    split workspace is the library's static device scratch (no allocation);
+    calls that overlap on one GPU race."""
+    ds, refs = _descs(q, k_cache, v_cache, out, cu_seqlens_q, seqused_k, block_table)
+    stream = ctypes.c_void_p(_stream_handle(q.device))
+    _check(lib.pa_unified_attention_noalloc(*refs, int(max_seqlen_q), int(max_seqlen_k),
+                                            float(softmax_scale), int(bool(causal)),
+                                            ctypes.byref(opts) if opts is not None else None,
+                                            stream))
     return out
 
 

@@ -25,7 +25,7 @@ HIP_FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-function",
 ]
-SOURCES = ["pa_api.cpp", "pa_kernels.hip", "pa_cache_kernels.hip"]
+SOURCES = ["pa_api.cpp", "pa_kernels.hip", "pa_cache_kernels.hip", "pa_noalloc.hip"]
 
 
 def hipcc() -> str:

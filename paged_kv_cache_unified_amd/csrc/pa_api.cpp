@@ -494,7 +494,7 @@ int validate_lse(const pa_tensor* lse, const Shapes& s, const pa_tensor* q, cons
 }
 
 // Where a call's split workspace comes from.
-enum class WsMode { kLibrary, kCaller };
+enum class WsMode { kLibrary, kCaller, kStatic };
 
 int run(const pa_tensor* q, const pa_tensor* k, const pa_tensor* v, pa_tensor* out,
         const pa_tensor* lse, const pa_tensor* cu, const pa_tensor* sk, const pa_tensor* bt,
@@ -525,6 +525,19 @@ int run(const pa_tensor* q, const pa_tensor* k, const pa_tensor* v, pa_tensor* o
       rc = grow_workspace(w, plan.ws_bytes, stream);
       if (rc != PA_OK) return rc;
       ws = w->ptr;
+    }
+  } else if (ws_mode == WsMode::kStatic) {
+    if (opt && opt->check_contents)
+      return fail(PA_ERR_UNSUPPORTED, "check_contents synchronises and copies to the host; "
+                                      "not available without allocation");
+    if (plan.ws_bytes > (size_t)PA_NOALLOC_SCRATCH_BYTES)
+      return fail(PA_ERR_WORKSPACE,
+                  "this batch needs %zu bytes of split workspace; the static scratch holds %zu "
+                  "(use pa_unified_attention_ex with a caller workspace)",
+                  plan.ws_bytes, (size_t)PA_NOALLOC_SCRATCH_BYTES);
+    if (plan.ws_bytes) {
+      const hipError_t e = pa::noalloc_scratch(&ws);
+      if (e != hipSuccess) return fail(PA_ERR_HIP, "static scratch address: %s", hipGetErrorString(e));
     }
   } else if (plan.ws_bytes) {
     if (!ws) return fail(PA_ERR_WORKSPACE, "workspace of %zu bytes required", plan.ws_bytes);
@@ -639,6 +652,17 @@ int pa_unified_attention_ex(const pa_tensor* q, const pa_tensor* k_cache, const 
   return run(q, k_cache, v_cache, out, nullptr, cu_seqlens_q, seqused_k, block_table,
              max_seqlen_q, max_seqlen_k, softmax_scale, causal, opt, WsMode::kCaller, workspace,
              workspace_bytes, stream);
+}
+
+int pa_unified_attention_noalloc(const pa_tensor* q, const pa_tensor* k_cache,
+                                 const pa_tensor* v_cache, pa_tensor* out,
+                                 const pa_tensor* cu_seqlens_q, const pa_tensor* seqused_k,
+                                 const pa_tensor* block_table, int32_t max_seqlen_q,
+                                 int32_t max_seqlen_k, float softmax_scale, int32_t causal,
+                                 const pa_options* opt, void* stream) {
+  return run(q, k_cache, v_cache, out, nullptr, cu_seqlens_q, seqused_k, block_table,
+             max_seqlen_q, max_seqlen_k, softmax_scale, causal, opt, WsMode::kStatic, nullptr, 0,
+             stream);
 }
 
 int pa_unified_attention_lse(const pa_tensor* q, const pa_tensor* k_cache,

@@ -115,6 +115,10 @@ struct CacheWriteParams {
 
 hipError_t launch_cache_write(const CacheWriteParams& p, bool kv8, bool f16, hipStream_t stream);
 
+// Device address of the static scratch (PA_NOALLOC_SCRATCH_BYTES) on the
+// current device; looked up once per device (pa_noalloc.hip).
+hipError_t noalloc_scratch(void** out);
+
 // Launchers (pa_kernels.hip, one object per head size d).  Return the
 // hipError_t of the launch.
 // wide = false launches the narrow-only specialization (every tile <= 16 rows).

@@ -374,3 +374,23 @@ def test_lse_and_merge_validation():
     assert rc_merge(o=torch.zeros(T, Hq, 32, dtype=torch.bfloat16),
                     oa=torch.zeros(T, Hq, 32, dtype=torch.bfloat16),
                     ob=torch.zeros(T, Hq, 32, dtype=torch.bfloat16)) == "PA_ERR_UNSUPPORTED"
+
+
+def test_noalloc_refuses_before_touching_the_device():
+    """pa_unified_attention_noalloc: an empty batch is OK, a plan that needs
+    more workspace than the static scratch and check_contents are refused on
+    the host (no device needed for either)."""
+    b = build_batch("big", [1] * 8, [60000] * 8, 32, 8, 128, True, seed=310, device="cpu")
+    out = b.new_out()
+    opts = pa.options(force_num_splits=1000)
+    assert pa.workspace_bytes(*b.args(out)[:9], opts) > pa.NOALLOC_SCRATCH_BYTES
+    with pytest.raises(pa.PaError) as e:
+        pa.unified_attention_noalloc(*b.args(out), opts=opts)
+    assert e.value.status == -7 and "static scratch" in str(e.value)
+    small = build_batch("small", [1, 1], [100, 200], 32, 8, 128, True, seed=311, device="cpu")
+    with pytest.raises(pa.PaError) as e:
+        pa.unified_attention_noalloc(*small.args(small.new_out()),
+                                     opts=pa.options(check_contents=True))
+    assert e.value.status == -4
+    empty = build_batch("empty", [], [], 32, 8, 128, True, seed=312, device="cpu")
+    pa.unified_attention_noalloc(*empty.args(empty.new_out()))
