@@ -90,7 +90,9 @@ typedef struct {
                                tiles (128 rows, 32 per wave), and the wide
                                code path even for tiles of <= 16 rows; 3: as 1
                                but one work-group per item on the unified
-                               kernel                                         */
+                               kernel; 4: wide tiles of 256 rows on the
+                               eight-wave kernel (two wave groups in opposite
+                               phases; head_dim 64/128, 16-bit caches)        */
   int32_t check_contents;   /* !=0: copy the metadata to the host (synchronous)
                                and return PA_ERR_CONTENT if it breaks the
                                preconditions listed below                      */

@@ -40,6 +40,7 @@ struct Shapes {
 struct Plan {
   int32_t tile_tokens, tile_rows, num_slots, slots_direct, n_split, split_keys;
   bool wide;        // launch the specialization with the wide-tile path
+  bool eight;       // wide plan on the eight-wave kernel (256-row tiles)
   bool lpt;         // grid plan with longest-first unit order
   bool persistent;  // persistent decode kernel with per-sequence split counts
   bool balanced;    // persistent: even split of the block stream, chunks sized on the device
@@ -215,13 +216,15 @@ int make_plan(const Shapes& s, int32_t max_q, int32_t max_k, const pa_options* o
   const bool narrow_fits = mq * G <= pa::kNarrowRows;
   if ((force_tile == 1 || force_tile == 3) && !narrow_fits)
     return fail(PA_ERR_UNSUPPORTED, "force_tile=%d needs max_seqlen_q * G <= 16", force_tile);
-  if (force_tile < 0 || force_tile > 3)
-    return fail(PA_ERR_UNSUPPORTED, "force_tile must be 0, 1, 2 or 3");
+  if (force_tile < 0 || force_tile > 4)
+    return fail(PA_ERR_UNSUPPORTED, "force_tile must be 0, 1, 2, 3 or 4");
   // wide tiles (32 rows per wave, fp32 accumulators of the whole d) exist for
   // d = 64 and 128; other head sizes run every tile on the narrow path
   const bool wide_ok = s.D == 64 || s.D == 128;
-  if (force_tile == 2 && !wide_ok)
-    return fail(PA_ERR_UNSUPPORTED, "force_tile=2 (wide tiles) needs head_dim 64 or 128");
+  if ((force_tile == 2 || force_tile == 4) && !wide_ok)
+    return fail(PA_ERR_UNSUPPORTED, "force_tile=%d (wide tiles) needs head_dim 64 or 128", force_tile);
+  if (force_tile == 4 && s.kv8)
+    return fail(PA_ERR_UNSUPPORTED, "force_tile=4 (eight-wave tiles) needs 16-bit caches");
   const bool narrow = force_tile == 1 || force_tile == 3 || (force_tile == 0 && narrow_fits);
   // (the decode kernel's idle ring slots re-read pool block 0, so the pool
   // must hold at least one block)
@@ -297,7 +300,8 @@ int make_plan(const Shapes& s, int32_t max_q, int32_t max_k, const pa_options* o
     p.num_slots = (int32_t)(s.T / p.tile_tokens + s.S);
   } else {
     p.wide = true;
-    p.tile_tokens = (int32_t)(pa::kTileRows / G);
+    p.eight = force_tile == 4;
+    p.tile_tokens = (int32_t)((p.eight ? pa::kTileRows8 : pa::kTileRows) / G);
     if (mq <= p.tile_tokens) {
       p.slots_direct = 1;
       p.num_slots = (int32_t)s.S;
@@ -604,10 +608,11 @@ int run(const pa_tensor* q, const pa_tensor* k, const pa_tensor* v, pa_tensor* o
     if (e != hipSuccess) return fail(PA_ERR_HIP, "rank launch: %s", hipGetErrorString(e));
   }
   if (plan.nwg > 0) {
-    hipError_t e = plan.persistent
-                       ? pa::launch_decode(p, (int)s.D, (int)s.G, s.kv8, s.f16, plan.nwg, stream)
-                       : pa::launch_fwd(p, (int)s.D, (int)s.G, plan.wide, s.kv8, s.f16, plan.nwg,
-                                        stream);
+    hipError_t e =
+        plan.persistent ? pa::launch_decode(p, (int)s.D, (int)s.G, s.kv8, s.f16, plan.nwg, stream)
+        : plan.eight    ? pa::launch_fwd8(p, (int)s.D, (int)s.G, s.f16, plan.nwg, stream)
+                        : pa::launch_fwd(p, (int)s.D, (int)s.G, plan.wide, s.kv8, s.f16, plan.nwg,
+                                         stream);
     if (e != hipSuccess) return fail(PA_ERR_HIP, "forward launch: %s", hipGetErrorString(e));
   }
   if (plan.n_split > 1) {

@@ -12,6 +12,7 @@ constexpr int kBlockSize = 16;    // keys of a sub-block, the unit the kernels a
 constexpr int kStageKeys = 64;    // keys staged in LDS per pipeline step
 constexpr int kThreads = 256;     // 4 wave64s per work-group
 constexpr int kTileRows = 128;    // packed rows of a wide query tile (32 per wave)
+constexpr int kTileRows8 = 256;   // packed rows of an eight-wave wide tile (32 per wave)
 constexpr int kNarrowRows = 16;   // rows of a narrow (decode) tile
 constexpr int kMaxSplitKeys = 4096;  // keys per split: at most 64 blocks per wave (narrow)
 constexpr int kMaxDecodeSeqs = 2048; // sequences the persistent decode kernel can enumerate
@@ -129,6 +130,8 @@ hipError_t noalloc_scratch(void** out);
                               int64_t num_workgroups, hipStream_t stream);                     \
   hipError_t launch_decode_d##DV(const FwdParams& p, int group, bool kv8, bool f16,             \
                                  int64_t num_workgroups, hipStream_t stream);                  \
+  hipError_t launch_fwd8_d##DV(const FwdParams& p, int group, bool f16, int64_t num_workgroups, \
+                               hipStream_t stream);                                            \
   int decode_blocks_per_cu_d##DV(int group, bool kv8, bool f16);                                \
   hipError_t launch_merge_d##DV(const MergeParams& p, bool f16, hipStream_t stream);            \
   hipError_t launch_merge2_d##DV(const Merge2Params& p, bool f16, hipStream_t stream);
@@ -150,6 +153,12 @@ PA_DECLARE_HEAD_DIM(256)
 inline hipError_t launch_fwd(const FwdParams& p, int head_dim, int group, bool wide, bool kv8,
                              bool f16, int64_t num_workgroups, hipStream_t stream) {
   PA_BY_HEAD_DIM(head_dim, launch_fwd, p, group, wide, kv8, f16, num_workgroups, stream)
+  return hipErrorInvalidValue;
+}
+// Eight-wave grid kernel (wide tiles of 256 rows; d = 64 and 128, 16-bit caches).
+inline hipError_t launch_fwd8(const FwdParams& p, int head_dim, int group, bool f16,
+                              int64_t num_workgroups, hipStream_t stream) {
+  PA_BY_HEAD_DIM(head_dim, launch_fwd8, p, group, f16, num_workgroups, stream)
   return hipErrorInvalidValue;
 }
 inline hipError_t launch_merge(const MergeParams& p, int head_dim, bool f16, hipStream_t stream) {

@@ -154,6 +154,12 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rs, uint32_t voff, 
   __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (PA_LDS void*)(uintptr_t)lds, 16, voff, 0, 0, 0);
 }
 __device__ __forceinline__ void wait_dma() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// Work-group barrier that orders LDS accesses only (this wave's LDS reads and
+// writes have completed; outstanding global loads, LDS DMA included, keep
+// running, unlike __syncthreads, whose fence waits for every memory access)
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
 // x *= s in place (tied operands keep a conditionally rescaled accumulator in
 // its own registers instead of a copy per branch)
 __device__ __forceinline__ void scale_inplace(float& x, float s) {
@@ -472,13 +478,13 @@ __device__ __forceinline__ void load_q(const FwdParams& p, const Item& it, int r
   }
 }
 
-// Shared-memory budgets.
-template <int D>
+// Shared-memory budgets (NW: waves of the work-group).
+template <int D, int NW = 4>
 struct NarrowCfg {
   static constexpr int BLK_BYTES = kBlockSize * D * 2;
-  static constexpr int VBUF_BYTES = 4 * 2 * BLK_BYTES;            // 2 V buffers per wave
+  static constexpr int VBUF_BYTES = NW * 2 * BLK_BYTES;           // 2 V buffers per wave
   static constexpr int RED_STRIDE = D + 4;                        // floats per merged row
-  static constexpr int RED_BYTES = (2 * 64 + 4 * 16 * RED_STRIDE) * 4;
+  static constexpr int RED_BYTES = (2 * 16 * NW + NW * 16 * RED_STRIDE) * 4;
   static constexpr int SMEM = VBUF_BYTES > RED_BYTES ? VBUF_BYTES : RED_BYTES;
 };
 
@@ -486,7 +492,7 @@ struct NarrowCfg {
 // Narrow tiles (<= 16 packed rows: decode steps, short chunks).
 //
 // All 16 columns of one MFMA tile hold the tile's rows in every wave; wave w
-// owns the item's cache blocks w, w+4, w+8, ... and streams them on its own,
+// of the NW waves owns the item's cache blocks w, w+NW, ... and streams them on its own,
 // with no work-group barrier until the final merge.  Each wave keeps a ring of
 // P blocks in flight in registers: K lands directly in the A-operand layout of
 // S^T = K Q^T (lane: key l16, d-chunk h4 + 4 ks), V in natural row order and
@@ -494,14 +500,14 @@ struct NarrowCfg {
 // ids of the wave's (at most 64) blocks are fetched once into one VGPR and
 // read per block with readlane, so no KV load waits on a block-table load.
 // ---------------------------------------------------------------------------
-template <int D, int G, int P, bool KV8, bool F16>
+template <int D, int G, int P, bool KV8, bool F16, int NW = 4>
 __device__ __forceinline__ void attend_narrow(const FwdParams& p, const Item& it,
                                               unsigned char* smem) {
   using E = Elem<F16>;
   constexpr int ESZ = Kv<KV8>::ESZ;
   using raw8 = typename Kv<KV8>::raw8;
   using Lay = Layout<D>;
-  using Cfg = NarrowCfg<D>;
+  using Cfg = NarrowCfg<D, NW>;
   constexpr int CPR = Lay::CPR;
   constexpr int BLK_BYTES = Lay::BLK_BYTES;
   constexpr int KS = D / 32;
@@ -520,10 +526,10 @@ __device__ __forceinline__ void attend_narrow(const FwdParams& p, const Item& it
 
   const int blk0 = it.kbeg / kBlockSize;
   const int nblk = it.kend > it.kbeg ? (it.kend + kBlockSize - 1) / kBlockSize - blk0 : 0;
-  const int nb = nblk > wave ? (nblk - wave + 3) / 4 : 0;     // <= 64: split_keys <= 4096
+  const int nb = nblk > wave ? (nblk - wave + NW - 1) / NW : 0;   // <= 64: split_keys <= 4096
   const int32_t* btrow = p.bt + (int64_t)it.s * p.bt_stride;
   int ids = 0;
-  if (lane < nb) ids = sub_block_id(btrow, blk0 + wave + 4 * lane, p.bshift);
+  if (lane < nb) ids = sub_block_id(btrow, blk0 + wave + NW * lane, p.bshift);
 
   const int slot_stride = p.num_kv_heads * D;
   const unsigned char* kbase = p.k + (int64_t)it.kvh * D * ESZ;
@@ -566,7 +572,7 @@ __device__ __forceinline__ void attend_narrow(const FwdParams& p, const Item& it
     for (int j = 0; j < P; ++j) {
       const int i = i0 + j;
       if (i < nb) {
-        const int kb = (blk0 + wave + 4 * i) * kBlockSize;
+        const int kb = (blk0 + wave + NW * i) * kBlockSize;
         unsigned char* vbuf = vbuf0 + (i & 1) * BLK_BYTES;
 #pragma unroll
         for (int u = 0; u < VPL; ++u)
@@ -624,12 +630,12 @@ __device__ __forceinline__ void attend_narrow(const FwdParams& p, const Item& it
     }
   }
 
-  // merge the four waves' states of the same 16 rows
+  // merge the NW waves' states of the same 16 rows
   l = sum_across_groups(l);
   __syncthreads();                        // every wave is done with its V buffers
   float* red_m = reinterpret_cast<float*>(smem);
-  float* red_l = red_m + 64;
-  float* red_o = red_m + 128;             // [wave][row][RED_STRIDE]
+  float* red_l = red_m + 16 * NW;
+  float* red_o = red_m + 32 * NW;         // [wave][row][RED_STRIDE]
   constexpr int RS = Cfg::RED_STRIDE;
   if (h4 == 0) {
     red_m[wave * 16 + l16] = m;
@@ -644,16 +650,16 @@ __device__ __forceinline__ void attend_narrow(const FwdParams& p, const Item& it
   const int n = tid >> 4;
   const int d0 = (tid & 15) * DPER;
   if (n >= it.rows) return;
-  float mw[4], M = kNegInf;
+  float mw[NW], M = kNegInf;
 #pragma unroll
-  for (int w = 0; w < 4; ++w) {
+  for (int w = 0; w < NW; ++w) {
     mw[w] = red_m[w * 16 + n];
     M = fmaxf(M, mw[w]);
   }
   const float M_use = M == kNegInf ? 0.f : M;
-  float wt[4], Ls = 0.f;
+  float wt[NW], Ls = 0.f;
 #pragma unroll
-  for (int w = 0; w < 4; ++w) {
+  for (int w = 0; w < NW; ++w) {
     wt[w] = exp2_fast(mw[w] - M_use);
     Ls += wt[w] * red_l[w * 16 + n];
   }
@@ -664,7 +670,7 @@ __device__ __forceinline__ void attend_narrow(const FwdParams& p, const Item& it
   for (int e = 0; e < DPER; e += 2) {
     f32x2 a = {0.f, 0.f};
 #pragma unroll
-    for (int w = 0; w < 4; ++w)
+    for (int w = 0; w < NW; ++w)
       a += wt[w] * *reinterpret_cast<const f32x2*>(red_o + (w * 16 + n) * RS + d0 + e);
     o[e] = a[0] * inv;
     o[e + 1] = a[1] * inv;
@@ -1106,9 +1112,389 @@ __device__ __forceinline__ void attend_wide(const FwdParams& p, const Item& it,
   }
 }
 
+// ---------------------------------------------------------------------------
+// Eight-wave wide tiles (up to 256 packed rows; d = 64 and 128; 16-bit caches).
+//
+// Waves 0-3 (group A) and 4-7 (group B) each own 32 rows, and waves w and w + 4
+// share SIMD w.  The two groups run in opposite phases, half a stage apart,
+// with a work-group barrier at every half-step: while one group issues its
+// MFMA block (P V of the previous stage and S^T = K Q^T of the current one)
+// the other computes the softmax of its last scores, so every SIMD has a
+// matrix-core stream and a vector-ALU stream from two different waves.
+//
+//   half-step 2t    : A  P V(t-1), S(t)     B  softmax(t-1)
+//   half-step 2t+1  : A  softmax(t)         B  P V(t-1), S(t)
+//
+// Stage t's K is read at half-steps 2t and 2t+1, its V at 2t+2 and 2t+3.  K
+// and V stages go global -> LDS by 16-byte DMA into a ring of four stage
+// buffers, issued two stages (four half-steps) ahead, at even half-steps into
+// the buffer stage t - 2 released; each wave waits for its own part of the
+// stage needed next (vmcnt) before the barrier that publishes it.  The
+// softmax of a stage takes the max over all 64 keys first, then moves the
+// reference (rescaling O and l) at most once, so both halves' weights share
+// one reference.  Row and key layouts are those of the four-wave path.
+// ---------------------------------------------------------------------------
 // cache blocks in flight per wave on the narrow path (d = 256: one, for registers)
 template <int D>
 constexpr int narrow_ring() { return D == 256 ? 1 : 2; }
+
+constexpr int kWide8Threads = 512;
+
+template <int D>
+struct Wide8Cfg {
+  static constexpr int NW = 8;
+  static constexpr int NBUF = 4;                            // stage buffers in the ring
+  static constexpr int AHEAD = 2;                           // stages loaded ahead of use
+  static constexpr int CPR = D / 8;
+  static constexpr int TENSOR_BYTES = kStageKeys * D * 2;
+  static constexpr int STAGE_BYTES = 2 * TENSOR_BYTES;     // K, then V
+  static constexpr int OFFS_OFFSET = NBUF * STAGE_BYTES;
+  // sub-block byte offsets of the unit; the loads of the stages past the end
+  // read padding entries (and touch no memory)
+  static constexpr int OFFS_ENTRIES = kMaxSplitKeys / kBlockSize + 4 * (AHEAD + 1);
+  static constexpr int SMEM_RAW = OFFS_OFFSET + OFFS_ENTRIES * 8;
+  static constexpr int SMEM = SMEM_RAW > NarrowCfg<D, 8>::SMEM ? SMEM_RAW : NarrowCfg<D, 8>::SMEM;
+  static constexpr int RPI = 64 / CPR;                      // key rows per wave-wide 1 KB DMA
+  static constexpr int DPW = kStageKeys / (NW * RPI);       // DMAs per wave per tensor per stage
+};
+
+template <int D, int G, bool F16>
+__device__ __forceinline__ void attend_wide8(const FwdParams& p, const Item& it,
+                                             unsigned char* smem) {
+  using E = Elem<F16>;
+  using Cfg = Wide8Cfg<D>;
+  using WC = WideCfg<D>;                 // LDS chunk swizzles
+  constexpr int CPR = Cfg::CPR;
+  constexpr int KS = D / 16;             // contraction steps of S^T = K Q^T
+  constexpr int DT = D / 32;             // 32-wide d tiles of O^T
+  constexpr int TB = Cfg::TENSOR_BYTES;
+  constexpr int SB = Cfg::STAGE_BYTES;
+  constexpr int RPI = Cfg::RPI;
+  constexpr int DPW = Cfg::DPW;
+  constexpr int NBUF = Cfg::NBUF;
+  constexpr int NW = Cfg::NW;
+  constexpr float kThr = 8.f;            // log2 headroom before the reference max moves
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = uniform(tid >> 6);
+  const int grp = wave >> 2;             // 0: group A, 1: group B
+  const int l32 = lane & 31;
+  const int h = lane >> 5;
+
+  const int row = wave * 32 + l32;
+  const bool row_ok = row < it.rows;
+  const int t_in = row / G;
+  const int head = it.kvh * G + row % G;
+  const float c = fmaxf(fabsf(p.scale_log2), 1e-30f);
+  const uint32_t qflip = p.scale_log2 < 0.f ? 0x80008000u : 0u;
+  u32x4 qB[KS];                          // B operand of S^T: d = 16 ks + 8 h + e
+  {
+    const uint16_t* qp = p.q + (int64_t)(it.q0 + it.tok0 + (row_ok ? t_in : 0)) * p.q_st +
+                         (int64_t)head * p.q_sh + 8 * h;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (row_ok) v = *reinterpret_cast<const u32x4*>(qp + 16 * ks);
+      v ^= qflip;
+      qB[ks] = v;
+    }
+  }
+  const int kbeg = it.kbeg, kend = it.kend;
+  const int klim = p.causal ? min(kend, it.diag + it.tok0 + t_in + 1) : kend;
+  // keys below w_kmin are admissible for every row of this wave (no mask);
+  // keys at or past w_kend are admissible for none of them
+  const bool wave_rows = wave * 32 < it.rows;
+  const int w_kmin = p.causal ? min(kend, it.diag + it.tok0 + (wave * 32) / G + 1) : kend;
+  const int w_last = min(wave * 32 + 31, it.rows - 1);
+  const int w_kend = !wave_rows ? kbeg : (p.causal ? min(kend, it.diag + it.tok0 + w_last / G + 1) : kend);
+  const int n_stage = kend > kbeg ? (kend - kbeg + kStageKeys - 1) / kStageKeys : 0;
+  const int w_nst = uniform(w_kend > kbeg ? (w_kend - kbeg + kStageKeys - 1) / kStageKeys : 0);
+
+  const int blk0 = kbeg / kBlockSize;
+  const int nblk = kend > kbeg ? (kend + kBlockSize - 1) / kBlockSize - blk0 : 0;
+  const int32_t* btrow = p.bt + (int64_t)it.s * p.bt_stride;
+  const int64_t head_off = (int64_t)it.kvh * D;
+  int64_t* offs = reinterpret_cast<int64_t*>(smem + Cfg::OFFS_OFFSET);
+  for (int i = tid; i < 4 * (n_stage + Cfg::AHEAD + 1); i += kWide8Threads)
+    offs[i] = i < nblk ? (sub_block_base(p, sub_block_id(btrow, blk0 + i, p.bshift)) + head_off) * 2
+                       : 0;
+  __syncthreads();
+
+  // ---- DMA of one stage: DPW 1 KB loads per tensor per wave.  Load u of wave
+  // w covers key rows r0 = (u NW + w) RPI .. + RPI; lane i fetches the chunk
+  // the swizzled layout keeps at LDS slot i % CPR of row r0 + i / CPR.
+  const int slot_elems = p.num_kv_heads * D;
+  int ld_gk[DPW], ld_gv[DPW];
+#pragma unroll
+  for (int u = 0; u < DPW; ++u) {
+    const int r = (u * NW + wave) * RPI + lane / CPR;
+    const int sl = lane % CPR;
+    ld_gk[u] = ((r % kBlockSize) * slot_elems + (sl ^ WC::fk(r)) * 8) * 2;
+    ld_gv[u] = ((r % kBlockSize) * slot_elems + (sl ^ WC::fv(r)) * 8) * 2;
+  }
+  const uint32_t lds0 = uniform((int)(uint32_t)(uintptr_t)smem);
+  const int kend_u = uniform(kend), blk0_u = uniform(blk0);
+  // stage st into ring buffer BUF (st % NBUF, a constant at every call site)
+  auto issue_stage = [&](int st, auto bufc) {
+    constexpr int buf = decltype(bufc)::value;
+#pragma unroll
+    for (int u = 0; u < DPW; ++u) {
+      const int r0 = (u * NW + wave) * RPI;
+      const int jl = st * (kStageKeys / kBlockSize) + r0 / kBlockSize;
+      const int64_t boff = uniform64(offs[jl]);
+      const int valid = min(max(kend_u - (blk0_u + jl) * kBlockSize, 0), kBlockSize);
+      const int nrec = uniform(valid * slot_elems * 2);
+      const __amdgpu_buffer_rsrc_t rk =
+          __builtin_amdgcn_make_buffer_rsrc(uniform_ptr(p.k + boff), (short)0, nrec, 0x00020000);
+      const __amdgpu_buffer_rsrc_t rv =
+          __builtin_amdgcn_make_buffer_rsrc(uniform_ptr(p.v + boff), (short)0, nrec, 0x00020000);
+      const uint32_t dst = lds0 + buf * SB + r0 * CPR * 16;
+      dma16(rk, ld_gk[u], dst);
+      dma16(rv, ld_gv[u], dst + TB);
+    }
+  };
+
+  // ---- per-lane LDS read offsets (within a stage buffer)
+  int koff[KS];                          // K operand: key row l32 (+32 kb), chunk 2 ks + h
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) koff[ks] = (l32 * CPR + ((2 * ks + h) ^ WC::fk(l32))) * 16;
+  const int j16 = lane & 15;
+  const int tr_row = 4 * h + (j16 >> 2);
+  int voff[DT];                          // V^T operand: transpose read of 4 rows x 16 d
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) {
+    const int chunk = 4 * dt + 2 * ((lane >> 4) & 1) + ((j16 & 3) >> 1);
+    voff[dt] = TB + (tr_row * CPR + (chunk ^ WC::fv(tr_row))) * 16 + 8 * (j16 & 1);
+  }
+
+  f32x16 acc[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[dt][r] = 0.f;
+  float m = kNegInf;                     // reference max (raw score units)
+  float l = 0.f;                         // this lane's half of the row sum
+  const float thr = kThr / c;
+  f32x16 sc[2];                          // S^T of the stage, from the MFMA block to the softmax
+  u32x4 pb[4];                           // P^T operands of the stage's four 16-key slices
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sc[i][r] = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) pb[i] = u32x4{0u, 0u, 0u, 0u};
+
+  // MFMA block: O^T += V^T P^T of the previous stage (if pv), then S^T = K Q^T
+  // of this stage (if s).  Consecutive MFMAs of a product alternate between
+  // independent accumulators (the d tiles of O^T, the two score halves); the
+  // products run one after the other, so the scores and the P^T operands are
+  // never live at the same time.
+  constexpr int NSTEP = 4 * DT;          // == 2 KS: MFMAs of each product per stage
+  auto pv_operand = [&](const unsigned char* Vb, int j) -> u32x4 {
+    const int sl = j / DT, dt = j % DT;
+    const unsigned char* a = Vb + sl * 16 * CPR * 16 + voff[dt];
+    const i16x4 a0 = lds_read_tr((PA_LDS bf16x4*)(a));
+    const i16x4 a1 = lds_read_tr((PA_LDS bf16x4*)(a + 8 * CPR * 16));
+    return u32x4{__builtin_bit_cast(u32x2, a0)[0], __builtin_bit_cast(u32x2, a0)[1],
+                 __builtin_bit_cast(u32x2, a1)[0], __builtin_bit_cast(u32x2, a1)[1]};
+  };
+  auto k_operand = [&](const unsigned char* Kb, int j) -> u32x4 {
+    const int i = j & 1, ks = j >> 1;    // score half i, contraction step ks
+    return *reinterpret_cast<const u32x4*>(Kb + i * 32 * CPR * 16 + koff[ks]);
+  };
+  auto zero_scores = [&]() {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sc[i][r] = 0.f;
+  };
+  // KBUF: ring buffer of stage t (its K); stage t - 1 (its V) is the one before
+  auto mfma_block = [&](auto kbufc, bool do_s, bool do_pv) {
+    constexpr int KBUF = decltype(kbufc)::value;
+    const unsigned char* Kb = smem + KBUF * SB;
+    const unsigned char* Vb = smem + ((KBUF + NBUF - 1) % NBUF) * SB;
+    // each product's operand reads run LA steps ahead of its MFMAs (source
+    // order is issue order)
+    constexpr int LA = 4;
+    if (do_pv) {
+      u32x4 win[LA];
+#pragma unroll
+      for (int j = 0; j < LA; ++j) win[j] = pv_operand(Vb, j);
+#pragma unroll
+      for (int j = 0; j < NSTEP; ++j) {
+        const u32x4 cur = win[j % LA];
+        if (j + LA < NSTEP) win[j % LA] = pv_operand(Vb, j + LA);
+        acc[j % DT] = E::mma32(cur, pb[j / DT], acc[j % DT]);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x100, 2 * LA, 0);     // LA steps of reads
+#pragma unroll
+      for (int j = 0; j < NSTEP - LA; ++j) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);        // an MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);        // the reads LA steps ahead
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, LA, 0);
+    }
+    if (do_s) {
+      zero_scores();
+      u32x4 win[LA];
+#pragma unroll
+      for (int j = 0; j < LA; ++j) win[j] = k_operand(Kb, j);
+#pragma unroll
+      for (int j = 0; j < NSTEP; ++j) {
+        const u32x4 cur = win[j % LA];
+        if (j + LA < NSTEP) win[j % LA] = k_operand(Kb, j + LA);
+        sc[j & 1] = E::mma32(cur, qB[j >> 1], sc[j & 1]);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x100, LA, 0);
+#pragma unroll
+      for (int j = 0; j < NSTEP - LA; ++j) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, LA, 0);
+    }
+  };
+
+  // softmax of stage st (its scores in sc): mask where a row limit falls in
+  // the stage, stage max over all 64 keys, (rare) move of the reference with
+  // O and l rescaled, weights into the P^T operands.
+  auto softmax = [&](int st) {
+    const int kst = kbeg + st * kStageKeys;
+    if (kst + kStageKeys > w_kmin) {
+      // element (i, r) is key 32 i + 8(r/4) + r%4 + 4h of the stage
+      const int rel = klim - kst - 4 * h;
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (32 * i + 8 * (r >> 2) + (r & 3) >= rel) sc[i][r] = kNegInf;
+    }
+    float mx = sc[0][0];
+#pragma unroll
+    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, sc[0][r]);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[1][r]);
+    mx = swap_halves_max(mx);
+    const float mnew = fmaxf(m, mx);
+    if (__builtin_amdgcn_ballot_w64(mnew > m + thr)) {
+      const float alpha = m == kNegInf ? 0.f : exp2_fast((m - mnew) * c);
+      m = mnew;
+      l *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          float x = acc[dt][r];
+          scale_inplace(x, alpha);
+          acc[dt][r] = x;
+        }
+    }
+    const float mc = m == kNegInf ? 0.f : m * c;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      float pr[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        pr[r] = exp2_fast(__builtin_fmaf(sc[i][r], c, -mc));
+        l += pr[r];
+      }
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) pb[2 * i + (r >> 3)][(r & 7) >> 1] = E::pack2(pr[r], pr[r + 1]);
+    }
+  };
+
+  // ---- the half-step loop: n_stage + 1 steps of two half-steps; both groups
+  // meet the same barriers (one per half-step but the last).  The barriers
+  // order LDS only: the DMA stages are ordered by each wave's vmcnt waits.
+  using B0 = std::integral_constant<int, 0>;
+  using B1 = std::integral_constant<int, 1>;
+  using B2 = std::integral_constant<int, 2>;
+  using B3 = std::integral_constant<int, 3>;
+  issue_stage(0, B0());
+  issue_stage(1, B1());
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * DPW) : "memory");   // stage 0 landed
+  lds_barrier();
+  // One step t (two half-steps) of group A or B; stage t lives in buffer KB,
+  // stage t + 2 goes to buffer KB + 2.  Returns false after the last step.
+  // Each group has its own loop, unrolled over the ring so every LDS address
+  // is a per-lane register plus an immediate.
+  auto step_a = [&](int t, auto kbc) -> bool {
+    constexpr int KB = decltype(kbc)::value;
+    issue_stage(t + Cfg::AHEAD, std::integral_constant<int, (KB + Cfg::AHEAD) % NBUF>());
+    mfma_block(kbc, t < w_nst, t >= 1 && t - 1 < w_nst);
+    lds_barrier();
+    if (t < w_nst) softmax(t);
+    if (t == n_stage) return false;
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * DPW) : "memory");
+    lds_barrier();
+    return true;
+  };
+  auto step_b = [&](int t, auto kbc) -> bool {
+    constexpr int KB = decltype(kbc)::value;
+    issue_stage(t + Cfg::AHEAD, std::integral_constant<int, (KB + Cfg::AHEAD) % NBUF>());
+    if (t >= 1 && t - 1 < w_nst) softmax(t - 1);
+    lds_barrier();
+    mfma_block(kbc, t < w_nst, t >= 1 && t - 1 < w_nst);
+    if (t == n_stage) return false;
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * DPW) : "memory");
+    lds_barrier();
+    return true;
+  };
+  if (grp == 0) {
+    for (int t = 0;; t += NBUF)
+      if (!step_a(t, B0()) || !step_a(t + 1, B1()) || !step_a(t + 2, B2()) || !step_a(t + 3, B3()))
+        break;
+  } else {
+    for (int t = 0;; t += NBUF)
+      if (!step_b(t, B0()) || !step_b(t + 1, B1()) || !step_b(t + 2, B2()) || !step_b(t + 3, B3()))
+        break;
+  }
+
+  // ---- epilogue: lanes l and l ^ 32 together hold the row
+  const float lt = swap_halves_sum(l);
+  if (!row_ok) return;
+  const float inv = lt > 0.f ? p.out_scale / lt : 0.f;
+  const int64_t tok = it.q0 + it.tok0 + t_in;
+  if (p.ws_rparts && it.sigma == 0 && h == 0)
+    p.ws_rparts[tok * p.num_q_heads + head] = it.parts;   // the row's part count, for pa_merge
+  if (it.parts == 1) {
+    if (h == 0) store_lse(p.lse_out, p.lse_st, tok, head, lt > 0.f ? m * c + __log2f(lt) : kNegInf);
+    uint16_t* op = p.out + tok * p.o_st + (int64_t)head * p.o_sh + 4 * h;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const u32x2 w = {E::pack2(acc[dt][4 * j] * inv, acc[dt][4 * j + 1] * inv),
+                         E::pack2(acc[dt][4 * j + 2] * inv, acc[dt][4 * j + 3] * inv)};
+        *reinterpret_cast<u32x2*>(op + 32 * dt + 8 * j) = w;
+      }
+  } else {
+    const int64_t r = ((int64_t)it.sigma * p.total_q + tok) * p.num_q_heads + head;
+    float* wp = p.ws_o + r * D + 4 * h;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const f32x4 v = {acc[dt][4 * j] * inv, acc[dt][4 * j + 1] * inv,
+                         acc[dt][4 * j + 2] * inv, acc[dt][4 * j + 3] * inv};
+        *reinterpret_cast<f32x4*>(wp + 32 * dt + 8 * j) = v;
+      }
+    if (h == 0) p.ws_lse[r] = lt > 0.f ? m * c + __log2f(lt) : kNegInf;
+  }
+}
+
+// The eight-wave unified grid kernel: wide tiles of up to 256 rows on the
+// ping-pong path, narrow tiles on the narrow path with eight waves.
+template <int D, int G, bool F16>
+__global__ __launch_bounds__(kWide8Threads) __attribute__((amdgpu_waves_per_eu(2)))
+void pa_fwd8_kernel(FwdParams p) {
+  __shared__ __attribute__((aligned(16))) unsigned char smem[Wide8Cfg<D>::SMEM];
+  Item it;
+  if (!decode_item<G>(p, it)) return;
+  if (it.rows <= p.narrow_rows) attend_narrow<D, G, narrow_ring<D>(), false, F16, 8>(p, it, smem);
+  else attend_wide8<D, G, F16>(p, it, smem);
+}
 
 // WIDE = false: every tile of the batch is narrow (the plan guarantees it).
 // KV8: the caches hold fp8 E4M3 codes.  F16: q, out (and 16-bit caches) are
@@ -1746,6 +2132,16 @@ hipError_t launch_fwd_t(const FwdParams& p, bool wide, int64_t nwg, hipStream_t 
   return hipGetLastError();
 }
 
+template <int D, int G, bool F16>
+hipError_t launch_fwd8_t(const FwdParams& p, int64_t nwg, hipStream_t stream) {
+  if constexpr (D == 64 || D == 128) {
+    hipLaunchKernelGGL((pa_fwd8_kernel<D, G, F16>), dim3((unsigned)nwg), dim3(kWide8Threads), 0,
+                       stream, p);
+    return hipGetLastError();
+  }
+  return hipErrorInvalidValue;                       // no eight-wave tiles for this head size
+}
+
 template <int D, int G, bool KV8, bool F16>
 hipError_t launch_decode_t(const FwdParams& p, int64_t nwg, hipStream_t stream) {
   hipLaunchKernelGGL((pa_decode_kernel<D, G, KV8, F16>), dim3((unsigned)nwg), dim3(kThreads), 0,
@@ -1821,6 +2217,12 @@ hipError_t launch_merge2_t(const Merge2Params& p, int64_t rows, hipStream_t stre
 hipError_t PA_SFX(launch_decode_d)(const FwdParams& p, int group, bool kv8, bool f16, int64_t nwg,
                                   hipStream_t stream) {
   PA_DISPATCH(group, kv8, f16, return (launch_decode_t<DD, GG, KK, FF>(p, nwg, stream)));
+  return hipErrorInvalidValue;
+}
+
+hipError_t PA_SFX(launch_fwd8_d)(const FwdParams& p, int group, bool f16, int64_t nwg,
+                                hipStream_t stream) {
+  PA_DISPATCH(group, false, f16, return (launch_fwd8_t<DD, GG, FF>(p, nwg, stream)));
   return hipErrorInvalidValue;
 }
 

@@ -455,3 +455,47 @@ def test_library_workspace_grows_under_two_threads():
     for w in range(2):
         for i, e in enumerate(expect):
             assert torch.equal(bits(outs[w][i]), bits(e)), (w, i)
+
+
+EIGHT_HEADS = [(32, 8), (4, 2), (16, 1), (32, 4), (8, 8)]
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("heads", EIGHT_HEADS, ids=lambda h: f"hq{h[0]}_hkv{h[1]}")
+@pytest.mark.parametrize("causal", [True, False], ids=["causal", "noncausal"])
+def test_eight_wave_tiles(d, heads, causal):
+    """force_tile = 4: 256-row tiles on the eight-wave kernel (two wave groups
+    in opposite phases), ragged query lengths that end tiles anywhere, rows
+    without keys, a decode row (narrow path with eight waves)."""
+    require_gpu()
+    hq, hkv = heads
+    rng = np.random.default_rng(2000 + 7 * d + hq + 3 * hkv + int(causal))
+    q_lens = np.array([300, 1, 65, 129, 0, 17, 256, 5, 40])
+    k_lens = np.array([max(int(x), int(ql)) for x, ql in
+                       zip(rng.integers(1, 1500, size=len(q_lens)), q_lens)])
+    k_lens[1] = 700
+    if causal:
+        k_lens[7] = 3          # 5 queries over 3 keys: first two rows have no key
+    b = build_batch("eight", q_lens, k_lens, hq, hkv, d, causal, seed=int(rng.integers(1 << 30)),
+                    device=DEV)
+    plan = pa.plan_describe(*b.args(b.new_out())[:9], opts=pa.options(force_tile=4))
+    assert plan["tile_rows"] == 256 // (hq // hkv) * (hq // hkv)
+    say(f"eight-wave d={d} hq={hq} hkv={hkv} causal={causal}")
+    out = run_pa(b, opts=pa.options(force_tile=4))
+    torch.cuda.synchronize()
+    full_parity(b, out, f"eight d{d} {heads} causal={causal}")
+
+
+@pytest.mark.parametrize("splits", [2, 7])
+def test_eight_wave_tiles_with_splits_and_permutation(splits):
+    require_gpu()
+    b = build_batch("eight_split", [300, 1, 64, 200], [3000, 900, 2100, 200], 32, 8, 128, True,
+                    seed=94 + splits, device=DEV)
+    b2 = repermute_pool(b, seed=95)
+    opts = pa.options(force_tile=4, force_num_splits=splits)
+    say(f"eight-wave splits={splits}")
+    o1 = run_pa(b, opts=opts)
+    o2 = run_pa(b2, opts=opts)
+    torch.cuda.synchronize()
+    assert torch.equal(bits(o1), bits(o2))
+    full_parity(b, o1, f"eight splits={splits}")
