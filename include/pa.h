@@ -41,8 +41,8 @@
 extern "C" {
 #endif
 
-#define PA_VERSION 4   /* 4: pa_workspace_bytes; 3: fp16 (PA_F16), block sizes 32 and 64, head
-                          sizes 96 and 256 */
+#define PA_VERSION 5   /* 5: pa_plan_info.partial_rows; 4: pa_workspace_bytes; 3: fp16
+                          (PA_F16), block sizes 32 and 64, head sizes 96 and 256 */
 
 /* Return codes.  Every failure is reported before anything is launched, with
  * one exception: PA_ERR_HIP, which may also come from the launch itself. */
@@ -131,6 +131,12 @@ typedef struct {
                             sequences): work-group b takes the (b / Hkv)-th
                             (sequence, query tile, key split) in order of
                             decreasing key count, kv-head b % Hkv            */
+  int32_t reserved;
+  int64_t partial_rows;  /* (token, q-head) rows of split partial outputs the
+                            workspace holds (0: no split).  Fixed parts:
+                            num_splits copies of the batch's rows.  Even
+                            split: slots of tile_tokens tokens, one per
+                            (sequence, chunk it touches)                     */
 } pa_plan_info;
 
 /*

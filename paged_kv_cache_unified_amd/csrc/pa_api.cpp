@@ -49,6 +49,8 @@ struct Plan {
   size_t ws_bytes;
   size_t ws_lse_offset;
   size_t ws_parts_offset;   // row part counts [T * Hq] int32
+  size_t ws_base_offset;    // even split: part-0 partial row of each row [T * Hq] int32
+  int64_t partial_rows;     // rows of the partial-output region (0: no split)
   size_t ws_lpt_offset;     // longest-first unit order [lpt_units] int4
   int64_t lpt_units;
 };
@@ -279,10 +281,28 @@ int make_plan(const Shapes& s, int32_t max_q, int32_t max_k, const pa_options* o
     if (p.balanced && !s.kv8 && !(opt && opt->decode_grid > 0))
       p.nwg = std::max<int64_t>(8, (int64_t)std::max(num_cus, 1) / 8 * 8);
     if (p.n_split > 1) {
-      const size_t rows = (size_t)s.T * (size_t)s.Hq * (size_t)p.n_split;
+      // fixed parts: n_split part-major copies of the batch's rows.  Even
+      // split: compact slots of max_seqlen_q tokens, one per (sequence, chunk
+      // it touches), at most chunks + sequences of them; the chunk count is
+      // bounded from the grid and the largest possible stream
+      size_t rows = (size_t)s.T * (size_t)s.Hq * (size_t)p.n_split;
+      if (p.balanced) {
+        const int64_t workers = p.nwg * 4;
+        const int64_t mkb = std::max<int64_t>((mk + pa::kBlockSize - 1) / pa::kBlockSize, 1);
+        const int64_t all_max = s.S * mkb * s.Hkv;
+        const int64_t kpw_max = std::max<int64_t>(
+            1, (all_max + workers * pa::kMaxSplitKeys / pa::kBlockSize - 1) /
+                   (workers * pa::kMaxSplitKeys / pa::kBlockSize));
+        const int64_t cmin = p.split_keys / pa::kBlockSize;
+        const int64_t chunks = std::min<int64_t>(workers * kpw_max / s.Hkv + 1,
+                                                 (s.S * mkb + cmin - 1) / cmin);
+        rows = (size_t)(chunks + s.S) * (size_t)mq * (size_t)s.Hq;
+      }
+      p.partial_rows = (int64_t)rows;
       p.ws_lse_offset = align256(rows * (size_t)s.D * sizeof(float));
       p.ws_parts_offset = p.ws_lse_offset + align256(rows * sizeof(float));
-      p.ws_bytes = p.ws_parts_offset + align256((size_t)s.T * (size_t)s.Hq * sizeof(int32_t));
+      p.ws_base_offset = p.ws_parts_offset + align256((size_t)s.T * (size_t)s.Hq * sizeof(int32_t));
+      p.ws_bytes = p.ws_base_offset + (p.balanced ? align256((size_t)s.T * (size_t)s.Hq * sizeof(int32_t)) : 0);
     }
     *out = p;
     return PA_OK;
@@ -341,6 +361,7 @@ int make_plan(const Shapes& s, int32_t max_q, int32_t max_k, const pa_options* o
   size_t off = 0;
   if (n_split > 1) {
     const size_t rows = (size_t)s.T * (size_t)s.Hq * (size_t)n_split;
+    p.partial_rows = (int64_t)rows;
     p.ws_lse_offset = align256(rows * (size_t)s.D * sizeof(float));
     p.ws_parts_offset = p.ws_lse_offset + align256(rows * sizeof(float));
     off = p.ws_parts_offset + align256((size_t)s.T * (size_t)s.Hq * sizeof(int32_t));
@@ -585,6 +606,10 @@ int run(const pa_tensor* q, const pa_tensor* k, const pa_tensor* v, pa_tensor* o
   p.ws_rparts = plan.n_split > 1
                    ? reinterpret_cast<int32_t*>(static_cast<char*>(ws) + plan.ws_parts_offset)
                    : nullptr;
+  p.ws_rbase = plan.n_split > 1 && plan.balanced
+                   ? reinterpret_cast<int32_t*>(static_cast<char*>(ws) + plan.ws_base_offset)
+                   : nullptr;
+  p.dq_tokens = plan.tile_tokens;
   p.num_items = (int32_t)plan.num_items;
   p.items_per_xcd = (int32_t)(plan.nwg / 8);
   p.kv_major = plan.wide ? 1 : 0;
@@ -626,6 +651,8 @@ int run(const pa_tensor* q, const pa_tensor* k, const pa_tensor* v, pa_tensor* o
     mp.num_q_heads = (int32_t)s.Hq;
     mp.n_split = plan.n_split;
     mp.row_parts = p.ws_rparts;
+    mp.row_base = p.ws_rbase;
+    mp.part_stride_c = (int64_t)plan.tile_tokens * s.Hq;
     mp.even = plan.balanced ? 1 : 0;
     mp.lse_out = p.lse_out;
     mp.lse_st = p.lse_st;
@@ -804,6 +831,7 @@ int pa_plan_describe(const pa_tensor* q, const pa_tensor* k_cache, const pa_tens
   info->workspace_bytes = (int64_t)plan.ws_bytes;
   info->persistent = plan.persistent ? 1 : 0;
   info->balanced = plan.balanced ? 1 : 0;
+  info->partial_rows = (s.T == 0 || s.S == 0) ? 0 : plan.partial_rows;
   return PA_OK;
 }
 

@@ -21,6 +21,7 @@ constexpr int kEvenMinContext = 1024; // decode batches with shorter rows keep o
 constexpr int kEvenMaxParts = 256;   // even split: chunks grow so a row has at most ~this many parts
 constexpr int kDecodeRing = 2;        // cache blocks in flight per wave (persistent decode; 3 measured no faster)
 constexpr int kLptMaxSeqs = 2048;   // longest-first order: LDS tables of 3 ints per sequence
+constexpr int kCompactRow = 1 << 30; // row part count flag: the parts sit in compact slots (ws_rbase)
 
 // Everything the forward kernel needs, by value.  Strides in elements.
 struct FwdParams {
@@ -54,7 +55,10 @@ struct FwdParams {
                            // block) stream is cut into equal chunks of at least
                            // split_keys / 16 blocks, one or more per wave
   int32_t* ws_rparts;      // n_split > 1: parts of each row (token, q-head) [T * Hq],
-                           // written by the row's first part
+                           // written by the row's first part (| kCompactRow: see ws_rbase)
+  int32_t* ws_rbase;       // even split: partial row of each row's part 0 [T * Hq]; part sg
+                           // is at + sg * dq_tokens * Hq (slots of dq_tokens tokens)
+  int32_t dq_tokens;       // even split: query tokens per partial slot (max_seqlen_q)
   int32_t num_items;       // num_slots * num_kv_heads * n_split
   int32_t items_per_xcd;   // ceil(num_items / 8): contiguous item range per XCD
   int32_t kv_major;        // item order: 1 = (kv-head, slot, split), 0 = (slot, kv-head, split)
@@ -74,6 +78,8 @@ struct MergeParams {
   const float* ws_lse;
   const int32_t* row_parts;  // [T * Hq]: parts of each row; rows with one part were
                              // written by the forward kernel and are skipped
+  const int32_t* row_base;   // [T * Hq]: part-0 partial row of rows flagged kCompactRow
+  int64_t part_stride_c;     // partial rows between consecutive parts of such a row
   uint16_t* out;
   int64_t o_st, o_sh;
   int32_t total_q;

@@ -1553,7 +1553,8 @@ struct DecodeCfg {
   static constexpr int PREF_OFFSET = IDS_OFFSET + 4 * 2 * kMaxItemBlocks * 4;  // int [S + 1]
   static constexpr int Q0_OFFSET = PREF_OFFSET + (kMaxDecodeSeqs + 1) * 4;   // int [S + 1]
   static constexpr int LEN_OFFSET = Q0_OFFSET + (kMaxDecodeSeqs + 1) * 4;   // int [S]
-  static constexpr int SCAN_OFFSET = (LEN_OFFSET + kMaxDecodeSeqs * 4 + 7) / 8 * 8;  // 4 x i64
+  static constexpr int SLOT_OFFSET = LEN_OFFSET + kMaxDecodeSeqs * 4;        // int [S + 1]
+  static constexpr int SCAN_OFFSET = (SLOT_OFFSET + (kMaxDecodeSeqs + 1) * 4 + 7) / 8 * 8;  // 4 x i64
   static constexpr int SMEM = SCAN_OFFSET + 32;
 };
 
@@ -1568,6 +1569,7 @@ __device__ __forceinline__ int seq_parts(const FwdParams& p, int ql, int L, int 
 struct DItem {
   int valid;
   int s, kvh, sigma, units;
+  int slot;              // even split: partial slot of the item (the sequence's first slot + sigma)
   int q0, q_len, rows, L, diag;
   int kbeg, kend, kmin;
   int blk0, nb;          // first block and number of blocks of the item
@@ -1630,6 +1632,7 @@ void pa_decode_kernel(FwdParams p) {
   int* pref = reinterpret_cast<int*>(smem + Cfg::PREF_OFFSET);
   int* q0t = reinterpret_cast<int*>(smem + Cfg::Q0_OFFSET);
   int* lent = reinterpret_cast<int*>(smem + Cfg::LEN_OFFSET);
+  int* slots = reinterpret_cast<int*>(smem + Cfg::SLOT_OFFSET);
   int* wsum = reinterpret_cast<int*>(smem + Cfg::SCAN_OFFSET);
   int* idsw = reinterpret_cast<int*>(smem + Cfg::IDS_OFFSET) + wave * 2 * kMaxItemBlocks;
 
@@ -1654,9 +1657,11 @@ void pa_decode_kernel(FwdParams p) {
     if (p.balanced) return ql > 0 ? max((lent[s] + kBlockSize - 1) / kBlockSize, 1) : 0;
     return seq_parts(p, ql, lent[s], target);
   };
-  {
+  // exclusive prefix over the sequences of f(s) into out[0..S] (threads own
+  // contiguous runs of sequences); contains barriers
+  auto scan_seqs = [&](auto&& f, int* out) {
     int local = 0;
-    for (int s = s0; s < s1; ++s) local += seq_units(s);
+    for (int s = s0; s < s1; ++s) local += f(s);
     int incl = local;
 #pragma unroll
     for (int d = 1; d < 64; d <<= 1) {
@@ -1669,12 +1674,13 @@ void pa_decode_kernel(FwdParams p) {
     for (int w = 0; w < wave; ++w) base += wsum[w];
     int run = base + incl - local;
     for (int s = s0; s < s1; ++s) {
-      pref[s] = run;
-      run += seq_units(s);
+      out[s] = run;
+      run += f(s);
     }
-    if (tid == kThreads - 1) pref[S] = base + incl;
+    if (tid == kThreads - 1) out[S] = base + incl;
     __syncthreads();
-  }
+  };
+  scan_seqs(seq_units, pref);
   // fixed parts: items, kv-heads included; even split: the blocks of the
   // per-sequence stream (one kv-head's worth)
   const int n_units = uniform(pref[S]) * (p.balanced ? 1 : Hkv);
@@ -1689,6 +1695,13 @@ void pa_decode_kernel(FwdParams p) {
     const int kpw = max(1, (all + cap - 1) / cap);
     chunk = max((all + workers * kpw - 1) / (workers * kpw), target / kBlockSize);
     n_pairs = (n_units + chunk - 1) / chunk * Hkv;
+    // partial slots: a sequence gets one per chunk it touches (its parts), so
+    // the batch needs at most (chunks + sequences) slots, whatever its token
+    // count; slot(s, part) = slots[s] + part
+    scan_seqs([&](int s) -> int {
+      const int x0 = pref[s], x1 = pref[s + 1];
+      return x1 > x0 ? (x1 - 1) / chunk - x0 / chunk + 1 : 0;
+    }, slots);
   }
   // Fixed parts: items are dealt to XCDs in contiguous ranges (work-group w
   // runs on XCD w % 8); the waves of one XCD stride through its range, and
@@ -1748,6 +1761,7 @@ void pa_decode_kernel(FwdParams p) {
     d.kmin = p.causal ? min(d.kend, d.diag + 1) : d.kend;
     d.blk0 = b0;
     d.nb = d.kend > d.kbeg ? (d.kend + kBlockSize - 1) / kBlockSize - b0 : 0;
+    d.slot = uniform(slots[lo]) + d.sigma;
     d.c = q;
     d.next = pos + (b1 - b0);
     return d;
@@ -1931,12 +1945,21 @@ void pa_decode_kernel(FwdParams p) {
 
     // ---- this wave's rows of the item ----
     l = sum_across_groups(l);
-    if (l16 < cur.rows) {
+    // (a token past max_seqlen_q, a broken precondition, has no partial slot)
+    if (l16 < cur.rows && l16 / G < p.dq_tokens) {
       const float inv = l > 0.f ? p.out_scale / l : 0.f;
       const int64_t tok = cur.q0 + l16 / G;
       const int hn = cur.kvh * G + l16 % G;
-      if (p.ws_rparts && cur.sigma == 0 && h4 == 0)
-        p.ws_rparts[tok * p.num_q_heads + hn] = cur.units;  // the row's part count, for pa_merge
+      // partial row of part sigma: even split, compact slots of dq_tokens
+      // tokens each; fixed parts, part-major over the batch's tokens
+      const int64_t prow = p.balanced
+          ? ((int64_t)cur.slot * p.dq_tokens + l16 / G) * p.num_q_heads + hn
+          : ((int64_t)cur.sigma * p.total_q + tok) * p.num_q_heads + hn;
+      if (p.ws_rparts && cur.sigma == 0 && h4 == 0) {
+        // the row's part count (and, compact, its part-0 row), for pa_merge
+        p.ws_rparts[tok * p.num_q_heads + hn] = cur.units | (p.balanced ? kCompactRow : 0);
+        if (p.balanced) p.ws_rbase[tok * p.num_q_heads + hn] = (int32_t)prow;
+      }
       if (cur.units == 1) {
         if (h4 == 0) store_lse(p.lse_out, p.lse_st, tok, hn, l > 0.f ? m + __log2f(l) : kNegInf);
         uint16_t* op = p.out + tok * p.o_st + (int64_t)hn * p.o_sh + 4 * h4;
@@ -1947,11 +1970,10 @@ void pa_decode_kernel(FwdParams p) {
           *reinterpret_cast<u32x2*>(op + 16 * dt) = w;
         }
       } else {
-        const int64_t r = ((int64_t)cur.sigma * p.total_q + tok) * p.num_q_heads + hn;
-        float* wp = p.ws_o + r * D + 4 * h4;
+        float* wp = p.ws_o + prow * D + 4 * h4;
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) *reinterpret_cast<f32x4*>(wp + 16 * dt) = acc[dt] * inv;
-        if (h4 == 0) p.ws_lse[r] = l > 0.f ? m + __log2f(l) : kNegInf;
+        if (h4 == 0) p.ws_lse[prow] = l > 0.f ? m + __log2f(l) : kNegInf;
       }
     }
     if (!nxt.valid) break;
@@ -1975,10 +1997,25 @@ void pa_decode_kernel(FwdParams p) {
 // Log-sum-exp merge of key-split partials (all lse in the log2 domain):
 // w_sigma = 2^(lse_sigma - max lse), out = sum w O_sigma / sum w.  Parts with no
 // key carry lse = -inf and are skipped (their O is never read).
-// Parts of a row, written by the forward kernel's first part (1: the row was
-// written straight to out and is skipped).
-__device__ __forceinline__ int merge_parts(const MergeParams& p, int64_t row) {
-  return p.row_parts[row];
+// Parts of a row and where they are, from the forward kernel's first part (1
+// part: the row was written straight to out and is skipped).  Part sg of the
+// row is partial row base + sg * stride: part-major over the batch's rows, or
+// (compact even split) consecutive slots from the row's recorded base.
+struct MergeRow {
+  int parts;
+  int64_t base, stride;
+};
+__device__ __forceinline__ MergeRow merge_row(const MergeParams& p, int64_t row, int64_t nrows) {
+  const int raw = p.row_parts[row];
+  MergeRow r;
+  r.parts = raw & ~kCompactRow;
+  r.base = row;
+  r.stride = nrows;
+  if (raw & kCompactRow) {
+    r.base = p.row_base[row];
+    r.stride = p.part_stride_c;
+  }
+  return r;
 }
 
 template <bool F16>
@@ -2012,21 +2049,23 @@ __global__ __launch_bounds__(256) void pa_merge_rows_kernel(MergeParams p) {
   const int64_t row = (int64_t)blockIdx.x * RPB + threadIdx.x / TPR;
   const int64_t nrows = (int64_t)p.total_q * p.num_q_heads;
   if (row >= nrows) return;
-  const int n_part = merge_parts(p, row);
+  const MergeRow mr = merge_row(p, row, nrows);
+  const int n_part = mr.parts;
   if (n_part <= 1) return;
   const int d0 = (threadIdx.x % TPR) * 4;
   float M = kNegInf;
 #pragma unroll 4
-  for (int sg = 0; sg < n_part; ++sg) M = fmaxf(M, p.ws_lse[sg * nrows + row]);
+  for (int sg = 0; sg < n_part; ++sg) M = fmaxf(M, p.ws_lse[mr.base + sg * mr.stride]);
   f32x4 a = {0.f, 0.f, 0.f, 0.f};
   float ws = 0.f;
   if (M != kNegInf) {
     // loads do not wait on the weights (a part's slot exists for every
     // sg < n_part), so the parts' loads overlap
 #pragma unroll 4
-    for (int sg = 0; sg < n_part; ++sg)
-      merge_add(p.ws_lse[sg * nrows + row],
-                *reinterpret_cast<const f32x4*>(p.ws_o + (sg * nrows + row) * D + d0), M, a, ws);
+    for (int sg = 0; sg < n_part; ++sg) {
+      const int64_t r = mr.base + sg * mr.stride;
+      merge_add(p.ws_lse[r], *reinterpret_cast<const f32x4*>(p.ws_o + r * D + d0), M, a, ws);
+    }
   }
   merge_store<F16>(p, row, d0, a, ws, M);
 }
@@ -2042,13 +2081,14 @@ __global__ __launch_bounds__(256) void pa_merge_wide_kernel(MergeParams p) {
   __shared__ float mred[4];
   const int64_t row = blockIdx.x;
   const int64_t nrows = (int64_t)p.total_q * p.num_q_heads;
-  const int n_part = merge_parts(p, row);
+  const MergeRow mr = merge_row(p, row, nrows);
+  const int n_part = mr.parts;
   if (n_part <= 1) return;   // uniform over the work-group
   const int t = threadIdx.x;
   const int g = t / TPG;
   const int d0 = (t % TPG) * 4;
   float M = kNegInf;
-  for (int sg = t; sg < n_part; sg += 256) M = fmaxf(M, p.ws_lse[sg * nrows + row]);
+  for (int sg = t; sg < n_part; sg += 256) M = fmaxf(M, p.ws_lse[mr.base + sg * mr.stride]);
 #pragma unroll
   for (int d = 32; d >= 1; d >>= 1) M = fmaxf(M, __shfl_xor(M, d));
   if ((t & 63) == 0) mred[t >> 6] = M;
@@ -2058,9 +2098,10 @@ __global__ __launch_bounds__(256) void pa_merge_wide_kernel(MergeParams p) {
   float ws = 0.f;
   if (M != kNegInf && g < NG) {
 #pragma unroll 4
-    for (int sg = g; sg < n_part; sg += NG)
-      merge_add(p.ws_lse[sg * nrows + row],
-                *reinterpret_cast<const f32x4*>(p.ws_o + (sg * nrows + row) * D + d0), M, a, ws);
+    for (int sg = g; sg < n_part; sg += NG) {
+      const int64_t r = mr.base + sg * mr.stride;
+      merge_add(p.ws_lse[r], *reinterpret_cast<const f32x4*>(p.ws_o + r * D + d0), M, a, ws);
+    }
   }
   if (g < NG) {
     *reinterpret_cast<f32x4*>(&red[g][d0]) = a;

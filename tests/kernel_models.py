@@ -122,12 +122,18 @@ def decode_kernel(b: Batch, plan: Dict, ring: int = 2) -> Trace:
     n_units = pref[S] * (1 if balanced else Hkv)
     workers = nwg * 4
     chunk, n_pairs = 1, 0
+    slots = [0] * (S + 1)
     if balanced:
         all_ = n_units * Hkv
         cap = workers * MAX_ITEM_BLOCKS
         kpw = max(1, cdiv(all_, cap))
         chunk = max(cdiv(all_, workers * kpw), target // SUB)
         n_pairs = cdiv(n_units, chunk) * Hkv
+        # compact partial slots: one per chunk a sequence touches
+        for s in range(S):
+            x0, x1 = pref[s], pref[s + 1]
+            slots[s + 1] = slots[s] + ((x1 - 1) // chunk - x0 // chunk + 1 if x1 > x0 else 0)
+    tq = int(plan["tile_tokens"])
     n_items = 0 if balanced else n_units
     per_xcd = (n_items + 7) >> 3
     wpx = (nwg >> 3) * 4
@@ -185,6 +191,7 @@ def decode_kernel(b: Batch, plan: Dict, ring: int = 2) -> Trace:
                 x0 = pref[s]
                 b0 = pos - x0
                 b1 = min(nbe, b0 + (xe - pos))
+                d.update(slot=slots[s] + c - x0 // chunk)
                 d.update(s=s, kvh=q - c * Hkv, sigma=c - x0 // chunk,
                          units=(x0 + nbe - 1) // chunk - x0 // chunk + 1, q0=q0t[s],
                          q_len=q0t[s + 1] - q0t[s], L=L, kbeg=b0 * SUB,
@@ -241,9 +248,14 @@ def decode_kernel(b: Batch, plan: Dict, ring: int = 2) -> Trace:
                                      cur["q_len"], (blk, wave)))
                 if cur["units"] > 1:
                     for r in range(min(rows, NARROW_ROWS)):
+                        if r // G >= tq:
+                            continue
                         tok = cur["q0"] + r // G
                         hn = cur["kvh"] * G + r % G
-                        tr.ws_rows.append((cur["sigma"] * b.T + tok) * b.num_q_heads + hn)
+                        if balanced:
+                            tr.ws_rows.append((cur["slot"] * tq + r // G) * b.num_q_heads + hn)
+                        else:
+                            tr.ws_rows.append((cur["sigma"] * b.T + tok) * b.num_q_heads + hn)
                 if not nxt["valid"]:
                     break
                 cur, nxt = nxt, nx2
@@ -408,7 +420,9 @@ def check_trace(b: Batch, plan: Dict, tr: Trace) -> None:
     for s, j, kvh in tr.live_loads:
         assert 0 <= j < cdiv(b.L(s), SUB) and 0 <= kvh < b.num_kv_heads, \
             f"live load of sequence {s} sub-block {j} kv-head {kvh}"
-    # workspace rows inside the n_split * T * Hq partials the host sized
+    # workspace rows inside the partials the host sized, each written once
+    bound = int(plan["partial_rows"])
     for r in tr.ws_rows:
-        assert 0 <= r < n_split * T * Hq, f"workspace row {r} past {n_split * T * Hq}"
+        assert 0 <= r < bound, f"workspace row {r} past {bound}"
+    assert len(set(tr.ws_rows)) == len(tr.ws_rows), "two parts write one partial row"
     assert tr.max_stream_pos <= INT32_MAX

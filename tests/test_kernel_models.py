@@ -143,6 +143,8 @@ def test_models_catch_a_planted_bound_error():
     assert most > 1
     with pytest.raises(AssertionError):
         check_trace(b, dict(plan, num_splits=most - 1), tr)
+    with pytest.raises(AssertionError):
+        check_trace(b, dict(plan, partial_rows=max(tr.ws_rows)), tr)
     shorter = Batch(b.q_lens, [min(x, 4000) for x in b.k_lens], 32, 8, 128, 16, max_k=9000)
     with pytest.raises(AssertionError):
         check_trace(shorter, plan, tr)
