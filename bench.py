@@ -336,6 +336,10 @@ def main():
     ap.add_argument("--cache-write", action="store_true",
                     help="time pa_cache_write instead: each sequence's new tokens (its "
                          "last q_s positions) written into the workload's caches")
+    ap.add_argument("--ceilings", action="store_true",
+                    help="only measure this GPU's practical matrix ceilings: a library bf16 "
+                         "GEMM (random and all-zero operands), the prefill workload with random and all-zero q/k/v, and torch's "
+                         "dense attention on the prefill-equivalent shapes")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a 1 GiB device-to-device copy three times (the known-size "
                          "kernel that scales rocprofv3 FETCH_SIZE / WRITE_SIZE into bytes)")
@@ -360,6 +364,9 @@ def main():
 
     import paged_kv_cache_unified_amd as pa
     from workloads import WORKLOADS, make_workload
+    if args.ceilings:
+        measure_ceilings(pa, make_workload, args)
+        return
 
     if args.workload not in WORKLOADS:
         sys.exit(f"unknown workload {args.workload}; choose from {sorted(WORKLOADS)}")
@@ -430,6 +437,77 @@ CONFIG_WORKLOADS = [
     "long_q16_noncausal_16seq_ctx32k_128k",
     "decode_256seq_ctx1k_fp8",
 ]
+
+
+def _event_time(fn, n=20, warm=5):
+    """Mean GPU time of fn over n back-to-back calls (s), events on the current stream."""
+    import torch
+    for _ in range(warm):
+        fn()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(n):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / n * 1e-3
+
+
+def measure_ceilings(pa, make_workload, args):
+    """What this GPU's matrix cores sustain in practice, beside the published
+    peak the roofline uses: a library GEMM (operands drawn from N(0, 1), and
+    all zeros: the gap is the clock the chip gives up under data-dependent
+    power), the prefill
+    workload through this library with random and with all-zero q/k/v (same
+    code path, no rescale either way after the first key), and torch's dense
+    attention on shapes equivalent to that prefill.  One JSON line per item."""
+    import torch
+    import torch.nn.functional as F
+    dev = torch.device("cuda:0")
+    out = []
+    for kind in ("normal", "zeros"):
+        n = 8192
+        mk = (lambda: torch.randn(n, n, device=dev, dtype=torch.bfloat16)) if kind == "normal" \
+            else (lambda: torch.zeros(n, n, device=dev, dtype=torch.bfloat16))
+        a, c = mk(), mk()
+        t = _event_time(lambda: a @ c)
+        out.append({"ceiling": "bf16 GEMM 8192^3 (torch.matmul)", "operands": kind,
+                    "us": round(t * 1e6, 1), "TFLOPs": round(2 * n ** 3 / t / 1e12, 1),
+                    "frac_of_2.5PF": round(2 * n ** 3 / t / 2.5e15, 4)})
+        del a, c
+    name = "prefill512x8_only"
+    b = make_workload(name, device=dev)
+    res = torch.empty_like(b.q)
+    fargs = b.args(res)
+    opts = pa.options()
+    ws = torch.empty(max(1, pa.workspace_bytes(*fargs[:9], opts)), dtype=torch.uint8, device=dev)
+    flops = algorithmic_work(b)[2]
+    for kind in ("normal", "zeros"):
+        if kind == "zeros":
+            b.q.zero_()
+            b.k_cache.zero_()
+            b.v_cache.zero_()
+        t = _event_time(lambda: pa.unified_attention(*fargs, opts=opts, workspace=ws))
+        out.append({"ceiling": f"{name} through this library", "qkv": kind,
+                    "us": round(t * 1e6, 1), "TFLOPs": round(flops / t / 1e12, 1),
+                    "frac_of_2.5PF": round(flops / t / 2.5e15, 4)})
+    del b, res, ws
+    torch.cuda.empty_cache()
+    # dense attention at the prefill's size: 8 sequences x 32 heads, 512 queries
+    # over 2048 keys (the longest chunk's context), and a square causal 2048
+    for (B, H, Sq, Sk, causal) in ((8, 32, 512, 2048, False), (8, 32, 2048, 2048, True)):
+        q = torch.randn(B, H, Sq, 128, device=dev, dtype=torch.bfloat16)
+        k = torch.randn(B, H, Sk, 128, device=dev, dtype=torch.bfloat16)
+        v = torch.randn(B, H, Sk, 128, device=dev, dtype=torch.bfloat16)
+        fl = 4 * B * H * Sq * Sk * 128 * (0.5 if causal else 1.0)
+        t = _event_time(lambda: F.scaled_dot_product_attention(q, k, v, is_causal=causal))
+        out.append({"ceiling": "torch scaled_dot_product_attention (dense)", "shape": [B, H, Sq, Sk, 128],
+                    "causal": causal, "us": round(t * 1e6, 1), "TFLOPs": round(fl / t / 1e12, 1),
+                    "frac_of_2.5PF": round(fl / t / 2.5e15, 4)})
+        del q, k, v
+    for o in out:
+        print(json.dumps(o), flush=True)
 
 
 def measure(pa, b, args, steps, warmup, n_cold):
