@@ -238,6 +238,38 @@ __device__ __forceinline__ float sum_across_groups(float x) {
   return x;
 }
 
+// Online softmax of one 16-key block on the 16-column tiles (narrow path and
+// decode kernel).  x holds this lane's 4 scores of the block in log2 units
+// (masked keys at -inf); m, l and acc are its row's running state, shared by
+// the 4 lanes of the row.  The reference max m moves, and O and l are
+// rescaled, only when a score of the wave exceeds its row's reference by more
+// than 2^8 (or a row sees its first key).  O and l share the reference, so
+// this is exact, and every weight stays at most 256.  The common path has no
+// cross-lane step and no rescale: the test is one ballot of the lanes' own
+// scores, and only the rare move takes the row max over the lane groups.
+template <int DT>
+__device__ __forceinline__ void block_weights(const float (&x)[4], float& m, float& l,
+                                              f32x4 (&acc)[DT], float (&pr)[4]) {
+  constexpr float kThr = 8.f;
+  const float mx = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+  if (__builtin_amdgcn_ballot_w64(mx > m + kThr)) {        // wave-uniform
+    const float m_new = fmaxf(m, max_across_groups(mx));
+    const float alpha = m_new == m ? 1.f : exp2_fast(m - m_new);   // m = -inf: 0
+    m = m_new;
+    l *= alpha;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) acc[dt] *= alpha;
+  }
+  const float m_use = m == kNegInf ? 0.f : m;
+  float rs = 0.f;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    pr[r] = exp2_fast(x[r] - m_use);
+    rs += pr[r];
+  }
+  l += rs;
+}
+
 // LDS layouts of one (block, kv-head) tile of 16 keys x D, in 16-byte chunks.
 //  K: chunk (key, dc) at index dc*16 + (key ^ dc): an A-operand read (16 keys
 //     at one d-chunk per lane group) is 256 contiguous bytes, and the
@@ -591,25 +623,13 @@ __device__ __forceinline__ void attend_narrow(const FwdParams& p, const Item& it
         }
         const bool need_mask = kb + kBlockSize > it.kmin;
         float x[4];
-        float mx = kNegInf;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           x[r] = sc[r] * p.scale_log2;
           if (need_mask && kb + 4 * h4 + r >= klim) x[r] = kNegInf;
-          mx = fmaxf(mx, x[r]);
         }
-        mx = max_across_groups(mx);
-        const float m_new = fmaxf(m, mx);
-        const float m_use = m_new == kNegInf ? 0.f : m_new;
-        const float alpha = exp2_fast(m - m_use);
-        float pr[4], rs = 0.f;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          pr[r] = exp2_fast(x[r] - m_use);
-          rs += pr[r];
-        }
-        l = l * alpha + rs;
-        m = m_new;
+        float pr[4];
+        block_weights<DT>(x, m, l, acc, pr);
         const u32x2 pB = {E::pack2(pr[0], pr[1]), E::pack2(pr[2], pr[3])};
         const bool vmask = kb + kBlockSize > it.kend;
 #pragma unroll
@@ -623,7 +643,6 @@ __device__ __forceinline__ void attend_narrow(const FwdParams& p, const Item& it
             for (int e = 0; e < 4; ++e)
               if (kb + 4 * h4 + e >= it.kend) va[e] = 0;
           }
-          acc[dt] *= alpha;
           acc[dt] = E::mma16k16(__builtin_bit_cast(u32x2, va), pB, acc[dt]);
         }
       }
@@ -1904,25 +1923,13 @@ void pa_decode_kernel(FwdParams p) {
         if (live) {
           const bool need_mask = kb + kBlockSize > cur.kmin;
           float x[4];
-          float mx = kNegInf;
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             x[r] = sc[r] * p.scale_log2;
             if (need_mask && kb + 4 * h4 + r >= klim) x[r] = kNegInf;
-            mx = fmaxf(mx, x[r]);
           }
-          mx = max_across_groups(mx);
-          const float m_new = fmaxf(m, mx);
-          const float m_use = m_new == kNegInf ? 0.f : m_new;
-          const float alpha = exp2_fast(m - m_use);
-          float pr[4], rs = 0.f;
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            pr[r] = exp2_fast(x[r] - m_use);
-            rs += pr[r];
-          }
-          l = l * alpha + rs;
-          m = m_new;
+          float pr[4];
+          block_weights<DT>(x, m, l, acc, pr);
           const u32x2 pB = {E::pack2(pr[0], pr[1]), E::pack2(pr[2], pr[3])};
           const bool vmask = kb + kBlockSize > cur.kend;
 #pragma unroll
@@ -1936,7 +1943,6 @@ void pa_decode_kernel(FwdParams p) {
               for (int e = 0; e < 4; ++e)
                 if (kb + 4 * h4 + e >= cur.kend) va[e] = 0;
             }
-            acc[dt] *= alpha;
             acc[dt] = E::mma16k16(__builtin_bit_cast(u32x2, va), pB, acc[dt]);
           }
         }
