@@ -2012,13 +2012,16 @@ struct MergeRow {
   int64_t base, stride;
 };
 __device__ __forceinline__ MergeRow merge_row(const MergeParams& p, int64_t row, int64_t nrows) {
+  // both words in one round trip: the base is loaded whether or not the row
+  // turns out compact (the array exists whenever a plan has compact rows)
   const int raw = p.row_parts[row];
+  const int cbase = p.row_base ? p.row_base[row] : 0;
   MergeRow r;
   r.parts = raw & ~kCompactRow;
   r.base = row;
   r.stride = nrows;
   if (raw & kCompactRow) {
-    r.base = p.row_base[row];
+    r.base = cbase;
     r.stride = p.part_stride_c;
   }
   return r;
@@ -2036,14 +2039,42 @@ __device__ __forceinline__ void merge_store(const MergeParams& p, int64_t row, i
   *reinterpret_cast<u32x2*>(op) = w;
 }
 
-// One part into the running sums; a part with no key (lse = -inf) adds
-// nothing, whatever its O slot holds (selects, not multiplies by 0).
-__device__ __forceinline__ void merge_add(float ls, f32x4 o, float M, f32x4& a, float& ws) {
-  const bool live = ls != kNegInf;
-  const float w = live ? exp2_fast(ls - M) : 0.f;
+// One part into running sums kept against the largest lse seen so far (M):
+// a larger lse moves M and rescales the sums first.  A part with no key
+// (lse = -inf) adds nothing, whatever its O slot holds (a branch, not a
+// multiply by 0).
+__device__ __forceinline__ void merge_add(float ls, f32x4 o, float& M, f32x4& a, float& ws) {
+  if (ls == kNegInf) return;
+  if (ls > M) {
+    const float s = M == kNegInf ? 0.f : exp2_fast(M - ls);
+    ws *= s;
+    a *= s;
+    M = ls;
+  }
+  const float w = exp2_fast(ls - M);
   ws += w;
+  a += w * o;
+}
+
+// Parts sg0, sg0 + step, ... of a row into (M, a, ws), four at a time: the
+// lse and O loads of the four are issued before any of them is combined (a
+// part's slot exists for every sg < parts).
+template <int D>
+__device__ __forceinline__ void merge_parts(const MergeParams& p, const MergeRow& mr, int d0,
+                                            int sg0, int step, float& M, f32x4& a, float& ws) {
+  for (int sg = sg0; sg < mr.parts; sg += 4 * step) {
+    float ls[4];
+    f32x4 o[4];
 #pragma unroll
-  for (int e = 0; e < 4; ++e) a[e] += live ? w * o[e] : 0.f;
+    for (int k = 0; k < 4; ++k) {
+      const int q = sg + k * step;
+      const int64_t r = mr.base + (int64_t)min(q, mr.parts - 1) * mr.stride;
+      ls[k] = q < mr.parts ? p.ws_lse[r] : kNegInf;
+      o[k] = *reinterpret_cast<const f32x4*>(p.ws_o + r * D + d0);
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k) merge_add(ls[k], o[k], M, a, ws);
+  }
 }
 
 // Few parts per row: D/4 threads per row, each loops over the parts.
@@ -2060,19 +2091,9 @@ __global__ __launch_bounds__(256) void pa_merge_rows_kernel(MergeParams p) {
   if (n_part <= 1) return;
   const int d0 = (threadIdx.x % TPR) * 4;
   float M = kNegInf;
-#pragma unroll 4
-  for (int sg = 0; sg < n_part; ++sg) M = fmaxf(M, p.ws_lse[mr.base + sg * mr.stride]);
   f32x4 a = {0.f, 0.f, 0.f, 0.f};
   float ws = 0.f;
-  if (M != kNegInf) {
-    // loads do not wait on the weights (a part's slot exists for every
-    // sg < n_part), so the parts' loads overlap
-#pragma unroll 4
-    for (int sg = 0; sg < n_part; ++sg) {
-      const int64_t r = mr.base + sg * mr.stride;
-      merge_add(p.ws_lse[r], *reinterpret_cast<const f32x4*>(p.ws_o + r * D + d0), M, a, ws);
-    }
-  }
+  merge_parts<D>(p, mr, d0, 0, 1, M, a, ws);
   merge_store<F16>(p, row, d0, a, ws, M);
 }
 
@@ -2084,45 +2105,44 @@ __global__ __launch_bounds__(256) void pa_merge_wide_kernel(MergeParams p) {
   constexpr int NG = 256 / TPG;              // groups (d = 96: 10, 16 threads in none)
   __shared__ float red[NG][D + 4];
   __shared__ float wred[NG];
-  __shared__ float mred[4];
+  __shared__ float mred[NG];
   const int64_t row = blockIdx.x;
   const int64_t nrows = (int64_t)p.total_q * p.num_q_heads;
   const MergeRow mr = merge_row(p, row, nrows);
-  const int n_part = mr.parts;
-  if (n_part <= 1) return;   // uniform over the work-group
+  if (mr.parts <= 1) return;   // uniform over the work-group
   const int t = threadIdx.x;
   const int g = t / TPG;
   const int d0 = (t % TPG) * 4;
   float M = kNegInf;
-  for (int sg = t; sg < n_part; sg += 256) M = fmaxf(M, p.ws_lse[mr.base + sg * mr.stride]);
-#pragma unroll
-  for (int d = 32; d >= 1; d >>= 1) M = fmaxf(M, __shfl_xor(M, d));
-  if ((t & 63) == 0) mred[t >> 6] = M;
-  __syncthreads();
-  M = fmaxf(fmaxf(mred[0], mred[1]), fmaxf(mred[2], mred[3]));
   f32x4 a = {0.f, 0.f, 0.f, 0.f};
   float ws = 0.f;
-  if (M != kNegInf && g < NG) {
-#pragma unroll 4
-    for (int sg = g; sg < n_part; sg += NG) {
-      const int64_t r = mr.base + sg * mr.stride;
-      merge_add(p.ws_lse[r], *reinterpret_cast<const f32x4*>(p.ws_o + r * D + d0), M, a, ws);
-    }
-  }
   if (g < NG) {
+    merge_parts<D>(p, mr, d0, g, NG, M, a, ws);
     *reinterpret_cast<f32x4*>(&red[g][d0]) = a;
-    if (t % TPG == 0) wred[g] = ws;
+    if (t % TPG == 0) {
+      wred[g] = ws;
+      mred[g] = M;
+    }
   }
   __syncthreads();
   if (g != 0) return;
+  // the groups' sums, each against its own largest lse
+  float Mt = kNegInf;
+#pragma unroll
+  for (int k = 0; k < NG; ++k) Mt = fmaxf(Mt, mred[k]);
   float wt = 0.f;
   f32x4 o = {0.f, 0.f, 0.f, 0.f};
+  if (Mt != kNegInf) {
 #pragma unroll
-  for (int k = 0; k < NG; ++k) {
-    wt += wred[k];
-    o += *reinterpret_cast<const f32x4*>(&red[k][d0]);
+    for (int k = 0; k < NG; ++k) {
+      const float mk = mred[k];
+      if (mk == kNegInf) continue;
+      const float s = exp2_fast(mk - Mt);
+      wt += s * wred[k];
+      o += s * *reinterpret_cast<const f32x4*>(&red[k][d0]);
+    }
   }
-  merge_store<F16>(p, row, d0, o, wt, M);
+  merge_store<F16>(p, row, d0, o, wt, Mt);
 }
 
 // Two partial results over disjoint key sets (natural-log lse):
