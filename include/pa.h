@@ -41,7 +41,7 @@
 extern "C" {
 #endif
 
-#define PA_VERSION 5   /* 5: pa_plan_info.partial_rows; 4: pa_workspace_bytes; 3: fp16
+#define PA_VERSION 6   /* 6: pa_plan_info.unit_xcd; 5: pa_plan_info.partial_rows; 4: pa_workspace_bytes; 3: fp16
                           (PA_F16), block sizes 32 and 64, head sizes 96 and 256 */
 
 /* Return codes.  Every failure is reported before anything is launched, with
@@ -131,7 +131,11 @@ typedef struct {
                             sequences): work-group b takes the (b / Hkv)-th
                             (sequence, query tile, key split) in order of
                             decreasing key count, kv-head b % Hkv            */
-  int32_t reserved;
+  int32_t unit_xcd;      /* 1 (longest_first plans whose every sequence is
+                            one tile): work-group b takes rank
+                            8 (b / 8 / Hkv) + b % 8 and kv-head b / 8 % Hkv,
+                            so the kv-heads of a unit run together on one
+                            XCD (b % 8)                                       */
   int64_t partial_rows;  /* (token, q-head) rows of split partial outputs the
                             workspace holds (0: no split).  Fixed parts:
                             num_splits copies of the batch's rows.  Even

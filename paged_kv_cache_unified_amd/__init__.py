@@ -45,7 +45,7 @@ class PaPlanInfo(ctypes.Structure):
                 ("num_splits", ctypes.c_int32), ("split_keys", ctypes.c_int32),
                 ("num_workgroups", ctypes.c_int64), ("workspace_bytes", ctypes.c_int64),
                 ("persistent", ctypes.c_int32), ("balanced", ctypes.c_int32),
-                ("longest_first", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("longest_first", ctypes.c_int32), ("unit_xcd", ctypes.c_int32),
                 ("partial_rows", ctypes.c_int64)]
 
     def as_dict(self):

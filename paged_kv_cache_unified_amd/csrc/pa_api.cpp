@@ -42,6 +42,7 @@ struct Plan {
   bool wide;        // launch the specialization with the wide-tile path
   bool eight;       // wide plan on the eight-wave kernel (256-row tiles)
   bool lpt;         // grid plan with longest-first unit order
+  bool unit_xcd;    // lpt: a unit's kv-heads on one XCD (units share no K/V)
   bool persistent;  // persistent decode kernel with per-sequence split counts
   bool balanced;    // persistent: even split of the block stream, chunks sized on the device
   int64_t num_items;
@@ -368,6 +369,13 @@ int make_plan(const Shapes& s, int32_t max_q, int32_t max_k, const pa_options* o
   }
   if (p.lpt) {
     p.lpt_units = (int64_t)p.num_slots * n_split;     // units the grid can hold
+    // Every sequence in one tile: no two units read the same K/V (their key
+    // ranges are disjoint), so nothing is gained by keeping a kv-head's
+    // units on one XCD's L2.  The kv-heads of one unit, which read the same
+    // cache blocks (each block holds every kv-head), then run side by side
+    // on one XCD instead, as the decode kernel's waves do.
+    p.unit_xcd = p.slots_direct != 0;
+    if (p.unit_xcd) p.nwg = (p.lpt_units + 7) / 8 * 8 * s.Hkv;
     p.ws_lpt_offset = off;
     off += align256((size_t)p.lpt_units * 4 * sizeof(int32_t));
   }
@@ -616,6 +624,7 @@ int run(const pa_tensor* q, const pa_tensor* k, const pa_tensor* v, pa_tensor* o
   p.sub_sb = (int64_t)pa::kBlockSize * s.Hkv * s.D;
   p.bshift = s.B == 64 ? 2 : (s.B == 32 ? 1 : 0);
   p.lpt = plan.lpt ? 1 : 0;
+  p.unit_xcd = plan.unit_xcd ? 1 : 0;
   p.lpt_units = (int32_t)plan.lpt_units;
   p.lpt_order = plan.lpt ? reinterpret_cast<int4*>(static_cast<char*>(ws) + plan.ws_lpt_offset)
                          : nullptr;
@@ -822,6 +831,7 @@ int pa_plan_describe(const pa_tensor* q, const pa_tensor* k_cache, const pa_tens
   }
   info->tile_tokens = plan.tile_tokens;
   info->longest_first = plan.lpt ? 1 : 0;
+  info->unit_xcd = plan.unit_xcd ? 1 : 0;
   info->tile_rows = plan.tile_rows;
   info->num_slots = plan.num_slots;
   info->slots_direct = plan.slots_direct;

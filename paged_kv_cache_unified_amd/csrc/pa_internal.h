@@ -65,6 +65,8 @@ struct FwdParams {
   int32_t causal;
   int32_t narrow_rows;     // tiles with at most this many packed rows take the narrow path
   int32_t lpt;             // grid plans: units in longest-first order (block b -> rank b / Hkv)
+  int32_t unit_xcd;        // lpt: the kv-heads of a unit run together on one XCD
+                           // (block b -> rank 8 (b / 8 / Hkv) + b % 8, kv-head b / 8 % Hkv)
   int32_t lpt_units;       // entries of lpt_order (the grid's unit capacity)
   int4* lpt_order;         // [lpt_units] (s, tile, split, -) of each rank, from pa_rank_kernel
   float scale_log2;        // softmax_scale * k_scale * log2(e)

@@ -451,9 +451,14 @@ template <int G>
 __device__ __forceinline__ bool decode_item(const FwdParams& p, Item& it) {
   if (p.lpt) {
     // block b -> unit rank b / Hkv, kv-head b % Hkv: with 8 kv-heads every
-    // XCD (b % 8) serves one kv-head, so K/V of its sequences stay in its L2
-    const int r = blockIdx.x / p.num_kv_heads;
-    const int kvh = blockIdx.x % p.num_kv_heads;
+    // XCD (b % 8) serves one kv-head, so K/V of its sequences stay in its L2.
+    // Units that share no K/V (every sequence one tile) instead put a unit's
+    // kv-heads on consecutive blocks of one XCD: rank 8 (b / 8 / Hkv) + b % 8,
+    // kv-head b / 8 % Hkv, so they read each cache block at about one time.
+    const int j = (int)blockIdx.x >> 3;
+    const int r = p.unit_xcd ? (j / p.num_kv_heads) * 8 + ((int)blockIdx.x & 7)
+                             : (int)blockIdx.x / p.num_kv_heads;
+    const int kvh = p.unit_xcd ? j % p.num_kv_heads : (int)blockIdx.x % p.num_kv_heads;
     if (r >= p.lpt_units) return false;              // the grid is rounded up to 8 blocks
     const int4 u = p.lpt_order[r];                   // written by pa_rank_kernel
     if (u.x < 0) return false;

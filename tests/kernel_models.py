@@ -313,7 +313,12 @@ def fwd_kernel(b: Batch, plan: Dict) -> Trace:
     kv_major = Tq * G > NARROW_ROWS          # wide plans number items kv-head major
     for blk in range(nwg):
         if lpt:
-            r, kvh = blk // Hkv, blk % Hkv
+            if plan.get("unit_xcd"):
+                # a unit's kv-heads on consecutive blocks of one XCD
+                j = blk >> 3
+                r, kvh = (j // Hkv) * 8 + (blk & 7), j % Hkv
+            else:
+                r, kvh = blk // Hkv, blk % Hkv
             if r >= lpt_units:
                 continue
             s, tile, sigma = order[r]

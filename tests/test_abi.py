@@ -33,7 +33,7 @@ def test_header_functions_are_exported():
 
 def test_version_and_status_strings():
     import __graft_entry__
-    assert pa.version() == __graft_entry__.header_version() == 5
+    assert pa.version() == __graft_entry__.header_version() == 6
     for code in range(-9, 1):
         assert pa.lib.pa_status_string(code).decode()
     assert pa.lib.pa_status_string(-100).decode() == "unknown status"

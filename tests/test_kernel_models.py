@@ -100,7 +100,7 @@ def test_decode_kernel_work_model(B):
 @pytest.mark.parametrize("B", [16, 32, 64])
 def test_grid_kernel_work_model(B):
     rng = np.random.default_rng(8000 + B)
-    lpt = 0
+    lpt = unit_xcd = 0
     for trial in range(24):
         b, nb = random_batch(rng, decode=trial % 4 == 0, B=B)
         opts = None
@@ -115,9 +115,10 @@ def test_grid_kernel_work_model(B):
             check_trace(b, plan, decode_kernel(b, plan))
             continue
         lpt += plan["longest_first"]
+        unit_xcd += plan["unit_xcd"]
         tr = fwd_kernel(b, plan)
         check_trace(b, plan, tr)
-    assert lpt >= 5
+    assert lpt >= 5 and unit_xcd >= 1, (lpt, unit_xcd)
 
 
 def test_even_split_with_overstated_context_stays_in_the_workspace():
