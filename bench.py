@@ -431,6 +431,8 @@ def main():
 CONFIG_WORKLOADS = [
     "mixed_prefill512x8_decode248",
     "prefill512x8_only",
+    "prefill512x8_only_d96",
+    "prefill512x8_only_d256",
     "decode248_only",
     "decode_gqa8_64seq_ctx2k_4k",
     "long_decode_16seq_ctx32k_128k",

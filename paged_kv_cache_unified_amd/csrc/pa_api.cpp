@@ -223,9 +223,11 @@ int make_plan(const Shapes& s, int32_t max_q, int32_t max_k, const pa_options* o
     return fail(PA_ERR_UNSUPPORTED, "force_tile must be 0, 1, 2, 3 or 4");
   // wide tiles (32 rows per wave, fp32 accumulators of the whole d) exist for
   // d = 64 and 128; other head sizes run every tile on the narrow path
-  const bool wide_ok = s.D == 64 || s.D == 128;
-  if ((force_tile == 2 || force_tile == 4) && !wide_ok)
-    return fail(PA_ERR_UNSUPPORTED, "force_tile=%d (wide tiles) needs head_dim 64 or 128", force_tile);
+  const bool wide_ok = s.D == 64 || s.D == 96 || s.D == 128;
+  if (force_tile == 2 && !wide_ok)
+    return fail(PA_ERR_UNSUPPORTED, "force_tile=2 (wide tiles) needs head_dim 64, 96 or 128");
+  if (force_tile == 4 && !(s.D == 64 || s.D == 128))
+    return fail(PA_ERR_UNSUPPORTED, "force_tile=4 (eight-wave tiles) needs head_dim 64 or 128");
   if (force_tile == 4 && s.kv8)
     return fail(PA_ERR_UNSUPPORTED, "force_tile=4 (eight-wave tiles) needs 16-bit caches");
   const bool narrow = force_tile == 1 || force_tile == 3 || (force_tile == 0 && narrow_fits);

@@ -758,8 +758,14 @@ __device__ __forceinline__ void attend_narrow(const FwdParams& p, const Item& it
 // touching memory) into the other of two LDS buffers while stage st is
 // computed: one barrier per stage, no staging registers.
 // ---------------------------------------------------------------------------
+// Head size of the wide path's LDS layout: d = 96 uses the d = 128 one.
+constexpr int wide_layout_dim(int d) { return d == 96 ? 128 : d; }
+// A buffer offset past the records of any cache block (reads as zeros).
+constexpr int kPadOffset = 1 << 30;
+
 template <int D>
 struct WideCfg {
+  static_assert(D == 64 || D == 128, "wide-tile LDS layouts exist for d = 64 and 128");
   static constexpr int CPR = D / 8;                        // 16-byte chunks per key row
   static constexpr int TENSOR_BYTES = kStageKeys * D * 2;  // K (or V) of one stage
   static constexpr int STAGE_BYTES = 2 * TENSOR_BYTES;
@@ -812,7 +818,11 @@ template <int D, int G, bool KV8, bool F16>
 __device__ __forceinline__ void attend_wide(const FwdParams& p, const Item& it,
                                             unsigned char* smem) {
   using E = Elem<F16>;
-  using Cfg = WideCfg<D>;
+  // LDS layout of the stages: d = 96 rides in the d = 128 layout, its key
+  // rows padded with zeros to 16 chunks (the padding chunks load as zeros and
+  // no MFMA reads them), so the swizzles and DMA shapes of d = 128 serve it
+  constexpr int DL = wide_layout_dim(D);
+  using Cfg = WideCfg<DL>;
   constexpr int ESZ = Kv<KV8>::ESZ;
   using raw8 = typename Kv<KV8>::raw8;
   constexpr int CPR = Cfg::CPR;
@@ -881,10 +891,12 @@ __device__ __forceinline__ void attend_wide(const FwdParams& p, const Item& it,
   const int slot_elems = p.num_kv_heads * D;
   const int ld_r = wave * RPI + lane / CPR;          // key row of load u = 0
   const int ld_p = lane % CPR;                       // slot (bf16) or chunk (fp8) in the row
-  const int ld_gk = ((ld_r % kBlockSize) * slot_elems +
-                     (KV8 ? ld_p : (ld_p ^ Cfg::fk(ld_r))) * 8) * ESZ;
-  const int ld_gv = ((ld_r % kBlockSize) * slot_elems +
-                     (KV8 ? ld_p : (ld_p ^ Cfg::fv(ld_r))) * 8) * ESZ;
+  // (a padding chunk, d = 96: an offset past every block's records, so the
+  // load returns zeros without a memory access)
+  const int ld_ck = KV8 ? ld_p : (ld_p ^ Cfg::fk(ld_r));
+  const int ld_cv = KV8 ? ld_p : (ld_p ^ Cfg::fv(ld_r));
+  const int ld_gk = ld_ck < D / 8 ? ((ld_r % kBlockSize) * slot_elems + ld_ck * 8) * ESZ : kPadOffset;
+  const int ld_gv = ld_cv < D / 8 ? ((ld_r % kBlockSize) * slot_elems + ld_cv * 8) * ESZ : kPadOffset;
   const int ld_sk = (ld_r * CPR + (ld_p ^ Cfg::fk(ld_r))) * 16;   // fp8: LDS slot of the chunk
   const int ld_sv = (ld_r * CPR + (ld_p ^ Cfg::fv(ld_r))) * 16;
   const uint32_t lds0 = uniform((int)(uint32_t)(uintptr_t)smem) + wave * RPI * CPR * 16;
@@ -896,7 +908,7 @@ __device__ __forceinline__ void attend_wide(const FwdParams& p, const Item& it,
     for (int u = 0; u < CPT; ++u) {
       // block within the stage: u (d = 128: 4 key rows per load) or 2u + wave/2
       // (d = 64: 8 key rows per load)
-      const int bi = D == 128 ? u : 2 * u + ((wave & 2) ? 1 : 0);
+      const int bi = DL == 128 ? u : 2 * u + ((wave & 2) ? 1 : 0);
       const int jl = st * (kStageKeys / kBlockSize) + bi;
       const int64_t boff = uniform64(offs[jl]);
       // keys of the block inside the item (0 past its end: no memory access,
@@ -1527,8 +1539,9 @@ template <int D, int G, bool WIDE, bool KV8, bool F16>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
 void pa_fwd_kernel(FwdParams p) {
   // wide tiles exist for d = 64 and 128 only (the plan gives other sizes narrow tiles)
-  constexpr bool HAS_WIDE = WIDE && (D == 64 || D == 128);
-  constexpr int SMEM = HAS_WIDE ? WideCfg<D>::SMEM : NarrowCfg<D>::SMEM;
+  constexpr bool HAS_WIDE = WIDE && (D == 64 || D == 96 || D == 128);
+  constexpr int WSMEM = WideCfg<wide_layout_dim(HAS_WIDE ? D : 128)>::SMEM;
+  constexpr int SMEM = HAS_WIDE && WSMEM > NarrowCfg<D>::SMEM ? WSMEM : NarrowCfg<D>::SMEM;
   __shared__ __attribute__((aligned(16))) unsigned char smem[SMEM];
   Item it;
   if (!decode_item<G>(p, it)) return;
@@ -2190,7 +2203,7 @@ __global__ __launch_bounds__(256) void pa_merge2_kernel(Merge2Params p) {
 
 template <int D, int G, bool KV8, bool F16>
 hipError_t launch_fwd_t(const FwdParams& p, bool wide, int64_t nwg, hipStream_t stream) {
-  if constexpr (D == 64 || D == 128) {
+  if constexpr (D == 64 || D == 96 || D == 128) {
     if (wide) {
       hipLaunchKernelGGL((pa_fwd_kernel<D, G, true, KV8, F16>), dim3((unsigned)nwg),
                          dim3(kThreads), 0, stream, p);

@@ -1,6 +1,7 @@
-"""GPU parity at head sizes 96 and 256 (the decode and narrow paths; prefill
-chunks run as narrow tiles of 16 / G tokens at these sizes), with forced
-splits, fp8 and fp16 caches, and the merges."""
+"""GPU parity at head sizes 96 and 256: the decode and narrow paths, wide
+tiles at d = 96 (in the d = 128 LDS layout with zero padding; d = 256 runs
+prefill chunks as narrow tiles of 16 / G tokens), with forced splits, fp8 and
+fp16 caches, and the merges."""
 
 import pytest
 import torch
@@ -24,6 +25,8 @@ CASES = {
     "prefill_splits": ([64, 9], [2500, 90], 16, 4, True, dict(force_num_splits=3), "bf16"),
     "fp8_decode": ([1] * 5, [40, 300, 1000, 65, 4000], 32, 8, True, {}, "fp8_e4m3fn"),
     "f16_mixed": ([50, 1, 1], [700, 64, 2000], 32, 8, True, {}, "f16"),
+    "fp8_prefill": ([70, 1, 33], [600, 50, 2000], 32, 8, True, {}, "fp8_e4m3fn"),
+    "wide_forced": ([1, 3, 1, 16], [500, 40, 1200, 16], 32, 8, True, dict(force_tile=2), "bf16"),
 }
 
 
@@ -32,6 +35,8 @@ CASES = {
 def test_head_size_parity(case, d):
     require_gpu()
     q_lens, k_lens, hq, hkv, causal, opt, kv = CASES[case]
+    if d == 256 and opt.get("force_tile") == 2:
+        pytest.skip("no wide tiles at d = 256")
     extra = dict(k_scale=1 / 32, v_scale=1 / 16) if kv == "fp8_e4m3fn" else {}
     b = build_batch(f"d{d}_{case}", q_lens, k_lens, hq, hkv, d, causal, seed=700 + d + len(case),
                     device=DEV, kv_dtype=kv, **extra)

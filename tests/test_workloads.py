@@ -42,7 +42,7 @@ def test_workload_lengths(name):
         assert (k[q == 512] >= 512).all() and (k[q == 512] <= 2048).all()
         assert k[q == 1].min() >= 4 and k[q == 1].max() <= 8192
         assert not (q[:8] == 512).all()            # shuffled order
-    if name == "prefill512x8_only":
+    if name.startswith("prefill512x8_only"):
         assert len(q) == 8 and (q == 512).all()
     if name == "decode248_only":
         assert len(q) == 248 and (q == 1).all()
@@ -58,6 +58,9 @@ def test_mixed_subsets_share_draws():
     qp, kp, _ = lengths("prefill512x8_only")
     qd, kd, _ = lengths("decode248_only")
     assert (kp == k[q == 512]).all() and (kd == k[q == 1]).all()
+    for d in (96, 256):
+        qx, kx, _ = lengths(f"prefill512x8_only_d{d}")
+        assert (qx == qp).all() and (kx == kp).all()
 
 
 def test_pool_structure():

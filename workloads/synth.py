@@ -339,6 +339,10 @@ WORKLOADS = {
     "decode_256seq_ctx1k": (2, 32, 8, 128, True),
     "mixed_prefill512x8_decode248": (3, 32, 8, 128, True),
     "prefill512x8_only": (3, 32, 8, 128, True),
+    # the same prefill chunks at head sizes 96 and 256 (these sizes run
+    # prefill on narrow tiles)
+    "prefill512x8_only_d96": (3, 32, 8, 96, True),
+    "prefill512x8_only_d256": (3, 32, 8, 256, True),
     "decode248_only": (3, 32, 8, 128, True),
     "decode_gqa8_64seq_ctx2k_4k": (4, 32, 4, 128, True),
     "long_decode_16seq_ctx32k_128k": (5, 32, 8, 128, True),
@@ -362,7 +366,8 @@ def workload_lengths(name: str, children) -> Tuple[np.ndarray, np.ndarray, Optio
     if name in ("decode_256seq_ctx1k", "decode_256seq_ctx1k_fp8"):
         L = rng_len.integers(1000, 1100, size=256, endpoint=True)
         return np.ones(256, np.int64), L, None
-    if name in ("mixed_prefill512x8_decode248", "prefill512x8_only", "decode248_only"):
+    if name in ("mixed_prefill512x8_decode248", "prefill512x8_only", "decode248_only",
+                "prefill512x8_only_d96", "prefill512x8_only_d256"):
         prefix = rng_len.integers(0, 1536, size=8, endpoint=True)
         Lp = prefix + 512
         Ld = np.clip(np.round(np.exp(rng_len.normal(math.log(400.0), 1.0, size=248))), 4, 8192)
@@ -371,7 +376,7 @@ def workload_lengths(name: str, children) -> Tuple[np.ndarray, np.ndarray, Optio
         ks = np.concatenate([Lp, Ld])
         order = rng_ord.permutation(256)
         qs, ks = qs[order], ks[order]
-        if name == "prefill512x8_only":
+        if name.startswith("prefill512x8_only"):
             keep = qs > 1
             return qs[keep], ks[keep], None
         if name == "decode248_only":
