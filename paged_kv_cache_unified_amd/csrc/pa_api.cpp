@@ -223,9 +223,6 @@ int make_plan(const Shapes& s, int32_t max_q, int32_t max_k, const pa_options* o
     return fail(PA_ERR_UNSUPPORTED, "force_tile must be 0, 1, 2, 3 or 4");
   // wide tiles (32 rows per wave, fp32 accumulators of the whole d) exist for
   // d = 64 and 128; other head sizes run every tile on the narrow path
-  const bool wide_ok = s.D == 64 || s.D == 96 || s.D == 128;
-  if (force_tile == 2 && !wide_ok)
-    return fail(PA_ERR_UNSUPPORTED, "force_tile=2 (wide tiles) needs head_dim 64, 96 or 128");
   if (force_tile == 4 && !(s.D == 64 || s.D == 128))
     return fail(PA_ERR_UNSUPPORTED, "force_tile=4 (eight-wave tiles) needs head_dim 64 or 128");
   if (force_tile == 4 && s.kv8)
@@ -315,12 +312,6 @@ int make_plan(const Shapes& s, int32_t max_q, int32_t max_k, const pa_options* o
     p.slots_direct = 1;
     p.num_slots = (int32_t)s.S;
     p.wide = false;
-  } else if (!wide_ok) {
-    // narrow tiles of 16 / G tokens; a sequence spans several of them
-    p.wide = false;
-    p.tile_tokens = (int32_t)std::max<int64_t>(1, pa::kNarrowRows / G);
-    p.slots_direct = 0;
-    p.num_slots = (int32_t)(s.T / p.tile_tokens + s.S);
   } else {
     p.wide = true;
     p.eight = force_tile == 4;

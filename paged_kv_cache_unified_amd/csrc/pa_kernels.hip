@@ -765,7 +765,7 @@ constexpr int kPadOffset = 1 << 30;
 
 template <int D>
 struct WideCfg {
-  static_assert(D == 64 || D == 128, "wide-tile LDS layouts exist for d = 64 and 128");
+  static_assert(D == 64 || D == 128 || D == 256, "wide-tile LDS layouts: d = 64, 128, 256");
   static constexpr int CPR = D / 8;                        // 16-byte chunks per key row
   static constexpr int TENSOR_BYTES = kStageKeys * D * 2;  // K (or V) of one stage
   static constexpr int STAGE_BYTES = 2 * TENSOR_BYTES;
@@ -781,9 +781,9 @@ struct WideCfg {
   // 16 keys one K-operand read takes at a fixed chunk over 16 bank windows;
   // fv does the same for the 4 rows x 4 chunks of each half-wave of a V
   // transpose read.  Both depend on r % 16 only.
-  static __device__ __forceinline__ int fk(int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); }
+  static __device__ __forceinline__ int fk(int r) { return D >= 128 ? (r & 15) : ((r >> 1) & 7); }
   static __device__ __forceinline__ int fv(int r) {
-    return D == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1);
+    return D >= 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1);
   }
 };
 
@@ -889,16 +889,27 @@ __device__ __forceinline__ void attend_wide(const FwdParams& p, const Item& it,
   // s ^ f(r)).  fp8: each lane loads its row chunk's 8 codes into registers
   // and, after the stage's compute, writes them as bf16 to the swizzled slot.
   const int slot_elems = p.num_kv_heads * D;
-  const int ld_r = wave * RPI + lane / CPR;          // key row of load u = 0
+  // Load u of a wave covers stage rows u * 4 RPI + wave * RPI + [0, RPI);
+  // this lane takes row ld_r of them (+ u * 4 RPI) and slot / chunk ld_p.
+  // The swizzle depends on the row mod 16, which is ld_r's except at d = 256
+  // (8 rows per load: odd loads are rows 8 .. 15 of their block), hence NV
+  // address sets, load u using set u % NV.
+  constexpr int NV = DL == 256 ? 2 : 1;
+  const int ld_r = wave * RPI + lane / CPR;
   const int ld_p = lane % CPR;                       // slot (bf16) or chunk (fp8) in the row
-  // (a padding chunk, d = 96: an offset past every block's records, so the
-  // load returns zeros without a memory access)
-  const int ld_ck = KV8 ? ld_p : (ld_p ^ Cfg::fk(ld_r));
-  const int ld_cv = KV8 ? ld_p : (ld_p ^ Cfg::fv(ld_r));
-  const int ld_gk = ld_ck < D / 8 ? ((ld_r % kBlockSize) * slot_elems + ld_ck * 8) * ESZ : kPadOffset;
-  const int ld_gv = ld_cv < D / 8 ? ((ld_r % kBlockSize) * slot_elems + ld_cv * 8) * ESZ : kPadOffset;
-  const int ld_sk = (ld_r * CPR + (ld_p ^ Cfg::fk(ld_r))) * 16;   // fp8: LDS slot of the chunk
-  const int ld_sv = (ld_r * CPR + (ld_p ^ Cfg::fv(ld_r))) * 16;
+  int ld_gk[NV], ld_gv[NV], ld_sk[NV], ld_sv[NV];
+#pragma unroll
+  for (int v = 0; v < NV; ++v) {
+    const int r = ld_r + v * 4 * RPI;                // stage row mod 16 of loads u = v (mod NV)
+    // (a padding chunk, d = 96: an offset past every block's records, so the
+    // load returns zeros without a memory access)
+    const int ck = KV8 ? ld_p : (ld_p ^ Cfg::fk(r));
+    const int cv = KV8 ? ld_p : (ld_p ^ Cfg::fv(r));
+    ld_gk[v] = ck < D / 8 ? ((r % kBlockSize) * slot_elems + ck * 8) * ESZ : kPadOffset;
+    ld_gv[v] = cv < D / 8 ? ((r % kBlockSize) * slot_elems + cv * 8) * ESZ : kPadOffset;
+    ld_sk[v] = (ld_r * CPR + (ld_p ^ Cfg::fk(r))) * 16;   // fp8: LDS slot of the chunk
+    ld_sv[v] = (ld_r * CPR + (ld_p ^ Cfg::fv(r))) * 16;
+  }
   const uint32_t lds0 = uniform((int)(uint32_t)(uintptr_t)smem) + wave * RPI * CPR * 16;
   raw8 kraw[KV8 ? CPT : 1], vraw[KV8 ? CPT : 1];
   // wave-uniform copies: the per-block address and bound arithmetic is scalar
@@ -906,9 +917,9 @@ __device__ __forceinline__ void attend_wide(const FwdParams& p, const Item& it,
   auto load_stage = [&](int st, int buf) {
 #pragma unroll
     for (int u = 0; u < CPT; ++u) {
-      // block within the stage: u (d = 128: 4 key rows per load) or 2u + wave/2
-      // (d = 64: 8 key rows per load)
-      const int bi = DL == 128 ? u : 2 * u + ((wave & 2) ? 1 : 0);
+      // block within the stage of this wave's rows: 2u + wave/2 (d = 64), u
+      // (d = 128) or u/2 (d = 256)
+      const int bi = (u * 4 * RPI + wave * RPI) / kBlockSize;
       const int jl = st * (kStageKeys / kBlockSize) + bi;
       const int64_t boff = uniform64(offs[jl]);
       // keys of the block inside the item (0 past its end: no memory access,
@@ -920,12 +931,12 @@ __device__ __forceinline__ void attend_wide(const FwdParams& p, const Item& it,
       const __amdgpu_buffer_rsrc_t rv =
           __builtin_amdgcn_make_buffer_rsrc(uniform_ptr(p.v + boff), (short)0, nrec, 0x00020000);
       if constexpr (KV8) {
-        kraw[u] = bload8<true>(rk, ld_gk);
-        vraw[u] = bload8<true>(rv, ld_gv);
+        kraw[u] = bload8<true>(rk, ld_gk[u % NV]);
+        vraw[u] = bload8<true>(rv, ld_gv[u % NV]);
       } else {
         const uint32_t dst = lds0 + buf * SB + u * 4 * RPI * CPR * 16;
-        dma16(rk, ld_gk, dst);
-        dma16(rv, ld_gv, dst + TB);
+        dma16(rk, ld_gk[u % NV], dst);
+        dma16(rv, ld_gv[u % NV], dst + TB);
       }
     }
   };
@@ -935,8 +946,9 @@ __device__ __forceinline__ void attend_wide(const FwdParams& p, const Item& it,
       unsigned char* base = smem + buf * SB;
 #pragma unroll
       for (int u = 0; u < CPT; ++u) {
-        *reinterpret_cast<u32x4*>(base + u * 4 * RPI * CPR * 16 + ld_sk) = to_elem8<F16>(kraw[u]);
-        *reinterpret_cast<u32x4*>(base + TB + u * 4 * RPI * CPR * 16 + ld_sv) = to_elem8<F16>(vraw[u]);
+        *reinterpret_cast<u32x4*>(base + u * 4 * RPI * CPR * 16 + ld_sk[u % NV]) = to_elem8<F16>(kraw[u]);
+        *reinterpret_cast<u32x4*>(base + TB + u * 4 * RPI * CPR * 16 + ld_sv[u % NV]) =
+            to_elem8<F16>(vraw[u]);
       }
     }
   };
@@ -1539,7 +1551,7 @@ template <int D, int G, bool WIDE, bool KV8, bool F16>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
 void pa_fwd_kernel(FwdParams p) {
   // wide tiles exist for d = 64 and 128 only (the plan gives other sizes narrow tiles)
-  constexpr bool HAS_WIDE = WIDE && (D == 64 || D == 96 || D == 128);
+  constexpr bool HAS_WIDE = WIDE;
   constexpr int WSMEM = WideCfg<wide_layout_dim(HAS_WIDE ? D : 128)>::SMEM;
   constexpr int SMEM = HAS_WIDE && WSMEM > NarrowCfg<D>::SMEM ? WSMEM : NarrowCfg<D>::SMEM;
   __shared__ __attribute__((aligned(16))) unsigned char smem[SMEM];
@@ -2203,16 +2215,12 @@ __global__ __launch_bounds__(256) void pa_merge2_kernel(Merge2Params p) {
 
 template <int D, int G, bool KV8, bool F16>
 hipError_t launch_fwd_t(const FwdParams& p, bool wide, int64_t nwg, hipStream_t stream) {
-  if constexpr (D == 64 || D == 96 || D == 128) {
-    if (wide) {
-      hipLaunchKernelGGL((pa_fwd_kernel<D, G, true, KV8, F16>), dim3((unsigned)nwg),
-                         dim3(kThreads), 0, stream, p);
-      return hipGetLastError();
-    }
-  } else if (wide) {
-    return hipErrorInvalidValue;                     // no wide tiles for this head size
+  if (wide) {
+    hipLaunchKernelGGL((pa_fwd_kernel<D, G, true, KV8, F16>), dim3((unsigned)nwg), dim3(kThreads),
+                       0, stream, p);
+    return hipGetLastError();
   }
-    hipLaunchKernelGGL((pa_fwd_kernel<D, G, false, KV8, F16>), dim3((unsigned)nwg), dim3(kThreads),
+  hipLaunchKernelGGL((pa_fwd_kernel<D, G, false, KV8, F16>), dim3((unsigned)nwg), dim3(kThreads),
                        0, stream, p);
   return hipGetLastError();
 }

@@ -102,8 +102,8 @@ def test_head_ratio_and_unsupported():
     k = torch.zeros(b["k_cache"].shape[0], 16, 2, 128, dtype=torch.bfloat16)
     q = torch.zeros(6, 6, 128, dtype=torch.bfloat16)
     assert status_of(q=q, out=torch.zeros_like(q), k_cache=k, v_cache=k.clone())[0] == "PA_ERR_UNSUPPORTED"
-    # head sizes 64, 96, 128, 256 are built (256 on narrow tiles only, no
-    # eight-wave tiles at 96), others are not
+    # head sizes 64, 96, 128, 256 are built (no eight-wave tiles at 96 and
+    # 256), others are not
     q = torch.zeros(6, 8, 32, dtype=torch.bfloat16)
     k = torch.zeros(b["k_cache"].shape[0], 16, 2, 32, dtype=torch.bfloat16)
     assert status_of(q=q, out=torch.zeros_like(q), k_cache=k, v_cache=k.clone())[0] == "PA_ERR_UNSUPPORTED"
@@ -111,12 +111,8 @@ def test_head_ratio_and_unsupported():
         bb = build_batch("abi", [1, 40, 2], [5, 70, 40], 8, 2, d, True, seed=1)
         args = bb.args(torch.empty_like(bb.q))[:9]
         assert pa.plan_describe(*args)["persistent"] == 0
-        assert pa.plan_describe(*args)["tile_rows"] == (128 if d == 96 else 16)
-        if d == 256:
-            with pytest.raises(pa.PaError, match="PA_ERR_UNSUPPORTED"):
-                pa.plan_describe(*args, opts=pa.options(force_tile=2))
-        else:
-            assert pa.plan_describe(*args, opts=pa.options(force_tile=2))["tile_rows"] == 128
+        assert pa.plan_describe(*args)["tile_rows"] == 128
+        assert pa.plan_describe(*args, opts=pa.options(force_tile=2))["tile_rows"] == 128
         with pytest.raises(pa.PaError, match="PA_ERR_UNSUPPORTED"):
             pa.plan_describe(*args, opts=pa.options(force_tile=4))
     # block sizes 16, 32 and 64 are built (the host plan accepts them), others are not
