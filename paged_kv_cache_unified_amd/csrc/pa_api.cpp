@@ -221,8 +221,7 @@ int make_plan(const Shapes& s, int32_t max_q, int32_t max_k, const pa_options* o
     return fail(PA_ERR_UNSUPPORTED, "force_tile=%d needs max_seqlen_q * G <= 16", force_tile);
   if (force_tile < 0 || force_tile > 4)
     return fail(PA_ERR_UNSUPPORTED, "force_tile must be 0, 1, 2, 3 or 4");
-  // wide tiles (32 rows per wave, fp32 accumulators of the whole d) exist for
-  // d = 64 and 128; other head sizes run every tile on the narrow path
+  // eight-wave tiles exist for d = 64 and 128 over 16-bit caches
   if (force_tile == 4 && !(s.D == 64 || s.D == 128))
     return fail(PA_ERR_UNSUPPORTED, "force_tile=4 (eight-wave tiles) needs head_dim 64 or 128");
   if (force_tile == 4 && s.kv8)
