@@ -814,6 +814,48 @@ __device__ __forceinline__ i16x4 lds_read_tr(const PA_LDS bf16x4* __restrict__ a
   return __builtin_bit_cast(i16x4, __builtin_amdgcn_ds_read_tr16_b64_v4bf16((PA_LDS bf16x4*)a));
 }
 
+// Epilogue of a 32-row wave on the 32x32 layouts: lanes l and l ^ 32
+// together hold row l % 32.  One-part rows go to out (and the lse export),
+// rows of split sequences to the workspace as normalised fp32 partials with
+// their log2-domain lse.
+template <int D, int G, bool F16>
+__device__ __forceinline__ void wide_epilogue(const FwdParams& p, const Item& it,
+                                              f32x16 (&acc)[D / 32], float m, float l, float c,
+                                              bool row_ok, int t_in, int head, int h) {
+  using E = Elem<F16>;
+  constexpr int DT = D / 32;
+  const float lt = swap_halves_sum(l);
+  if (!row_ok) return;
+  const float inv = lt > 0.f ? p.out_scale / lt : 0.f;
+  const int64_t tok = it.q0 + it.tok0 + t_in;
+  if (p.ws_rparts && it.sigma == 0 && h == 0)
+    p.ws_rparts[tok * p.num_q_heads + head] = it.parts;   // the row's part count, for pa_merge
+  if (it.parts == 1) {
+    if (h == 0) store_lse(p.lse_out, p.lse_st, tok, head, lt > 0.f ? m * c + __log2f(lt) : kNegInf);
+    uint16_t* op = p.out + tok * p.o_st + (int64_t)head * p.o_sh + 4 * h;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const u32x2 w = {E::pack2(acc[dt][4 * j] * inv, acc[dt][4 * j + 1] * inv),
+                         E::pack2(acc[dt][4 * j + 2] * inv, acc[dt][4 * j + 3] * inv)};
+        *reinterpret_cast<u32x2*>(op + 32 * dt + 8 * j) = w;
+      }
+  } else {
+    const int64_t r = ((int64_t)it.sigma * p.total_q + tok) * p.num_q_heads + head;
+    float* wp = p.ws_o + r * D + 4 * h;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const f32x4 v = {acc[dt][4 * j] * inv, acc[dt][4 * j + 1] * inv,
+                         acc[dt][4 * j + 2] * inv, acc[dt][4 * j + 3] * inv};
+        *reinterpret_cast<f32x4*>(wp + 32 * dt + 8 * j) = v;
+      }
+    if (h == 0) p.ws_lse[r] = lt > 0.f ? m * c + __log2f(lt) : kNegInf;
+  }
+}
+
 template <int D, int G, bool KV8, bool F16>
 __device__ __forceinline__ void attend_wide(const FwdParams& p, const Item& it,
                                             unsigned char* smem) {
@@ -1127,37 +1169,7 @@ __device__ __forceinline__ void attend_wide(const FwdParams& p, const Item& it,
     m = mm;
   }
 
-  // ---- epilogue: lanes l and l ^ 32 together hold the row
-  const float lt = swap_halves_sum(l);
-  if (!row_ok) return;
-  const float inv = lt > 0.f ? p.out_scale / lt : 0.f;
-  const int64_t tok = it.q0 + it.tok0 + t_in;
-  if (p.ws_rparts && it.sigma == 0 && h == 0)
-    p.ws_rparts[tok * p.num_q_heads + head] = it.parts;   // the row's part count, for pa_merge
-  if (it.parts == 1) {
-    if (h == 0) store_lse(p.lse_out, p.lse_st, tok, head, lt > 0.f ? m * c + __log2f(lt) : kNegInf);
-    uint16_t* op = p.out + tok * p.o_st + (int64_t)head * p.o_sh + 4 * h;
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const u32x2 w = {E::pack2(acc[dt][4 * j] * inv, acc[dt][4 * j + 1] * inv),
-                         E::pack2(acc[dt][4 * j + 2] * inv, acc[dt][4 * j + 3] * inv)};
-        *reinterpret_cast<u32x2*>(op + 32 * dt + 8 * j) = w;
-      }
-  } else {
-    const int64_t r = ((int64_t)it.sigma * p.total_q + tok) * p.num_q_heads + head;
-    float* wp = p.ws_o + r * D + 4 * h;
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const f32x4 v = {acc[dt][4 * j] * inv, acc[dt][4 * j + 1] * inv,
-                         acc[dt][4 * j + 2] * inv, acc[dt][4 * j + 3] * inv};
-        *reinterpret_cast<f32x4*>(wp + 32 * dt + 8 * j) = v;
-      }
-    if (h == 0) p.ws_lse[r] = lt > 0.f ? m * c + __log2f(lt) : kNegInf;
-  }
+  wide_epilogue<D, G, F16>(p, it, acc, m, l, c, row_ok, t_in, head, h);
 }
 
 // ---------------------------------------------------------------------------
@@ -1499,37 +1511,7 @@ __device__ __forceinline__ void attend_wide8(const FwdParams& p, const Item& it,
         break;
   }
 
-  // ---- epilogue: lanes l and l ^ 32 together hold the row
-  const float lt = swap_halves_sum(l);
-  if (!row_ok) return;
-  const float inv = lt > 0.f ? p.out_scale / lt : 0.f;
-  const int64_t tok = it.q0 + it.tok0 + t_in;
-  if (p.ws_rparts && it.sigma == 0 && h == 0)
-    p.ws_rparts[tok * p.num_q_heads + head] = it.parts;   // the row's part count, for pa_merge
-  if (it.parts == 1) {
-    if (h == 0) store_lse(p.lse_out, p.lse_st, tok, head, lt > 0.f ? m * c + __log2f(lt) : kNegInf);
-    uint16_t* op = p.out + tok * p.o_st + (int64_t)head * p.o_sh + 4 * h;
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const u32x2 w = {E::pack2(acc[dt][4 * j] * inv, acc[dt][4 * j + 1] * inv),
-                         E::pack2(acc[dt][4 * j + 2] * inv, acc[dt][4 * j + 3] * inv)};
-        *reinterpret_cast<u32x2*>(op + 32 * dt + 8 * j) = w;
-      }
-  } else {
-    const int64_t r = ((int64_t)it.sigma * p.total_q + tok) * p.num_q_heads + head;
-    float* wp = p.ws_o + r * D + 4 * h;
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const f32x4 v = {acc[dt][4 * j] * inv, acc[dt][4 * j + 1] * inv,
-                         acc[dt][4 * j + 2] * inv, acc[dt][4 * j + 3] * inv};
-        *reinterpret_cast<f32x4*>(wp + 32 * dt + 8 * j) = v;
-      }
-    if (h == 0) p.ws_lse[r] = lt > 0.f ? m * c + __log2f(lt) : kNegInf;
-  }
+  wide_epilogue<D, G, F16>(p, it, acc, m, l, c, row_ok, t_in, head, h);
 }
 
 // The eight-wave unified grid kernel: wide tiles of up to 256 rows on the
