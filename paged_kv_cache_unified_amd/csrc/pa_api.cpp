@@ -533,13 +533,14 @@ int run(const pa_tensor* q, const pa_tensor* k, const pa_tensor* v, pa_tensor* o
     rc = validate_lse(lse, s, q, k, v, out);
     if (rc != PA_OK) return rc;
   }
-  if (s.T == 0 || s.S == 0) return PA_OK;
+  // the options are checked for every batch, an empty one included
   bool have_dev = false;
   const int ncu = device_cu_count(&have_dev);
   const int dbpc = have_dev ? decode_blocks_per_cu_cached((int)s.D, (int)s.G, s.kv8, s.f16) : 2;
   Plan plan;
   rc = make_plan(s, max_q, max_k, opt, ncu, dbpc, &plan);
   if (rc != PA_OK) return rc;
+  if (s.T == 0 || s.S == 0) return PA_OK;
   hipStream_t stream = reinterpret_cast<hipStream_t>(stream_v);
   std::unique_lock<std::mutex> ws_lock;   // held until the kernels are enqueued
   if (ws_mode == WsMode::kLibrary) {
@@ -782,12 +783,12 @@ size_t pa_workspace_size(const pa_tensor* q, const pa_tensor* k_cache, const pa_
   if (validate(q, k_cache, v_cache, out, cu_seqlens_q, seqused_k, block_table, max_seqlen_q,
                max_seqlen_k, &s) != PA_OK)
     return (size_t)-1;
-  if (s.T == 0 || s.S == 0) return 0;
   bool have_dev = false;
   const int ncu = device_cu_count(&have_dev);
   const int dbpc = have_dev ? decode_blocks_per_cu_cached((int)s.D, (int)s.G, s.kv8, s.f16) : 2;
   Plan plan;
   if (make_plan(s, max_seqlen_q, max_seqlen_k, opt, ncu, dbpc, &plan) != PA_OK) return (size_t)-1;
+  if (s.T == 0 || s.S == 0) return 0;           // (options checked above)
   return plan.ws_bytes;
 }
 

@@ -396,3 +396,21 @@ def test_noalloc_refuses_before_touching_the_device():
     assert e.value.status == -4
     empty = build_batch("empty", [], [], 32, 8, 128, True, seed=312, device="cpu")
     pa.unified_attention_noalloc(*empty.args(empty.new_out()))
+
+
+def test_empty_batch_still_checks_the_options():
+    """An empty batch (no sequence, or no query token) launches nothing, but
+    its options are checked as for any other batch: an unsupported force_tile
+    fails the call and gives no workspace size."""
+    for S in (0, 2):
+        b = build_batch("abi", [0] * S, [5] * S, 8, 2, 128, True, seed=2)
+        a = dict(q=b.q, k_cache=b.k_cache, v_cache=b.v_cache, out=torch.empty_like(b.q),
+                 cu_seqlens_q=b.cu_seqlens_q, seqused_k=b.seqused_k, block_table=b.block_table,
+                 max_seqlen_q=1, max_seqlen_k=16, softmax_scale=0.1, causal=True)
+        assert b.q.shape[0] == 0
+        assert pa.STATUS[call(a, pa.options(force_tile=7))] == "PA_ERR_UNSUPPORTED"
+        assert pa.STATUS[call(a, pa.options())] == "PA_OK"
+        args = b.args(torch.empty_like(b.q))[:9]
+        with pytest.raises(pa.PaError, match="force_tile must be"):
+            pa.workspace_bytes(*args, pa.options(force_tile=7))
+        assert pa.workspace_bytes(*args, pa.options()) == 0
