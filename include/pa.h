@@ -41,8 +41,10 @@
 extern "C" {
 #endif
 
-#define PA_VERSION 6   /* 6: pa_plan_info.unit_xcd, wide tiles at head sizes 96 and 256; 5: pa_plan_info.partial_rows; 4: pa_workspace_bytes; 3: fp16
-                          (PA_F16), block sizes 32 and 64, head sizes 96 and 256 */
+#define PA_VERSION 6   /* 6: pa_plan_info.unit_xcd, wide tiles at head sizes 96
+                          and 256; 5: pa_plan_info.partial_rows; 4:
+                          pa_workspace_bytes; 3: fp16 (PA_F16), block sizes
+                          32 and 64, head sizes 96 and 256 */
 
 /* Return codes.  Every failure is reported before anything is launched, with
  * one exception: PA_ERR_HIP, which may also come from the launch itself. */

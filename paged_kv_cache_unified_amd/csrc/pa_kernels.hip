@@ -19,7 +19,7 @@
 //    serves G heads (the packing of a kv-head's query heads into the query
 //    dimension that the unified-kernel page adopts).  Tiles of at most 16
 //    packed rows take the narrow path (four waves split the keys), larger ones
-//    the wide path (each wave owns 32 rows, 32x32x16 MFMA; d = 64 and 128).
+//    the wide path (each wave owns 32 rows, 32x32x16 MFMA; every head size).
 //    Wide plans run their units longest-first, in the order pa_rank_kernel
 //    sorts them into.
 //  * pa_decode_kernel: persistent decode for batches whose every sequence is
@@ -1532,7 +1532,6 @@ void pa_fwd8_kernel(FwdParams p) {
 template <int D, int G, bool WIDE, bool KV8, bool F16>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
 void pa_fwd_kernel(FwdParams p) {
-  // wide tiles exist for d = 64 and 128 only (the plan gives other sizes narrow tiles)
   constexpr bool HAS_WIDE = WIDE;
   constexpr int WSMEM = WideCfg<wide_layout_dim(HAS_WIDE ? D : 128)>::SMEM;
   constexpr int SMEM = HAS_WIDE && WSMEM > NarrowCfg<D>::SMEM ? WSMEM : NarrowCfg<D>::SMEM;
