@@ -50,7 +50,7 @@ def plan_of(b: Batch, num_blocks: int, opts=None, num_cus=256):
 def random_batch(rng, decode: bool, B: int):
     hkv = int(rng.choice([1, 2, 4, 8]))
     g = int(rng.choice([1, 2, 4, 8, 16]))
-    d = int(rng.choice([64, 128]))
+    d = int(rng.choice([64, 96, 128, 256]))
     S = int(rng.choice([1, 3, 17, 64, 255, 600] if decode else [1, 3, 17, 64]))
     kind = rng.integers(4) if S <= 64 else int(rng.choice([0, 1, 3]))
     if kind == 0:
