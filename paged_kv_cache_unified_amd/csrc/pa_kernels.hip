@@ -431,12 +431,13 @@ __global__ __launch_bounds__(kThreads) void pa_rank_kernel(FwdParams p) {
   };
   walk([&](int, int, int, int w) { atomicAdd(&hist[w], 1); });
   __syncthreads();
-  if (tid == 0) {                                    // first rank of each stage count
-    int r = 0;
-    for (int w = 64; w >= 0; --w) {
-      next[w] = r;
-      r += hist[w];
-    }
+  {
+    // first rank of each stage count: an exclusive scan of the counts taken
+    // from the longest (64 stages) down, thread t holding stage count 64 - t
+    const int c = tid <= 64 ? hist[64 - tid] : 0;
+    int all;
+    const int first = block_exclusive_scan(c, scr, &all);
+    if (tid <= 64) next[64 - tid] = first;
   }
   __syncthreads();
   walk([&](int s, int tile, int sg, int w) {
@@ -1528,9 +1529,11 @@ void pa_fwd8_kernel(FwdParams p) {
 
 // WIDE = false: every tile of the batch is narrow (the plan guarantees it).
 // KV8: the caches hold fp8 E4M3 codes.  F16: q, out (and 16-bit caches) are
-// fp16, else bf16.
+// fp16, else bf16.  Two work-groups per CU, except wide tiles at d = 256,
+// whose registers (accumulators in AGPRs) allow one wave per SIMD.
 template <int D, int G, bool WIDE, bool KV8, bool F16>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
+__global__ __launch_bounds__(kThreads)
+__attribute__((amdgpu_waves_per_eu(WIDE && D == 256 ? 1 : 2)))
 void pa_fwd_kernel(FwdParams p) {
   constexpr bool HAS_WIDE = WIDE;
   constexpr int WSMEM = WideCfg<wide_layout_dim(HAS_WIDE ? D : 128)>::SMEM;
@@ -2278,11 +2281,11 @@ hipError_t launch_merge2_t(const Merge2Params& p, int64_t rows, hipStream_t stre
   do {                                                                                \
     constexpr int DD = PA_TU_HEAD_DIM;                                                \
     if (K8_) {                                                                        \
-      constexpr bool KK = true;                                                       \
+      [[maybe_unused]] constexpr bool KK = true;                                      \
       if (F16_) { constexpr bool FF = true; PA_DISPATCH_G(G_, CALL); }                \
       else { constexpr bool FF = false; PA_DISPATCH_G(G_, CALL); }                    \
     } else {                                                                          \
-      constexpr bool KK = false;                                                      \
+      [[maybe_unused]] constexpr bool KK = false;                                     \
       if (F16_) { constexpr bool FF = true; PA_DISPATCH_G(G_, CALL); }                \
       else { constexpr bool FF = false; PA_DISPATCH_G(G_, CALL); }                    \
     }                                                                                 \
