@@ -635,10 +635,13 @@ int run(const pa_tensor* q, const pa_tensor* k, const pa_tensor* v, pa_tensor* o
     if (e != hipSuccess) return fail(PA_ERR_HIP, "rank launch: %s", hipGetErrorString(e));
   }
   if (plan.nwg > 0) {
+    // wide tiles of a plan whose every sequence is one tile read K/V that no
+    // other tile reads: the kernel variant with streaming loads
+    const int wide = plan.wide ? (plan.slots_direct ? 2 : 1) : 0;
     hipError_t e =
         plan.persistent ? pa::launch_decode(p, (int)s.D, (int)s.G, s.kv8, s.f16, plan.nwg, stream)
         : plan.eight    ? pa::launch_fwd8(p, (int)s.D, (int)s.G, s.f16, plan.nwg, stream)
-                        : pa::launch_fwd(p, (int)s.D, (int)s.G, plan.wide, s.kv8, s.f16, plan.nwg,
+                        : pa::launch_fwd(p, (int)s.D, (int)s.G, wide, s.kv8, s.f16, plan.nwg,
                                          stream);
     if (e != hipSuccess) return fail(PA_ERR_HIP, "forward launch: %s", hipGetErrorString(e));
   }

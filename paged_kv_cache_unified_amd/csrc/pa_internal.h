@@ -130,11 +130,13 @@ hipError_t noalloc_scratch(void** out);
 
 // Launchers (pa_kernels.hip, one object per head size d).  Return the
 // hipError_t of the launch.
-// wide = false launches the narrow-only specialization (every tile <= 16 rows).
+// wide = 0 launches the narrow-only specialization (every tile <= 16 rows), 1
+// the wide one, 2 the wide one with streaming K/V loads (no tile's K/V is read
+// by another tile: every sequence one tile; 16-bit caches, else as 1).
 // kv8: the caches hold fp8 E4M3 codes (else 16-bit elements); f16: q, out and
 // 16-bit caches are fp16 (else bf16).
 #define PA_DECLARE_HEAD_DIM(DV)                                                                  \
-  hipError_t launch_fwd_d##DV(const FwdParams& p, int group, bool wide, bool kv8, bool f16,     \
+  hipError_t launch_fwd_d##DV(const FwdParams& p, int group, int wide, bool kv8, bool f16,      \
                               int64_t num_workgroups, hipStream_t stream);                     \
   hipError_t launch_decode_d##DV(const FwdParams& p, int group, bool kv8, bool f16,             \
                                  int64_t num_workgroups, hipStream_t stream);                  \
@@ -158,7 +160,7 @@ PA_DECLARE_HEAD_DIM(256)
     default: break;                                     \
   }
 
-inline hipError_t launch_fwd(const FwdParams& p, int head_dim, int group, bool wide, bool kv8,
+inline hipError_t launch_fwd(const FwdParams& p, int head_dim, int group, int wide, bool kv8,
                              bool f16, int64_t num_workgroups, hipStream_t stream) {
   PA_BY_HEAD_DIM(head_dim, launch_fwd, p, group, wide, kv8, f16, num_workgroups, stream)
   return hipErrorInvalidValue;

@@ -147,11 +147,21 @@ __device__ __forceinline__ void* uniform_ptr(const void* ptr) {
   const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
   return reinterpret_cast<void*>(((uint64_t)hi << 32) | lo);
 }
+// Cache policy of K/V buffer loads that nothing else in the call reads again
+// (every byte of a decode batch's cache, and of any batch whose sequences are
+// one tile each): the non-temporal (nt) bit of the cache-policy operand, which
+// marks the data as streaming.  Measured on this GPU against ordinary loads:
+// the 256 x 1k-key decode batch 178 against 199 us, the 16 x 32k-128k decode
+// batch 796 against 886 us.  K/V that other query tiles of a sequence read
+// again keep ordinary loads.
+constexpr int kStreamLoad = 2;
+
 // 16-byte global -> LDS DMA: lane i's 16 bytes (at voffset of the buffer
 // resource) land at LDS byte address lds + 16 i.  Callers wait with
-// wait_dma() before the barrier that publishes the data.
+// wait_dma() before the barrier that publishes the data.  AUX: cache policy.
+template <int AUX = 0>
 __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rs, uint32_t voff, uint32_t lds) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (PA_LDS void*)(uintptr_t)lds, 16, voff, 0, 0, 0);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (PA_LDS void*)(uintptr_t)lds, 16, voff, 0, 0, AUX);
 }
 __device__ __forceinline__ void wait_dma() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 // Work-group barrier that orders LDS accesses only (this wave's LDS reads and
@@ -191,12 +201,12 @@ template <bool KV8>
 __device__ __forceinline__ typename Kv<KV8>::raw8 gload8(const unsigned char* ptr) {
   return *reinterpret_cast<const typename Kv<KV8>::raw8*>(ptr);
 }
-template <bool KV8>
+template <bool KV8, int AUX = 0>     // AUX: cache policy
 __device__ __forceinline__ typename Kv<KV8>::raw8 bload8(__amdgpu_buffer_rsrc_t r, int byte_off) {
   if constexpr (KV8)
-    return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, byte_off, 0, 0));
+    return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, byte_off, 0, AUX));
   else
-    return __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0);
+    return __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, AUX);
 }
 
 // Natural-log lse of a row from its log2-domain value (kept in the library's
@@ -857,7 +867,9 @@ __device__ __forceinline__ void wide_epilogue(const FwdParams& p, const Item& it
   }
 }
 
-template <int D, int G, bool KV8, bool F16>
+// STREAM: the tile's K/V stages are read by no other tile (16-bit caches:
+// streaming DMA loads).
+template <int D, int G, bool KV8, bool F16, bool STREAM>
 __device__ __forceinline__ void attend_wide(const FwdParams& p, const Item& it,
                                             unsigned char* smem) {
   using E = Elem<F16>;
@@ -978,8 +990,8 @@ __device__ __forceinline__ void attend_wide(const FwdParams& p, const Item& it,
         vraw[u] = bload8<true>(rv, ld_gv[u % NV]);
       } else {
         const uint32_t dst = lds0 + buf * SB + u * 4 * RPI * CPR * 16;
-        dma16(rk, ld_gk[u % NV], dst);
-        dma16(rv, ld_gv[u % NV], dst + TB);
+        dma16<STREAM ? kStreamLoad : 0>(rk, ld_gk[u % NV], dst);
+        dma16<STREAM ? kStreamLoad : 0>(rv, ld_gv[u % NV], dst + TB);
       }
     }
   };
@@ -1527,15 +1539,17 @@ void pa_fwd8_kernel(FwdParams p) {
   else attend_wide8<D, G, F16>(p, it, smem);
 }
 
-// WIDE = false: every tile of the batch is narrow (the plan guarantees it).
-// KV8: the caches hold fp8 E4M3 codes.  F16: q, out (and 16-bit caches) are
-// fp16, else bf16.  Two work-groups per CU, except wide tiles at d = 256,
-// whose registers (accumulators in AGPRs) allow one wave per SIMD.
-template <int D, int G, bool WIDE, bool KV8, bool F16>
+// WIDE = 0: every tile of the batch is narrow (the plan guarantees it); 1:
+// wide tiles; 2: wide tiles whose K/V no other tile reads (every sequence one
+// tile; 16-bit caches), loaded as streaming data.  KV8: the caches hold fp8
+// E4M3 codes.  F16: q, out (and 16-bit caches) are fp16, else bf16.  Two
+// work-groups per CU, except wide tiles at d = 256, whose registers
+// (accumulators in AGPRs) allow one wave per SIMD.
+template <int D, int G, int WIDE, bool KV8, bool F16>
 __global__ __launch_bounds__(kThreads)
-__attribute__((amdgpu_waves_per_eu(WIDE && D == 256 ? 1 : 2)))
+__attribute__((amdgpu_waves_per_eu(WIDE != 0 && D == 256 ? 1 : 2)))
 void pa_fwd_kernel(FwdParams p) {
-  constexpr bool HAS_WIDE = WIDE;
+  constexpr bool HAS_WIDE = WIDE != 0;
   constexpr int WSMEM = WideCfg<wide_layout_dim(HAS_WIDE ? D : 128)>::SMEM;
   constexpr int SMEM = HAS_WIDE && WSMEM > NarrowCfg<D>::SMEM ? WSMEM : NarrowCfg<D>::SMEM;
   __shared__ __attribute__((aligned(16))) unsigned char smem[SMEM];
@@ -1544,7 +1558,7 @@ void pa_fwd_kernel(FwdParams p) {
   if (it.rows <= p.narrow_rows) {
     attend_narrow<D, G, narrow_ring<D>(), KV8, F16>(p, it, smem);
   } else {
-    if constexpr (HAS_WIDE) attend_wide<D, G, KV8, F16>(p, it, smem);
+    if constexpr (HAS_WIDE) attend_wide<D, G, KV8, F16, WIDE == 2>(p, it, smem);
   }
 }
 
@@ -1855,6 +1869,12 @@ void pa_decode_kernel(FwdParams p) {
   // fetch gets a resource of zero records, so its loads return zeros without
   // touching memory while the wait counts stay the same on every path.
   constexpr int RING = Cfg::RING;
+  // Every cache byte is read once per call: streaming loads (measured: the
+  // 256 x 1k-key batch 178 against 199 us).  fp8 K is the exception: a wave
+  // reads each 128-byte key row with four 8-byte-per-lane loads, and with
+  // streaming loads the fp8 batch took 129 against 105 us; with only V
+  // streaming it takes 90.
+  constexpr int KAUX = KV8 ? 0 : kStreamLoad;
   raw8 kst[RING][KS];
   raw8 vst[RING][VPL];
   const int blk_extent = kBlockSize * slot_stride * ESZ;    // bytes of one block, all heads
@@ -1866,9 +1886,9 @@ void pa_decode_kernel(FwdParams p) {
     const __amdgpu_buffer_rsrc_t rv =
         __builtin_amdgcn_make_buffer_rsrc((void*)(p.v + boff), (short)0, nrec, 0x00020000);
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) kst[j][ks] = bload8<KV8>(rk, (koff + 32 * ks) * ESZ);
+    for (int ks = 0; ks < KS; ++ks) kst[j][ks] = bload8<KV8, KAUX>(rk, (koff + 32 * ks) * ESZ);
 #pragma unroll
-    for (int u = 0; u < VPL; ++u) vst[j][u] = bload8<KV8>(rv, voff[u] * ESZ);
+    for (int u = 0; u < VPL; ++u) vst[j][u] = bload8<KV8, kStreamLoad>(rv, voff[u] * ESZ);
   };
 
   // items m (cur), m+1 (nxt), m+2 (nx2): ids of cur and nxt live in LDS, ids of
@@ -2198,13 +2218,20 @@ __global__ __launch_bounds__(256) void pa_merge2_kernel(Merge2Params p) {
 }
 
 template <int D, int G, bool KV8, bool F16>
-hipError_t launch_fwd_t(const FwdParams& p, bool wide, int64_t nwg, hipStream_t stream) {
+hipError_t launch_fwd_t(const FwdParams& p, int wide, int64_t nwg, hipStream_t stream) {
+  if constexpr (!KV8) {
+    if (wide == 2) {
+      hipLaunchKernelGGL((pa_fwd_kernel<D, G, 2, KV8, F16>), dim3((unsigned)nwg),
+                         dim3(kThreads), 0, stream, p);
+      return hipGetLastError();
+    }
+  }
   if (wide) {
-    hipLaunchKernelGGL((pa_fwd_kernel<D, G, true, KV8, F16>), dim3((unsigned)nwg), dim3(kThreads),
+    hipLaunchKernelGGL((pa_fwd_kernel<D, G, 1, KV8, F16>), dim3((unsigned)nwg), dim3(kThreads),
                        0, stream, p);
     return hipGetLastError();
   }
-  hipLaunchKernelGGL((pa_fwd_kernel<D, G, false, KV8, F16>), dim3((unsigned)nwg), dim3(kThreads),
+  hipLaunchKernelGGL((pa_fwd_kernel<D, G, 0, KV8, F16>), dim3((unsigned)nwg), dim3(kThreads),
                        0, stream, p);
   return hipGetLastError();
 }
@@ -2308,7 +2335,7 @@ int PA_SFX(decode_blocks_per_cu_d)(int group, bool kv8, bool f16) {
   return 0;
 }
 
-hipError_t PA_SFX(launch_fwd_d)(const FwdParams& p, int group, bool wide, bool kv8, bool f16,
+hipError_t PA_SFX(launch_fwd_d)(const FwdParams& p, int group, int wide, bool kv8, bool f16,
                                int64_t nwg, hipStream_t stream) {
   PA_DISPATCH(group, kv8, f16, return (launch_fwd_t<DD, GG, KK, FF>(p, wide, nwg, stream)));
   return hipErrorInvalidValue;

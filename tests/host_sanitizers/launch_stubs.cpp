@@ -8,7 +8,7 @@
 namespace pa {
 
 #define PA_STUB_HEAD_DIM(DV)                                                                   \
-  hipError_t launch_fwd_d##DV(const FwdParams&, int, bool, bool, bool, int64_t, hipStream_t) { \
+  hipError_t launch_fwd_d##DV(const FwdParams&, int, int, bool, bool, int64_t, hipStream_t) {  \
     return hipErrorInvalidValue;                                                               \
   }                                                                                            \
   hipError_t launch_decode_d##DV(const FwdParams&, int, bool, bool, int64_t, hipStream_t) {    \
