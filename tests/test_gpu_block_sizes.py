@@ -31,6 +31,8 @@ CASES = {
     "mixed": ([300, 1, 40, 1, 129], [900, 77, 40, 1500, 200], 32, 4, 128, True, {}, "bf16"),
     "mixed_noncausal": ([64, 1, 17], [300, 100, 1000], 8, 8, 64, False, {}, "bf16"),
     "wide_splits": ([200, 33], [2500, 90], 32, 8, 128, True, dict(force_num_splits=3), "bf16"),
+    # every sequence one wide tile: streaming K/V loads
+    "one_tile_wide": ([5, 32, 17, 1, 32], [40, 3000, 17, 900, 32], 32, 8, 128, True, {}, "bf16"),
     # fp8 caches
     "decode_fp8": ([1] * 6, [40, 300, 1000, 65, 4000, 1], 32, 8, 128, True, {}, "fp8_e4m3fn"),
     "mixed_fp8": ([100, 1, 1], [700, 64, 2000], 32, 8, 128, True, {}, "fp8_e4m3fn"),

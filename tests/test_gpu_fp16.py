@@ -25,6 +25,7 @@ CASES = {
     "mixed": ([300, 1, 40, 1, 129], [900, 77, 40, 1500, 200], 32, 4, 128, True, {}, "f16"),
     "mixed_noncausal_d64": ([64, 1, 17], [300, 100, 1000], 8, 8, 64, False, {}, "f16"),
     "wide_splits": ([200, 33], [2500, 90], 32, 8, 128, True, dict(force_num_splits=3), "f16"),
+    "one_tile_wide": ([5, 32, 17, 1, 32], [40, 3000, 17, 900, 32], 32, 8, 128, False, {}, "f16"),
     "fp8_cache_decode": ([1] * 6, [40, 300, 1000, 65, 4000, 1], 32, 8, 128, True, {}, "fp8_e4m3fn"),
     "fp8_cache_mixed": ([100, 1, 1], [700, 64, 2000], 32, 8, 128, True, {}, "fp8_e4m3fn"),
 }

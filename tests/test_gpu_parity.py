@@ -293,6 +293,37 @@ def test_longest_first_ragged_units(splits):
     full_parity(b, out, f"longest-first splits={splits}")
 
 
+@pytest.mark.parametrize("causal,splits", [(True, 0), (False, 0), (True, 3)],
+                         ids=["causal", "noncausal", "causal_splits3"])
+def test_one_tile_wide_plans(causal, splits):
+    """Every sequence one wide tile (at most 32 tokens at G = 4): the kernel
+    variant whose K/V loads stream, since no other tile reads them.  Against
+    the oracle (out starts as NaN), and bit-exact under block permutation and
+    NaN poison of unowned slots."""
+    require_gpu()
+    q_lens = [5, 32, 17, 1, 32, 0, 9]
+    k_lens = [40, 3000, 17, 900, 32, 10, 1300]
+    if not causal:
+        k_lens[2] = 300
+    b = build_batch("one_tile", q_lens, k_lens, 32, 8, 128, causal, seed=131 + splits, device=DEV)
+    opts = None if splits == 0 else pa.options(force_num_splits=splits)
+    plan = pa.plan_describe(*b.args(torch.empty_like(b.q))[:9], opts=opts)
+    assert plan["slots_direct"] == 1 and plan["tile_rows"] == 128 and plan["persistent"] == 0
+    assert plan["longest_first"] == 1 and plan["unit_xcd"] == 1
+    say(f"one-tile wide causal={causal} splits={plan['num_splits']}")
+    b2 = repermute_pool(b, seed=132 + splits)
+    clean = build_batch("one_tile", q_lens, k_lens, 32, 8, 128, causal, seed=131 + splits,
+                        device=DEV, poison=False)
+    clean.k_cache = torch.where(torch.isnan(b.k_cache), torch.zeros_like(b.k_cache), b.k_cache)
+    clean.v_cache = torch.where(torch.isnan(b.v_cache), torch.zeros_like(b.v_cache), b.v_cache)
+    o1, o2, o3 = run_pa(b, opts=opts), run_pa(b2, opts=opts), run_pa(clean, opts=opts)
+    torch.cuda.synchronize()
+    assert torch.isfinite(o1.float()).all()
+    assert torch.equal(bits(o1), bits(o2))
+    assert torch.equal(bits(o1), bits(o3))
+    full_parity(b, o1, f"one-tile wide causal={causal} splits={splits}")
+
+
 def test_many_sequences_with_wide_tiles_keep_index_order():
     """More than 2048 sequences with a wide tile: index-ordered grid."""
     require_gpu()
