@@ -147,13 +147,14 @@ __device__ __forceinline__ void* uniform_ptr(const void* ptr) {
   const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
   return reinterpret_cast<void*>(((uint64_t)hi << 32) | lo);
 }
-// Cache policy of K/V buffer loads that nothing else in the call reads again
-// (every byte of a decode batch's cache, and of any batch whose sequences are
-// one tile each): the non-temporal (nt) bit of the cache-policy operand, which
-// marks the data as streaming.  Measured on this GPU against ordinary loads:
-// the 256 x 1k-key decode batch 178 against 199 us, the 16 x 32k-128k decode
-// batch 796 against 886 us.  K/V that other query tiles of a sequence read
-// again keep ordinary loads.
+// Cache policy of K/V loads that nothing else in the call reads again: the
+// non-temporal (nt) bit of the cache-policy operand, which marks the data as
+// streaming.  Used by the persistent decode kernel and by the wide tiles of
+// plans whose sequences are one tile each.  Measured on this GPU against
+// ordinary loads: the 256 x 1k-key decode batch 178 against 199 us, the 16 x
+// 32k-128k decode batch 796 against 886 us.  K/V that other query tiles of a
+// sequence read again keep ordinary loads, and so does the grid's narrow path
+// (streaming made the narrow-only grids slower).
 constexpr int kStreamLoad = 2;
 
 // 16-byte global -> LDS DMA: lane i's 16 bytes (at voffset of the buffer
