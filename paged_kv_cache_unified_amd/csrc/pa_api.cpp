@@ -622,7 +622,14 @@ int run(const pa_tensor* q, const pa_tensor* k, const pa_tensor* v, pa_tensor* o
   p.lpt_order = plan.lpt ? reinterpret_cast<int4*>(static_cast<char*>(ws) + plan.ws_lpt_offset)
                          : nullptr;
   p.causal = causal ? 1 : 0;
-  p.narrow_rows = (opt && opt->force_tile == 2) ? 0 : pa::kNarrowRows;
+  // Rows of at most 16 take the narrow path, except in longest-first wide
+  // plans over 16-bit caches at d = 64 and 128: there a decode row or short chunk
+  // takes a wide tile too, whose K/V stream (its sequence is one tile).  On the
+  // 248-decode-row + 8-chunk batch that measured 188.8-188.9 us back to back
+  // against 196.9-200.4 with narrow decode rows (same box).
+  const bool rows_wide =
+      plan.wide && !plan.eight && plan.lpt && !s.kv8 && (s.D == 64 || s.D == 128);
+  p.narrow_rows = ((opt && opt->force_tile == 2) || rows_wide) ? 0 : pa::kNarrowRows;
   // fp8 caches: k_scale folds into the score scale, v_scale into the output
   const double k_scale = s.kv8 && opt && opt->k_scale != 0.f ? opt->k_scale : 1.0;
   const double v_scale = s.kv8 && opt && opt->v_scale != 0.f ? opt->v_scale : 1.0;

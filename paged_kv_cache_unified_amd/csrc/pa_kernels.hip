@@ -1541,8 +1541,11 @@ void pa_fwd8_kernel(FwdParams p) {
 }
 
 // WIDE = 0: every tile of the batch is narrow (the plan guarantees it); 1:
-// wide tiles; 2: wide tiles whose K/V no other tile reads (every sequence one
-// tile; 16-bit caches), loaded as streaming data.  KV8: the caches hold fp8
+// wide tiles (16-bit caches at d = 64 and 128: those of one-tile sequences
+// stream their K/V; at d = 96 and 256 the second copy of the wide path in the
+// kernel measured 1.5% and 4% slower on prefill, so they do not); 2:
+// wide tiles whose K/V no other tile reads (every sequence one tile; 16-bit
+// caches), loaded as streaming data.  KV8: the caches hold fp8
 // E4M3 codes.  F16: q, out (and 16-bit caches) are fp16, else bf16.  Two
 // work-groups per CU, except wide tiles at d = 256, whose registers
 // (accumulators in AGPRs) allow one wave per SIMD.
@@ -1559,7 +1562,16 @@ void pa_fwd_kernel(FwdParams p) {
   if (it.rows <= p.narrow_rows) {
     attend_narrow<D, G, narrow_ring<D>(), KV8, F16>(p, it, smem);
   } else {
-    if constexpr (HAS_WIDE) attend_wide<D, G, KV8, F16, WIDE == 2>(p, it, smem);
+    if constexpr (HAS_WIDE) {
+      // a sequence of one tile: no other tile reads its K/V (decode rows and
+      // short chunks next to prefill tiles), so they stream
+      if constexpr (WIDE == 1 && !KV8 && (D == 64 || D == 128)) {
+        if (it.q_len <= p.tile_tokens) attend_wide<D, G, KV8, F16, true>(p, it, smem);
+        else attend_wide<D, G, KV8, F16, false>(p, it, smem);
+      } else {
+        attend_wide<D, G, KV8, F16, WIDE == 2>(p, it, smem);
+      }
+    }
   }
 }
 
