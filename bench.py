@@ -323,6 +323,10 @@ def main():
     ap.add_argument("--config-steps", type=int, default=20,
                     help="back-to-back calls timed per config workload")
     ap.add_argument("--config-warmup", type=int, default=5)
+    ap.add_argument("--config-warm-seconds", type=float, default=0.3,
+                    help="config workloads: keep warming up (untimed) at least this long; "
+                         "five calls right after a workload is generated measured up to 20%% "
+                         "slow (the GPU not yet at its steady state)")
     ap.add_argument("--config-cold", type=int, default=20,
                     help="cold-cache calls per config workload")
     ap.add_argument("--force-tile", type=int, default=0,
@@ -415,7 +419,8 @@ def main():
         for name in CONFIG_WORKLOADS:
             print(f"bench: config {name}", file=sys.stderr, flush=True)
             cb = make_workload(name, device=dev)
-            cm = measure(pa, cb, args, args.config_steps, args.config_warmup, args.config_cold)
+            cm = measure(pa, cb, args, args.config_steps, args.config_warmup, args.config_cold,
+                         args.config_warm_seconds)
             res["configs"][name] = {k: cm[k] for k in (
                 "us_per_launch_events", "us_per_launch_cold_p10_p50_p90", "us_per_batch",
                 "algorithmic_bytes_per_launch", "algorithmic_flops_per_launch", "roofline",
@@ -512,10 +517,12 @@ def measure_ceilings(pa, make_workload, args):
         print(json.dumps(o), flush=True)
 
 
-def measure(pa, b, args, steps, warmup, n_cold):
+def measure(pa, b, args, steps, warmup, n_cold, warm_seconds=0.0):
     """Times one workload: `steps` back-to-back calls (wall clock and a pair of
     HIP events on the launch stream), then `n_cold` calls each after a 1 GiB
-    read that evicts the Infinity Cache; returns the bench fields of it."""
+    read that evicts the Infinity Cache; returns the bench fields of it.
+    Untimed warm-up: `warmup` calls, continued until `warm_seconds` have
+    passed."""
     import torch
     dev = b.q.device
     out = torch.empty_like(b.q)
@@ -536,8 +543,13 @@ def measure(pa, b, args, steps, warmup, n_cold):
             pa.unified_attention(*call_args, opts=opts, workspace=ws)
 
     stream = torch.cuda.current_stream(dev)
-    for _ in range(warmup):
+    t_warm = time.perf_counter() + warm_seconds
+    n = 0
+    while n < warmup or time.perf_counter() < t_warm:
         call()
+        n += 1
+        if n % 50 == 0:
+            torch.cuda.synchronize()
     torch.cuda.synchronize()
 
     # timed region: exactly K steps back to back, bracketed by synchronisation
