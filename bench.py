@@ -1,8 +1,9 @@
 """Benchmark of unified paged attention on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                    [--no-cpu-baseline] [--cold N] [--no-configs] [--config-steps K]
-                    [--config-warmup W] [--config-cold N] [--force-tile T]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--warm-seconds S]
+                    [--workload NAME] [--no-cpu-baseline] [--cold N] [--no-configs]
+                    [--config-steps K] [--config-warmup W] [--config-warm-seconds S]
+                    [--config-cold N] [--force-tile T]
                     [--force-splits S] [--decode-grid G] [--cache-write]
                     [--summarize DIR] [--calibrate-copy]
 
@@ -101,7 +102,7 @@ def traffic_record(workload):
 
 
 PROF_COMMANDS = """cd /tmp && export TMPDIR=/tmp
-rocprofv3 --kernel-trace --stats -d $OUT/trace_{w} -o run -- python3 $REPO/bench.py --workload {w} --steps 20 --warmup 5 --no-cpu-baseline --no-configs --cold 0
+rocprofv3 --kernel-trace --stats -d $OUT/trace_{w} -o run -- python3 $REPO/bench.py --workload {w} --steps 20 --warmup 5 --warm-seconds 0.3 --no-cpu-baseline --no-configs --cold 0
 rocprofv3 --pmc FETCH_SIZE -d $OUT/pmc_FETCH_SIZE_{w} -o run -- python3 $REPO/bench.py --workload {w} --steps 3 --warmup 1 --no-cpu-baseline --no-configs --cold 0
 rocprofv3 --pmc WRITE_SIZE -d $OUT/pmc_WRITE_SIZE_{w} -o run -- python3 $REPO/bench.py --workload {w} --steps 3 --warmup 1 --no-cpu-baseline --no-configs --cold 0
 rocprofv3 --pmc MfmaUtil MfmaFlopsBF16 LdsBankConflict LdsUtil VALUBusy VmemLatency -d $OUT/pmc_MFMA_{w} -o run -- python3 $REPO/bench.py --workload {w} --steps 3 --warmup 1 --no-cpu-baseline --no-configs --cold 0
@@ -315,6 +316,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--warm-seconds", type=float, default=0.0,
+                    help="keep warming up (untimed) at least this long after the --warmup "
+                         "calls (0: exactly --warmup calls)")
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cold", type=int, default=100, help="extra cold-cache timed calls")
@@ -381,7 +385,7 @@ def main():
     if args.cache_write:
         bench_cache_write(pa, b, args, dev)
         return
-    m = measure(pa, b, args, args.steps, args.warmup, args.cold)
+    m = measure(pa, b, args, args.steps, args.warmup, args.cold, args.warm_seconds)
 
     res = {
         "metric": METRIC,
