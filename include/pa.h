@@ -202,7 +202,7 @@ int pa_unified_attention(const pa_tensor* q, const pa_tensor* k_cache,
 
 /*
  * pa_unified_attention_ex — as above with options and a caller workspace.
- * workspace may be NULL iff pa_workspace_size(...) returns 0 for the same
+ * workspace may be NULL iff pa_workspace_bytes(...) returns 0 for the same
  * arguments and options; it must be 256-byte aligned, device memory, at least
  * that many bytes, and not used by anything else until the work enqueued here
  * has finished.  opt may be NULL (defaults).
