@@ -968,29 +968,20 @@ __device__ __forceinline__ void attend_wide(const FwdParams& p, const Item& it,
   }
   const uint32_t lds0 = uniform((int)(uint32_t)(uintptr_t)smem) + wave * RPI * CPR * 16;
   raw8 kraw[KV8 ? CPT : 1], vraw[KV8 ? CPT : 1];
-  // wave-uniform copies: the per-block address and bound arithmetic is scalar.
-  // Record counts of a block: every key (blocks before n_full), the keys
-  // before kend (block n_full), none past it (no memory access: zeros).
-  const int key_bytes = uniform(p.num_kv_heads * D * ESZ);
-  const int n_full = uniform(kend > kbeg ? kend / kBlockSize - blk0 : 0);
-  const int rec_full = kBlockSize * key_bytes;
-  const int rec_tail = uniform((kend % kBlockSize) * key_bytes);
+  // wave-uniform copies: the per-block address and bound arithmetic is scalar
+  const int kend_u = uniform(kend), blk0_u = uniform(blk0);
   auto load_stage = [&](int st, int buf) {
-    // the stage's block offsets, read together (one LDS round trip)
-    int64_t bo[CPT];
 #pragma unroll
     for (int u = 0; u < CPT; ++u) {
       // block within the stage of this wave's rows: 2u + wave/2 (d = 64), u
       // (d = 128) or u/2 (d = 256)
       const int bi = (u * 4 * RPI + wave * RPI) / kBlockSize;
-      bo[u] = offs[st * (kStageKeys / kBlockSize) + bi];
-    }
-#pragma unroll
-    for (int u = 0; u < CPT; ++u) {
-      const int bi = (u * 4 * RPI + wave * RPI) / kBlockSize;
       const int jl = st * (kStageKeys / kBlockSize) + bi;
-      const int64_t boff = uniform64(bo[u]);
-      const int nrec = jl < n_full ? rec_full : (jl == n_full ? rec_tail : 0);
+      const int64_t boff = uniform64(offs[jl]);
+      // keys of the block inside the item (0 past its end: no memory access,
+      // the DMA writes zeros)
+      const int valid = min(max(kend_u - (blk0_u + jl) * kBlockSize, 0), kBlockSize);
+      const int nrec = uniform(valid * p.num_kv_heads * D * ESZ);
       const __amdgpu_buffer_rsrc_t rk =
           __builtin_amdgcn_make_buffer_rsrc(uniform_ptr(p.k + boff), (short)0, nrec, 0x00020000);
       const __amdgpu_buffer_rsrc_t rv =
