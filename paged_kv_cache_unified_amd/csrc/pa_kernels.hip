@@ -337,16 +337,25 @@ __device__ __forceinline__ bool fill_item(const FwdParams& p, int s, int tile, i
   return true;
 }
 
+// Inclusive prefix sum over the 64 lanes of a wave in six DPP moves: row
+// shifts by 1, 2, 4 and 8 lanes (zero from outside the 16-lane row) scan each
+// row, then lane 15 is broadcast into row 1 and 3 and lane 31 into rows 2 and
+// 3.  All vector ALU work, no LDS round trip per step.
+__device__ __forceinline__ int wave_incl_scan(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, false);   // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, false);   // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, false);   // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, false);   // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);   // row_bcast:15
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);   // row_bcast:31
+  return x;
+}
+
 // Exclusive prefix sum over the work-group (256 threads); *total receives the
 // sum.  scratch: 8 ints of LDS.  Contains barriers: call from every thread.
 __device__ __forceinline__ int block_exclusive_scan(int v, int* scratch, int* total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  int x = v;
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const int y = __shfl_up(x, d);
-    if (lane >= d) x += y;
-  }
+  const int x = wave_incl_scan(v);
   if (lane == 63) scratch[wave] = x;
   __syncthreads();
   int before = 0, all = 0;
@@ -1722,12 +1731,7 @@ void pa_decode_kernel(FwdParams p) {
   auto scan_seqs = [&](auto&& f, int* out) {
     int local = 0;
     for (int s = s0; s < s1; ++s) local += f(s);
-    int incl = local;
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-      const int y = __shfl_up(incl, d);
-      if (lane >= d) incl += y;
-    }
+    const int incl = wave_incl_scan(local);
     if (lane == 63) wsum[wave] = incl;
     __syncthreads();
     int base = 0;
@@ -1853,12 +1857,24 @@ void pa_decode_kernel(FwdParams p) {
   const int tr_half = (l16 & 1) * 8;
   unsigned char* vbuf0 = smem + wave * Cfg::RING * BLK_BYTES;
 
+  // Block ids of item d: lane l holds those of blocks l, l + 64, ... .  The
+  // table row is read through a buffer resource that ends at the item's last
+  // entry, and no lane branches around its load, so the loads of every item
+  // in flight go out together (one round trip, not one per load).  Lanes past
+  // the item's blocks hold ids that are never read (every use checks the
+  // block index against nb); their loads past the resource read 0 without a
+  // memory access.
   auto load_ids = [&](const DItem& d, int (&v)[IDL]) {
+    const int bsh = p.bshift;
+    const int entries = d.valid && d.nb > 0 ? ((d.blk0 + d.nb - 1) >> bsh) + 1 : 0;
+    const __amdgpu_buffer_rsrc_t rt = __builtin_amdgcn_make_buffer_rsrc(
+        uniform_ptr(p.bt + (int64_t)(d.valid ? d.s : 0) * p.bt_stride), (short)0,
+        uniform(entries * 4), 0x00020000);
 #pragma unroll
     for (int k = 0; k < IDL; ++k) {
-      v[k] = 0;
-      if (d.valid && lane + 64 * k < d.nb)
-        v[k] = sub_block_id(p.bt + (int64_t)d.s * p.bt_stride, d.blk0 + lane + 64 * k, p.bshift);
+      const int j = d.blk0 + lane + 64 * k;
+      const int e = __builtin_amdgcn_raw_buffer_load_b32(rt, (j >> bsh) * 4, 0, 0);
+      v[k] = (e << bsh) | (j & ((1 << bsh) - 1));
     }
   };
   auto store_ids = [&](int buf, const int (&v)[IDL]) {
@@ -1906,28 +1922,30 @@ void pa_decode_kernel(FwdParams p) {
 
   // items m (cur), m+1 (nxt), m+2 (nx2): ids of cur and nxt live in LDS, ids of
   // nx2 in VGPRs until cur finishes; Q of nxt is prefetched.
+  // Set-up: the block ids and Q of the current item, then its first ring
+  // loads, whose block ids come straight from registers; the next two items
+  // are described and their block ids (and the next Q) loaded after that.
   DItem cur = p.balanced ? describe(gw, gw / Hkv * chunk) : describe(0, 0);
-  DItem nxt = after(cur);
-  int cb = 0;
-  {
-    int v[IDL];
-    load_ids(cur, v);
-    store_ids(0, v);
-    load_ids(nxt, v);
-    store_ids(1, v);
-  }
-  DItem nx2 = after(nxt);
-  int ids_v2[IDL];
-  load_ids(nx2, ids_v2);
+  int ids_v0[IDL], ids_v1[IDL], ids_v2[IDL];
+  load_ids(cur, ids_v0);
   // Q of the next item is loaded one item ahead (d = 256: at the switch, for
   // registers)
   constexpr bool QPRE = D <= 128;
   u32x4 qB[KS], qB_n[KS];
   load_qb(cur, qB);
-  if constexpr (QPRE) load_qb(nxt, qB_n);
+  int cb = 0;
   // the first RING blocks of the first item (idle slots load nothing)
 #pragma unroll
-  for (int j = 0; j < RING; ++j) issue(cur.kvh, cur.nb > j ? uniform(idsw[j]) : 0, cur.nb > j, j);
+  for (int j = 0; j < RING; ++j)
+    issue(cur.kvh, cur.nb > j ? __builtin_amdgcn_readlane(ids_v0[0], j) : 0, cur.nb > j, j);
+  // the next two items are described while those blocks are in flight
+  DItem nxt = after(cur);
+  load_ids(nxt, ids_v1);
+  DItem nx2 = after(nxt);
+  load_ids(nx2, ids_v2);
+  if constexpr (QPRE) load_qb(nxt, qB_n);
+  store_ids(0, ids_v0);
+  store_ids(1, ids_v1);
 
   while (true) {
     const int* ids_c = idsw + cb * kMaxItemBlocks;
