@@ -1646,6 +1646,20 @@ struct DItem {
                          // fixed parts: the wave's next item ordinal
 };
 
+// Largest s in [0, S) with pref[s] <= key, for a non-decreasing table with
+// pref[0] = 0 <= key (key wave-uniform, S <= 2048, the table holding 2049
+// entries): two 64-lane ballots, over every 32nd entry and then over the 32
+// entries of the group found, instead of a chain of dependent LDS reads.
+__device__ __forceinline__ int seq_of(const int* pref, int S, int key) {
+  const int lane = threadIdx.x & 63;
+  const int i1 = lane * 32;                          // <= 2016
+  const bool le1 = i1 < S && pref[i1] <= key;
+  const int g = uniform(__popcll(__ballot(le1)) - 1);
+  const int i2 = g * 32 + (lane & 31);               // <= 2047
+  const bool le2 = lane < 32 && i2 < S && pref[i2] <= key;
+  return uniform(g * 32 + __popcll(__ballot(le2)) - 1);
+}
+
 // Item -> (sequence, part, kv-head) from the LDS tables only.
 template <int G>
 __device__ __forceinline__ DItem describe_item(const FwdParams& p, const int* pref,
@@ -1656,11 +1670,7 @@ __device__ __forceinline__ DItem describe_item(const FwdParams& p, const int* pr
   if (!d.valid) return d;
   const int unit = item / p.num_kv_heads;
   d.kvh = item - unit * p.num_kv_heads;
-  int lo = 0, hi = p.num_seqs - 1;     // largest s with pref[s] <= unit
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (uniform(pref[mid]) <= unit) lo = mid; else hi = mid - 1;
-  }
+  const int lo = seq_of(pref, p.num_seqs, unit);   // largest s with pref[s] <= unit
   d.s = lo;
   d.sigma = unit - uniform(pref[lo]);
   d.units = uniform(pref[lo + 1]) - uniform(pref[lo]);
@@ -1705,49 +1715,73 @@ void pa_decode_kernel(FwdParams p) {
   int* wsum = reinterpret_cast<int*>(smem + Cfg::SCAN_OFFSET);
   int* idsw = reinterpret_cast<int*>(smem + Cfg::IDS_OFFSET) + wave * 2 * kMaxItemBlocks;
 
-  // ---- stage per-sequence metadata; prefix sums of per-sequence units ----
+  // ---- per-sequence metadata and prefix sums of per-sequence units ----
+  // Thread t owns sequences s0 .. s1 - 1 and keeps their query lengths,
+  // contexts, units and first positions in registers, so the scans read no
+  // LDS but the per-wave totals; the tables go to LDS for the item lookups.
   const int S = p.num_seqs;
   const int Hkv = p.num_kv_heads;
+  constexpr int CM = (kMaxDecodeSeqs + kThreads - 1) / kThreads;   // sequences per thread, at most
   const int C = (S + kThreads - 1) / kThreads;
   const int s0 = min(S, tid * C), s1 = min(S, s0 + C);
-  for (int s = s0; s < s1; ++s) {
-    q0t[s] = p.cu_q[s];
-    lent[s] = context_len(p, s);
-  }
-  if (tid == 0) q0t[S] = p.cu_q[S];
   const int workers = (int)gridDim.x * 4;
   const int target = p.split_keys;                   // fixed parts: keys per part
-  __syncthreads();
-  // units of a sequence per kv-head: its parts (fixed), or its blocks in the
-  // stream (even split; a row with no key still takes one position, so its
-  // zero output gets written)
-  auto seq_units = [&](int s) -> int {
-    const int ql = q0t[s + 1] - q0t[s];
-    if (p.balanced) return ql > 0 ? max((lent[s] + kBlockSize - 1) / kBlockSize, 1) : 0;
-    return seq_parts(p, ql, lent[s], target);
-  };
-  // exclusive prefix over the sequences of f(s) into out[0..S] (threads own
-  // contiguous runs of sequences); contains barriers
-  auto scan_seqs = [&](auto&& f, int* out) {
-    int local = 0;
-    for (int s = s0; s < s1; ++s) local += f(s);
-    const int incl = wave_incl_scan(local);
-    if (lane == 63) wsum[wave] = incl;
-    __syncthreads();
-    int base = 0;
-    for (int w = 0; w < wave; ++w) base += wsum[w];
-    int run = base + incl - local;
-    for (int s = s0; s < s1; ++s) {
-      out[s] = run;
-      run += f(s);
+  int ur[CM], xr[CM];                                // units and first position of s0 + c
+#pragma unroll
+  for (int c = 0; c < CM; ++c) {
+    ur[c] = 0;
+    if (c >= C) continue;                            // (uniform: batches of <= 256 take one)
+    const int s = s0 + c;
+    const int sc = min(s, S - 1);                    // a valid index (S >= 1: the host launches
+                                                     // nothing for an empty batch), so the
+                                                     // loads need no branch
+    const int q0 = p.cu_q[sc];
+    const int ql = p.cu_q[sc + 1] - q0;
+    const int L = context_len(p, sc);
+    const bool own = c < C && s < s1;
+    if (own) {
+      q0t[s] = q0;
+      lent[s] = L;
     }
-    if (tid == kThreads - 1) out[S] = base + incl;
+    // units of a sequence per kv-head: its parts (fixed), or its blocks in
+    // the stream (even split; a row with no key still takes one position, so
+    // its zero output gets written)
+    const int u = p.balanced ? (ql > 0 ? max((L + kBlockSize - 1) / kBlockSize, 1) : 0)
+                             : seq_parts(p, ql, L, target);
+    if (own) ur[c] = u;
+  }
+  if (tid == 0) q0t[S] = p.cu_q[S];
+  // exclusive prefix over the sequences of v[] (this thread's run) into
+  // out[0..S], per-wave totals in wsum[slot0 .. slot0 + 3]; one barrier.
+  // Returns the total; first[c] receives the prefix of sequence s0 + c.
+  auto scan_seqs = [&](const int (&v)[CM], int (&first)[CM], int* out, int slot0) -> int {
+    int local = 0;
+#pragma unroll
+    for (int c = 0; c < CM; ++c) local += v[c];
+    const int incl = wave_incl_scan(local);
+    if (lane == 63) wsum[slot0 + wave] = incl;
     __syncthreads();
+    int base = 0, total = 0;
+#pragma unroll
+    for (int w = 0; w < kThreads / 64; ++w) {
+      const int t = wsum[slot0 + w];
+      base += w < wave ? t : 0;
+      total += t;
+    }
+    int run = base + incl - local;
+#pragma unroll
+    for (int c = 0; c < CM; ++c) {
+      first[c] = run;
+      if (c < C && s0 + c < s1) out[s0 + c] = run;
+      run += v[c];
+    }
+    if (tid == 0) out[S] = total;
+    return uniform(total);
   };
-  scan_seqs(seq_units, pref);
+  const int n_seq_units = scan_seqs(ur, xr, pref, 0);
   // fixed parts: items, kv-heads included; even split: the blocks of the
   // per-sequence stream (one kv-head's worth)
-  const int n_units = uniform(pref[S]) * (p.balanced ? 1 : Hkv);
+  const int n_units = n_seq_units * (p.balanced ? 1 : Hkv);
   // Even split: the stream is cut into n_chunks chunks of `chunk` blocks, and
   // every (chunk, kv-head) pair is one wave's work: kpw pairs per wave, each at
   // most kMaxItemBlocks blocks (one item's block-id table) and at least
@@ -1762,11 +1796,15 @@ void pa_decode_kernel(FwdParams p) {
     // partial slots: a sequence gets one per chunk it touches (its parts), so
     // the batch needs at most (chunks + sequences) slots, whatever its token
     // count; slot(s, part) = slots[s] + part
-    scan_seqs([&](int s) -> int {
-      const int x0 = pref[s], x1 = pref[s + 1];
-      return x1 > x0 ? (x1 - 1) / chunk - x0 / chunk + 1 : 0;
-    }, slots);
+    int vr[CM], unused[CM];
+#pragma unroll
+    for (int c = 0; c < CM; ++c) {
+      const int x0 = xr[c], x1 = xr[c] + ur[c];
+      vr[c] = x1 > x0 ? (x1 - 1) / chunk - x0 / chunk + 1 : 0;
+    }
+    scan_seqs(vr, unused, slots, 4);
   }
+  __syncthreads();                                   // the tables, for every wave's lookups
   // Fixed parts: items are dealt to XCDs in contiguous ranges (work-group w
   // runs on XCD w % 8); the waves of one XCD stride through its range, and
   // consecutive items (the kv-heads of one sequence, which read the same cache
@@ -1801,11 +1839,7 @@ void pa_decode_kernel(FwdParams p) {
     if (!d.valid) return d;
     const int c = q / Hkv;
     const int xe = min((c + 1) * chunk, n_units);
-    int lo = 0, hi = S - 1;                            // largest s with its first block <= pos
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (uniform(pref[mid]) <= pos) lo = mid; else hi = mid - 1;
-    }
+    const int lo = seq_of(pref, S, pos);               // largest s with its first block <= pos
     const int L = uniform(lent[lo]);
     const int nbe = max((L + kBlockSize - 1) / kBlockSize, 1);
     const int x0 = uniform(pref[lo]);                  // the sequence's first position

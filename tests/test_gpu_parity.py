@@ -272,6 +272,32 @@ def test_many_sequences_fall_back_to_grid():
     full_parity(b, out, "many sequences")
 
 
+@pytest.mark.parametrize("S,kind,splits", [(700, "ragged", 0), (1500, "uniform", 0),
+                                           (1500, "uniform", 3), (2048, "ragged", 0)],
+                         ids=["s700_even", "s1500_fixed", "s1500_fixed_split3", "s2048_fixed"])
+def test_persistent_decode_many_sequences(S, kind, splits):
+    """The persistent decode kernel up to its 2048 sequences: each thread of a
+    work-group owns up to 8 sequences of the per-sequence tables (lengths,
+    prefix sums of units and partial slots) that every item lookup searches;
+    empty sequences (q = 0) among them."""
+    require_gpu()
+    rng = np.random.default_rng(S + splits)
+    if kind == "ragged":
+        k = np.clip(np.round(np.exp(rng.normal(np.log(120.0), 1.0, size=S))), 1, 3000).astype(int)
+    else:
+        k = rng.integers(150, 200, size=S)
+    q = np.ones(S, int)
+    q[rng.random(S) < 0.02] = 0
+    b = build_batch("many_decode", q, k, 8, 2, 64, True, seed=S + splits, device=DEV)
+    opts = pa.options(force_num_splits=splits) if splits else None
+    plan = pa.plan_describe(*b.args(torch.empty_like(b.q))[:9], opts=opts)
+    assert plan["persistent"] == 1 and plan["balanced"] == (1 if kind == "ragged" and S < 2048 else 0)
+    say(f"persistent decode S={S} {kind} splits={plan['num_splits']} balanced={plan['balanced']}")
+    out = run_pa(b, opts=opts)
+    torch.cuda.synchronize()
+    full_parity(b, out, f"persistent decode S={S} {kind}")
+
+
 @pytest.mark.parametrize("splits", [0, 3])
 def test_longest_first_ragged_units(splits):
     """Wide plans rank (sequence, tile, split) units longest-first on the device:
